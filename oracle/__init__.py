@@ -1,0 +1,46 @@
+"""Plain CPU oracle for the DFlash drafting hot path (test infrastructure).
+
+This package is the independent reference that the GPU path is checked
+against.  It is slow on purpose: numpy only, float64 arithmetic, one step
+per line of the method, no blocking or fusion.  It shares no code with the
+HIP library and imports nothing from it.
+
+Only the test suite, the package smoke check and the CPU-baseline leg of the
+benchmark may import it.  The product path never routes through it.
+
+Parity status per function (what pins it, see ``tests/test_oracle_*.py``):
+
+* ``to_bf16``          pinned: equals torch's CPU bfloat16 conversion.
+* ``feature_layers``   pinned: the layer rule's arithmetic for 32/36 layers.
+* ``rmsnorm``          pinned: torch ``F.rms_norm`` in float64.
+* ``rope``             pinned: complex multiplication by exp(i*theta*p);
+                       relative-position property.
+* ``attention``        pinned: torch ``scaled_dot_product_attention``
+                       (float64, explicit mask, repeated KV heads).
+* ``swiglu``           pinned: torch ``F.silu``.
+* ``select``           pinned: ``np.argsort(kind="stable")`` / brute force.
+* ``verify_accept``    pinned: the 8-drafted / 6-matched example; brute force
+                       over all tiny (d, G).
+* ``per_token_cost``   pinned: (3+20)/6 and (3+20)/2 from the cost example.
+* ``DraftOracle``      composition of the above; the whole draft forward's
+                       values are "parity unpinned" by the pages (they print
+                       no activation or token for any weights) and are pinned
+                       through the decomposition and invariants: batch /
+                       window / conv-identity / GQA-to-MHA reductions.
+* ``spec_generate``    pinned: equals ``greedy_ar`` exactly (lossless).
+"""
+from .dflash_oracle import (  # noqa: F401
+    DraftOracle,
+    RequestState,
+    attention,
+    feature_layers,
+    per_token_cost,
+    rmsnorm,
+    rope,
+    select,
+    swiglu,
+    to_bf16,
+    to_f32,
+    verify_accept,
+)
+from .tiny_target import OracleDrafter, TinyTarget, greedy_ar, spec_generate  # noqa: F401
