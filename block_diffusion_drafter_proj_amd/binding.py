@@ -1,0 +1,182 @@
+"""ctypes binding of libdflash.so, one Python function per C entry point.
+
+The functions keep the C names and only marshal arguments: device memory is
+passed as raw pointers (``tensor.data_ptr()``), streams as the HIP stream
+handle (``torch.cuda.current_stream().cuda_stream``).  Every nonzero status
+raises ``DFlashError`` carrying the status and ``dflash_last_error()``.
+
+The library must have been built (``python -m
+block_diffusion_drafter_proj_amd.build``); importing this module without it
+raises ImportError: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdflash.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "dflash.h")
+
+MAX_LAYERS = 16
+MAX_FEAT = 8
+MAX_BATCH = 256
+PAGE = 16
+TOPK = 16
+
+BF16 = 0
+F32 = 1
+
+OK, E_INVALID, E_CAPACITY, E_UNSUPPORTED, E_HIP, E_DEVICE = range(6)
+STATUS_NAMES = {0: "OK", 1: "E_INVALID", 2: "E_CAPACITY", 3: "E_UNSUPPORTED", 4: "E_HIP", 5: "E_DEVICE"}
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"dflash {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class DFlashConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "vocab", "n_layers",
+        "block_size", "n_feat", "dtype", "mask_token_id", "page_size", "window", "conv2",
+        "topk", "max_batch", "max_pages", "max_pages_per_req", "max_position",
+        "max_inject_rows")] + [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+
+
+class DFlashLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "wqkv", "wo", "wgateup", "wdown", "attn_norm", "mlp_norm", "conv")]
+
+
+class DFlashWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("embed", "lm_head", "fc", "fc_norm", "final_norm")] + [
+        ("layers", DFlashLayerWeights * MAX_LAYERS)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m block_diffusion_drafter_proj_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, vp, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+        pi32 = ctypes.POINTER(ctypes.c_int32)
+        sigs = {
+            "dflash_abi_version": (i32, []),
+            "dflash_last_error": (ctypes.c_char_p, []),
+            "dflash_validate_config": (i32, [ctypes.POINTER(DFlashConfig)]),
+            "dflash_feature_layers": (i32, [i32, i32, pi32]),
+            "dflash_workspace_bytes": (sz, [ctypes.POINTER(DFlashConfig)]),
+            "dflash_kv_pool_bytes": (sz, [ctypes.POINTER(DFlashConfig)]),
+            "dflash_create": (i32, [ctypes.POINTER(DFlashConfig), ctypes.POINTER(DFlashWeights),
+                                    vp, vp, ctypes.POINTER(vp)]),
+            "dflash_destroy": (None, [vp]),
+            "dflash_bind_request": (i32, [vp, i32, pi32, i32, i32]),
+            "dflash_context_length": (i32, [vp, i32]),
+            "dflash_inject_context": (i32, [vp, vp, i32, pi32, pi32, ctypes.POINTER(vp), vp]),
+            "dflash_draft_block": (i32, [vp, vp, i32, pi32, vp, vp, vp, vp, vp, vp]),
+            "dflash_verify_accept": (i32, [vp, vp, i32, vp, vp, vp, vp, vp]),
+            "dflash_check": (i32, [vp, vp]),
+        }
+        for name, (res, args) in sigs.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _i32s(vals):
+    vals = [int(v) for v in vals]
+    return (ctypes.c_int32 * max(1, len(vals)))(*vals)
+
+
+def _check(status: int):
+    if status != OK:
+        raise DFlashError(status, dflash_last_error())
+
+
+def dflash_abi_version() -> int:
+    return lib().dflash_abi_version()
+
+
+def dflash_last_error() -> str:
+    return lib().dflash_last_error().decode()
+
+
+def dflash_validate_config(cfg: DFlashConfig) -> None:
+    _check(lib().dflash_validate_config(ctypes.byref(cfg)))
+
+
+def dflash_feature_layers(n_target_layers: int, k: int) -> list[int]:
+    out = (ctypes.c_int32 * max(1, k))()
+    _check(lib().dflash_feature_layers(n_target_layers, k, out))
+    return list(out[:k])
+
+
+def dflash_workspace_bytes(cfg: DFlashConfig) -> int:
+    return int(lib().dflash_workspace_bytes(ctypes.byref(cfg)))
+
+
+def dflash_kv_pool_bytes(cfg: DFlashConfig) -> int:
+    return int(lib().dflash_kv_pool_bytes(ctypes.byref(cfg)))
+
+
+def dflash_create(cfg: DFlashConfig, w: DFlashWeights, kv_pool: int, workspace: int) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().dflash_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(kv_pool),
+                               ctypes.c_void_p(workspace), ctypes.byref(h)))
+    return h.value
+
+
+def dflash_destroy(h: int) -> None:
+    lib().dflash_destroy(ctypes.c_void_p(h))
+
+
+def dflash_bind_request(h: int, slot: int, page_ids, start_pos: int = 0) -> None:
+    _check(lib().dflash_bind_request(ctypes.c_void_p(h), slot, _i32s(page_ids), len(page_ids), start_pos))
+
+
+def dflash_context_length(h: int, slot: int) -> int:
+    return lib().dflash_context_length(ctypes.c_void_p(h), slot)
+
+
+def dflash_inject_context(h: int, stream: int, slots, n_new, hidden_ptrs, debug_f: int = 0) -> None:
+    arr = (ctypes.c_void_p * MAX_FEAT)(*[ctypes.c_void_p(p) for p in hidden_ptrs])
+    _check(lib().dflash_inject_context(ctypes.c_void_p(h), ctypes.c_void_p(stream), len(slots),
+                                       _i32s(slots), _i32s(n_new), arr, ctypes.c_void_p(debug_f or None)))
+
+
+def dflash_draft_block(h: int, stream: int, slots, last_token: int, draft: int, topk_ids: int = 0,
+                       topk_logits: int = 0, debug_logits: int = 0, debug_hidden: int = 0) -> None:
+    vp = ctypes.c_void_p
+    _check(lib().dflash_draft_block(vp(h), vp(stream), len(slots), _i32s(slots), vp(last_token or None),
+                                    vp(draft or None), vp(topk_ids or None), vp(topk_logits or None),
+                                    vp(debug_logits or None), vp(debug_hidden or None)))
+
+
+def dflash_verify_accept(h: int, stream: int, n_req: int, draft: int, target_greedy: int,
+                         accept_len: int, committed: int, last_token: int) -> None:
+    vp = ctypes.c_void_p
+    _check(lib().dflash_verify_accept(vp(h), vp(stream), n_req, vp(draft or None),
+                                      vp(target_greedy or None), vp(accept_len or None),
+                                      vp(committed or None), vp(last_token or None)))
+
+
+def dflash_check(h: int, stream: int) -> None:
+    _check(lib().dflash_check(ctypes.c_void_p(h), ctypes.c_void_p(stream)))
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/dflash.h declares."""
+    import re
+
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", txt)))

@@ -1,0 +1,381 @@
+// Draft attention over the injected context KV and the block's own KV.
+//
+// Each of the B block rows attends to every visible context position of its
+// request and to all B block rows, itself included: attention inside the
+// block is bidirectional ([guide] section 3.1, the block is drafted in one
+// forward) and the context K/V are those written from the target's features
+// ([guide] section 3.2).  Query head j reads KV head j / (Hq / Hkv) (GQA);
+// scores are scaled by 1/sqrt(dh).
+//
+// Layout: a KV page holds 16 positions of one layer as [K | V] x Hkv heads;
+// K is stored [16 positions][dh] and V transposed, [dh][16 positions], so
+// that both MFMA products read their reduction dimension contiguously.
+//
+// k_qkv_post   RoPE on the block's q and k at positions n .. n+B-1, rounding
+//              to the storage dtype; q to [req][Hq][16][dh], block k/v to one
+//              extra page per request (rows >= B zero).
+// k_attn       split-K over pages (flash-decoding): a workgroup takes one
+//              request, one KV head and a run of pages; each wave owns one
+//              query head of the group and its 16 query rows.  S^T = K Q^T and
+//              O^T = V^T P^T run on 16x16 MFMA tiles, 32 keys per step, with
+//              an online softmax per query row (fp32; P enters the bf16 MFMA
+//              as an exact hi + lo pair).  Invalid keys (past ctx_len,
+//              before the window, block rows >= B) get probability 0 and their
+//              V is zeroed, so stale or poisoned page contents never leak in.
+// k_combine    merges the per-split (max, sum, O) into the attention output.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dflash {
+
+namespace {
+
+template <typename T> constexpr bool kSplitP = false;
+template <> constexpr bool kSplitP<bf16> = true;
+
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16> { typedef bf16x4 type; };
+template <> struct Vec4<float> { typedef f32x4 type; };
+
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void k_qkv_post(QkvPostParams p, SlotArgs sl) {
+  const int r = blockIdx.x;
+  const int hh = blockIdx.y;
+  const int t = threadIdx.x;
+  const int ld = (p.Hq + 2 * p.Hkv) * DH;
+  const int n = p.state[sl.slots[r]].ctx_len + 1;
+  const float* src = p.qkv + (long long)r * p.B * ld + hh * DH;
+  constexpr int H2 = DH / 2;
+  const long long page_elems = 2LL * p.Hkv * 16 * DH;
+  if (hh < p.Hq + p.Hkv) {
+    T* dst;
+    if (hh < p.Hq)
+      dst = reinterpret_cast<T*>(p.qb) + (long long)(r * p.Hq + hh) * 16 * DH;
+    else
+      dst = reinterpret_cast<T*>(p.blk) + r * page_elems + (long long)(hh - p.Hq) * 16 * DH;
+    for (int e = t; e < 16 * H2; e += 256) {
+      const int i = e / H2;
+      const int j = e - i * H2;
+      float y1 = 0.f, y2 = 0.f;
+      if (i < p.B) {
+        const float x1 = src[(long long)i * ld + j];
+        const float x2 = src[(long long)i * ld + j + H2];
+        const long long ti = (long long)(n + i) * H2 + j;
+        const float c = p.cos_t[ti], s = p.sin_t[ti];
+        y1 = x1 * c - x2 * s;
+        y2 = x2 * c + x1 * s;
+      }
+      dst[i * DH + j] = from_f<T>(y1);
+      dst[i * DH + j + H2] = from_f<T>(y2);
+    }
+  } else {
+    const int g = hh - p.Hq - p.Hkv;
+    T* dst = reinterpret_cast<T*>(p.blk) + r * page_elems + (long long)(p.Hkv + g) * 16 * DH;
+    for (int e = t; e < 16 * DH; e += 256) {
+      const int i = e & 15;
+      const int d = e >> 4;
+      const float x = i < p.B ? src[(long long)i * ld + d] : 0.f;
+      dst[d * 16 + i] = from_f<T>(x);
+    }
+  }
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(1024) void k_attn(AttnParams p, SlotArgs sl) {
+  typedef typename Frag8<T>::type Frag;
+  typedef typename Vec4<T>::type V4;
+  constexpr int NJ = DH / 32;
+  constexpr int ND = DH / 16;
+  const float NEG = -INFINITY;
+
+  const int s = blockIdx.x;
+  const int gkv = blockIdx.y;
+  const int r = blockIdx.z;
+  const int G = p.Hq / p.Hkv;
+  const int wave = threadIdx.x >> 6;
+  const int h = gkv * G + wave;
+  const int lane = lane_id();
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int slot = sl.slots[r];
+  const SlotState st = p.state[slot];
+  const int hi = st.ctx_len;
+  int lo = st.kv_begin;
+  if (p.window > 0) lo = max(lo, hi - p.window);
+  const int lp0 = lo / 16;
+  const int n_lp = hi > lo ? (hi - 1) / 16 - lp0 + 1 : 0;
+  const int n_units = n_lp + 1;
+  const int u_begin = s * p.pps;
+  const int u_end = min(u_begin + p.pps, n_units);
+  const long long page_elems = 2LL * p.Hkv * 16 * DH;
+  const T* pool = reinterpret_cast<const T*>(p.pool);
+  const T* blk = reinterpret_cast<const T*>(p.blk);
+
+  Frag qf[NJ];
+  {
+    const T* qrow = reinterpret_cast<const T*>(p.qb) + ((long long)(r * p.Hq + h) * 16 + l16) * DH;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) qf[j] = load8<T>(qrow + 32 * j + 8 * g4);
+  }
+
+  float m_run = NEG, l_run = 0.f;
+  f32x4 o[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int u = u_begin; u < u_end; u += 2) {
+    const T* base[2];
+    bool valid[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int uu = u + t;
+      base[t] = nullptr;
+      int pos0 = 0;
+      bool is_blk = false;
+      if (uu < u_end) {
+        if (uu < n_lp) {
+          const int lp = lp0 + uu;
+          const int idx = p.window > 0 ? lp % st.n_pages : lp;
+          const int page = p.page_table[(long long)slot * p.pt_stride + idx];
+          if (page >= 0 && page < p.max_pages) {
+            base[t] = pool + (long long)page * page_elems;
+          } else if (lane == 0 && wave == 0) {
+            atomicOr(p.err, 2u);
+          }
+          pos0 = lp * 16;
+        } else {
+          base[t] = blk + (long long)r * page_elems;
+          is_blk = true;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 4 * g4 + i;
+        valid[t][i] = base[t] != nullptr &&
+                      (is_blk ? key < p.B : (pos0 + key >= lo && pos0 + key < hi));
+      }
+    }
+
+    float sv[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (base[t]) {
+        const T* kb = base[t] + (long long)gkv * 16 * DH + l16 * DH;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) sacc = mfma_step(load8<T>(kb + 32 * j + 8 * g4), qf[j], sacc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[4 * t + i] = valid[t][i] ? sacc[i] * p.scale : NEG;
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = (m_run == NEG) ? 0.f : expf(m_run - m_new);
+    float pe[8];
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pe[e] = (sv[e] == NEG) ? 0.f : expf(sv[e] - m_new);
+      ls += pe[e];
+    }
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    l_run = l_run * corr + ls;
+    m_run = m_new;
+    // P enters the PV product at fp32 accuracy: for bf16 storage it is split
+    // into hi + lo bf16 parts (two MFMAs); rounding P itself to bf16 would add
+    // 2^-9 relative noise per key, which the near-cancelling average over many
+    // keys amplifies.
+    Frag pf, pf_lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pf[e] = from_f<T>(pe[e]);
+      pf_lo[e] = from_f<T>(pe[e] - to_f(pf[e]));
+    }
+
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      o[dt] = o[dt] * corr;
+      Frag vf;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        V4 v4;
+        if (base[t]) {
+          const T* vb = base[t] + (long long)(p.Hkv + gkv) * 16 * DH + (16 * dt + l16) * 16 + 4 * g4;
+          v4 = *reinterpret_cast<const V4*>(vb);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v4[i] = (T)0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vf[4 * t + i] = valid[t][i] ? v4[i] : (T)0.0f;
+      }
+      o[dt] = mfma_step(vf, pf, o[dt]);
+      if (kSplitP<T>) o[dt] = mfma_step(vf, pf_lo, o[dt]);
+    }
+  }
+
+  const long long pb = ((long long)(r * p.Hq + h) * p.n_splits + s) * 16 + l16;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p.part_o[pb * DH + 16 * dt + 4 * g4 + i] = o[dt][i];
+  if (g4 == 0) {
+    p.part_ml[pb * 2 + 0] = m_run;
+    p.part_ml[pb * 2 + 1] = l_run;
+  }
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void k_combine(CombineParams p) {
+  const int h = blockIdx.x;
+  const int r = blockIdx.y;
+  const int t = threadIdx.x;
+  const int q = t >> 4;
+  const int dd = t & 15;
+  if (q >= p.B) return;
+  constexpr int NC = DH / 16;
+  const long long base = (long long)(r * p.Hq + h) * p.n_splits * 16;
+  float mx = -INFINITY;
+  for (int s = 0; s < p.n_splits; ++s) mx = fmaxf(mx, p.part_ml[(base + s * 16 + q) * 2]);
+  float L = 0.f;
+  float acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = 0.f;
+  for (int s = 0; s < p.n_splits; ++s) {
+    const long long rw = base + s * 16 + q;
+    const float ms = p.part_ml[rw * 2];
+    if (ms == -INFINITY) continue;
+    const float w = expf(ms - mx);
+    L += p.part_ml[rw * 2 + 1] * w;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] += w * p.part_o[rw * DH + dd + 16 * c];
+  }
+  const float inv = 1.0f / L;
+  T* out = reinterpret_cast<T*>(p.out) + (long long)(r * p.B + q) * p.ldo + h * DH;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) out[dd + 16 * c] = from_f<T>(acc[c] * inv);
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void k_scatter(ScatterParams p) {
+  const int row = blockIdx.x;
+  const int l = blockIdx.y;
+  const int t = threadIdx.x;
+  constexpr int H2 = DH / 2;
+  if (row == 0 && l == 0 && t < p.n_req) {
+    const InjectReq q = p.req[t];
+    p.state[q.slot].ctx_len = q.pos0 + q.count;
+  }
+  int ri = 0;
+  while (ri + 1 < p.n_req && row >= p.req[ri + 1].row_start) ++ri;
+  const InjectReq rq = p.req[ri];
+  const int pos = rq.pos0 + (row - rq.row_start);
+  if (p.window > 0 && pos < rq.final_ctx - p.window) return;
+  const int n_pages = p.state[rq.slot].n_pages;
+  const int lp = pos / 16;
+  const int idx = p.window > 0 ? lp % n_pages : lp;
+  const int page = p.page_table[(long long)rq.slot * p.pt_stride + idx];
+  if (page < 0 || page >= p.max_pages) {
+    if (t == 0) atomicOr(p.err, 4u);
+    return;
+  }
+  const long long page_elems = 2LL * p.Hkv * 16 * DH;
+  T* pg = reinterpret_cast<T*>(p.pool) + l * p.layer_stride + page * page_elems;
+  const float* src = p.kv + (long long)row * (p.L * 2 * p.Hkv * DH) + (long long)l * 2 * p.Hkv * DH;
+  const int slotpos = pos & 15;
+  for (int e = t; e < p.Hkv * H2; e += 256) {
+    const int g = e / H2;
+    const int j = e - g * H2;
+    const float x1 = src[g * DH + j];
+    const float x2 = src[g * DH + j + H2];
+    const long long ti = (long long)pos * H2 + j;
+    const float c = p.cos_t[ti], s = p.sin_t[ti];
+    T* kd = pg + (long long)(g * 16 + slotpos) * DH;
+    kd[j] = from_f<T>(x1 * c - x2 * s);
+    kd[j + H2] = from_f<T>(x2 * c + x1 * s);
+  }
+  for (int e = t; e < p.Hkv * DH; e += 256) {
+    const int g = e / DH;
+    const int d = e - g * DH;
+    pg[(long long)(p.Hkv + g) * 16 * DH + d * 16 + slotpos] = from_f<T>(src[(p.Hkv + g) * DH + d]);
+  }
+}
+
+template <typename T>
+void qkv_post_t(int dh, int n_req, const QkvPostParams& p, const SlotArgs& sl, hipStream_t s) {
+  dim3 grid(n_req, p.Hq + 2 * p.Hkv);
+  if (dh == 128)
+    hipLaunchKernelGGL((k_qkv_post<T, 128>), grid, dim3(256), 0, s, p, sl);
+  else
+    hipLaunchKernelGGL((k_qkv_post<T, 64>), grid, dim3(256), 0, s, p, sl);
+}
+
+template <typename T>
+void attn_t(int dh, int n_req, const AttnParams& p, const SlotArgs& sl, hipStream_t s) {
+  dim3 grid(p.n_splits, p.Hkv, n_req);
+  dim3 block(64 * (p.Hq / p.Hkv));
+  if (dh == 128)
+    hipLaunchKernelGGL((k_attn<T, 128>), grid, block, 0, s, p, sl);
+  else
+    hipLaunchKernelGGL((k_attn<T, 64>), grid, block, 0, s, p, sl);
+}
+
+template <typename T>
+void combine_t(int dh, int n_req, const CombineParams& p, hipStream_t s) {
+  dim3 grid(p.Hq, n_req);
+  if (dh == 128)
+    hipLaunchKernelGGL((k_combine<T, 128>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_combine<T, 64>), grid, dim3(256), 0, s, p);
+}
+
+template <typename T>
+void scatter_t(int dh, const ScatterParams& p, hipStream_t s) {
+  dim3 grid(p.rows, p.L);
+  if (dh == 128)
+    hipLaunchKernelGGL((k_scatter<T, 128>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_scatter<T, 64>), grid, dim3(256), 0, s, p);
+}
+
+}  // namespace
+
+void launch_qkv_post(int dtype, int dh, int n_req, const QkvPostParams& p, const SlotArgs& sl,
+                     hipStream_t s) {
+  if (dtype == DFLASH_BF16)
+    qkv_post_t<bf16>(dh, n_req, p, sl, s);
+  else
+    qkv_post_t<float>(dh, n_req, p, sl, s);
+}
+
+void launch_attention(int dtype, int dh, int n_req, const AttnParams& p, const SlotArgs& sl,
+                      hipStream_t s) {
+  if (dtype == DFLASH_BF16)
+    attn_t<bf16>(dh, n_req, p, sl, s);
+  else
+    attn_t<float>(dh, n_req, p, sl, s);
+}
+
+void launch_combine(int dtype, int dh, int n_req, const CombineParams& p, hipStream_t s) {
+  if (dtype == DFLASH_BF16)
+    combine_t<bf16>(dh, n_req, p, s);
+  else
+    combine_t<float>(dh, n_req, p, s);
+}
+
+void launch_scatter(int dtype, int dh, const ScatterParams& p, hipStream_t s) {
+  if (p.rows <= 0) return;
+  if (dtype == DFLASH_BF16)
+    scatter_t<bf16>(dh, p, s);
+  else
+    scatter_t<float>(dh, p, s);
+}
+
+}  // namespace dflash

@@ -1,0 +1,87 @@
+// Device helpers shared by the gfx950 kernels: storage types, 8-element
+// operand fragments and the 16x16 MFMA step that consumes them.
+//
+// MFMA operand layout used throughout (v_mfma_f32_16x16x32_bf16 and
+// v_mfma_f32_16x16x4_f32 on CDNA4, wave64):
+//   A fragment: lane l supplies row (l % 16), 8 consecutive k values of the
+//               32-wide k step starting at 8 * (l / 16);
+//   B fragment: lane l supplies column (l % 16), the same 8 k values;
+//   C/D       : lane l holds column (l % 16), rows 4 * (l / 16) + 0..3.
+// The kernels only rely on A and B agreeing on which k a lane supplies, so
+// any consistent permutation of k inside a fragment is allowed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dflash {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// 8 storage elements as one MFMA operand fragment.
+template <typename T> struct Frag8;
+template <> struct Frag8<bf16> { typedef bf16x8 type; };
+template <> struct Frag8<float> { typedef f32x8 type; };
+
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+
+template <typename T> __device__ __forceinline__ T from_f(float x);
+// round-to-nearest-even float -> bfloat16 (the compiler's conversion is RNE)
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+
+template <typename T>
+__device__ __forceinline__ typename Frag8<T>::type load8(const T* p) {
+  return *reinterpret_cast<const typename Frag8<T>::type*>(p);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Frag8<T>::type zero8() {
+  typename Frag8<T>::type z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (T)0.0f;
+  return z;
+}
+
+// acc += A(16x32) * B(32x16) for one 32-wide k step.
+__device__ __forceinline__ f32x4 mfma_step(bf16x8 a, bf16x8 b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+// fp32: the lane's 8 k values go to 8 separate 16x16x4 MFMAs; element e of
+// every lane forms the 4-wide k step e.
+__device__ __forceinline__ f32x4 mfma_step(f32x8 a, f32x8 b, f32x4 acc) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Sum over the 64 lanes of a wave (butterfly; every lane gets the result).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Order-preserving map of a float to an unsigned key (larger float, larger key).
+__device__ __forceinline__ uint32_t float_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Packed argmax key: larger logit wins, ties go to the lower id.
+__device__ __forceinline__ uint64_t argmax_key(float logit, int id, int vocab) {
+  return ((uint64_t)float_key(logit) << 32) | (uint32_t)(vocab - 1 - id);
+}
+
+}  // namespace dflash

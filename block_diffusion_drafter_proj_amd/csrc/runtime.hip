@@ -1,0 +1,668 @@
+// Host runtime behind the C ABI in include/dflash.h: argument validation,
+// the host mirror of every request slot, the workspace carve-up and the
+// launch sequence of each call.  Contains no device code.
+//
+// Call sequences (all kernels on the caller's stream, no synchronisation):
+//   inject : per chunk of rows  fc GEMM (virtual concat of the n_feat hidden
+//            arrays) -> RMSNorm -> all-layer K/V GEMM -> RoPE + page scatter
+//   draft  : per layer  RMSNorm -> QKV GEMM -> q/k RoPE -> attention (split
+//            over pages) -> combine -> O GEMM + residual -> RMSNorm ->
+//            gate/up GEMM + SwiGLU -> down GEMM + residual;
+//            then final RMSNorm -> LM head GEMM + argmax -> decode ids
+//   verify : one kernel
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace dflash;
+
+namespace {
+
+thread_local std::string g_err;
+
+dflash_status fail(dflash_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+dflash_status hip_fail(hipError_t e, const char* what) {
+  return fail(DFLASH_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t elt(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
+
+// Upper bound of (requests x attention splits) handled in one draft call.
+int part_pairs(const dflash_config& c) { return c.max_batch + (512 + c.n_kv_heads - 1) / c.n_kv_heads; }
+
+struct Layout {
+  size_t state, err, page_table, cos_t, sin_t;
+  size_t h, xa, xo, qkv, qb, blk, part_o, part_ml, z, keys;
+  size_t u, f, kvo;
+  size_t total;
+};
+
+Layout make_layout(const dflash_config& c) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t e = elt(c);
+  const size_t M = (size_t)c.max_batch * c.block_size;
+  const size_t qd = (size_t)c.n_q_heads * c.head_dim;
+  const size_t qkvw = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const size_t page_elems = 2ull * c.n_kv_heads * 16 * c.head_dim;
+  const size_t R = c.max_inject_rows;
+  L.state = take(sizeof(SlotState) * c.max_batch);
+  L.err = take(16);
+  L.page_table = take(sizeof(int32_t) * c.max_batch * (size_t)c.max_pages_per_req);
+  L.cos_t = take(sizeof(float) * (size_t)c.max_position * (c.head_dim / 2));
+  L.sin_t = take(sizeof(float) * (size_t)c.max_position * (c.head_dim / 2));
+  L.h = take(sizeof(float) * M * c.hidden);
+  L.xa = take(e * M * c.hidden);
+  L.xo = take(e * M * qd);
+  L.qkv = take(sizeof(float) * M * qkvw);
+  L.qb = take(e * (size_t)c.max_batch * c.n_q_heads * 16 * c.head_dim);
+  L.blk = take(e * (size_t)c.max_batch * page_elems);
+  const size_t pp = (size_t)part_pairs(c) * c.n_q_heads * 16;
+  L.part_o = take(sizeof(float) * pp * c.head_dim);
+  L.part_ml = take(sizeof(float) * pp * 2);
+  L.z = take(e * M * c.ffn);
+  L.keys = take(sizeof(unsigned long long) * M);
+  L.u = take(sizeof(float) * R * c.hidden);
+  L.f = take(e * R * c.hidden);
+  L.kvo = take(sizeof(float) * R * (size_t)c.n_layers * 2 * c.n_kv_heads * c.head_dim);
+  L.total = off;
+  return L;
+}
+
+dflash_status validate(const dflash_config* c) {
+  if (!c) return fail(DFLASH_E_INVALID, "config is NULL");
+  auto bad = [&](const char* what) { return fail(DFLASH_E_INVALID, "config: %s", what); };
+  if (c->hidden <= 0 || c->hidden % 256 || c->hidden > 8192) return bad("hidden must be a multiple of 256 in (0, 8192]");
+  if (c->head_dim != 64 && c->head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (c->n_kv_heads <= 0 || c->n_q_heads <= 0 || c->n_q_heads % c->n_kv_heads)
+    return bad("n_q_heads must be a positive multiple of n_kv_heads");
+  if (c->n_q_heads / c->n_kv_heads > 16) return bad("at most 16 query heads per KV head");
+  if ((c->n_q_heads * c->head_dim) % 256) return bad("n_q_heads*head_dim must be a multiple of 256");
+  if (c->ffn <= 0 || c->ffn % 256) return bad("ffn must be a positive multiple of 256");
+  if (c->vocab <= 0) return bad("vocab must be positive");
+  if (c->n_layers < 1 || c->n_layers > DFLASH_MAX_LAYERS) return bad("n_layers out of range");
+  if (c->block_size < 1 || c->block_size > 16) return bad("block_size must be in [1, 16]");
+  if (c->n_feat < 1 || c->n_feat > DFLASH_MAX_FEAT) return bad("n_feat out of range");
+  if (c->dtype != DFLASH_BF16 && c->dtype != DFLASH_F32) return bad("unknown dtype");
+  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return bad("mask_token_id out of range");
+  if (c->page_size != DFLASH_PAGE_SIZE) return bad("page_size must be 16");
+  if (c->window < 0 || c->window % 16) return bad("window must be 0 or a positive multiple of 16");
+  if (c->conv2 != 0 && c->conv2 != 1) return bad("conv2 must be 0 or 1");
+  if (c->topk != 0 && c->topk != DFLASH_MAX_TOPK) return bad("topk must be 0 or 16");
+  if (c->topk && c->vocab < DFLASH_MAX_TOPK) return bad("topk needs vocab >= 16");
+  if (c->max_batch < 1 || c->max_batch > DFLASH_MAX_BATCH) return bad("max_batch out of range");
+  if (c->max_pages < 1) return bad("max_pages must be positive");
+  if (c->max_pages_per_req < 1) return bad("max_pages_per_req must be positive");
+  if (c->window && c->max_pages_per_req < c->window / 16 + 1)
+    return bad("max_pages_per_req must hold window/16 + 1 pages");
+  if (c->max_position < c->block_size + 2) return bad("max_position too small");
+  if (c->max_inject_rows < 1) return bad("max_inject_rows must be positive");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) return bad("rms_eps and rope_theta must be positive");
+  return DFLASH_OK;
+}
+
+struct HostSlot {
+  bool bound = false;
+  int ctx_len = 0, kv_begin = 0, n_pages = 0;
+};
+
+}  // namespace
+
+struct dflash_handle {
+  dflash_config cfg;
+  dflash_weights w;
+  char* kv;
+  char* ws;
+  Layout lay;
+  std::vector<HostSlot> slots;
+  bool dev_init = false;
+};
+
+namespace {
+
+template <typename P>
+P* at(dflash_handle* h, size_t off) {
+  return reinterpret_cast<P*>(h->ws + off);
+}
+
+dflash_status ensure_device(dflash_handle* h) {
+  if (h->dev_init) return DFLASH_OK;
+  const dflash_config& c = h->cfg;
+  const int half = c.head_dim / 2;
+  std::vector<float> cs((size_t)c.max_position * half), sn((size_t)c.max_position * half);
+  for (int p = 0; p < c.max_position; ++p)
+    for (int j = 0; j < half; ++j) {
+      const double inv = pow((double)c.rope_theta, -(2.0 * j) / (double)c.head_dim);
+      const double a = (double)p * inv;
+      cs[(size_t)p * half + j] = (float)cos(a);
+      sn[(size_t)p * half + j] = (float)sin(a);
+    }
+  hipError_t e;
+  if ((e = hipMemcpy(h->ws + h->lay.cos_t, cs.data(), cs.size() * 4, hipMemcpyHostToDevice)))
+    return hip_fail(e, "rope table upload");
+  if ((e = hipMemcpy(h->ws + h->lay.sin_t, sn.data(), sn.size() * 4, hipMemcpyHostToDevice)))
+    return hip_fail(e, "rope table upload");
+  if ((e = hipMemset(h->ws + h->lay.state, 0, sizeof(SlotState) * c.max_batch)))
+    return hip_fail(e, "state init");
+  if ((e = hipMemset(h->ws + h->lay.err, 0, 16))) return hip_fail(e, "state init");
+  if ((e = hipMemset(h->ws + h->lay.page_table, 0xff,
+                     sizeof(int32_t) * c.max_batch * (size_t)c.max_pages_per_req)))
+    return hip_fail(e, "page table init");
+  if ((e = hipDeviceSynchronize())) return hip_fail(e, "device init");
+  h->dev_init = true;
+  return DFLASH_OK;
+}
+
+dflash_status check_slots(dflash_handle* h, int32_t n_req, const int32_t* slots) {
+  if (n_req < 1 || n_req > h->cfg.max_batch) return fail(DFLASH_E_INVALID, "n_req %d out of [1, %d]", n_req, h->cfg.max_batch);
+  if (!slots) return fail(DFLASH_E_INVALID, "slots is NULL");
+  std::vector<char> seen(h->cfg.max_batch, 0);
+  for (int i = 0; i < n_req; ++i) {
+    const int s = slots[i];
+    if (s < 0 || s >= h->cfg.max_batch) return fail(DFLASH_E_INVALID, "slot %d out of range", s);
+    if (seen[s]) return fail(DFLASH_E_INVALID, "slot %d listed twice", s);
+    seen[s] = 1;
+    if (!h->slots[s].bound) return fail(DFLASH_E_INVALID, "slot %d is not bound", s);
+  }
+  return DFLASH_OK;
+}
+
+dflash_status launched(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, what);
+  return DFLASH_OK;
+}
+
+const char* wptr(const void* p, size_t elem_off, size_t e) {
+  return reinterpret_cast<const char*>(p) + elem_off * e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dflash_abi_version(void) { return DFLASH_ABI_VERSION; }
+
+const char* dflash_last_error(void) { return g_err.c_str(); }
+
+dflash_status dflash_validate_config(const dflash_config* cfg) { return validate(cfg); }
+
+dflash_status dflash_feature_layers(int32_t n_target_layers, int32_t k, int32_t* out) {
+  if (!out) return fail(DFLASH_E_INVALID, "out is NULL");
+  if (k < 2 || n_target_layers < 4) return fail(DFLASH_E_INVALID, "need k >= 2 and n_target_layers >= 4");
+  const int first = 1, last = n_target_layers - 3;
+  for (int i = 0; i < k; ++i) out[i] = first + (i * (last - first)) / (k - 1);
+  return DFLASH_OK;
+}
+
+size_t dflash_workspace_bytes(const dflash_config* cfg) {
+  if (validate(cfg) != DFLASH_OK) return 0;
+  return make_layout(*cfg).total;
+}
+
+size_t dflash_kv_pool_bytes(const dflash_config* cfg) {
+  if (validate(cfg) != DFLASH_OK) return 0;
+  return (size_t)cfg->n_layers * cfg->max_pages * 2ull * cfg->n_kv_heads * 16 * cfg->head_dim * elt(*cfg);
+}
+
+dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, void* kv_pool,
+                            void* workspace, dflash_handle** out) {
+  if (!out) return fail(DFLASH_E_INVALID, "out is NULL");
+  *out = nullptr;
+  dflash_status st = validate(cfg);
+  if (st) return st;
+  if (!w) return fail(DFLASH_E_INVALID, "weights is NULL");
+  if (!kv_pool || !workspace) return fail(DFLASH_E_INVALID, "kv_pool and workspace must be set");
+  if ((reinterpret_cast<uintptr_t>(kv_pool) | reinterpret_cast<uintptr_t>(workspace)) & 255)
+    return fail(DFLASH_E_INVALID, "kv_pool and workspace must be 256-byte aligned");
+  if (!w->embed || !w->lm_head || !w->fc || !w->fc_norm || !w->final_norm)
+    return fail(DFLASH_E_INVALID, "a model weight pointer is NULL");
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const dflash_layer_weights& lw = w->layers[l];
+    if (!lw.wqkv || !lw.wo || !lw.wgateup || !lw.wdown || !lw.attn_norm || !lw.mlp_norm)
+      return fail(DFLASH_E_INVALID, "layer %d: a weight pointer is NULL", l);
+    if (cfg->conv2 && !lw.conv) return fail(DFLASH_E_INVALID, "layer %d: conv taps are NULL", l);
+  }
+  dflash_handle* h = new dflash_handle();
+  h->cfg = *cfg;
+  h->w = *w;
+  h->kv = reinterpret_cast<char*>(kv_pool);
+  h->ws = reinterpret_cast<char*>(workspace);
+  h->lay = make_layout(*cfg);
+  h->slots.resize(cfg->max_batch);
+  *out = h;
+  return DFLASH_OK;
+}
+
+void dflash_destroy(dflash_handle* h) { delete h; }
+
+int32_t dflash_context_length(const dflash_handle* h, int32_t slot) {
+  if (!h || slot < 0 || slot >= h->cfg.max_batch || !h->slots[slot].bound) return -1;
+  return h->slots[slot].ctx_len;
+}
+
+dflash_status dflash_bind_request(dflash_handle* h, int32_t slot, const int32_t* page_ids,
+                                  int32_t n_pages, int32_t start_pos) {
+  if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
+  const dflash_config& c = h->cfg;
+  if (slot < 0 || slot >= c.max_batch) return fail(DFLASH_E_INVALID, "slot %d out of range", slot);
+  if (n_pages < 1 || n_pages > c.max_pages_per_req)
+    return fail(DFLASH_E_INVALID, "n_pages %d out of [1, %d]", n_pages, c.max_pages_per_req);
+  if (!page_ids) return fail(DFLASH_E_INVALID, "page_ids is NULL");
+  for (int i = 0; i < n_pages; ++i)
+    if (page_ids[i] < 0 || page_ids[i] >= c.max_pages)
+      return fail(DFLASH_E_INVALID, "page id %d out of [0, %d)", page_ids[i], c.max_pages);
+  if (c.window && n_pages < c.window / 16 + 1)
+    return fail(DFLASH_E_INVALID, "a window of %d needs at least %d pages", c.window, c.window / 16 + 1);
+  if (start_pos < 0 || start_pos + c.block_size + 1 > c.max_position)
+    return fail(DFLASH_E_INVALID, "start_pos %d out of range", start_pos);
+  if (!c.window && start_pos > n_pages * 16)
+    return fail(DFLASH_E_INVALID, "start_pos %d beyond the bound pages", start_pos);
+  dflash_status st = ensure_device(h);
+  if (st) return st;
+  hipError_t e;
+  if ((e = hipMemcpy(h->ws + h->lay.page_table + sizeof(int32_t) * (size_t)slot * c.max_pages_per_req,
+                     page_ids, sizeof(int32_t) * n_pages, hipMemcpyHostToDevice)))
+    return hip_fail(e, "page table upload");
+  SlotState s{start_pos, start_pos, n_pages, 0};
+  if ((e = hipMemcpy(h->ws + h->lay.state + sizeof(SlotState) * slot, &s, sizeof(s),
+                     hipMemcpyHostToDevice)))
+    return hip_fail(e, "slot state upload");
+  HostSlot& hs = h->slots[slot];
+  hs.bound = true;
+  hs.ctx_len = start_pos;
+  hs.kv_begin = start_pos;
+  hs.n_pages = n_pages;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_req,
+                                    const int32_t* slots, const int32_t* n_new,
+                                    const void* const* hidden, void* debug_f) {
+  if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
+  const dflash_config& c = h->cfg;
+  dflash_status st = check_slots(h, n_req, slots);
+  if (st) return st;
+  if (!n_new) return fail(DFLASH_E_INVALID, "n_new is NULL");
+  if (!hidden) return fail(DFLASH_E_INVALID, "hidden is NULL");
+  for (int k = 0; k < c.n_feat; ++k)
+    if (!hidden[k]) return fail(DFLASH_E_INVALID, "hidden[%d] is NULL", k);
+  long long total = 0;
+  for (int i = 0; i < n_req; ++i) {
+    const HostSlot& hs = h->slots[slots[i]];
+    if (n_new[i] < 0) return fail(DFLASH_E_INVALID, "n_new[%d] is negative", i);
+    const long long end = (long long)hs.ctx_len + n_new[i];
+    if (!c.window && end > (long long)hs.n_pages * 16)
+      return fail(DFLASH_E_CAPACITY, "slot %d: %lld positions exceed %d bound pages", slots[i], end, hs.n_pages);
+    if (end + c.block_size + 1 > c.max_position)
+      return fail(DFLASH_E_CAPACITY, "slot %d: position %lld beyond max_position", slots[i], end);
+    total += n_new[i];
+  }
+  if (total == 0) return DFLASH_OK;
+  st = ensure_device(h);
+  if (st) return st;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t e = elt(c);
+  const int d = c.hidden;
+  const int kvw = c.n_layers * 2 * c.n_kv_heads * c.head_dim;
+  const int R = c.max_inject_rows;
+
+  // walk requests in call order, cutting chunks of <= R rows and <= kMaxChunkReq requests
+  int req = 0, used = 0;  // current request and rows of it already emitted
+  long long row0 = 0;     // global row of the chunk start
+  while (row0 < total) {
+    ScatterParams sp{};
+    int rows = 0;
+    sp.n_req = 0;
+    while (rows < R && req < n_req && sp.n_req < kMaxChunkReq) {
+      const int left = n_new[req] - used;
+      if (left == 0) {
+        ++req;
+        used = 0;
+        continue;
+      }
+      const int take = std::min(left, R - rows);
+      const HostSlot& hs = h->slots[slots[req]];
+      InjectReq& q = sp.req[sp.n_req++];
+      q.row_start = rows;
+      q.count = take;
+      q.slot = slots[req];
+      q.pos0 = hs.ctx_len + used;
+      q.final_ctx = hs.ctx_len + n_new[req];
+      rows += take;
+      used += take;
+      if (used == n_new[req]) {
+        ++req;
+        used = 0;
+      }
+    }
+
+    GemmParams g{};
+    for (int k = 0; k < c.n_feat; ++k) g.a[k] = wptr(hidden[k], (size_t)row0 * d, e);
+    g.a_parts = c.n_feat;
+    g.a_part_k = d;
+    g.lda = d;
+    g.M = rows;
+    g.w[0] = h->w.fc;
+    g.seg_rows = d;
+    g.N = d;
+    g.K = c.n_feat * d;
+    g.out_f32 = at<float>(h, h->lay.u);
+    g.ldo = d;
+    launch_gemm(c.dtype, EPI_STORE, g, s);
+
+    NormParams np{};
+    np.x = at<float>(h, h->lay.u);
+    np.ldx = d;
+    np.gamma = h->w.fc_norm;
+    np.eps = c.rms_eps;
+    np.out = h->ws + h->lay.f;
+    np.ldo = d;
+    np.d = d;
+    np.M = rows;
+    launch_rmsnorm(c.dtype, np, s);
+    if (debug_f) {
+      hipError_t err = hipMemcpyAsync(reinterpret_cast<char*>(debug_f) + (size_t)row0 * d * e,
+                                      h->ws + h->lay.f, (size_t)rows * d * e,
+                                      hipMemcpyDeviceToDevice, s);
+      if (err) return hip_fail(err, "debug_f copy");
+    }
+
+    GemmParams kv{};
+    kv.a[0] = h->ws + h->lay.f;
+    kv.a_parts = 1;
+    kv.a_part_k = d;
+    kv.lda = d;
+    kv.M = rows;
+    for (int l = 0; l < c.n_layers; ++l)
+      kv.w[l] = wptr(h->w.layers[l].wqkv, (size_t)c.n_q_heads * c.head_dim * d, e);
+    kv.seg_rows = 2 * c.n_kv_heads * c.head_dim;
+    kv.N = kvw;
+    kv.K = d;
+    kv.out_f32 = at<float>(h, h->lay.kvo);
+    kv.ldo = kvw;
+    launch_gemm(c.dtype, EPI_STORE, kv, s);
+
+    sp.kv = at<float>(h, h->lay.kvo);
+    sp.rows = rows;
+    sp.L = c.n_layers;
+    sp.Hkv = c.n_kv_heads;
+    sp.cos_t = at<float>(h, h->lay.cos_t);
+    sp.sin_t = at<float>(h, h->lay.sin_t);
+    sp.pool = h->kv;
+    sp.layer_stride = (long long)c.max_pages * 2 * c.n_kv_heads * 16 * c.head_dim;
+    sp.page_table = at<int>(h, h->lay.page_table);
+    sp.pt_stride = c.max_pages_per_req;
+    sp.state = at<SlotState>(h, h->lay.state);
+    sp.window = c.window;
+    sp.max_pages = c.max_pages;
+    sp.err = at<unsigned int>(h, h->lay.err);
+    launch_scatter(c.dtype, c.head_dim, sp, s);
+    st = launched("inject");
+    if (st) return st;
+    row0 += rows;
+  }
+  for (int i = 0; i < n_req; ++i) h->slots[slots[i]].ctx_len += n_new[i];
+  return DFLASH_OK;
+}
+
+dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
+                                 const int32_t* slots, const int32_t* last_token, int32_t* draft,
+                                 int32_t* topk_ids, float* topk_logits, float* debug_logits,
+                                 float* debug_hidden) {
+  if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
+  const dflash_config& c = h->cfg;
+  dflash_status st = check_slots(h, n_req, slots);
+  if (st) return st;
+  if (!draft) return fail(DFLASH_E_INVALID, "draft is NULL");
+  if (c.conv2 && !last_token) return fail(DFLASH_E_INVALID, "conv2 needs last_token");
+  if (c.topk && (!topk_ids || !topk_logits)) return fail(DFLASH_E_INVALID, "topk needs topk_ids and topk_logits");
+  if (c.conv2 || c.topk) return fail(DFLASH_E_UNSUPPORTED, "conv2 / topk are not implemented yet");
+  int max_units = 1;
+  for (int i = 0; i < n_req; ++i) {
+    const HostSlot& hs = h->slots[slots[i]];
+    if (hs.ctx_len + c.block_size + 1 > c.max_position)
+      return fail(DFLASH_E_CAPACITY, "slot %d: block positions beyond max_position", slots[i]);
+    int lo = hs.kv_begin;
+    if (c.window) lo = std::max(lo, hs.ctx_len - c.window);
+    const int n_lp = hs.ctx_len > lo ? (hs.ctx_len - 1) / 16 - lo / 16 + 1 : 0;
+    max_units = std::max(max_units, n_lp + 1);
+  }
+  st = ensure_device(h);
+  if (st) return st;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t e = elt(c);
+  const int d = c.hidden, B = c.block_size, M = n_req * B;
+  const int qd = c.n_q_heads * c.head_dim;
+  const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  SlotArgs sl{};
+  for (int i = 0; i < n_req; ++i) sl.slots[i] = slots[i];
+
+  // attention split plan: about 512 workgroups, pairs bounded by the workspace
+  int splits = std::max(1, (512 + n_req * c.n_kv_heads - 1) / (n_req * c.n_kv_heads));
+  splits = std::min(splits, max_units);
+  while (splits > 1 && n_req * splits > part_pairs(c)) --splits;
+  const int pps = (max_units + splits - 1) / splits;
+  splits = (max_units + pps - 1) / pps;
+
+  float* hbuf = at<float>(h, h->lay.h);
+  const size_t page_layer = (size_t)c.max_pages * 2 * c.n_kv_heads * 16 * c.head_dim;
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    const dflash_layer_weights& lw = h->w.layers[l];
+    NormParams n1{};
+    n1.x = hbuf;
+    n1.ldx = d;
+    if (l == 0) {
+      n1.init_row = wptr(h->w.embed, (size_t)c.mask_token_id * d, e);
+      n1.x_init = hbuf;
+    }
+    n1.gamma = lw.attn_norm;
+    n1.eps = c.rms_eps;
+    n1.out = h->ws + h->lay.xa;
+    n1.ldo = d;
+    n1.d = d;
+    n1.M = M;
+    n1.dbg = debug_hidden ? debug_hidden + (size_t)l * M * d : nullptr;
+    launch_rmsnorm(c.dtype, n1, s);
+
+    GemmParams g{};
+    g.a[0] = h->ws + h->lay.xa;
+    g.a_parts = 1;
+    g.a_part_k = d;
+    g.lda = d;
+    g.M = M;
+    g.w[0] = lw.wqkv;
+    g.seg_rows = qkvw;
+    g.N = qkvw;
+    g.K = d;
+    g.out_f32 = at<float>(h, h->lay.qkv);
+    g.ldo = qkvw;
+    launch_gemm(c.dtype, EPI_STORE, g, s);
+
+    QkvPostParams qp{};
+    qp.qkv = at<float>(h, h->lay.qkv);
+    qp.B = B;
+    qp.Hq = c.n_q_heads;
+    qp.Hkv = c.n_kv_heads;
+    qp.state = at<SlotState>(h, h->lay.state);
+    qp.cos_t = at<float>(h, h->lay.cos_t);
+    qp.sin_t = at<float>(h, h->lay.sin_t);
+    qp.qb = h->ws + h->lay.qb;
+    qp.blk = h->ws + h->lay.blk;
+    launch_qkv_post(c.dtype, c.head_dim, n_req, qp, sl, s);
+
+    AttnParams ap{};
+    ap.qb = h->ws + h->lay.qb;
+    ap.blk = h->ws + h->lay.blk;
+    ap.pool = h->kv + (size_t)l * page_layer * e;
+    ap.page_table = at<int>(h, h->lay.page_table);
+    ap.pt_stride = c.max_pages_per_req;
+    ap.state = at<SlotState>(h, h->lay.state);
+    ap.max_pages = c.max_pages;
+    ap.window = c.window;
+    ap.Hq = c.n_q_heads;
+    ap.Hkv = c.n_kv_heads;
+    ap.B = B;
+    ap.pps = pps;
+    ap.n_splits = splits;
+    ap.scale = (float)(1.0 / sqrt((double)c.head_dim));
+    ap.part_o = at<float>(h, h->lay.part_o);
+    ap.part_ml = at<float>(h, h->lay.part_ml);
+    ap.err = at<unsigned int>(h, h->lay.err);
+    launch_attention(c.dtype, c.head_dim, n_req, ap, sl, s);
+
+    CombineParams cp{};
+    cp.part_o = ap.part_o;
+    cp.part_ml = ap.part_ml;
+    cp.n_splits = splits;
+    cp.Hq = c.n_q_heads;
+    cp.B = B;
+    cp.out = h->ws + h->lay.xo;
+    cp.ldo = qd;
+    launch_combine(c.dtype, c.head_dim, n_req, cp, s);
+
+    GemmParams go{};
+    go.a[0] = h->ws + h->lay.xo;
+    go.a_parts = 1;
+    go.a_part_k = qd;
+    go.lda = qd;
+    go.M = M;
+    go.w[0] = lw.wo;
+    go.seg_rows = d;
+    go.N = d;
+    go.K = qd;
+    go.resid = hbuf;
+    go.ldr = d;
+    launch_gemm(c.dtype, EPI_RESID, go, s);
+
+    NormParams n2{};
+    n2.x = hbuf;
+    n2.ldx = d;
+    n2.gamma = lw.mlp_norm;
+    n2.eps = c.rms_eps;
+    n2.out = h->ws + h->lay.xa;
+    n2.ldo = d;
+    n2.d = d;
+    n2.M = M;
+    launch_rmsnorm(c.dtype, n2, s);
+
+    GemmParams gu{};
+    gu.a[0] = h->ws + h->lay.xa;
+    gu.a_parts = 1;
+    gu.a_part_k = d;
+    gu.lda = d;
+    gu.M = M;
+    gu.w[0] = lw.wgateup;
+    gu.w_up = wptr(lw.wgateup, (size_t)c.ffn * d, e);
+    gu.seg_rows = c.ffn;
+    gu.N = c.ffn;
+    gu.K = d;
+    gu.out_t = h->ws + h->lay.z;
+    gu.ldt = c.ffn;
+    launch_gemm(c.dtype, EPI_SWIGLU, gu, s);
+
+    GemmParams gd{};
+    gd.a[0] = h->ws + h->lay.z;
+    gd.a_parts = 1;
+    gd.a_part_k = c.ffn;
+    gd.lda = c.ffn;
+    gd.M = M;
+    gd.w[0] = lw.wdown;
+    gd.seg_rows = d;
+    gd.N = d;
+    gd.K = c.ffn;
+    gd.resid = hbuf;
+    gd.ldr = d;
+    launch_gemm(c.dtype, EPI_RESID, gd, s);
+    st = launched("draft layer");
+    if (st) return st;
+  }
+
+  NormParams nf{};
+  nf.x = hbuf;
+  nf.ldx = d;
+  nf.gamma = h->w.final_norm;
+  nf.eps = c.rms_eps;
+  nf.out = h->ws + h->lay.xa;
+  nf.ldo = d;
+  nf.d = d;
+  nf.M = M;
+  nf.dbg = debug_hidden ? debug_hidden + (size_t)c.n_layers * M * d : nullptr;
+  nf.zero_keys = at<unsigned long long>(h, h->lay.keys);
+  launch_rmsnorm(c.dtype, nf, s);
+
+  GemmParams gl{};
+  gl.a[0] = h->ws + h->lay.xa;
+  gl.a_parts = 1;
+  gl.a_part_k = d;
+  gl.lda = d;
+  gl.M = M;
+  gl.w[0] = h->w.lm_head;
+  gl.seg_rows = c.vocab;
+  gl.N = c.vocab;
+  gl.K = d;
+  gl.keys = at<unsigned long long>(h, h->lay.keys);
+  gl.dbg = debug_logits;
+  gl.ld_dbg = c.vocab;
+  launch_gemm(c.dtype, EPI_ARGMAX, gl, s);
+  launch_finalize(at<unsigned long long>(h, h->lay.keys), M, c.vocab, draft, s);
+  return launched("draft head");
+}
+
+dflash_status dflash_verify_accept(dflash_handle* h, void* stream, int32_t n_req,
+                                   const int32_t* draft, const int32_t* target_greedy,
+                                   int32_t* accept_len, int32_t* committed, int32_t* last_token) {
+  if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
+  if (n_req < 1 || n_req > h->cfg.max_batch) return fail(DFLASH_E_INVALID, "n_req %d out of [1, %d]", n_req, h->cfg.max_batch);
+  if (!draft || !target_greedy || !accept_len || !committed || !last_token)
+    return fail(DFLASH_E_INVALID, "a verify pointer is NULL");
+  dflash_status st = ensure_device(h);
+  if (st) return st;
+  launch_verify(n_req, h->cfg.block_size, h->cfg.vocab, draft, target_greedy, accept_len,
+                committed, last_token, at<unsigned int>(h, h->lay.err),
+                reinterpret_cast<hipStream_t>(stream));
+  return launched("verify");
+}
+
+dflash_status dflash_check(dflash_handle* h, void* stream) {
+  if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
+  if (!h->dev_init) return DFLASH_OK;
+  hipError_t e;
+  if ((e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)))) return hip_fail(e, "sync");
+  unsigned int word = 0;
+  if ((e = hipMemcpy(&word, h->ws + h->lay.err, sizeof(word), hipMemcpyDeviceToHost)))
+    return hip_fail(e, "error word read");
+  if (word) {
+    if ((e = hipMemset(h->ws + h->lay.err, 0, sizeof(word)))) return hip_fail(e, "error word clear");
+    return fail(DFLASH_E_DEVICE, "device error word 0x%x (1: token id out of range, 2/4: page id out of range)", word);
+  }
+  return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,238 @@
+/*
+ * dflash.h — C ABI of the DFlash drafting hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources are web pages about DFlash, cited by page and section):
+ *
+ *   [guide]  "DFlash：块扩散加速的 LLM 推测解码技术" (txtmix.com DFlash guide)
+ *   [news]   "DFlash 2 发布：并行草稿继续压低大模型推理延迟" (openai-hub.com)
+ *   [repo]   llmapis.com post on the DFlash repository
+ *
+ * One speculative cycle maps onto three calls ([guide] section 4):
+ *
+ *   dflash_inject_context  target features of new positions -> draft KV cache
+ *                          ([guide] section 3.2)
+ *   dflash_draft_block     one forward of the block-diffusion draft over B mask
+ *                          positions -> B greedy draft tokens ([guide] 3.1, 3.2)
+ *   dflash_verify_accept   longest draft prefix matching the target's greedy
+ *                          tokens ([news] "DFlash 2 的核心：一次写一块")
+ *
+ * plus the host-side feature-layer rule dflash_feature_layers ([guide] 3.2).
+ *
+ * Memory: the caller allocates every device buffer (weights, KV pool,
+ * workspace, inputs, outputs); the library borrows weights, the KV pool and
+ * the workspace for the handle's lifetime and everything else for the call.
+ * Library calls never allocate device memory.  The handle itself is host
+ * memory holding the configuration, the borrowed pointers and a host mirror
+ * of each request slot's lengths and pages.
+ *
+ * Execution: every compute call validates its arguments on the host, then
+ * enqueues kernels on the given stream (a hipStream_t; NULL = the default
+ * stream) and returns without synchronising.  Outputs are valid once the
+ * stream has reached the enqueued work.  Calls on one handle must not run
+ * concurrently; distinct handles are independent.
+ *
+ * Errors: a nonzero status means nothing was enqueued and no state changed,
+ * except DFLASH_E_HIP, which reports a failure of the HIP runtime itself
+ * (after which the handle's device state is undefined).  dflash_last_error()
+ * returns a thread-local message for the last failing call.  Token ids read
+ * from device memory that fall outside [0, vocab) are clamped and recorded
+ * in a sticky device error word that dflash_check reports.
+ *
+ * Data types: DFLASH_BF16 stores weights, hidden states, the KV cache and
+ * activations in bfloat16 and accumulates in fp32; DFLASH_F32 stores them in
+ * fp32.  Norms, softmax, the residual stream and logits are fp32 in both.
+ *
+ * Weight layout: every matrix is row-major [out_features, in_features]
+ * (torch.nn.Linear layout).  Vectors are [hidden].
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_ABI_VERSION 1
+#define DFLASH_MAX_LAYERS 16
+#define DFLASH_MAX_FEAT 8
+#define DFLASH_MAX_BATCH 256
+#define DFLASH_PAGE_SIZE 16
+#define DFLASH_MAX_TOPK 16
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_E_INVALID = 1,     /* bad argument or configuration */
+  DFLASH_E_CAPACITY = 2,    /* an inject would exceed the slot's bound pages */
+  DFLASH_E_UNSUPPORTED = 3, /* valid but not implemented for this shape */
+  DFLASH_E_HIP = 4,         /* the HIP runtime reported an error */
+  DFLASH_E_DEVICE = 5       /* sticky device error word was set */
+} dflash_status;
+
+typedef enum { DFLASH_BF16 = 0, DFLASH_F32 = 1 } dflash_dtype;
+
+/* Shapes of one draft model and the capacity of one handle.
+ * Requirements (checked by dflash_validate_config):
+ *   hidden, ffn, n_q_heads*head_dim and n_feat*hidden multiples of 256;
+ *   head_dim 64 or 128; n_q_heads a multiple of n_kv_heads with
+ *   n_q_heads/n_kv_heads <= 16; 1 <= block_size <= 16; page_size == 16;
+ *   1 <= n_layers <= DFLASH_MAX_LAYERS; 1 <= n_feat <= DFLASH_MAX_FEAT;
+ *   0 <= mask_token_id < vocab; window 0 (unbounded) or a positive multiple
+ *   of 16; topk 0 or 16; max_batch <= DFLASH_MAX_BATCH. */
+typedef struct dflash_config {
+  int32_t hidden;            /* d */
+  int32_t n_q_heads;         /* Hq */
+  int32_t n_kv_heads;        /* Hkv (grouped-query attention) */
+  int32_t head_dim;          /* dh */
+  int32_t ffn;               /* F, SwiGLU width */
+  int32_t vocab;             /* V, shared LM head rows */
+  int32_t n_layers;          /* L draft layers ([guide] 3.1: 5, or 8) */
+  int32_t block_size;        /* B mask positions per draft ([guide] 3.1: 16, or 10) */
+  int32_t n_feat;            /* K target layers concatenated ([guide] 3.2: 5) */
+  int32_t dtype;             /* dflash_dtype */
+  int32_t mask_token_id;     /* embedding row used for every block position */
+  int32_t page_size;         /* KV page, must be 16 tokens */
+  int32_t window;            /* draft sliding window in tokens ([repo]); 0 = none */
+  int32_t conv2;             /* 1 = DFlash-2 two-tap conv ([guide] 7) */
+  int32_t topk;              /* 0, or 16 = keep top-16 per position ([guide] 7) */
+  int32_t max_batch;         /* request slots */
+  int32_t max_pages;         /* pages in the KV pool (per layer) */
+  int32_t max_pages_per_req; /* page-table width per slot */
+  int32_t max_position;      /* positions < max_position (RoPE table rows) */
+  int32_t max_inject_rows;   /* rows per internal inject chunk (workspace size) */
+  float rms_eps;             /* RMSNorm epsilon */
+  float rope_theta;          /* RoPE base */
+} dflash_config;
+
+/* Per-layer weights (device pointers, dtype of the config).
+ *   wqkv      [(Hq + 2*Hkv)*dh, d]  rows: q heads, then k heads, then v heads
+ *   wo        [d, Hq*dh]
+ *   wgateup   [2*F, d]              rows: gate, then up
+ *   wdown     [d, F]
+ *   attn_norm [d], mlp_norm [d]     RMSNorm gains
+ *   conv      [4][2][d] two-tap conv taps (w0, w1) at the four conv points, or
+ *             NULL when conv2 == 0 */
+typedef struct dflash_layer_weights {
+  const void *wqkv, *wo, *wgateup, *wdown, *attn_norm, *mlp_norm, *conv;
+} dflash_layer_weights;
+
+/* Model weights (device pointers).
+ *   embed [V, d] and lm_head [V, d] are the target's, shared by the draft
+ *   ([guide] 3.1); fc [d, n_feat*d] and fc_norm [d] form the context
+ *   projection ([guide] 3.2); final_norm [d] is the draft's last RMSNorm. */
+typedef struct dflash_weights {
+  const void *embed, *lm_head, *fc, *fc_norm, *final_norm;
+  dflash_layer_weights layers[DFLASH_MAX_LAYERS];
+} dflash_weights;
+
+typedef struct dflash_handle dflash_handle;
+
+/* ABI version of the loaded library (DFLASH_ABI_VERSION). */
+int32_t dflash_abi_version(void);
+
+/* Thread-local message of the last failing call ("" if none). */
+const char *dflash_last_error(void);
+
+/* Checks a configuration; DFLASH_OK or DFLASH_E_INVALID. Host only. */
+dflash_status dflash_validate_config(const dflash_config *cfg);
+
+/* Feature-layer rule ([guide] 3.2): the k 0-based target layers, spaced
+ * evenly with integer floor over [1, n_target_layers-3] (layer 2 to the
+ * third-from-last in 1-based numbering), written to out[0..k).  Needs
+ * k >= 2 and n_target_layers >= 4.  Host only. */
+dflash_status dflash_feature_layers(int32_t n_target_layers, int32_t k, int32_t *out);
+
+/* Bytes of device workspace / KV pool a handle with this config needs
+ * (0 for an invalid config).  The KV pool is n_layers * max_pages pages of
+ * 2 * n_kv_heads * 16 * head_dim elements; the caller may hand out pages to
+ * slots in any order. */
+size_t dflash_workspace_bytes(const dflash_config *cfg);
+size_t dflash_kv_pool_bytes(const dflash_config *cfg);
+
+/* Creates a handle borrowing weights, kv_pool and workspace (device buffers
+ * of at least the sizes above, 256-byte aligned).  Device initialisation
+ * (RoPE table, slot state) happens on the first call that needs the device,
+ * on the current HIP device.  Returns DFLASH_E_INVALID on a bad config or a
+ * NULL pointer. */
+dflash_status dflash_create(const dflash_config *cfg, const dflash_weights *w,
+                            void *kv_pool, void *workspace, dflash_handle **out);
+
+/* Releases the host handle (borrowed device memory is untouched). */
+void dflash_destroy(dflash_handle *h);
+
+/* Binds request slot `slot` to KV pages page_ids[0..n_pages) (host array of
+ * pool page indices, each < max_pages, n_pages <= max_pages_per_req) and
+ * resets its lengths: the next inject writes position `start_pos`, positions
+ * below it are never visible.  With a window W the pages form a ring that
+ * needs n_pages >= W/16 + 1; without one, positions below
+ * 16*n_pages fit.  Synchronous (uploads the page table). */
+dflash_status dflash_bind_request(dflash_handle *h, int32_t slot, const int32_t *page_ids,
+                                  int32_t n_pages, int32_t start_pos);
+
+/* Host mirror of a slot's committed context length (positions injected). */
+int32_t dflash_context_length(const dflash_handle *h, int32_t slot);
+
+/* Steps 1 and 2 ([guide] 3.2): for each of the n_req requests, the target
+ * hidden states of n_new[i] new positions ctx_len .. ctx_len+n_new[i]-1 are
+ * concatenated over the n_feat layers, projected by fc, RMSNormed by fc_norm
+ * and written through every draft layer's K/V projection (K with RoPE at the
+ * absolute position) into the slot's KV pages.
+ *   slots   host [n_req] distinct bound slots
+ *   n_new   host [n_req] >= 0 rows per request
+ *   hidden  host array of n_feat device pointers, each [sum(n_new), d] in the
+ *           config dtype, rows grouped by request in call order, feature
+ *           layers in ascending target-layer order
+ *   debug_f optional device [sum(n_new), d] (config dtype): the projected,
+ *           normalised context feature; NULL in timed runs
+ * DFLASH_E_CAPACITY if a slot without window would run past its pages or
+ * past max_position. */
+dflash_status dflash_inject_context(dflash_handle *h, void *stream, int32_t n_req,
+                                    const int32_t *slots, const int32_t *n_new,
+                                    const void *const *hidden, void *debug_f);
+
+/* Steps 3 and 4 ([guide] 3.1, 3.2, 7): one forward of the draft over B mask
+ * positions n .. n+B-1 (n = ctx_len + 1) of each request: pre-norm layers with
+ * bidirectional attention over the visible context KV and the block, GQA,
+ * SwiGLU; the draft's final RMSNorm; the shared LM head; greedy argmax with
+ * ties to the lowest id.
+ *   slots        host [n_req] distinct bound slots with ctx_len >= 1
+ *   last_token   device [n_req] int32 last verified token (conv2 only, else
+ *                may be NULL): the block start of the two-tap conv reads its
+ *                embedding
+ *   draft        device [n_req, B] int32 output
+ *   topk_ids     device [n_req, B, 16] int32, topk_logits [n_req, B, 16] fp32:
+ *                top-16 by logit descending then id ascending (topk == 16),
+ *                else NULL
+ *   debug_logits optional device [n_req, B, V] fp32
+ *   debug_hidden optional device [L+1, n_req*B, d] fp32: residual stream
+ *                before layer 0 and after every layer */
+dflash_status dflash_draft_block(dflash_handle *h, void *stream, int32_t n_req,
+                                 const int32_t *slots, const int32_t *last_token,
+                                 int32_t *draft, int32_t *topk_ids, float *topk_logits,
+                                 float *debug_logits, float *debug_hidden);
+
+/* Step 5 ([news] "DFlash 2 的核心：一次写一块"; [guide] 3.3): a = number of
+ * leading positions where draft equals the target's greedy token; commits
+ * draft[0..a) followed by target_greedy[a], which becomes the next pending
+ * token.  A pure function of its inputs: it does not touch the KV cache.
+ *   draft         device [n_req, B] int32
+ *   target_greedy device [n_req, B+1] int32 target argmax at positions n..n+B
+ *   accept_len    device [n_req] int32 output, in [0, B]
+ *   committed     device [n_req, B+1] int32 output, -1 padded after a+1 tokens
+ *   last_token    device [n_req] int32 output, = target_greedy[a] */
+dflash_status dflash_verify_accept(dflash_handle *h, void *stream, int32_t n_req,
+                                   const int32_t *draft, const int32_t *target_greedy,
+                                   int32_t *accept_len, int32_t *committed,
+                                   int32_t *last_token);
+
+/* Synchronises `stream` and reads the sticky device error word; returns
+ * DFLASH_E_DEVICE (and clears the word) if a kernel recorded an
+ * out-of-range token id, else DFLASH_OK. */
+dflash_status dflash_check(dflash_handle *h, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */
