@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
             "dflash_draft_block": (i32, [vp, vp, i32, pi32, vp, vp, vp, vp, vp, vp]),
             "dflash_verify_accept": (i32, [vp, vp, i32, vp, vp, vp, vp, vp]),
             "dflash_check": (i32, [vp, vp]),
+            "dflash_profile_begin": (i32, [vp, ctypes.c_uint32]),
+            "dflash_profile_end": (i32, [vp, ctypes.POINTER(ctypes.c_float), pi32]),
         }
         for name, (res, args) in sigs.items():
             f = getattr(L, name)
@@ -171,6 +173,22 @@ def dflash_verify_accept(h: int, stream: int, n_req: int, draft: int, target_gre
 
 def dflash_check(h: int, stream: int) -> None:
     _check(lib().dflash_check(ctypes.c_void_p(h), ctypes.c_void_p(stream)))
+
+
+KERNELS = ["fc_gemm", "norm", "kv_gemm", "scatter", "qkv_gemm", "qkv_post", "attn", "combine",
+           "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "finalize", "verify"]
+
+
+def dflash_profile_begin(h: int, mask: int) -> None:
+    _check(lib().dflash_profile_begin(ctypes.c_void_p(h), mask))
+
+
+def dflash_profile_end(h: int) -> dict:
+    """{kernel class: (total ms, launches)} for the classes that ran."""
+    ms = (ctypes.c_float * len(KERNELS))()
+    n = (ctypes.c_int32 * len(KERNELS))()
+    _check(lib().dflash_profile_end(ctypes.c_void_p(h), ms, n))
+    return {k: (float(ms[i]), int(n[i])) for i, k in enumerate(KERNELS) if n[i]}
 
 
 def declared_functions() -> list[str]:

@@ -129,6 +129,14 @@ struct HostSlot {
   int ctx_len = 0, kv_begin = 0, n_pages = 0;
 };
 
+// Launch timing: pairs of events per bracketed launch, reused across runs.
+struct Profiler {
+  uint32_t mask = 0;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<std::pair<int, size_t>> marks;  // (kernel class, first event index)
+};
+
 }  // namespace
 
 struct dflash_handle {
@@ -139,6 +147,7 @@ struct dflash_handle {
   Layout lay;
   std::vector<HostSlot> slots;
   bool dev_init = false;
+  Profiler prof;
 };
 
 namespace {
@@ -175,6 +184,31 @@ dflash_status ensure_device(dflash_handle* h) {
   h->dev_init = true;
   return DFLASH_OK;
 }
+
+// Bracket one launch of class `k` with events when timing is on for it.
+struct ProfScope {
+  dflash_handle* h;
+  hipStream_t s;
+  int k;
+  size_t idx;
+  bool on;
+  ProfScope(dflash_handle* h_, int k_, hipStream_t s_) : h(h_), s(s_), k(k_), idx(0), on(false) {
+    Profiler& p = h->prof;
+    if (!(p.mask & (1u << k))) return;
+    while (p.pool.size() < p.used + 2) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return;
+      p.pool.push_back(e);
+    }
+    idx = p.used;
+    p.used += 2;
+    on = hipEventRecord(p.pool[idx], s) == hipSuccess;
+  }
+  ~ProfScope() {
+    if (!on) return;
+    if (hipEventRecord(h->prof.pool[idx + 1], s) == hipSuccess) h->prof.marks.push_back({k, idx});
+  }
+};
 
 dflash_status check_slots(dflash_handle* h, int32_t n_req, const int32_t* slots) {
   if (n_req < 1 || n_req > h->cfg.max_batch) return fail(DFLASH_E_INVALID, "n_req %d out of [1, %d]", n_req, h->cfg.max_batch);
@@ -257,7 +291,11 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
   return DFLASH_OK;
 }
 
-void dflash_destroy(dflash_handle* h) { delete h; }
+void dflash_destroy(dflash_handle* h) {
+  if (!h) return;
+  for (hipEvent_t e : h->prof.pool) (void)hipEventDestroy(e);
+  delete h;
+}
 
 int32_t dflash_context_length(const dflash_handle* h, int32_t slot) {
   if (!h || slot < 0 || slot >= h->cfg.max_batch || !h->slots[slot].bound) return -1;
@@ -373,7 +411,7 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
     g.K = c.n_feat * d;
     g.out_f32 = at<float>(h, h->lay.u);
     g.ldo = d;
-    launch_gemm(c.dtype, EPI_STORE, g, s);
+    { ProfScope ps(h, DFLASH_KERNEL_FC_GEMM, s); launch_gemm(c.dtype, EPI_STORE, g, s); }
 
     NormParams np{};
     np.x = at<float>(h, h->lay.u);
@@ -384,7 +422,7 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
     np.ldo = d;
     np.d = d;
     np.M = rows;
-    launch_rmsnorm(c.dtype, np, s);
+    { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, np, s); }
     if (debug_f) {
       hipError_t err = hipMemcpyAsync(reinterpret_cast<char*>(debug_f) + (size_t)row0 * d * e,
                                       h->ws + h->lay.f, (size_t)rows * d * e,
@@ -405,7 +443,7 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
     kv.K = d;
     kv.out_f32 = at<float>(h, h->lay.kvo);
     kv.ldo = kvw;
-    launch_gemm(c.dtype, EPI_STORE, kv, s);
+    { ProfScope ps(h, DFLASH_KERNEL_KV_GEMM, s); launch_gemm(c.dtype, EPI_STORE, kv, s); }
 
     sp.kv = at<float>(h, h->lay.kvo);
     sp.rows = rows;
@@ -421,7 +459,7 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
     sp.window = c.window;
     sp.max_pages = c.max_pages;
     sp.err = at<unsigned int>(h, h->lay.err);
-    launch_scatter(c.dtype, c.head_dim, sp, s);
+    { ProfScope ps(h, DFLASH_KERNEL_SCATTER, s); launch_scatter(c.dtype, c.head_dim, sp, s); }
     st = launched("inject");
     if (st) return st;
     row0 += rows;
@@ -489,7 +527,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     n1.d = d;
     n1.M = M;
     n1.dbg = debug_hidden ? debug_hidden + (size_t)l * M * d : nullptr;
-    launch_rmsnorm(c.dtype, n1, s);
+    { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, n1, s); }
 
     GemmParams g{};
     g.a[0] = h->ws + h->lay.xa;
@@ -503,7 +541,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     g.K = d;
     g.out_f32 = at<float>(h, h->lay.qkv);
     g.ldo = qkvw;
-    launch_gemm(c.dtype, EPI_STORE, g, s);
+    { ProfScope ps(h, DFLASH_KERNEL_QKV_GEMM, s); launch_gemm(c.dtype, EPI_STORE, g, s); }
 
     QkvPostParams qp{};
     qp.qkv = at<float>(h, h->lay.qkv);
@@ -515,7 +553,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     qp.sin_t = at<float>(h, h->lay.sin_t);
     qp.qb = h->ws + h->lay.qb;
     qp.blk = h->ws + h->lay.blk;
-    launch_qkv_post(c.dtype, c.head_dim, n_req, qp, sl, s);
+    { ProfScope ps(h, DFLASH_KERNEL_QKV_POST, s); launch_qkv_post(c.dtype, c.head_dim, n_req, qp, sl, s); }
 
     AttnParams ap{};
     ap.qb = h->ws + h->lay.qb;
@@ -535,7 +573,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     ap.part_o = at<float>(h, h->lay.part_o);
     ap.part_ml = at<float>(h, h->lay.part_ml);
     ap.err = at<unsigned int>(h, h->lay.err);
-    launch_attention(c.dtype, c.head_dim, n_req, ap, sl, s);
+    { ProfScope ps(h, DFLASH_KERNEL_ATTN, s); launch_attention(c.dtype, c.head_dim, n_req, ap, sl, s); }
 
     CombineParams cp{};
     cp.part_o = ap.part_o;
@@ -545,7 +583,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     cp.B = B;
     cp.out = h->ws + h->lay.xo;
     cp.ldo = qd;
-    launch_combine(c.dtype, c.head_dim, n_req, cp, s);
+    { ProfScope ps(h, DFLASH_KERNEL_COMBINE, s); launch_combine(c.dtype, c.head_dim, n_req, cp, s); }
 
     GemmParams go{};
     go.a[0] = h->ws + h->lay.xo;
@@ -559,7 +597,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     go.K = qd;
     go.resid = hbuf;
     go.ldr = d;
-    launch_gemm(c.dtype, EPI_RESID, go, s);
+    { ProfScope ps(h, DFLASH_KERNEL_O_GEMM, s); launch_gemm(c.dtype, EPI_RESID, go, s); }
 
     NormParams n2{};
     n2.x = hbuf;
@@ -570,7 +608,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     n2.ldo = d;
     n2.d = d;
     n2.M = M;
-    launch_rmsnorm(c.dtype, n2, s);
+    { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, n2, s); }
 
     GemmParams gu{};
     gu.a[0] = h->ws + h->lay.xa;
@@ -585,7 +623,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     gu.K = d;
     gu.out_t = h->ws + h->lay.z;
     gu.ldt = c.ffn;
-    launch_gemm(c.dtype, EPI_SWIGLU, gu, s);
+    { ProfScope ps(h, DFLASH_KERNEL_GATEUP_GEMM, s); launch_gemm(c.dtype, EPI_SWIGLU, gu, s); }
 
     GemmParams gd{};
     gd.a[0] = h->ws + h->lay.z;
@@ -599,7 +637,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     gd.K = c.ffn;
     gd.resid = hbuf;
     gd.ldr = d;
-    launch_gemm(c.dtype, EPI_RESID, gd, s);
+    { ProfScope ps(h, DFLASH_KERNEL_DOWN_GEMM, s); launch_gemm(c.dtype, EPI_RESID, gd, s); }
     st = launched("draft layer");
     if (st) return st;
   }
@@ -615,7 +653,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   nf.M = M;
   nf.dbg = debug_hidden ? debug_hidden + (size_t)c.n_layers * M * d : nullptr;
   nf.zero_keys = at<unsigned long long>(h, h->lay.keys);
-  launch_rmsnorm(c.dtype, nf, s);
+  { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, nf, s); }
 
   GemmParams gl{};
   gl.a[0] = h->ws + h->lay.xa;
@@ -630,8 +668,11 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   gl.keys = at<unsigned long long>(h, h->lay.keys);
   gl.dbg = debug_logits;
   gl.ld_dbg = c.vocab;
-  launch_gemm(c.dtype, EPI_ARGMAX, gl, s);
-  launch_finalize(at<unsigned long long>(h, h->lay.keys), M, c.vocab, draft, s);
+  { ProfScope ps(h, DFLASH_KERNEL_LM_HEAD, s); launch_gemm(c.dtype, EPI_ARGMAX, gl, s); }
+  {
+    ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
+    launch_finalize(at<unsigned long long>(h, h->lay.keys), M, c.vocab, draft, s);
+  }
   return launched("draft head");
 }
 
@@ -644,10 +685,49 @@ dflash_status dflash_verify_accept(dflash_handle* h, void* stream, int32_t n_req
     return fail(DFLASH_E_INVALID, "a verify pointer is NULL");
   dflash_status st = ensure_device(h);
   if (st) return st;
-  launch_verify(n_req, h->cfg.block_size, h->cfg.vocab, draft, target_greedy, accept_len,
-                committed, last_token, at<unsigned int>(h, h->lay.err),
-                reinterpret_cast<hipStream_t>(stream));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  {
+    ProfScope ps(h, DFLASH_KERNEL_VERIFY, s);
+    launch_verify(n_req, h->cfg.block_size, h->cfg.vocab, draft, target_greedy, accept_len,
+                  committed, last_token, at<unsigned int>(h, h->lay.err), s);
+  }
   return launched("verify");
+}
+
+dflash_status dflash_profile_begin(dflash_handle* h, uint32_t mask) {
+  if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
+  h->prof.mask = mask & ((1u << DFLASH_KERNEL_COUNT) - 1);
+  h->prof.used = 0;
+  h->prof.marks.clear();
+  return DFLASH_OK;
+}
+
+dflash_status dflash_profile_end(dflash_handle* h, float* total_ms, int32_t* launches) {
+  if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
+  if (!total_ms || !launches) return fail(DFLASH_E_INVALID, "output arrays are NULL");
+  Profiler& p = h->prof;
+  for (int k = 0; k < DFLASH_KERNEL_COUNT; ++k) {
+    total_ms[k] = 0.f;
+    launches[k] = 0;
+  }
+  dflash_status st = DFLASH_OK;
+  if (!p.marks.empty()) {
+    hipError_t e = hipEventSynchronize(p.pool[p.marks.back().second + 1]);
+    if (e) st = hip_fail(e, "profile sync");
+    for (const auto& m : p.marks) {
+      float ms = 0.f;
+      if (!st && (e = hipEventElapsedTime(&ms, p.pool[m.second], p.pool[m.second + 1]))) {
+        st = hip_fail(e, "profile elapsed");
+        break;
+      }
+      total_ms[m.first] += ms;
+      launches[m.first] += 1;
+    }
+  }
+  p.mask = 0;
+  p.used = 0;
+  p.marks.clear();
+  return st;
 }
 
 dflash_status dflash_check(dflash_handle* h, void* stream) {

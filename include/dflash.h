@@ -227,6 +227,37 @@ dflash_status dflash_verify_accept(dflash_handle *h, void *stream, int32_t n_req
                                    int32_t *accept_len, int32_t *committed,
                                    int32_t *last_token);
 
+/* Kernel classes for optional launch timing. */
+typedef enum {
+  DFLASH_KERNEL_FC_GEMM = 0,     /* inject: concat + projection */
+  DFLASH_KERNEL_NORM = 1,        /* every RMSNorm */
+  DFLASH_KERNEL_KV_GEMM = 2,     /* inject: all-layer K/V projection */
+  DFLASH_KERNEL_SCATTER = 3,     /* inject: RoPE + page scatter */
+  DFLASH_KERNEL_QKV_GEMM = 4,
+  DFLASH_KERNEL_QKV_POST = 5,    /* block q/k RoPE, block KV page */
+  DFLASH_KERNEL_ATTN = 6,
+  DFLASH_KERNEL_COMBINE = 7,
+  DFLASH_KERNEL_O_GEMM = 8,
+  DFLASH_KERNEL_GATEUP_GEMM = 9,
+  DFLASH_KERNEL_DOWN_GEMM = 10,
+  DFLASH_KERNEL_LM_HEAD = 11,    /* vocabulary GEMM + argmax */
+  DFLASH_KERNEL_FINALIZE = 12,
+  DFLASH_KERNEL_VERIFY = 13,
+  DFLASH_KERNEL_COUNT = 14
+} dflash_kernel;
+
+/* Launch timing for measurement runs.  After dflash_profile_begin(h, mask),
+ * every launch of a kernel class whose bit (1 << dflash_kernel) is set in
+ * `mask` is bracketed by two HIP events recorded on the call's stream (the
+ * stream the kernel runs on).  dflash_profile_end synchronises on the last
+ * event, writes per class the summed duration in milliseconds and the
+ * launch count to total_ms[0..DFLASH_KERNEL_COUNT) and
+ * launches[0..DFLASH_KERNEL_COUNT) (host arrays), and turns timing off.
+ * Events are created on first use and kept by the handle; no device memory
+ * is allocated.  Timing off (the default) adds nothing to a call. */
+dflash_status dflash_profile_begin(dflash_handle *h, uint32_t mask);
+dflash_status dflash_profile_end(dflash_handle *h, float *total_ms, int32_t *launches);
+
 /* Synchronises `stream` and reads the sticky device error word; returns
  * DFLASH_E_DEVICE (and clears the word) if a kernel recorded an
  * out-of-range token id, else DFLASH_OK. */
