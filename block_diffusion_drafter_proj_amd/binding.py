@@ -74,8 +74,9 @@ def lib() -> ctypes.CDLL:
             "dflash_feature_layers": (i32, [i32, i32, pi32]),
             "dflash_workspace_bytes": (sz, [ctypes.POINTER(DFlashConfig)]),
             "dflash_kv_pool_bytes": (sz, [ctypes.POINTER(DFlashConfig)]),
+            "dflash_packed_weights_bytes": (sz, [ctypes.POINTER(DFlashConfig)]),
             "dflash_create": (i32, [ctypes.POINTER(DFlashConfig), ctypes.POINTER(DFlashWeights),
-                                    vp, vp, ctypes.POINTER(vp)]),
+                                    vp, vp, vp, ctypes.POINTER(vp)]),
             "dflash_destroy": (None, [vp]),
             "dflash_bind_request": (i32, [vp, i32, pi32, i32, i32]),
             "dflash_context_length": (i32, [vp, i32]),
@@ -130,10 +131,14 @@ def dflash_kv_pool_bytes(cfg: DFlashConfig) -> int:
     return int(lib().dflash_kv_pool_bytes(ctypes.byref(cfg)))
 
 
-def dflash_create(cfg: DFlashConfig, w: DFlashWeights, kv_pool: int, workspace: int) -> int:
+def dflash_packed_weights_bytes(cfg: DFlashConfig) -> int:
+    return int(lib().dflash_packed_weights_bytes(ctypes.byref(cfg)))
+
+
+def dflash_create(cfg: DFlashConfig, w: DFlashWeights, kv_pool: int, workspace: int, packed: int) -> int:
     h = ctypes.c_void_p()
     _check(lib().dflash_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(kv_pool),
-                               ctypes.c_void_p(workspace), ctypes.byref(h)))
+                               ctypes.c_void_p(workspace), ctypes.c_void_p(packed), ctypes.byref(h)))
     return h.value
 
 

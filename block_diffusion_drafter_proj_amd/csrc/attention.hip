@@ -47,6 +47,12 @@ __global__ __launch_bounds__(256) void k_qkv_post(QkvPostParams p, SlotArgs sl) 
   const int ld = (p.Hq + 2 * p.Hkv) * DH;
   const int n = p.state[sl.slots[r]].ctx_len + 1;
   const float* src = p.qkv + (long long)r * p.B * ld + hh * DH;
+  const long long plane = (long long)gridDim.x * p.B * ld;
+  auto rd = [&](long long off) {
+    float x = 0.f;
+    for (int q = 0; q < p.n_part; ++q) x += src[q * plane + off];
+    return x;
+  };
   constexpr int H2 = DH / 2;
   const long long page_elems = 2LL * p.Hkv * 16 * DH;
   if (hh < p.Hq + p.Hkv) {
@@ -60,8 +66,8 @@ __global__ __launch_bounds__(256) void k_qkv_post(QkvPostParams p, SlotArgs sl) 
       const int j = e - i * H2;
       float y1 = 0.f, y2 = 0.f;
       if (i < p.B) {
-        const float x1 = src[(long long)i * ld + j];
-        const float x2 = src[(long long)i * ld + j + H2];
+        const float x1 = rd((long long)i * ld + j);
+        const float x2 = rd((long long)i * ld + j + H2);
         const long long ti = (long long)(n + i) * H2 + j;
         const float c = p.cos_t[ti], s = p.sin_t[ti];
         y1 = x1 * c - x2 * s;
@@ -76,7 +82,7 @@ __global__ __launch_bounds__(256) void k_qkv_post(QkvPostParams p, SlotArgs sl) 
     for (int e = t; e < 16 * DH; e += 256) {
       const int i = e & 15;
       const int d = e >> 4;
-      const float x = i < p.B ? src[(long long)i * ld + d] : 0.f;
+      const float x = i < p.B ? rd((long long)i * ld + d) : 0.f;
       dst[d * 16 + i] = from_f<T>(x);
     }
   }
@@ -289,12 +295,18 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterParams p) {
   const long long page_elems = 2LL * p.Hkv * 16 * DH;
   T* pg = reinterpret_cast<T*>(p.pool) + l * p.layer_stride + page * page_elems;
   const float* src = p.kv + (long long)row * (p.L * 2 * p.Hkv * DH) + (long long)l * 2 * p.Hkv * DH;
+  const long long plane = (long long)p.rows * p.L * 2 * p.Hkv * DH;
+  auto rd = [&](int off) {
+    float x = 0.f;
+    for (int q = 0; q < p.n_part; ++q) x += src[q * plane + off];
+    return x;
+  };
   const int slotpos = pos & 15;
   for (int e = t; e < p.Hkv * H2; e += 256) {
     const int g = e / H2;
     const int j = e - g * H2;
-    const float x1 = src[g * DH + j];
-    const float x2 = src[g * DH + j + H2];
+    const float x1 = rd(g * DH + j);
+    const float x2 = rd(g * DH + j + H2);
     const long long ti = (long long)pos * H2 + j;
     const float c = p.cos_t[ti], s = p.sin_t[ti];
     T* kd = pg + (long long)(g * 16 + slotpos) * DH;
@@ -304,7 +316,7 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterParams p) {
   for (int e = t; e < p.Hkv * DH; e += 256) {
     const int g = e / DH;
     const int d = e - g * DH;
-    pg[(long long)(p.Hkv + g) * 16 * DH + d * 16 + slotpos] = from_f<T>(src[(p.Hkv + g) * DH + d]);
+    pg[(long long)(p.Hkv + g) * 16 * DH + d * 16 + slotpos] = from_f<T>(rd((p.Hkv + g) * DH + d));
   }
 }
 

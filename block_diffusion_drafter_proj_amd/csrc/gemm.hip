@@ -1,22 +1,28 @@
 // Weight-streaming GEMM for the draft's skinny products (M = batch * block rows).
 //
-// Y[M, N] = X[M, K] * W[N, K]^T.  At batch 1 every projection of the draft
-// forward is bound by streaming W from HBM (16 rows of activations against
-// each weight: 16 flop per byte), so the kernel is built around the weight
-// stream:
-//  * one workgroup (4 waves) owns a 16-row tile of W (two tiles for SwiGLU:
-//    gate and up rows of the same output columns);
-//  * the 4 waves split K in interleaved 256-element chunks; a lane streams 8
-//    contiguous 16-byte pieces of its W row per chunk (each wave reads 16
-//    rows x 512 contiguous bytes per chunk) while the next chunk is already
-//    in flight;
-//  * the products run on MFMA 16x16x32 bf16 (16x16x4 f32 for fp32 weights),
-//    the activation tile is the A operand read through L2;
-//  * the 4 per-wave partial tiles are summed through LDS in a fixed order
-//    (deterministic) and the epilogue is applied once per output.
-// Epilogues: plain fp32 store; residual add into the fp32 stream; SwiGLU
-// (silu(gate) * up, rounded to the storage dtype); greedy selection (packed
-// logit/id key, 64-bit atomic max per row, ties to the lowest id).
+// Y[M, N] = X[M, K] * W[N, K]^T.  At batch 1 every projection of the draft is
+// bound by streaming W from HBM (16 activation rows per weight: 16 flop per
+// byte), so the kernel is built around the weight stream:
+//
+//  * W is packed once (k_pack) into MFMA fragment order,
+//      Wp[tile][kstep][lane][8],  tile = 16 output rows, kstep = 32 of K,
+//    lane l holding row 16*tile + l%16, k = 32*kstep + 8*(l/16) .. +8, so one
+//    wave's fragment is 1 KB of contiguous memory (bf16).
+//  * A workgroup of NW waves (up to 16, one workgroup per CU) owns one K range
+//    (split p of P) and a strided set of output tiles.  Wave w owns KS
+//    k-steps of that range; its activation fragments for them are loaded once
+//    into registers.  For every tile the wave then streams KS contiguous
+//    fragments (KS KB) of W through a register ring of NBUF tiles, so the next
+//    tiles' weights are in flight while the current one is multiplied.
+//  * MFMA 16x16x32 bf16 (16x16x4 f32 for fp32 weights); the NW per-wave
+//    partial tiles are summed through LDS in a fixed order (deterministic),
+//    once per tile, and the epilogue runs once per output element.
+//
+// Epilogues: split-K partials (fp32, summed by the consuming kernel); residual
+// add; SwiGLU (gate and up tiles processed back to back, silu(gate) * up
+// rounded to the storage dtype); greedy selection (packed logit/id key,
+// running max per row across the workgroup's tiles, one 64-bit atomic max per
+// row and workgroup, ties to the lowest id).
 #include "common.h"
 #include "kernels.h"
 
@@ -24,175 +30,246 @@ namespace dflash {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kChunk = 256;
+constexpr int kFragElems = 64 * 8;  // elements of one wave fragment
 
-template <typename T>
-struct WRow {
-  const T* p;
-  bool ok;
+template <typename T, int MT>
+struct Shape {
+  static constexpr int KS = (sizeof(T) == 2 && MT == 1) ? 8 : 4;  // k-steps per wave per tile
+  static constexpr int NBUF = (sizeof(T) == 2 ? 16 : 8) / KS;     // tiles in the W ring
 };
 
-template <typename T>
-__device__ __forceinline__ void load_w(typename Frag8<T>::type (&w)[8], const T* row, bool ok,
-                                       int k0, int g) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) w[j] = ok ? load8<T>(row + k0 + 32 * j + 8 * g) : zero8<T>();
-}
-
-template <typename T>
-__device__ __forceinline__ const T* a_ptr(const GemmParams& p, int m, int k0) {
-  int part = k0 / p.a_part_k;
-  const T* base = reinterpret_cast<const T*>(p.a[part]);
-  return base + (long long)m * p.lda + (k0 - part * p.a_part_k);
-}
-
 template <typename T, int MT, int EPI>
-__global__ __launch_bounds__(256) void k_gemm(GemmParams p) {
-  constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
+__global__ __launch_bounds__(1024) void k_gemm(GemmParams p) {
+  constexpr int KS = Shape<T, MT>::KS;
+  constexpr int NBUF = Shape<T, MT>::NBUF;
+  constexpr int NSUB = (EPI == EPI_SWIGLU) ? 2 : 1;
   typedef typename Frag8<T>::type Frag;
-  __shared__ float red[kWaves][MT * NACC][16][17];
+  __shared__ float red[2][16][MT][256];
 
+  const int NW = blockDim.x >> 6;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const int tile = blockIdx.x;
+  const int GP = gridDim.x / p.P;
+  const int pidx = blockIdx.x / GP;
+  const int bl = blockIdx.x - pidx * GP;
+  const int S = p.K / 32;
+  const int s0 = pidx * (S / p.P) + wave * KS;
   const int m_base = blockIdx.y * 16 * MT;
-  const int n0 = tile * 16;
+  const int n_units = bl < p.tiles ? (p.tiles - 1 - bl) / GP + 1 : 0;
+  const int n_sub = n_units * NSUB;
 
-  // weight rows of this lane
-  const int seg = n0 / p.seg_rows;
-  const int seg_row = n0 - seg * p.seg_rows + r16;
-  const bool w_ok = (n0 + r16) < p.N;
-  const T* wrow = reinterpret_cast<const T*>(p.w[seg]) + (long long)seg_row * p.K;
-  const T* urow = (EPI == EPI_SWIGLU)
-                      ? reinterpret_cast<const T*>(p.w_up) + (long long)(n0 + r16) * p.K
-                      : nullptr;
-
-  bool a_ok[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) a_ok[mt] = (m_base + mt * 16 + r16) < p.M;
-
-  f32x4 acc[MT][NACC];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int q = 0; q < NACC; ++q) acc[mt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nchunks = p.K / kChunk;
-  Frag wc[8], wn[8];
-  Frag uc[8], un[8];
-  int c = wave;
-  if (c < nchunks) {
-    load_w<T>(wc, wrow, w_ok, c * kChunk, g);
-    if (EPI == EPI_SWIGLU) load_w<T>(uc, urow, w_ok, c * kChunk, g);
-  }
-  for (; c < nchunks; c += kWaves) {
-    const int k0 = c * kChunk;
-    const bool more = (c + kWaves) < nchunks;
-    if (more) {
-      load_w<T>(wn, wrow, w_ok, k0 + kWaves * kChunk, g);
-      if (EPI == EPI_SWIGLU) load_w<T>(un, urow, w_ok, k0 + kWaves * kChunk, g);
-    }
+  // activation fragments of this wave's k-steps, loaded once
+  Frag af[MT][KS];
+  {
+    const int k0 = s0 * 32;
+    const int part = k0 / p.a_part_k;
+    const T* abase = reinterpret_cast<const T*>(p.a[part]) + (k0 - part * p.a_part_k) + 8 * g;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const T* ar = a_ptr<T>(p, m_base + mt * 16 + r16, k0);
+      const int m = m_base + mt * 16 + r16;
+      const bool ok = m < p.M;
+      const T* ar = abase + (long long)m * p.lda;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        Frag a = a_ok[mt] ? load8<T>(ar + 32 * j + 8 * g) : zero8<T>();
-        acc[mt][0] = mfma_step(a, wc[j], acc[mt][0]);
-        if (EPI == EPI_SWIGLU) acc[mt][NACC - 1] = mfma_step(a, uc[j], acc[mt][NACC - 1]);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        wc[j] = wn[j];
-        if (EPI == EPI_SWIGLU) uc[j] = un[j];
-      }
+      for (int j = 0; j < KS; ++j) af[mt][j] = ok ? load8<T>(ar + 32 * j) : zero8<T>();
     }
   }
 
-  // cross-wave reduction (fixed order)
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int q = 0; q < NACC; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][mt * NACC + q][4 * g + i][r16] = acc[mt][q][i];
-  __syncthreads();
+  auto wsrc = [&](int sub) -> const T* {
+    const int u = sub / NSUB;
+    int t = bl + u * GP;
+    if (EPI == EPI_SWIGLU && (sub & 1)) t += p.up_tile_off;
+    int seg = 0, lt = t;
+    if (p.seg_tiles) {
+      seg = t / p.seg_tiles;
+      lt = t - seg * p.seg_tiles;
+    }
+    return reinterpret_cast<const T*>(p.w[seg]) + ((long long)lt * S + s0) * kFragElems + lane * 8;
+  };
 
+  Frag wb[NBUF][KS];
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b) {
+    if (b < n_sub) {
+      const T* src = wsrc(b);
+#pragma unroll
+      for (int j = 0; j < KS; ++j) wb[b][j] = load8<T>(src + j * kFragElems);
+    }
+  }
+
+  // epilogue: element e = t + it * blockDim of the 16 x 16 tile (per m-tile);
+  // workgroups with fewer than 4 waves take several elements per thread
   const int t = threadIdx.x;
-  const int row = t >> 4;
-  const int col = t & 15;
-  const int n = n0 + col;
+  constexpr int EIT = 4 * MT;  // iterations for the smallest workgroup (one wave)
+  float gate_v[EIT];
+  unsigned long long best[EIT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    float v[NACC];
+  for (int it = 0; it < EIT; ++it) {
+    gate_v[it] = 0.f;
+    best[it] = 0ull;
+  }
+
+  for (int i = 0; i < n_sub; i += NBUF) {
 #pragma unroll
-    for (int q = 0; q < NACC; ++q) {
-      float s = 0.f;
+    for (int b = 0; b < NBUF; ++b) {
+      const int sub = i + b;
+      if (sub < n_sub) {
+        f32x4 acc[MT];
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) s += red[w][mt * NACC + q][row][col];
-      v[q] = s;
-    }
-    const int m = m_base + mt * 16 + row;
-    const bool ok = (m < p.M) && (n < p.N);
-    if (EPI == EPI_STORE) {
-      if (ok) p.out_f32[(long long)m * p.ldo + n] = v[0];
-    } else if (EPI == EPI_RESID) {
-      if (ok) p.resid[(long long)m * p.ldr + n] += v[0];
-    } else if (EPI == EPI_SWIGLU) {
-      if (ok) {
-        float gt = v[0];
-        float s = gt / (1.0f + expf(-gt));
-        reinterpret_cast<T*>(p.out_t)[(long long)m * p.ldt + n] = from_f<T>(s * v[NACC - 1]);
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_step(af[mt][j], wb[b][j], acc[mt]);
+        if (sub + NBUF < n_sub) {
+          const T* src = wsrc(sub + NBUF);
+#pragma unroll
+          for (int j = 0; j < KS; ++j) wb[b][j] = load8<T>(src + j * kFragElems);
+        }
+        const int rb = sub & 1;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) red[rb][wave][mt][(4 * g + q) * 16 + r16] = acc[mt][q];
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < EIT; ++it) {
+          const int e = t + it * (int)blockDim.x;
+          if (e >= 256 * MT) break;
+          const int emt = e >> 8;
+          const int ecol = e & 15;
+          const int em = m_base + emt * 16 + ((e >> 4) & 15);
+          float v = 0.f;
+          for (int w2 = 0; w2 < NW; ++w2) v += red[rb][w2][emt][e & 255];
+          const int u = sub / NSUB;
+          const int tile = bl + u * GP;
+          const int n = tile * 16 + ecol;
+          const bool ok = em < p.M && n < p.N;
+          if (EPI == EPI_PARTIAL) {
+            if (ok) p.out_f32[((long long)pidx * p.M + em) * p.N + n] = v;
+          } else if (EPI == EPI_RESID) {
+            if (ok) p.resid[(long long)em * p.ldr + n] += v;
+          } else if (EPI == EPI_SWIGLU) {
+            if (!(sub & 1)) {
+              gate_v[it] = v;
+            } else if (ok) {
+              const float g0 = gate_v[it];
+              const float sg = g0 / (1.0f + expf(-g0));
+              reinterpret_cast<T*>(p.out_t)[(long long)em * p.ldt + n] = from_f<T>(sg * v);
+            }
+          } else {  // EPI_ARGMAX: all 16 columns of a row sit in 16 adjacent lanes
+            if (ok && p.dbg) p.dbg[(long long)em * p.ld_dbg + n] = v;
+            unsigned long long key = ok ? argmax_key(v, n, p.N) : 0ull;
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) {
+              const unsigned long long other = __shfl_xor(key, o, 64);
+              key = other > key ? other : key;
+            }
+            best[it] = key > best[it] ? key : best[it];
+          }
+        }
       }
-    } else {  // EPI_ARGMAX
-      if (ok && p.dbg) p.dbg[(long long)m * p.ld_dbg + n] = v[0];
-      unsigned long long key = ok ? argmax_key(v[0], n, p.N) : 0ull;
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) {
-        unsigned long long other = __shfl_xor(key, o, 64);
-        key = other > key ? other : key;
-      }
-      if (col == 0 && m < p.M) atomicMax(p.keys + m, key);
     }
   }
-}
-
-template <typename T, int EPI>
-void launch_t(const GemmParams& p, hipStream_t s) {
-  const int tiles = (p.N + 15) / 16;
-  const int mt = p.M <= 16 ? 1 : (p.M <= 32 ? 2 : 4);
-  dim3 grid(tiles, (p.M + 16 * mt - 1) / (16 * mt));
-  if (mt == 1)
-    hipLaunchKernelGGL((k_gemm<T, 1, EPI>), grid, dim3(256), 0, s, p);
-  else if (mt == 2)
-    hipLaunchKernelGGL((k_gemm<T, 2, EPI>), grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((k_gemm<T, 4, EPI>), grid, dim3(256), 0, s, p);
+  if (EPI == EPI_ARGMAX && n_units > 0) {
+#pragma unroll
+    for (int it = 0; it < EIT; ++it) {
+      const int e = t + it * (int)blockDim.x;
+      if (e >= 256 * MT) break;
+      const int em = m_base + (e >> 8) * 16 + ((e >> 4) & 15);
+      if ((e & 15) == 0 && em < p.M) atomicMax(p.keys + em, best[it]);
+    }
+  }
 }
 
 template <typename T>
-void launch_dt(int epi, const GemmParams& p, hipStream_t s) {
+__global__ __launch_bounds__(256) void k_pack(const T* src, T* dst, int N, int K, long long total) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int S = K / 32;
+  const int l = (int)(idx & 63);
+  const long long ts = idx >> 6;
+  const int s = (int)(ts % S);
+  const long long tile = ts / S;
+  const long long row = tile * 16 + (l & 15);
+  const int k = s * 32 + 8 * (l >> 4);
+  typedef typename Frag8<T>::type Frag;
+  const Frag v = row < N ? load8<T>(src + row * K + k) : zero8<T>();
+  *reinterpret_cast<Frag*>(dst + idx * 8) = v;
+}
+
+template <typename T, int EPI>
+void launch_t(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
+  // 16-row m-blocks; rows beyond 16 re-stream W (a batched kernel would not)
+  dim3 grid(pl.GP * p.P, (p.M + 15) / 16);
+  dim3 block(64 * pl.NW);
+  hipLaunchKernelGGL((k_gemm<T, 1, EPI>), grid, block, 0, s, p);
+}
+
+template <typename T>
+void launch_dt(int epi, const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
   switch (epi) {
-    case EPI_STORE: launch_t<T, EPI_STORE>(p, s); break;
-    case EPI_RESID: launch_t<T, EPI_RESID>(p, s); break;
-    case EPI_SWIGLU: launch_t<T, EPI_SWIGLU>(p, s); break;
-    default: launch_t<T, EPI_ARGMAX>(p, s); break;
+    case EPI_PARTIAL: launch_t<T, EPI_PARTIAL>(pl, p, s); break;
+    case EPI_RESID: launch_t<T, EPI_RESID>(pl, p, s); break;
+    case EPI_SWIGLU: launch_t<T, EPI_SWIGLU>(pl, p, s); break;
+    default: launch_t<T, EPI_ARGMAX>(pl, p, s); break;
   }
 }
 
 }  // namespace
 
-void launch_gemm(int dtype, int epi, const GemmParams& p, hipStream_t s) {
-  if (p.M <= 0 || p.N <= 0) return;
+int gemm_kblock(int dtype, int M) {
+  (void)M;
+  return 32 * (dtype == DFLASH_BF16 ? Shape<bf16, 1>::KS : Shape<float, 1>::KS);
+}
+
+// Split-K factor P, waves per workgroup NW and workgroups per split GP for a
+// GEMM of `tiles` 16-row output tiles over K.  Minimises the per-workgroup
+// stream (units per workgroup x K / P) with at most 256 workgroups (one per
+// CU), penalising fewer than 8 waves per workgroup.
+GemmPlan plan_gemm(int tiles, int K, int kblock, bool single_split) {
+  GemmPlan best{0, 0, 0};
+  double best_cost = 1e300;
+  const int kb = K / kblock;
+  for (int P = 1; P <= kb; ++P) {
+    if (kb % P) continue;
+    const int NW = kb / P;
+    if (NW > 16) continue;
+    if (single_split && P != 1) break;
+    const int gp_max = 256 / P;
+    if (gp_max < 1) break;
+    const int units = (tiles + gp_max - 1) / gp_max;
+    const int GP = (tiles + units - 1) / units;
+    const double eff = NW >= 8 ? 1.0 : NW / 8.0;
+    const double cost = (double)units * K / P / eff;
+    if (cost < best_cost * 0.999) {
+      best_cost = cost;
+      best = GemmPlan{P, NW, GP};
+    }
+  }
+  return best;
+}
+
+void launch_gemm(int dtype, int epi, const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
+  if (p.M <= 0 || p.tiles <= 0) return;
   if (dtype == DFLASH_BF16)
-    launch_dt<bf16>(epi, p, s);
+    launch_dt<bf16>(epi, pl, p, s);
   else
-    launch_dt<float>(epi, p, s);
+    launch_dt<float>(epi, pl, p, s);
+}
+
+size_t packed_elems(int N, int K) { return (size_t)((N + 15) / 16) * 16 * (size_t)K; }
+
+void launch_pack(int dtype, const void* src, void* dst, int N, int K, hipStream_t s) {
+  const long long total = (long long)((N + 15) / 16) * (K / 32) * 64;
+  const int blocks = (int)((total + 255) / 256);
+  if (dtype == DFLASH_BF16)
+    hipLaunchKernelGGL(k_pack<bf16>, dim3(blocks), dim3(256), 0, s,
+                       reinterpret_cast<const bf16*>(src), reinterpret_cast<bf16*>(dst), N, K, total);
+  else
+    hipLaunchKernelGGL(k_pack<float>, dim3(blocks), dim3(256), 0, s,
+                       reinterpret_cast<const float*>(src), reinterpret_cast<float*>(dst), N, K, total);
 }
 
 }  // namespace dflash

@@ -11,24 +11,25 @@ namespace dflash {
 constexpr int kMaxSeg = DFLASH_MAX_LAYERS;
 constexpr int kMaxChunkReq = 64;  // requests per inject scatter launch
 
-enum Epilogue { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
+enum Epilogue { EPI_PARTIAL = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
 
-// Y[M, N] = X[M, K] * W[N, K]^T with a fused epilogue.
+// Y[M, N] = X[M, K] * W[N, K]^T with a fused epilogue, W packed by launch_pack.
 //  X: virtual concatenation along k of a_parts row-major arrays, each
 //     [M, a_part_k] with row stride lda (elements).
-//  W: row-major; rows [s*seg_rows, (s+1)*seg_rows) live at w[s].  With one
-//     segment seg_rows may be any N (the last 16-row tile is guarded).
+//  W: packed 16-row tiles; tile t lives in segment t / seg_tiles at w[seg]
+//     (seg_tiles = 0: one segment holding every tile).
+//  P: split-K factor; EPI_PARTIAL writes out_f32[p][M][N] for each split.
 struct GemmParams {
   const void* a[DFLASH_MAX_FEAT];
   int a_parts, a_part_k, lda;
   int M;
   const void* w[kMaxSeg];
-  const void* w_up;  // EPI_SWIGLU: up-projection rows, same layout as w[0]
-  int seg_rows;
-  int N, K;
-  float* out_f32;  // EPI_STORE
-  int ldo;
-  void* out_t;  // EPI_SWIGLU (storage dtype)
+  int seg_tiles;
+  int tiles;  // output tiles (ceil(N / 16)); SwiGLU: gate tiles
+  int N, K, P;
+  int up_tile_off;  // EPI_SWIGLU: tile offset of the up rows in the packed matrix
+  float* out_f32;   // EPI_PARTIAL
+  void* out_t;      // EPI_SWIGLU (storage dtype)
   int ldt;
   float* resid;  // EPI_RESID
   int ldr;
@@ -37,18 +38,26 @@ struct GemmParams {
   int ld_dbg;
 };
 
-// Row-wise RMSNorm of fp32 rows into the storage dtype.
+struct GemmPlan {
+  int P, NW, GP;  // split-K factor, waves per workgroup, workgroups per split
+};
+
+// Row-wise RMSNorm of fp32 rows into the storage dtype.  The input row is
+//   x = (init_row ? init_row : x_in ? x_in[row] : 0) + sum_p part[p][row]
+// and is written back to x_out[row] when x_out is set.
 struct NormParams {
-  const float* x;      // [M, d] fp32 (ignored when init_row is set)
-  float* x_init;       // when init_row: receives init_row in every row
-  const void* init_row;  // storage dtype [d]: every row starts from it
+  const float* x_in;       // [M, ld] fp32 residual, or NULL
+  const void* init_row;    // storage dtype [d]: every row starts from it, or NULL
+  const float* part;       // [n_part][M][d] fp32 split-K partials, or NULL
+  int n_part;
+  float* x_out;            // [M, ld] receives x, or NULL
   int ldx;
   const void* gamma;  // storage dtype [d]
   float eps;
   void* out;  // storage dtype [M, d]
   int ldo;
   int d, M;
-  float* dbg;  // optional fp32 copy of the input rows [M, d]
+  float* dbg;  // optional fp32 copy of x [M, d]
   unsigned long long* zero_keys;  // optional: keys[row] = 0
 };
 
@@ -62,7 +71,8 @@ struct SlotState {
 };
 
 struct QkvPostParams {
-  const float* qkv;  // [n_req*B, (Hq+2Hkv)*dh]
+  const float* qkv;  // [n_part][n_req*B, (Hq+2Hkv)*dh] split-K partials
+  int n_part;
   int B, Hq, Hkv;
   const SlotState* state;
   const float* cos_t;  // [max_position, dh/2]
@@ -101,7 +111,8 @@ struct InjectReq {
   int row_start, count, slot, pos0, final_ctx;
 };
 struct ScatterParams {
-  const float* kv;  // [rows, L*2*Hkv*dh]
+  const float* kv;  // [n_part][rows, L*2*Hkv*dh] split-K partials
+  int n_part;
   int rows, L, Hkv;
   int n_req;
   InjectReq req[kMaxChunkReq];
@@ -117,7 +128,11 @@ struct ScatterParams {
   unsigned int* err;
 };
 
-void launch_gemm(int dtype, int epi, const GemmParams& p, hipStream_t s);
+int gemm_kblock(int dtype, int M);
+GemmPlan plan_gemm(int tiles, int K, int kblock, bool single_split);
+void launch_gemm(int dtype, int epi, const GemmPlan& pl, const GemmParams& p, hipStream_t s);
+size_t packed_elems(int N, int K);
+void launch_pack(int dtype, const void* src, void* dst, int N, int K, hipStream_t s);
 void launch_rmsnorm(int dtype, const NormParams& p, hipStream_t s);
 void launch_qkv_post(int dtype, int dh, int n_req, const QkvPostParams& p, const SlotArgs& sl,
                      hipStream_t s);

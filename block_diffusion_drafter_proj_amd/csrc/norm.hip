@@ -24,17 +24,19 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormParams p) {
   const T* init = reinterpret_cast<const T*>(p.init_row);
   const T* gamma = reinterpret_cast<const T*>(p.gamma);
   T* out = reinterpret_cast<T*>(p.out) + (long long)row * p.ldo;
+  const long long plane = (long long)p.M * p.d;
+
+  auto input = [&](int k) {
+    float x = init ? to_f(init[k]) : (p.x_in ? p.x_in[(long long)row * p.ldx + k] : 0.f);
+    for (int q = 0; q < p.n_part; ++q) x += p.part[q * plane + (long long)row * p.d + k];
+    return x;
+  };
 
   float ss = 0.f;
   for (int i = 0; i < per; ++i) {
     const int k = t + 256 * i;
-    float x;
-    if (init) {
-      x = to_f(init[k]);
-      p.x_init[(long long)row * p.ldx + k] = x;
-    } else {
-      x = p.x[(long long)row * p.ldx + k];
-    }
+    const float x = input(k);
+    if (p.x_out) p.x_out[(long long)row * p.ldx + k] = x;
     if (p.dbg) p.dbg[(long long)row * p.d + k] = x;
     ss += x * x;
   }
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormParams p) {
   const float r = 1.0f / sqrtf(tot / (float)p.d + p.eps);
   for (int i = 0; i < per; ++i) {
     const int k = t + 256 * i;
-    const float x = init ? to_f(init[k]) : p.x[(long long)row * p.ldx + k];
+    const float x = p.x_out ? p.x_out[(long long)row * p.ldx + k] : input(k);
     out[k] = from_f<T>(x * r * to_f(gamma[k]));
   }
   if (p.zero_keys && t == 0) p.zero_keys[row] = 0ull;

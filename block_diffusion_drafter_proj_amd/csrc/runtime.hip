@@ -48,9 +48,38 @@ size_t elt(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
 // Upper bound of (requests x attention splits) handled in one draft call.
 int part_pairs(const dflash_config& c) { return c.max_batch + (512 + c.n_kv_heads - 1) / c.n_kv_heads; }
 
+// Split-K factors of every GEMM (fixed by the shapes; the workspace holds
+// their partial planes).
+struct Plans {
+  GemmPlan qkv, o, gateup, down, lm, fc, kv;
+};
+
+int tiles_of(int n) { return (n + 15) / 16; }
+
+Plans make_plans(const dflash_config& c, int M) {
+  const int kb = gemm_kblock(c.dtype, M);
+  const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
+  const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  Plans p;
+  p.qkv = plan_gemm(tiles_of(qkvw), d, kb, false);
+  p.o = plan_gemm(tiles_of(d), qd, kb, false);
+  p.gateup = plan_gemm(tiles_of(c.ffn), d, kb, true);
+  p.down = plan_gemm(tiles_of(d), c.ffn, kb, false);
+  p.lm = plan_gemm(tiles_of(c.vocab), d, kb, true);
+  p.fc = plan_gemm(tiles_of(d), c.n_feat * d, kb, false);
+  p.kv = plan_gemm(c.n_layers * tiles_of(2 * c.n_kv_heads * c.head_dim), d, kb, false);
+  return p;
+}
+
+int max_p(const dflash_config& c, GemmPlan Plans::*f) {
+  int m = 1;
+  for (int M : {1, 1024}) m = std::max(m, (make_plans(c, M).*f).P);
+  return m;
+}
+
 struct Layout {
   size_t state, err, page_table, cos_t, sin_t;
-  size_t h, xa, xo, qkv, qb, blk, part_o, part_ml, z, keys;
+  size_t h, xa, xo, qkv, qb, blk, part_o, part_ml, z, keys, opart, dpart;
   size_t u, f, kvo;
   size_t total;
 };
@@ -77,7 +106,7 @@ Layout make_layout(const dflash_config& c) {
   L.h = take(sizeof(float) * M * c.hidden);
   L.xa = take(e * M * c.hidden);
   L.xo = take(e * M * qd);
-  L.qkv = take(sizeof(float) * M * qkvw);
+  L.qkv = take(sizeof(float) * max_p(c, &Plans::qkv) * M * qkvw);
   L.qb = take(e * (size_t)c.max_batch * c.n_q_heads * 16 * c.head_dim);
   L.blk = take(e * (size_t)c.max_batch * page_elems);
   const size_t pp = (size_t)part_pairs(c) * c.n_q_heads * 16;
@@ -85,11 +114,43 @@ Layout make_layout(const dflash_config& c) {
   L.part_ml = take(sizeof(float) * pp * 2);
   L.z = take(e * M * c.ffn);
   L.keys = take(sizeof(unsigned long long) * M);
-  L.u = take(sizeof(float) * R * c.hidden);
+  L.opart = take(sizeof(float) * max_p(c, &Plans::o) * M * c.hidden);
+  L.dpart = take(sizeof(float) * max_p(c, &Plans::down) * M * c.hidden);
+  L.u = take(sizeof(float) * max_p(c, &Plans::fc) * R * c.hidden);
   L.f = take(e * R * c.hidden);
-  L.kvo = take(sizeof(float) * R * (size_t)c.n_layers * 2 * c.n_kv_heads * c.head_dim);
+  L.kvo = take(sizeof(float) * max_p(c, &Plans::kv) * R * (size_t)c.n_layers * 2 * c.n_kv_heads * c.head_dim);
   L.total = off;
   return L;
+}
+
+// Packed (MFMA fragment order) copies of every weight matrix.
+struct PackedLayout {
+  size_t lm_head, fc, wqkv[DFLASH_MAX_LAYERS], wo[DFLASH_MAX_LAYERS], wgateup[DFLASH_MAX_LAYERS],
+      wdown[DFLASH_MAX_LAYERS];
+  size_t total;
+};
+
+PackedLayout make_packed(const dflash_config& c) {
+  PackedLayout P{};
+  size_t off = 0;
+  const size_t e = elt(c);
+  auto take = [&](int N, int K) {
+    size_t o = off;
+    off = align_up(off + packed_elems(N, K) * e);
+    return o;
+  };
+  const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
+  const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  P.lm_head = take(c.vocab, d);
+  P.fc = take(d, c.n_feat * d);
+  for (int l = 0; l < c.n_layers; ++l) {
+    P.wqkv[l] = take(qkvw, d);
+    P.wo[l] = take(d, qd);
+    P.wgateup[l] = take(2 * c.ffn, d);
+    P.wdown[l] = take(d, c.ffn);
+  }
+  P.total = off;
+  return P;
 }
 
 dflash_status validate(const dflash_config* c) {
@@ -121,6 +182,10 @@ dflash_status validate(const dflash_config* c) {
   if (c->max_position < c->block_size + 2) return bad("max_position too small");
   if (c->max_inject_rows < 1) return bad("max_inject_rows must be positive");
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) return bad("rms_eps and rope_theta must be positive");
+  // the LM head and SwiGLU GEMMs run unsplit: K = hidden must fit 16 waves
+  const int max_d = 16 * gemm_kblock(c->dtype, 1);
+  if (c->hidden > max_d)
+    return fail(DFLASH_E_UNSUPPORTED, "config: hidden above %d is not supported", max_d);
   return DFLASH_OK;
 }
 
@@ -144,7 +209,9 @@ struct dflash_handle {
   dflash_weights w;
   char* kv;
   char* ws;
+  char* packed;
   Layout lay;
+  PackedLayout pk;
   std::vector<HostSlot> slots;
   bool dev_init = false;
   Profiler prof;
@@ -180,6 +247,19 @@ dflash_status ensure_device(dflash_handle* h) {
   if ((e = hipMemset(h->ws + h->lay.page_table, 0xff,
                      sizeof(int32_t) * c.max_batch * (size_t)c.max_pages_per_req)))
     return hip_fail(e, "page table init");
+  // weights into MFMA fragment order (read once here)
+  const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
+  const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  launch_pack(c.dtype, h->w.lm_head, h->packed + h->pk.lm_head, c.vocab, d, nullptr);
+  launch_pack(c.dtype, h->w.fc, h->packed + h->pk.fc, d, c.n_feat * d, nullptr);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const dflash_layer_weights& lw = h->w.layers[l];
+    launch_pack(c.dtype, lw.wqkv, h->packed + h->pk.wqkv[l], qkvw, d, nullptr);
+    launch_pack(c.dtype, lw.wo, h->packed + h->pk.wo[l], d, qd, nullptr);
+    launch_pack(c.dtype, lw.wgateup, h->packed + h->pk.wgateup[l], 2 * c.ffn, d, nullptr);
+    launch_pack(c.dtype, lw.wdown, h->packed + h->pk.wdown[l], d, c.ffn, nullptr);
+  }
+  if ((e = hipGetLastError())) return hip_fail(e, "weight packing");
   if ((e = hipDeviceSynchronize())) return hip_fail(e, "device init");
   h->dev_init = true;
   return DFLASH_OK;
@@ -257,21 +337,28 @@ size_t dflash_workspace_bytes(const dflash_config* cfg) {
   return make_layout(*cfg).total;
 }
 
+size_t dflash_packed_weights_bytes(const dflash_config* cfg) {
+  if (validate(cfg) != DFLASH_OK) return 0;
+  return make_packed(*cfg).total;
+}
+
 size_t dflash_kv_pool_bytes(const dflash_config* cfg) {
   if (validate(cfg) != DFLASH_OK) return 0;
   return (size_t)cfg->n_layers * cfg->max_pages * 2ull * cfg->n_kv_heads * 16 * cfg->head_dim * elt(*cfg);
 }
 
 dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, void* kv_pool,
-                            void* workspace, dflash_handle** out) {
+                            void* workspace, void* packed, dflash_handle** out) {
   if (!out) return fail(DFLASH_E_INVALID, "out is NULL");
   *out = nullptr;
   dflash_status st = validate(cfg);
   if (st) return st;
   if (!w) return fail(DFLASH_E_INVALID, "weights is NULL");
-  if (!kv_pool || !workspace) return fail(DFLASH_E_INVALID, "kv_pool and workspace must be set");
-  if ((reinterpret_cast<uintptr_t>(kv_pool) | reinterpret_cast<uintptr_t>(workspace)) & 255)
-    return fail(DFLASH_E_INVALID, "kv_pool and workspace must be 256-byte aligned");
+  if (!kv_pool || !workspace || !packed)
+    return fail(DFLASH_E_INVALID, "kv_pool, workspace and packed must be set");
+  if ((reinterpret_cast<uintptr_t>(kv_pool) | reinterpret_cast<uintptr_t>(workspace) |
+       reinterpret_cast<uintptr_t>(packed)) & 255)
+    return fail(DFLASH_E_INVALID, "kv_pool, workspace and packed must be 256-byte aligned");
   if (!w->embed || !w->lm_head || !w->fc || !w->fc_norm || !w->final_norm)
     return fail(DFLASH_E_INVALID, "a model weight pointer is NULL");
   for (int l = 0; l < cfg->n_layers; ++l) {
@@ -285,7 +372,9 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
   h->w = *w;
   h->kv = reinterpret_cast<char*>(kv_pool);
   h->ws = reinterpret_cast<char*>(workspace);
+  h->packed = reinterpret_cast<char*>(packed);
   h->lay = make_layout(*cfg);
+  h->pk = make_packed(*cfg);
   h->slots.resize(cfg->max_batch);
   *out = h;
   return DFLASH_OK;
@@ -368,6 +457,7 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
   const int d = c.hidden;
   const int kvw = c.n_layers * 2 * c.n_kv_heads * c.head_dim;
   const int R = c.max_inject_rows;
+  const int kv_seg_tiles = tiles_of(2 * c.n_kv_heads * c.head_dim);
 
   // walk requests in call order, cutting chunks of <= R rows and <= kMaxChunkReq requests
   int req = 0, used = 0;  // current request and rows of it already emitted
@@ -398,6 +488,7 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
         used = 0;
       }
     }
+    const Plans pl = make_plans(c, rows);
 
     GemmParams g{};
     for (int k = 0; k < c.n_feat; ++k) g.a[k] = wptr(hidden[k], (size_t)row0 * d, e);
@@ -405,16 +496,17 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
     g.a_part_k = d;
     g.lda = d;
     g.M = rows;
-    g.w[0] = h->w.fc;
-    g.seg_rows = d;
+    g.w[0] = h->packed + h->pk.fc;
+    g.tiles = tiles_of(d);
     g.N = d;
     g.K = c.n_feat * d;
+    g.P = pl.fc.P;
     g.out_f32 = at<float>(h, h->lay.u);
-    g.ldo = d;
-    { ProfScope ps(h, DFLASH_KERNEL_FC_GEMM, s); launch_gemm(c.dtype, EPI_STORE, g, s); }
+    { ProfScope ps(h, DFLASH_KERNEL_FC_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.fc, g, s); }
 
     NormParams np{};
-    np.x = at<float>(h, h->lay.u);
+    np.part = at<float>(h, h->lay.u);
+    np.n_part = pl.fc.P;
     np.ldx = d;
     np.gamma = h->w.fc_norm;
     np.eps = c.rms_eps;
@@ -436,16 +528,19 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
     kv.a_part_k = d;
     kv.lda = d;
     kv.M = rows;
+    // the K/V rows of every layer's fused QKV weight, in place
     for (int l = 0; l < c.n_layers; ++l)
-      kv.w[l] = wptr(h->w.layers[l].wqkv, (size_t)c.n_q_heads * c.head_dim * d, e);
-    kv.seg_rows = 2 * c.n_kv_heads * c.head_dim;
+      kv.w[l] = h->packed + h->pk.wqkv[l] + (size_t)tiles_of(c.n_q_heads * c.head_dim) * 16 * d * e;
+    kv.seg_tiles = kv_seg_tiles;
+    kv.tiles = c.n_layers * kv_seg_tiles;
     kv.N = kvw;
     kv.K = d;
+    kv.P = pl.kv.P;
     kv.out_f32 = at<float>(h, h->lay.kvo);
-    kv.ldo = kvw;
-    { ProfScope ps(h, DFLASH_KERNEL_KV_GEMM, s); launch_gemm(c.dtype, EPI_STORE, kv, s); }
+    { ProfScope ps(h, DFLASH_KERNEL_KV_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.kv, kv, s); }
 
     sp.kv = at<float>(h, h->lay.kvo);
+    sp.n_part = pl.kv.P;
     sp.rows = rows;
     sp.L = c.n_layers;
     sp.Hkv = c.n_kv_heads;
@@ -498,6 +593,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   const int d = c.hidden, B = c.block_size, M = n_req * B;
   const int qd = c.n_q_heads * c.head_dim;
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const Plans pl = make_plans(c, M);
   SlotArgs sl{};
   for (int i = 0; i < n_req; ++i) sl.slots[i] = slots[i];
 
@@ -509,17 +605,34 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   splits = (max_units + pps - 1) / pps;
 
   float* hbuf = at<float>(h, h->lay.h);
+  float* dpart = at<float>(h, h->lay.dpart);
+  float* opart = at<float>(h, h->lay.opart);
   const size_t page_layer = (size_t)c.max_pages * 2 * c.n_kv_heads * 16 * c.head_dim;
+
+  auto gemm_in = [&](const void* a, int K) {
+    GemmParams g{};
+    g.a[0] = a;
+    g.a_parts = 1;
+    g.a_part_k = K;
+    g.lda = K;
+    g.M = M;
+    g.K = K;
+    return g;
+  };
 
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& lw = h->w.layers[l];
+    // residual: block init (layer 0) or h + previous layer's down-projection partials
     NormParams n1{};
-    n1.x = hbuf;
-    n1.ldx = d;
     if (l == 0) {
       n1.init_row = wptr(h->w.embed, (size_t)c.mask_token_id * d, e);
-      n1.x_init = hbuf;
+    } else {
+      n1.x_in = hbuf;
+      n1.part = dpart;
+      n1.n_part = pl.down.P;
     }
+    n1.x_out = hbuf;
+    n1.ldx = d;
     n1.gamma = lw.attn_norm;
     n1.eps = c.rms_eps;
     n1.out = h->ws + h->lay.xa;
@@ -529,22 +642,17 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     n1.dbg = debug_hidden ? debug_hidden + (size_t)l * M * d : nullptr;
     { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, n1, s); }
 
-    GemmParams g{};
-    g.a[0] = h->ws + h->lay.xa;
-    g.a_parts = 1;
-    g.a_part_k = d;
-    g.lda = d;
-    g.M = M;
-    g.w[0] = lw.wqkv;
-    g.seg_rows = qkvw;
+    GemmParams g = gemm_in(h->ws + h->lay.xa, d);
+    g.w[0] = h->packed + h->pk.wqkv[l];
+    g.tiles = tiles_of(qkvw);
     g.N = qkvw;
-    g.K = d;
+    g.P = pl.qkv.P;
     g.out_f32 = at<float>(h, h->lay.qkv);
-    g.ldo = qkvw;
-    { ProfScope ps(h, DFLASH_KERNEL_QKV_GEMM, s); launch_gemm(c.dtype, EPI_STORE, g, s); }
+    { ProfScope ps(h, DFLASH_KERNEL_QKV_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.qkv, g, s); }
 
     QkvPostParams qp{};
     qp.qkv = at<float>(h, h->lay.qkv);
+    qp.n_part = pl.qkv.P;
     qp.B = B;
     qp.Hq = c.n_q_heads;
     qp.Hkv = c.n_kv_heads;
@@ -585,22 +693,19 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     cp.ldo = qd;
     { ProfScope ps(h, DFLASH_KERNEL_COMBINE, s); launch_combine(c.dtype, c.head_dim, n_req, cp, s); }
 
-    GemmParams go{};
-    go.a[0] = h->ws + h->lay.xo;
-    go.a_parts = 1;
-    go.a_part_k = qd;
-    go.lda = qd;
-    go.M = M;
-    go.w[0] = lw.wo;
-    go.seg_rows = d;
+    GemmParams go = gemm_in(h->ws + h->lay.xo, qd);
+    go.w[0] = h->packed + h->pk.wo[l];
+    go.tiles = tiles_of(d);
     go.N = d;
-    go.K = qd;
-    go.resid = hbuf;
-    go.ldr = d;
-    { ProfScope ps(h, DFLASH_KERNEL_O_GEMM, s); launch_gemm(c.dtype, EPI_RESID, go, s); }
+    go.P = pl.o.P;
+    go.out_f32 = opart;
+    { ProfScope ps(h, DFLASH_KERNEL_O_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.o, go, s); }
 
     NormParams n2{};
-    n2.x = hbuf;
+    n2.x_in = hbuf;
+    n2.part = opart;
+    n2.n_part = pl.o.P;
+    n2.x_out = hbuf;
     n2.ldx = d;
     n2.gamma = lw.mlp_norm;
     n2.eps = c.rms_eps;
@@ -610,40 +715,32 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     n2.M = M;
     { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, n2, s); }
 
-    GemmParams gu{};
-    gu.a[0] = h->ws + h->lay.xa;
-    gu.a_parts = 1;
-    gu.a_part_k = d;
-    gu.lda = d;
-    gu.M = M;
-    gu.w[0] = lw.wgateup;
-    gu.w_up = wptr(lw.wgateup, (size_t)c.ffn * d, e);
-    gu.seg_rows = c.ffn;
+    GemmParams gu = gemm_in(h->ws + h->lay.xa, d);
+    gu.w[0] = h->packed + h->pk.wgateup[l];
+    gu.tiles = tiles_of(c.ffn);
+    gu.up_tile_off = tiles_of(c.ffn);
     gu.N = c.ffn;
-    gu.K = d;
+    gu.P = 1;
     gu.out_t = h->ws + h->lay.z;
     gu.ldt = c.ffn;
-    { ProfScope ps(h, DFLASH_KERNEL_GATEUP_GEMM, s); launch_gemm(c.dtype, EPI_SWIGLU, gu, s); }
+    { ProfScope ps(h, DFLASH_KERNEL_GATEUP_GEMM, s); launch_gemm(c.dtype, EPI_SWIGLU, pl.gateup, gu, s); }
 
-    GemmParams gd{};
-    gd.a[0] = h->ws + h->lay.z;
-    gd.a_parts = 1;
-    gd.a_part_k = c.ffn;
-    gd.lda = c.ffn;
-    gd.M = M;
-    gd.w[0] = lw.wdown;
-    gd.seg_rows = d;
+    GemmParams gd = gemm_in(h->ws + h->lay.z, c.ffn);
+    gd.w[0] = h->packed + h->pk.wdown[l];
+    gd.tiles = tiles_of(d);
     gd.N = d;
-    gd.K = c.ffn;
-    gd.resid = hbuf;
-    gd.ldr = d;
-    { ProfScope ps(h, DFLASH_KERNEL_DOWN_GEMM, s); launch_gemm(c.dtype, EPI_RESID, gd, s); }
+    gd.P = pl.down.P;
+    gd.out_f32 = dpart;
+    { ProfScope ps(h, DFLASH_KERNEL_DOWN_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.down, gd, s); }
     st = launched("draft layer");
     if (st) return st;
   }
 
   NormParams nf{};
-  nf.x = hbuf;
+  nf.x_in = hbuf;
+  nf.part = dpart;
+  nf.n_part = pl.down.P;
+  nf.x_out = hbuf;
   nf.ldx = d;
   nf.gamma = h->w.final_norm;
   nf.eps = c.rms_eps;
@@ -655,20 +752,15 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   nf.zero_keys = at<unsigned long long>(h, h->lay.keys);
   { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, nf, s); }
 
-  GemmParams gl{};
-  gl.a[0] = h->ws + h->lay.xa;
-  gl.a_parts = 1;
-  gl.a_part_k = d;
-  gl.lda = d;
-  gl.M = M;
-  gl.w[0] = h->w.lm_head;
-  gl.seg_rows = c.vocab;
+  GemmParams gl = gemm_in(h->ws + h->lay.xa, d);
+  gl.w[0] = h->packed + h->pk.lm_head;
+  gl.tiles = tiles_of(c.vocab);
   gl.N = c.vocab;
-  gl.K = d;
+  gl.P = 1;
   gl.keys = at<unsigned long long>(h, h->lay.keys);
   gl.dbg = debug_logits;
   gl.ld_dbg = c.vocab;
-  { ProfScope ps(h, DFLASH_KERNEL_LM_HEAD, s); launch_gemm(c.dtype, EPI_ARGMAX, gl, s); }
+  { ProfScope ps(h, DFLASH_KERNEL_LM_HEAD, s); launch_gemm(c.dtype, EPI_ARGMAX, pl.lm, gl, s); }
   {
     ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
     launch_finalize(at<unsigned long long>(h, h->lay.keys), M, c.vocab, draft, s);

@@ -94,7 +94,9 @@ class Drafter:
         if poison_kv:
             self.kv_pool.fill_(0xFF)  # NaN in bf16 and fp32
         self.workspace = torch.empty(wsb, dtype=torch.uint8, device=self.dev)
-        self.h = B.dflash_create(self.cfg, self.w, self.kv_pool.data_ptr(), self.workspace.data_ptr())
+        self.packed = torch.empty(B.dflash_packed_weights_bytes(self.cfg), dtype=torch.uint8, device=self.dev)
+        self.h = B.dflash_create(self.cfg, self.w, self.kv_pool.data_ptr(), self.workspace.data_ptr(),
+                                 self.packed.data_ptr())
 
     # -- helpers ------------------------------------------------------------
     @property

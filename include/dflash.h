@@ -144,20 +144,28 @@ dflash_status dflash_validate_config(const dflash_config *cfg);
  * k >= 2 and n_target_layers >= 4.  Host only. */
 dflash_status dflash_feature_layers(int32_t n_target_layers, int32_t k, int32_t *out);
 
-/* Bytes of device workspace / KV pool a handle with this config needs
- * (0 for an invalid config).  The KV pool is n_layers * max_pages pages of
- * 2 * n_kv_heads * 16 * head_dim elements; the caller may hand out pages to
- * slots in any order. */
+/* Bytes of device workspace / KV pool / packed weights a handle with this
+ * config needs (0 for an invalid config).  The KV pool is n_layers *
+ * max_pages pages of 2 * n_kv_heads * 16 * head_dim elements; the caller may
+ * hand out pages to slots in any order.  The packed-weights buffer receives a
+ * copy of every weight matrix in the library's streaming layout (MFMA
+ * fragment order: 16-row tiles, 32-column steps, 64 lanes x 8 elements). */
 size_t dflash_workspace_bytes(const dflash_config *cfg);
 size_t dflash_kv_pool_bytes(const dflash_config *cfg);
+size_t dflash_packed_weights_bytes(const dflash_config *cfg);
 
-/* Creates a handle borrowing weights, kv_pool and workspace (device buffers
- * of at least the sizes above, 256-byte aligned).  Device initialisation
- * (RoPE table, slot state) happens on the first call that needs the device,
- * on the current HIP device.  Returns DFLASH_E_INVALID on a bad config or a
- * NULL pointer. */
+/* Creates a handle borrowing weights, kv_pool, workspace and packed (device
+ * buffers of at least the sizes above, 256-byte aligned).  Device
+ * initialisation happens on the first call that needs the device (normally
+ * dflash_bind_request), on the current HIP device: the RoPE table, the slot
+ * state, and the packing of every weight matrix of `w` into `packed`.  The
+ * matrices of `w` are read only then; embed, the norm gains and the conv taps
+ * are read by every draft.  Returns DFLASH_E_INVALID on a bad config or a
+ * NULL pointer, DFLASH_E_UNSUPPORTED for a hidden size above 4096 (bf16) /
+ * 2048 (fp32). */
 dflash_status dflash_create(const dflash_config *cfg, const dflash_weights *w,
-                            void *kv_pool, void *workspace, dflash_handle **out);
+                            void *kv_pool, void *workspace, void *packed,
+                            dflash_handle **out);
 
 /* Releases the host handle (borrowed device memory is untouched). */
 void dflash_destroy(dflash_handle *h);

@@ -96,22 +96,38 @@ def test_create_rejects_null_and_misaligned_buffers():
     cfg = _cfg()
     w = _fake_weights(cfg.n_layers)
     with pytest.raises(B.DFlashError):
-        B.dflash_create(cfg, w, 0, 1 << 30)
+        B.dflash_create(cfg, w, 0, 1 << 30, 1 << 32)
     with pytest.raises(B.DFlashError):
-        B.dflash_create(cfg, w, (1 << 30) + 8, 1 << 31)
+        B.dflash_create(cfg, w, 1 << 30, 1 << 31, 0)
+    with pytest.raises(B.DFlashError):
+        B.dflash_create(cfg, w, (1 << 30) + 8, 1 << 31, 1 << 32)
     w.layers[1].wo = None
     with pytest.raises(B.DFlashError) as e:
-        B.dflash_create(cfg, w, 1 << 30, 1 << 31)
+        B.dflash_create(cfg, w, 1 << 30, 1 << 31, 1 << 32)
     assert "layer 1" in str(e.value)
     cfgc = _cfg("small_conv")
     with pytest.raises(B.DFlashError):
-        B.dflash_create(cfgc, _fake_weights(cfgc.n_layers, conv=False), 1 << 30, 1 << 31)
+        B.dflash_create(cfgc, _fake_weights(cfgc.n_layers, conv=False), 1 << 30, 1 << 31, 1 << 32)
+
+
+def test_packed_weights_bytes():
+    shape = synth.config("qwen3_8b")
+    cfg = make_config(shape, max_batch=1, max_pages=300, max_pages_per_req=300, max_position=8192)
+    d, F, V, L = 4096, 12288, 151936, 5
+    qkv = (32 + 16) * 128
+    expect = 2 * (V * d + d * 5 * d + L * (qkv * d + d * 4096 + 2 * F * d + d * F))
+    assert B.dflash_packed_weights_bytes(cfg) == expect
+    big = make_config(synth.config("small_bf16", hidden=8192), max_batch=1, max_pages=8,
+                      max_pages_per_req=8, max_position=512)
+    with pytest.raises(B.DFlashError) as e:
+        B.dflash_validate_config(big)
+    assert e.value.status == B.E_UNSUPPORTED
 
 
 @pytest.fixture()
 def handle():
     cfg = _cfg()
-    h = B.dflash_create(cfg, _fake_weights(cfg.n_layers), 1 << 30, 1 << 31)
+    h = B.dflash_create(cfg, _fake_weights(cfg.n_layers), 1 << 30, 1 << 31, 1 << 32)
     yield h, cfg
     B.dflash_destroy(h)
 
@@ -160,4 +176,4 @@ def test_null_handle_is_rejected():
     assert lib.dflash_check(None, None) == B.E_INVALID
     assert lib.dflash_context_length(None, 0) == -1
     out = ctypes.c_void_p()
-    assert lib.dflash_create(None, None, None, None, ctypes.byref(out)) == B.E_INVALID
+    assert lib.dflash_create(None, None, None, None, None, ctypes.byref(out)) == B.E_INVALID
