@@ -22,7 +22,11 @@
 //              as an exact hi + lo pair).  Invalid keys (past ctx_len,
 //              before the window, block rows >= B) get probability 0 and their
 //              V is zeroed, so stale or poisoned page contents never leak in.
-// k_combine    merges the per-split (max, sum, O) into the attention output.
+//              Each workgroup holds the G query heads of one KV head times KQ
+//              key subsets (up to 8 waves); the subsets are merged in LDS
+//              in a fixed order and the split's (max, sum, O) goes to global
+//              memory (with a single split the output is written directly).
+// k_combine    merges the splits of every (request, head, row) in split order.
 #include <math.h>
 
 #include "common.h"
@@ -40,7 +44,7 @@ template <> struct Vec4<bf16> { typedef bf16x4 type; };
 template <> struct Vec4<float> { typedef f32x4 type; };
 
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void k_qkv_post(QkvPostParams p, SlotArgs sl) {
+__global__ __launch_bounds__(1024) void k_qkv_post(QkvPostParams p, SlotArgs sl) {
   const int r = blockIdx.x;
   const int hh = blockIdx.y;
   const int t = threadIdx.x;
@@ -61,7 +65,7 @@ __global__ __launch_bounds__(256) void k_qkv_post(QkvPostParams p, SlotArgs sl) 
       dst = reinterpret_cast<T*>(p.qb) + (long long)(r * p.Hq + hh) * 16 * DH;
     else
       dst = reinterpret_cast<T*>(p.blk) + r * page_elems + (long long)(hh - p.Hq) * 16 * DH;
-    for (int e = t; e < 16 * H2; e += 256) {
+    for (int e = t; e < 16 * H2; e += blockDim.x) {
       const int i = e / H2;
       const int j = e - i * H2;
       float y1 = 0.f, y2 = 0.f;
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(256) void k_qkv_post(QkvPostParams p, SlotArgs sl) 
   } else {
     const int g = hh - p.Hq - p.Hkv;
     T* dst = reinterpret_cast<T*>(p.blk) + r * page_elems + (long long)(p.Hkv + g) * 16 * DH;
-    for (int e = t; e < 16 * DH; e += 256) {
+    for (int e = t; e < 16 * DH; e += blockDim.x) {
       const int i = e & 15;
       const int d = e >> 4;
       const float x = i < p.B ? rd((long long)i * ld + d) : 0.f;
@@ -89,19 +93,24 @@ __global__ __launch_bounds__(256) void k_qkv_post(QkvPostParams p, SlotArgs sl) 
 }
 
 template <typename T, int DH>
-__global__ __launch_bounds__(1024) void k_attn(AttnParams p, SlotArgs sl) {
+__global__ __launch_bounds__(512) void k_attn(AttnParams p, SlotArgs sl) {
   typedef typename Frag8<T>::type Frag;
   typedef typename Vec4<T>::type V4;
   constexpr int NJ = DH / 32;
   constexpr int ND = DH / 16;
   const float NEG = -INFINITY;
+  extern __shared__ float smem[];
 
   const int s = blockIdx.x;
   const int gkv = blockIdx.y;
   const int r = blockIdx.z;
   const int G = p.Hq / p.Hkv;
+  const int KQ = p.KQ;
+  const int S = p.n_splits;
   const int wave = threadIdx.x >> 6;
-  const int h = gkv * G + wave;
+  const int wq = wave % G;  // query head within the group
+  const int kq = wave / G;  // key subset
+  const int h = gkv * G + wq;
   const int lane = lane_id();
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
@@ -131,7 +140,8 @@ __global__ __launch_bounds__(1024) void k_attn(AttnParams p, SlotArgs sl) {
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int u = u_begin; u < u_end; u += 2) {
+  // pairs of units (32 keys); key subset kq takes every KQ-th pair of the split
+  for (int u = u_begin + 2 * kq; u < u_end; u += 2 * KQ) {
     const T* base[2];
     bool valid[2][4];
 #pragma unroll
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(1024) void k_attn(AttnParams p, SlotArgs sl) {
           const int page = p.page_table[(long long)slot * p.pt_stride + idx];
           if (page >= 0 && page < p.max_pages) {
             base[t] = pool + (long long)page * page_elems;
-          } else if (lane == 0 && wave == 0) {
+          } else if (lane == 0) {
             atomicOr(p.err, 2u);
           }
           pos0 = lp * 16;
@@ -164,17 +174,37 @@ __global__ __launch_bounds__(1024) void k_attn(AttnParams p, SlotArgs sl) {
       }
     }
 
+    // K of both units first; V is loaded once the scores are formed, so the
+    // two fragment sets never need registers at the same time
+    Frag kf[2][NJ];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (base[t]) {
+        const T* kb = base[t] + (long long)gkv * 16 * DH + l16 * DH + 8 * g4;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) kf[t][j] = load8<T>(kb + 32 * j);
+      }
+    }
+
     float sv[8];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
       if (base[t]) {
-        const T* kb = base[t] + (long long)gkv * 16 * DH + l16 * DH;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) sacc = mfma_step(load8<T>(kb + 32 * j + 8 * g4), qf[j], sacc);
+        for (int j = 0; j < NJ; ++j) sacc = mfma_step(kf[t][j], qf[j], sacc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[4 * t + i] = valid[t][i] ? sacc[i] * p.scale : NEG;
+    }
+    V4 vv[2][ND];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (base[t]) {
+        const T* vb = base[t] + (long long)(p.Hkv + gkv) * 16 * DH + l16 * 16 + 4 * g4;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) vv[t][dt] = *reinterpret_cast<const V4*>(vb + dt * 256);
+      }
     }
     float mx = sv[0];
 #pragma unroll
@@ -204,69 +234,116 @@ __global__ __launch_bounds__(1024) void k_attn(AttnParams p, SlotArgs sl) {
       pf[e] = from_f<T>(pe[e]);
       pf_lo[e] = from_f<T>(pe[e] - to_f(pf[e]));
     }
-
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
       o[dt] = o[dt] * corr;
       Frag vf;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        V4 v4;
-        if (base[t]) {
-          const T* vb = base[t] + (long long)(p.Hkv + gkv) * 16 * DH + (16 * dt + l16) * 16 + 4 * g4;
-          v4 = *reinterpret_cast<const V4*>(vb);
-        } else {
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v4[i] = (T)0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vf[4 * t + i] = valid[t][i] ? v4[i] : (T)0.0f;
-      }
+        for (int i = 0; i < 4; ++i) vf[4 * t + i] = valid[t][i] ? vv[t][dt][i] : (T)0.0f;
       o[dt] = mfma_step(vf, pf, o[dt]);
       if (kSplitP<T>) o[dt] = mfma_step(vf, pf_lo, o[dt]);
     }
   }
 
-  const long long pb = ((long long)(r * p.Hq + h) * p.n_splits + s) * 16 + l16;
+  // ---- merge the KQ key subsets of each query head (LDS, fixed order) ----
+  float* acc = smem;                       // [G][16][DH]
+  float* sml = smem + G * 16 * DH;         // [KQ][G][16][2]
+  float Mq = m_run, Lq = l_run;
+  if (KQ > 1) {
+    if (g4 == 0) {
+      sml[((kq * G + wq) * 16 + l16) * 2 + 0] = m_run;
+      sml[((kq * G + wq) * 16 + l16) * 2 + 1] = l_run;
+    }
+    __syncthreads();
+    Mq = NEG;
+    for (int kk = 0; kk < KQ; ++kk) Mq = fmaxf(Mq, sml[((kk * G + wq) * 16 + l16) * 2]);
+    Lq = 0.f;
+    for (int kk = 0; kk < KQ; ++kk) {
+      const float mk = sml[((kk * G + wq) * 16 + l16) * 2];
+      if (mk != NEG) Lq += sml[((kk * G + wq) * 16 + l16) * 2 + 1] * expf(mk - Mq);
+    }
+    const float f = (m_run == NEG) ? 0.f : expf(m_run - Mq);
+    float* a = acc + (wq * 16 + l16) * DH + 4 * g4;
+    for (int kk = 0; kk < KQ; ++kk) {
+      if (kq == kk) {
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt)
+        for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p.part_o[pb * DH + 16 * dt + 4 * g4 + i] = o[dt][i];
-  if (g4 == 0) {
-    p.part_ml[pb * 2 + 0] = m_run;
-    p.part_ml[pb * 2 + 1] = l_run;
+          for (int i = 0; i < 4; ++i) a[16 * dt + i] = (kk ? a[16 * dt + i] : 0.f) + f * o[dt][i];
+      }
+      __syncthreads();
+    }
+  } else {
+    float* a = acc + (wq * 16 + l16) * DH + 4 * g4;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[16 * dt + i] = o[dt][i];
+    __syncthreads();
+  }
+  // (Mq, Lq) of (wq, l16) live in the lanes of every key-subset wave; acc holds O
+
+  T* out = reinterpret_cast<T*>(p.out);
+  const int nel = G * 16 * DH;
+  if (S == 1) {
+    float* wts = sml + KQ * G * 16 * 2;  // [G][16]: 1 / L
+    if (kq == 0 && g4 == 0) wts[wq * 16 + l16] = 1.0f / Lq;
+    __syncthreads();
+    for (int e = threadIdx.x; e < nel; e += blockDim.x) {
+      const int w2 = e / (16 * DH), q = (e / DH) & 15, d = e % DH;
+      if (q < p.B)
+        out[(long long)(r * p.B + q) * p.ldo + (gkv * G + w2) * DH + d] = from_f<T>(acc[e] * wts[w2 * 16 + q]);
+    }
+    return;
+  }
+
+  // ---- split partial to global; k_combine merges the splits ----
+  if (kq == 0 && g4 == 0) {
+    const long long pb = ((long long)(r * p.Hq + h) * S + s) * 16 + l16;
+    p.part_ml[pb * 2 + 0] = Mq;
+    p.part_ml[pb * 2 + 1] = Lq;
+  }
+  for (int e = threadIdx.x; e < nel; e += blockDim.x) {
+    const int w2 = e / (16 * DH), rem = e % (16 * DH);
+    p.part_o[((long long)(r * p.Hq + gkv * G + w2) * S + s) * 16 * DH + rem] = acc[e];
   }
 }
 
+// One wave per (request, query head, block row): the split partials of the
+// row are merged in split order (max, rescaled sums), each lane owning DH/64
+// output columns, so every partial is read once and all loads of a lane are
+// independent.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_combine(CombineParams p) {
-  const int h = blockIdx.x;
-  const int r = blockIdx.y;
-  const int t = threadIdx.x;
-  const int q = t >> 4;
-  const int dd = t & 15;
-  if (q >= p.B) return;
-  constexpr int NC = DH / 16;
-  const long long base = (long long)(r * p.Hq + h) * p.n_splits * 16;
+  constexpr int C = DH / 64;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int q = wid % 16;
+  const int rh = wid / 16;  // r * Hq + h
+  if (rh >= p.n_rh || q >= p.B) return;
+  const int S = p.n_splits;
+  const long long pb = (long long)rh * S * 16 + q;
   float mx = -INFINITY;
-  for (int s = 0; s < p.n_splits; ++s) mx = fmaxf(mx, p.part_ml[(base + s * 16 + q) * 2]);
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, p.part_ml[(pb + s * 16) * 2]);
   float L = 0.f;
-  float acc[NC];
+  float acc[C];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) acc[c] = 0.f;
-  for (int s = 0; s < p.n_splits; ++s) {
-    const long long rw = base + s * 16 + q;
-    const float ms = p.part_ml[rw * 2];
-    if (ms == -INFINITY) continue;
-    const float w = expf(ms - mx);
-    L += p.part_ml[rw * 2 + 1] * w;
+  for (int c = 0; c < C; ++c) acc[c] = 0.f;
+  const float* po = p.part_o + pb * DH + lane * C;
+  for (int s = 0; s < S; ++s) {
+    const float ms = p.part_ml[(pb + s * 16) * 2];
+    const float w = ms == -INFINITY ? 0.f : expf(ms - mx);
+    L += p.part_ml[(pb + s * 16) * 2 + 1] * w;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] += w * p.part_o[rw * DH + dd + 16 * c];
+    for (int c = 0; c < C; ++c) acc[c] += w * po[(long long)s * 16 * DH + c];
   }
   const float inv = 1.0f / L;
-  T* out = reinterpret_cast<T*>(p.out) + (long long)(r * p.B + q) * p.ldo + h * DH;
+  const int r = rh / p.Hq, h = rh - r * p.Hq;
+  T* out = reinterpret_cast<T*>(p.out) + (long long)(r * p.B + q) * p.ldo + h * DH + lane * C;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) out[dd + 16 * c] = from_f<T>(acc[c] * inv);
+  for (int c = 0; c < C; ++c) out[c] = from_f<T>(acc[c] * inv);
 }
 
 template <typename T, int DH>
@@ -324,24 +401,26 @@ template <typename T>
 void qkv_post_t(int dh, int n_req, const QkvPostParams& p, const SlotArgs& sl, hipStream_t s) {
   dim3 grid(n_req, p.Hq + 2 * p.Hkv);
   if (dh == 128)
-    hipLaunchKernelGGL((k_qkv_post<T, 128>), grid, dim3(256), 0, s, p, sl);
+    hipLaunchKernelGGL((k_qkv_post<T, 128>), grid, dim3(1024), 0, s, p, sl);
   else
-    hipLaunchKernelGGL((k_qkv_post<T, 64>), grid, dim3(256), 0, s, p, sl);
+    hipLaunchKernelGGL((k_qkv_post<T, 64>), grid, dim3(512), 0, s, p, sl);
 }
 
 template <typename T>
 void attn_t(int dh, int n_req, const AttnParams& p, const SlotArgs& sl, hipStream_t s) {
   dim3 grid(p.n_splits, p.Hkv, n_req);
-  dim3 block(64 * (p.Hq / p.Hkv));
+  const int G = p.Hq / p.Hkv;
+  dim3 block(64 * G * p.KQ);
+  const size_t lds = attn_lds_bytes(p.Hq, p.Hkv, dh, p.KQ);
   if (dh == 128)
-    hipLaunchKernelGGL((k_attn<T, 128>), grid, block, 0, s, p, sl);
+    hipLaunchKernelGGL((k_attn<T, 128>), grid, block, lds, s, p, sl);
   else
-    hipLaunchKernelGGL((k_attn<T, 64>), grid, block, 0, s, p, sl);
+    hipLaunchKernelGGL((k_attn<T, 64>), grid, block, lds, s, p, sl);
 }
 
 template <typename T>
-void combine_t(int dh, int n_req, const CombineParams& p, hipStream_t s) {
-  dim3 grid(p.Hq, n_req);
+void combine_t(int dh, const CombineParams& p, hipStream_t s) {
+  dim3 grid((p.n_rh * 16 + 3) / 4);
   if (dh == 128)
     hipLaunchKernelGGL((k_combine<T, 128>), grid, dim3(256), 0, s, p);
   else
@@ -359,6 +438,11 @@ void scatter_t(int dh, const ScatterParams& p, hipStream_t s) {
 
 }  // namespace
 
+size_t attn_lds_bytes(int Hq, int Hkv, int dh, int KQ) {
+  const int G = Hq / Hkv;
+  return sizeof(float) * ((size_t)G * 16 * dh + (size_t)KQ * G * 16 * 2 + (size_t)G * 16);
+}
+
 void launch_qkv_post(int dtype, int dh, int n_req, const QkvPostParams& p, const SlotArgs& sl,
                      hipStream_t s) {
   if (dtype == DFLASH_BF16)
@@ -375,11 +459,12 @@ void launch_attention(int dtype, int dh, int n_req, const AttnParams& p, const S
     attn_t<float>(dh, n_req, p, sl, s);
 }
 
-void launch_combine(int dtype, int dh, int n_req, const CombineParams& p, hipStream_t s) {
+void launch_combine(int dtype, int dh, const CombineParams& p, hipStream_t s) {
+  if (p.n_rh <= 0) return;
   if (dtype == DFLASH_BF16)
-    combine_t<bf16>(dh, n_req, p, s);
+    combine_t<bf16>(dh, p, s);
   else
-    combine_t<float>(dh, n_req, p, s);
+    combine_t<float>(dh, p, s);
 }
 
 void launch_scatter(int dtype, int dh, const ScatterParams& p, hipStream_t s) {

@@ -93,16 +93,19 @@ struct AttnParams {
   int Hq, Hkv, B;
   int pps;       // units (pages) per split
   int n_splits;  // grid.x
+  int KQ;        // key subsets per workgroup (waves = Hq/Hkv * KQ)
   float scale;
   float* part_o;   // [n_req, Hq, n_splits, 16, dh]
   float* part_ml;  // [n_req, Hq, n_splits, 16, 2]
+  void* out;       // storage dtype [n_req*B, Hq*dh] (written here when n_splits == 1)
+  int ldo;
   unsigned int* err;
 };
 
 struct CombineParams {
   const float* part_o;
   const float* part_ml;
-  int n_splits, Hq, B;
+  int n_splits, n_rh, Hq, B;  // n_rh = n_req * Hq
   void* out;  // storage dtype [n_req*B, Hq*dh]
   int ldo;
 };
@@ -138,7 +141,8 @@ void launch_qkv_post(int dtype, int dh, int n_req, const QkvPostParams& p, const
                      hipStream_t s);
 void launch_attention(int dtype, int dh, int n_req, const AttnParams& p, const SlotArgs& sl,
                       hipStream_t s);
-void launch_combine(int dtype, int dh, int n_req, const CombineParams& p, hipStream_t s);
+size_t attn_lds_bytes(int Hq, int Hkv, int dh, int KQ);
+void launch_combine(int dtype, int dh, const CombineParams& p, hipStream_t s);
 void launch_scatter(int dtype, int dh, const ScatterParams& p, hipStream_t s);
 void launch_finalize(const unsigned long long* keys, int rows, int vocab, int* draft,
                      hipStream_t s);

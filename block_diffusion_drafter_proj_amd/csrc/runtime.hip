@@ -5,10 +5,12 @@
 // Call sequences (all kernels on the caller's stream, no synchronisation):
 //   inject : per chunk of rows  fc GEMM (virtual concat of the n_feat hidden
 //            arrays) -> RMSNorm -> all-layer K/V GEMM -> RoPE + page scatter
-//   draft  : per layer  RMSNorm -> QKV GEMM -> q/k RoPE -> attention (split
-//            over pages) -> combine -> O GEMM + residual -> RMSNorm ->
-//            gate/up GEMM + SwiGLU -> down GEMM + residual;
-//            then final RMSNorm -> LM head GEMM + argmax -> decode ids
+//   draft  : per layer  RMSNorm (+ residual) -> QKV GEMM -> q/k RoPE ->
+//            attention (split over pages, splits merged by the last
+//            workgroup) -> O GEMM -> RMSNorm (+ residual) -> gate/up GEMM +
+//            SwiGLU -> down GEMM; then RMSNorm (+ residual) -> LM head GEMM
+//            + argmax -> decode ids.  GEMMs split over K leave fp32 partials
+//            that the next kernel adds in a fixed order.
 //   verify : one kernel
 #include <math.h>
 #include <stdarg.h>
@@ -45,8 +47,23 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t elt(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
 
+// Attention splits: a fixed number of KV pages per split for the handle, so a
+// request's arithmetic does not depend on the other requests of a call.
+// Small batches use short splits (many workgroups per request); large batches
+// longer ones (fewer partials).  Contexts above 128 splits widen them.
+int max_units(const dflash_config& c) {
+  return c.window ? c.window / 16 + 2 : c.max_pages_per_req + 1;
+}
+int attn_pps(const dflash_config& c) {
+  int pps = 8;
+  while (pps < 64 && pps < c.max_batch) pps *= 2;
+  const int units = max_units(c);
+  pps = std::max(pps, (units + 127) / 128);
+  return pps;
+}
+int max_splits(const dflash_config& c) { return (max_units(c) + attn_pps(c) - 1) / attn_pps(c); }
 // Upper bound of (requests x attention splits) handled in one draft call.
-int part_pairs(const dflash_config& c) { return c.max_batch + (512 + c.n_kv_heads - 1) / c.n_kv_heads; }
+int part_pairs(const dflash_config& c) { return c.max_batch * max_splits(c); }
 
 // Split-K factors of every GEMM (fixed by the shapes; the workspace holds
 // their partial planes).
@@ -160,7 +177,7 @@ dflash_status validate(const dflash_config* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return bad("head_dim must be 64 or 128");
   if (c->n_kv_heads <= 0 || c->n_q_heads <= 0 || c->n_q_heads % c->n_kv_heads)
     return bad("n_q_heads must be a positive multiple of n_kv_heads");
-  if (c->n_q_heads / c->n_kv_heads > 16) return bad("at most 16 query heads per KV head");
+  if (c->n_q_heads / c->n_kv_heads > 8) return bad("at most 8 query heads per KV head");
   if ((c->n_q_heads * c->head_dim) % 256) return bad("n_q_heads*head_dim must be a multiple of 256");
   if (c->ffn <= 0 || c->ffn % 256) return bad("ffn must be a positive multiple of 256");
   if (c->vocab <= 0) return bad("vocab must be positive");
@@ -597,12 +614,12 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   SlotArgs sl{};
   for (int i = 0; i < n_req; ++i) sl.slots[i] = slots[i];
 
-  // attention split plan: about 512 workgroups, pairs bounded by the workspace
-  int splits = std::max(1, (512 + n_req * c.n_kv_heads - 1) / (n_req * c.n_kv_heads));
-  splits = std::min(splits, max_units);
-  while (splits > 1 && n_req * splits > part_pairs(c)) --splits;
-  const int pps = (max_units + splits - 1) / splits;
-  splits = (max_units + pps - 1) / pps;
+  // attention plan: KQ key subsets per workgroup (up to 8 waves) and the
+  // handle's fixed pages per split
+  const int G = c.n_q_heads / c.n_kv_heads;
+  const int KQ = std::max(1, 8 / G);
+  const int pps = attn_pps(c);
+  const int splits = (max_units + pps - 1) / pps;
 
   float* hbuf = at<float>(h, h->lay.h);
   float* dpart = at<float>(h, h->lay.dpart);
@@ -677,21 +694,27 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     ap.B = B;
     ap.pps = pps;
     ap.n_splits = splits;
+    ap.KQ = KQ;
     ap.scale = (float)(1.0 / sqrt((double)c.head_dim));
     ap.part_o = at<float>(h, h->lay.part_o);
     ap.part_ml = at<float>(h, h->lay.part_ml);
+    ap.out = h->ws + h->lay.xo;
+    ap.ldo = qd;
     ap.err = at<unsigned int>(h, h->lay.err);
     { ProfScope ps(h, DFLASH_KERNEL_ATTN, s); launch_attention(c.dtype, c.head_dim, n_req, ap, sl, s); }
-
-    CombineParams cp{};
-    cp.part_o = ap.part_o;
-    cp.part_ml = ap.part_ml;
-    cp.n_splits = splits;
-    cp.Hq = c.n_q_heads;
-    cp.B = B;
-    cp.out = h->ws + h->lay.xo;
-    cp.ldo = qd;
-    { ProfScope ps(h, DFLASH_KERNEL_COMBINE, s); launch_combine(c.dtype, c.head_dim, n_req, cp, s); }
+    if (splits > 1) {
+      CombineParams cp{};
+      cp.part_o = ap.part_o;
+      cp.part_ml = ap.part_ml;
+      cp.n_splits = splits;
+      cp.n_rh = n_req * c.n_q_heads;
+      cp.Hq = c.n_q_heads;
+      cp.B = B;
+      cp.out = ap.out;
+      cp.ldo = qd;
+      ProfScope ps(h, DFLASH_KERNEL_COMBINE, s);
+      launch_combine(c.dtype, c.head_dim, cp, s);
+    }
 
     GemmParams go = gemm_in(h->ws + h->lay.xo, qd);
     go.w[0] = h->packed + h->pk.wo[l];

@@ -77,7 +77,7 @@ typedef enum { DFLASH_BF16 = 0, DFLASH_F32 = 1 } dflash_dtype;
  * Requirements (checked by dflash_validate_config):
  *   hidden, ffn, n_q_heads*head_dim and n_feat*hidden multiples of 256;
  *   head_dim 64 or 128; n_q_heads a multiple of n_kv_heads with
- *   n_q_heads/n_kv_heads <= 16; 1 <= block_size <= 16; page_size == 16;
+ *   n_q_heads/n_kv_heads <= 8; 1 <= block_size <= 16; page_size == 16;
  *   1 <= n_layers <= DFLASH_MAX_LAYERS; 1 <= n_feat <= DFLASH_MAX_FEAT;
  *   0 <= mask_token_id < vocab; window 0 (unbounded) or a positive multiple
  *   of 16; topk 0 or 16; max_batch <= DFLASH_MAX_BATCH. */
@@ -244,7 +244,7 @@ typedef enum {
   DFLASH_KERNEL_QKV_GEMM = 4,
   DFLASH_KERNEL_QKV_POST = 5,    /* block q/k RoPE, block KV page */
   DFLASH_KERNEL_ATTN = 6,
-  DFLASH_KERNEL_COMBINE = 7,
+  DFLASH_KERNEL_COMBINE = 7,     /* merge of attention splits */
   DFLASH_KERNEL_O_GEMM = 8,
   DFLASH_KERNEL_GATEUP_GEMM = 9,
   DFLASH_KERNEL_DOWN_GEMM = 10,
