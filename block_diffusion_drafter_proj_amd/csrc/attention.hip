@@ -106,7 +106,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams p, SlotArgs sl) {
   const int r = blockIdx.z;
   const int G = p.Hq / p.Hkv;
   const int KQ = p.KQ;
-  const int S = p.n_splits;
+  const int S = p.n_splits;  // partial-buffer stride (splits of the longest request)
   const int wave = threadIdx.x >> 6;
   const int wq = wave % G;  // query head within the group
   const int kq = wave / G;  // key subset
@@ -122,8 +122,12 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams p, SlotArgs sl) {
   const int lp0 = lo / 16;
   const int n_lp = hi > lo ? (hi - 1) / 16 - lp0 + 1 : 0;
   const int n_units = n_lp + 1;
-  const int u_begin = s * p.pps;
-  const int u_end = min(u_begin + p.pps, n_units);
+  const int pps = split_pages(n_units, p.split_target, p.pps_cap);
+  const int n_split = (n_units + pps - 1) / pps;
+  if (s == 0 && gkv == 0 && threadIdx.x == 0) p.n_split[r] = n_split;
+  if (s >= n_split) return;
+  const int u_begin = s * pps;
+  const int u_end = min(u_begin + pps, n_units);
   const long long page_elems = 2LL * p.Hkv * 16 * DH;
   const T* pool = reinterpret_cast<const T*>(p.pool);
   const T* blk = reinterpret_cast<const T*>(p.blk);
@@ -140,49 +144,71 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams p, SlotArgs sl) {
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // pairs of units (32 keys); key subset kq takes every KQ-th pair of the split
-  for (int u = u_begin + 2 * kq; u < u_end; u += 2 * KQ) {
+  // page ids of the split's context units, one per lane (pps <= 64)
+  int my_page = -1;
+  {
+    const int uu = u_begin + lane;
+    if (uu < u_end && uu < n_lp) {
+      const int lp = lp0 + uu;
+      const int idx = p.window > 0 ? lp % st.n_pages : lp;
+      my_page = p.page_table[(long long)slot * p.pt_stride + idx];
+      if (my_page < 0 || my_page >= p.max_pages) {
+        atomicOr(p.err, 2u);
+        my_page = -1;
+      }
+    }
+  }
+  auto unit_base = [&](int uu, int& pos0, bool& is_blk) -> const T* {
+    pos0 = 0;
+    is_blk = false;
+    if (uu >= u_end) return nullptr;
+    if (uu < n_lp) {
+      const int page = __shfl(my_page, uu - u_begin, 64);
+      pos0 = (lp0 + uu) * 16;
+      return page >= 0 ? pool + (long long)page * page_elems : nullptr;
+    }
+    is_blk = true;
+    return blk + (long long)r * page_elems;
+  };
+
+  // pairs of units (32 keys); key subset kq takes every KQ-th pair of the
+  // split; the K/V fragments of the next pair are loaded while the current
+  // one is multiplied
+  Frag kf[2][NJ], kn[2][NJ];
+  V4 vv[2][ND], vn[2][ND];
+  auto load_pair = [&](int u, Frag (&kd)[2][NJ], V4 (&vd)[2][ND]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      int pos0;
+      bool is_blk;
+      const T* b = unit_base(u + t, pos0, is_blk);
+      if (b) {
+        const T* kb = b + (long long)gkv * 16 * DH + l16 * DH + 8 * g4;
+        const T* vb = b + (long long)(p.Hkv + gkv) * 16 * DH + l16 * 16 + 4 * g4;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) kd[t][j] = load8<T>(kb + 32 * j);
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) vd[t][dt] = *reinterpret_cast<const V4*>(vb + dt * 256);
+      }
+    }
+  };
+  int u = u_begin + 2 * kq;
+  if (u < u_end) load_pair(u, kf, vv);
+  for (; u < u_end; u += 2 * KQ) {
+    const bool more = u + 2 * KQ < u_end;
+    if (more) load_pair(u + 2 * KQ, kn, vn);
     const T* base[2];
     bool valid[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int uu = u + t;
-      base[t] = nullptr;
-      int pos0 = 0;
-      bool is_blk = false;
-      if (uu < u_end) {
-        if (uu < n_lp) {
-          const int lp = lp0 + uu;
-          const int idx = p.window > 0 ? lp % st.n_pages : lp;
-          const int page = p.page_table[(long long)slot * p.pt_stride + idx];
-          if (page >= 0 && page < p.max_pages) {
-            base[t] = pool + (long long)page * page_elems;
-          } else if (lane == 0) {
-            atomicOr(p.err, 2u);
-          }
-          pos0 = lp * 16;
-        } else {
-          base[t] = blk + (long long)r * page_elems;
-          is_blk = true;
-        }
-      }
+      int pos0;
+      bool is_blk;
+      base[t] = unit_base(u + t, pos0, is_blk);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = 4 * g4 + i;
         valid[t][i] = base[t] != nullptr &&
                       (is_blk ? key < p.B : (pos0 + key >= lo && pos0 + key < hi));
-      }
-    }
-
-    // K of both units first; V is loaded once the scores are formed, so the
-    // two fragment sets never need registers at the same time
-    Frag kf[2][NJ];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (base[t]) {
-        const T* kb = base[t] + (long long)gkv * 16 * DH + l16 * DH + 8 * g4;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) kf[t][j] = load8<T>(kb + 32 * j);
       }
     }
 
@@ -196,15 +222,6 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams p, SlotArgs sl) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[4 * t + i] = valid[t][i] ? sacc[i] * p.scale : NEG;
-    }
-    V4 vv[2][ND];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (base[t]) {
-        const T* vb = base[t] + (long long)(p.Hkv + gkv) * 16 * DH + l16 * 16 + 4 * g4;
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) vv[t][dt] = *reinterpret_cast<const V4*>(vb + dt * 256);
-      }
     }
     float mx = sv[0];
 #pragma unroll
@@ -244,6 +261,15 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams p, SlotArgs sl) {
         for (int i = 0; i < 4; ++i) vf[4 * t + i] = valid[t][i] ? vv[t][dt][i] : (T)0.0f;
       o[dt] = mfma_step(vf, pf, o[dt]);
       if (kSplitP<T>) o[dt] = mfma_step(vf, pf_lo, o[dt]);
+    }
+    if (more) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) kf[t][j] = kn[t][j];
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) vv[t][dt] = vn[t][dt];
+      }
     }
   }
 
@@ -287,7 +313,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams p, SlotArgs sl) {
 
   T* out = reinterpret_cast<T*>(p.out);
   const int nel = G * 16 * DH;
-  if (S == 1) {
+  if (n_split == 1) {
     float* wts = sml + KQ * G * 16 * 2;  // [G][16]: 1 / L
     if (kq == 0 && g4 == 0) wts[wq * 16 + l16] = 1.0f / Lq;
     __syncthreads();
@@ -323,24 +349,39 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p) {
   const int q = wid % 16;
   const int rh = wid / 16;  // r * Hq + h
   if (rh >= p.n_rh || q >= p.B) return;
+  const int r = rh / p.Hq, h = rh - r * p.Hq;
   const int S = p.n_splits;
+  const int ns = p.n_split[r];
+  if (ns <= 1) return;  // written by the attention kernel
   const long long pb = (long long)rh * S * 16 + q;
-  float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, p.part_ml[(pb + s * 16) * 2]);
+  const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + pb;
+  // lane s holds split s's (max, sum); weights are broadcast by shuffles
+  const float2 mine = lane < ns ? ml[lane * 16] : make_float2(-INFINITY, 0.f);
+  float mx = mine.x;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  const float w_mine = mine.x == -INFINITY ? 0.f : expf(mine.x - mx);
   float L = 0.f;
+  for (int s = 0; s < ns; ++s) L += __shfl(mine.y, s, 64) * __shfl(w_mine, s, 64);
   float acc[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) acc[c] = 0.f;
   const float* po = p.part_o + pb * DH + lane * C;
-  for (int s = 0; s < S; ++s) {
-    const float ms = p.part_ml[(pb + s * 16) * 2];
-    const float w = ms == -INFINITY ? 0.f : expf(ms - mx);
-    L += p.part_ml[(pb + s * 16) * 2 + 1] * w;
+  for (int s0 = 0; s0 < ns; s0 += 16) {
+    float v[16][C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc[c] += w * po[(long long)s * 16 * DH + c];
+    for (int k = 0; k < 16; ++k)
+#pragma unroll
+      for (int c = 0; c < C; ++c) v[k][c] = s0 + k < ns ? po[(long long)(s0 + k) * 16 * DH + c] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float w = __shfl(w_mine, (s0 + k) & 63, 64);
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        if (s0 + k < ns) acc[c] += w * v[k][c];
+    }
   }
   const float inv = 1.0f / L;
-  const int r = rh / p.Hq, h = rh - r * p.Hq;
   T* out = reinterpret_cast<T*>(p.out) + (long long)(r * p.B + q) * p.ldo + h * DH + lane * C;
 #pragma unroll
   for (int c = 0; c < C; ++c) out[c] = from_f<T>(acc[c] * inv);

@@ -91,8 +91,10 @@ struct AttnParams {
   int max_pages;
   int window;
   int Hq, Hkv, B;
-  int pps;       // units (pages) per split
-  int n_splits;  // grid.x
+  int split_target;  // splits aimed at per (request, KV head)
+  int pps_cap;       // at most this many pages per split
+  int* n_split;      // [n_req] out: splits of each request (read by k_combine)
+  int n_splits;      // grid.x: splits of the longest request
   int KQ;        // key subsets per workgroup (waves = Hq/Hkv * KQ)
   float scale;
   float* part_o;   // [n_req, Hq, n_splits, 16, dh]
@@ -105,6 +107,7 @@ struct AttnParams {
 struct CombineParams {
   const float* part_o;
   const float* part_ml;
+  const int* n_split;  // [n_req] splits of each request
   int n_splits, n_rh, Hq, B;  // n_rh = n_req * Hq
   void* out;  // storage dtype [n_req*B, Hq*dh]
   int ldo;
@@ -142,6 +145,12 @@ void launch_qkv_post(int dtype, int dh, int n_req, const QkvPostParams& p, const
 void launch_attention(int dtype, int dh, int n_req, const AttnParams& p, const SlotArgs& sl,
                       hipStream_t s);
 size_t attn_lds_bytes(int Hq, int Hkv, int dh, int KQ);
+// Pages per attention split of a request with n_units pages (the block counts
+// as one): about `target` splits, at most `cap` pages each.  Host and device.
+__host__ __device__ inline int split_pages(int n_units, int target, int cap) {
+  const int pps = (n_units + target - 1) / target;
+  return pps < 1 ? 1 : (pps > cap ? cap : pps);
+}
 void launch_combine(int dtype, int dh, const CombineParams& p, hipStream_t s);
 void launch_scatter(int dtype, int dh, const ScatterParams& p, hipStream_t s);
 void launch_finalize(const unsigned long long* keys, int rows, int vocab, int* draft,

@@ -47,21 +47,22 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t elt(const dflash_config& c) { return c.dtype == DFLASH_BF16 ? 2 : 4; }
 
-// Attention splits: a fixed number of KV pages per split for the handle, so a
-// request's arithmetic does not depend on the other requests of a call.
-// Small batches use short splits (many workgroups per request); large batches
-// longer ones (fewer partials).  Contexts above 128 splits widen them.
+// Attention splits: a request with u KV pages (the block counts as one) is
+// cut into about kSplitTarget(handle) splits of at most 64 pages; the cut
+// depends only on the handle and the request's own context, so a request's
+// arithmetic does not depend on the other requests of a call.  Small batches
+// aim at enough workgroups to cover the CUs, large batches at few partials.
+constexpr int kPpsCap = 64;
 int max_units(const dflash_config& c) {
   return c.window ? c.window / 16 + 2 : c.max_pages_per_req + 1;
 }
-int attn_pps(const dflash_config& c) {
-  int pps = 8;
-  while (pps < 64 && pps < c.max_batch) pps *= 2;
-  const int units = max_units(c);
-  pps = std::max(pps, (units + 127) / 128);
-  return pps;
+int split_target(const dflash_config& c) {
+  return std::min(64, std::max(1, 256 / (c.max_batch * c.n_kv_heads)));
 }
-int max_splits(const dflash_config& c) { return (max_units(c) + attn_pps(c) - 1) / attn_pps(c); }
+// ceil(u / ceil(u / T)) <= T; capped splits number at most ceil(u / 64)
+int max_splits(const dflash_config& c) {
+  return std::max(split_target(c), (max_units(c) + kPpsCap - 1) / kPpsCap);
+}
 // Upper bound of (requests x attention splits) handled in one draft call.
 int part_pairs(const dflash_config& c) { return c.max_batch * max_splits(c); }
 
@@ -96,7 +97,7 @@ int max_p(const dflash_config& c, GemmPlan Plans::*f) {
 
 struct Layout {
   size_t state, err, page_table, cos_t, sin_t;
-  size_t h, xa, xo, qkv, qb, blk, part_o, part_ml, z, keys, opart, dpart;
+  size_t h, xa, xo, qkv, qb, blk, part_o, part_ml, nsplit, z, keys, opart, dpart;
   size_t u, f, kvo;
   size_t total;
 };
@@ -129,6 +130,7 @@ Layout make_layout(const dflash_config& c) {
   const size_t pp = (size_t)part_pairs(c) * c.n_q_heads * 16;
   L.part_o = take(sizeof(float) * pp * c.head_dim);
   L.part_ml = take(sizeof(float) * pp * 2);
+  L.nsplit = take(sizeof(int) * c.max_batch);
   L.z = take(e * M * c.ffn);
   L.keys = take(sizeof(unsigned long long) * M);
   L.opart = take(sizeof(float) * max_p(c, &Plans::o) * M * c.hidden);
@@ -193,7 +195,9 @@ dflash_status validate(const dflash_config* c) {
   if (c->topk && c->vocab < DFLASH_MAX_TOPK) return bad("topk needs vocab >= 16");
   if (c->max_batch < 1 || c->max_batch > DFLASH_MAX_BATCH) return bad("max_batch out of range");
   if (c->max_pages < 1) return bad("max_pages must be positive");
-  if (c->max_pages_per_req < 1) return bad("max_pages_per_req must be positive");
+  if (c->max_pages_per_req < 1 || c->max_pages_per_req > 4095)
+    return bad("max_pages_per_req must be in [1, 4095] (contexts up to 65520 tokens)");
+  if (c->window > 65472) return bad("window must be at most 65472");
   if (c->window && c->max_pages_per_req < c->window / 16 + 1)
     return bad("max_pages_per_req must hold window/16 + 1 pages");
   if (c->max_position < c->block_size + 2) return bad("max_position too small");
@@ -592,15 +596,10 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   if (c.conv2 && !last_token) return fail(DFLASH_E_INVALID, "conv2 needs last_token");
   if (c.topk && (!topk_ids || !topk_logits)) return fail(DFLASH_E_INVALID, "topk needs topk_ids and topk_logits");
   if (c.conv2 || c.topk) return fail(DFLASH_E_UNSUPPORTED, "conv2 / topk are not implemented yet");
-  int max_units = 1;
   for (int i = 0; i < n_req; ++i) {
     const HostSlot& hs = h->slots[slots[i]];
     if (hs.ctx_len + c.block_size + 1 > c.max_position)
       return fail(DFLASH_E_CAPACITY, "slot %d: block positions beyond max_position", slots[i]);
-    int lo = hs.kv_begin;
-    if (c.window) lo = std::max(lo, hs.ctx_len - c.window);
-    const int n_lp = hs.ctx_len > lo ? (hs.ctx_len - 1) / 16 - lo / 16 + 1 : 0;
-    max_units = std::max(max_units, n_lp + 1);
   }
   st = ensure_device(h);
   if (st) return st;
@@ -614,12 +613,20 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   SlotArgs sl{};
   for (int i = 0; i < n_req; ++i) sl.slots[i] = slots[i];
 
-  // attention plan: KQ key subsets per workgroup (up to 8 waves) and the
-  // handle's fixed pages per split
+  // attention plan: KQ key subsets per workgroup (up to 8 waves); splits
+  // per request from its own context (the grid covers the longest)
   const int G = c.n_q_heads / c.n_kv_heads;
   const int KQ = std::max(1, 8 / G);
-  const int pps = attn_pps(c);
-  const int splits = (max_units + pps - 1) / pps;
+  const int target = split_target(c);
+  int splits = 1;
+  for (int i = 0; i < n_req; ++i) {
+    const HostSlot& hs = h->slots[slots[i]];
+    int lo = hs.kv_begin;
+    if (c.window) lo = std::max(lo, hs.ctx_len - c.window);
+    const int u = (hs.ctx_len > lo ? (hs.ctx_len - 1) / 16 - lo / 16 + 1 : 0) + 1;
+    const int pps = split_pages(u, target, kPpsCap);
+    splits = std::max(splits, (u + pps - 1) / pps);
+  }
 
   float* hbuf = at<float>(h, h->lay.h);
   float* dpart = at<float>(h, h->lay.dpart);
@@ -692,7 +699,9 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     ap.Hq = c.n_q_heads;
     ap.Hkv = c.n_kv_heads;
     ap.B = B;
-    ap.pps = pps;
+    ap.split_target = target;
+    ap.pps_cap = kPpsCap;
+    ap.n_split = at<int>(h, h->lay.nsplit);
     ap.n_splits = splits;
     ap.KQ = KQ;
     ap.scale = (float)(1.0 / sqrt((double)c.head_dim));
@@ -706,6 +715,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
       CombineParams cp{};
       cp.part_o = ap.part_o;
       cp.part_ml = ap.part_ml;
+      cp.n_split = ap.n_split;
       cp.n_splits = splits;
       cp.n_rh = n_req * c.n_q_heads;
       cp.Hq = c.n_q_heads;

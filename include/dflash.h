@@ -99,7 +99,7 @@ typedef struct dflash_config {
   int32_t topk;              /* 0, or 16 = keep top-16 per position ([guide] 7) */
   int32_t max_batch;         /* request slots */
   int32_t max_pages;         /* pages in the KV pool (per layer) */
-  int32_t max_pages_per_req; /* page-table width per slot */
+  int32_t max_pages_per_req; /* page-table width per slot, <= 4095 */
   int32_t max_position;      /* positions < max_position (RoPE table rows) */
   int32_t max_inject_rows;   /* rows per internal inject chunk (workspace size) */
   float rms_eps;             /* RMSNorm epsilon */
