@@ -83,6 +83,11 @@ CONFIGS = {
         hidden=768, n_q_heads=12, n_kv_heads=4, head_dim=64, ffn=2048,
         vocab=1500, n_layers=2, ctx=129, seed=14,
     ),
+    "small_window": dict(
+        hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1536,
+        vocab=3001, n_layers=2, window=128, batch=2, ctx=None,
+        ctx_range=(150, 420), seed=16,
+    ),
     "small_conv": dict(
         hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1536,
         vocab=3001, n_layers=2, conv2=1, topk=16, window=128, batch=2,

@@ -64,7 +64,7 @@ def test_verify_accept_matches_oracle(B):
     dr.check()
 
 
-def _setup(name, cycles=3, max_inject_rows=96, **over):
+def _setup(name, cycles=3, max_inject_rows=96, extra_pos=0, **over):
     dev = _dev()
     Drafter = _drafter()
     shape = synth.config(name, **over)
@@ -77,7 +77,7 @@ def _setup(name, cycles=3, max_inject_rows=96, **over):
     total = n_req * ppr + 5
     perm = synth.page_permutation(shape, total)
     dr = Drafter(shape, w, max_batch=n_req, max_pages=total, max_pages_per_req=ppr,
-                 max_position=max(ctxs) + cycles * (B + 1) + 2 * B + 8,
+                 max_position=max(ctxs) + extra_pos + cycles * (B + 1) + 2 * B + 8,
                  max_inject_rows=max_inject_rows, poison_kv=True)
     pages = [perm[r * ppr:(r + 1) * ppr] for r in range(n_req)]
     for r in range(n_req):
@@ -162,7 +162,7 @@ def _draft_both(dev, shape, dr, o, states, slots, last_tokens=None, free=False):
     return g_draft, ref_drafts, exempt
 
 
-@pytest.mark.parametrize("name", ["small_bf16", "small_block10", "small_dh64", "small_batch"])
+@pytest.mark.parametrize("name", ["small_bf16", "small_block10", "small_dh64", "small_batch", "small_window"])
 def test_draft_parity_lockstep(name):
     dev, shape, w, dr, ctxs, pages = _setup(name)
     o = DraftOracle(shape, w)
@@ -259,3 +259,27 @@ def test_free_running_within_tolerance(name):
     _inject_both(dev, shape, dr, o, states, list(range(n)), [0] * n, ctxs)
     _check_kv(shape, dr, o, states, pages, force=False)
     _draft_both(dev, shape, dr, o, states, list(range(n)), free=True)
+
+
+def test_window_ring_wraps_and_starts_late():
+    """Sliding window: the ring of W/16 + 1 pages wraps several times over
+    chunked injects; a request bound with a start position beyond 0 only ever
+    sees positions from there on."""
+    dev, shape, w, dr, ctxs, pages = _setup("small_window", max_inject_rows=40, extra_pos=200)
+    o = DraftOracle(shape, w)
+    # request 0 from position 0 in uneven chunks; request 1 starts at 200
+    dr.bind(1, pages[1], 200)
+    states = [o.new_request(0), o.new_request(200)]
+    done = [0, 200]
+    target = [ctxs[0], 200 + ctxs[1]]
+    while done != target:
+        for step in (37, 101, 64, 90, 150):
+            counts = [min(step, t - d) for t, d in zip(target, done)]
+            if sum(counts) == 0:
+                break
+            _inject_both(dev, shape, dr, o, states, [0, 1], done, counts)
+            done = [d + c for d, c in zip(done, counts)]
+    for r in (0, 1):
+        assert dr.context_length(r) == states[r].ctx_len
+    _check_kv(shape, dr, o, states, pages)
+    _draft_both(dev, shape, dr, o, states, [0, 1])
