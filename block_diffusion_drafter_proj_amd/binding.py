@@ -50,6 +50,10 @@ class DFlashLayerWeights(ctypes.Structure):
         "wqkv", "wo", "wgateup", "wdown", "attn_norm", "mlp_norm", "conv")]
 
 
+class DFlashDraftDebug(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("hidden", ctypes.c_void_p), ("hidden_in", ctypes.c_void_p)]
+
+
 class DFlashWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("embed", "lm_head", "fc", "fc_norm", "final_norm")] + [
         ("layers", DFlashLayerWeights * MAX_LAYERS)]
@@ -81,7 +85,7 @@ def lib() -> ctypes.CDLL:
             "dflash_bind_request": (i32, [vp, i32, pi32, i32, i32]),
             "dflash_context_length": (i32, [vp, i32]),
             "dflash_inject_context": (i32, [vp, vp, i32, pi32, pi32, ctypes.POINTER(vp), vp]),
-            "dflash_draft_block": (i32, [vp, vp, i32, pi32, vp, vp, vp, vp, vp, vp]),
+            "dflash_draft_block": (i32, [vp, vp, i32, pi32, vp, vp, vp, vp, ctypes.POINTER(DFlashDraftDebug)]),
             "dflash_verify_accept": (i32, [vp, vp, i32, vp, vp, vp, vp, vp]),
             "dflash_check": (i32, [vp, vp]),
             "dflash_profile_begin": (i32, [vp, ctypes.c_uint32]),
@@ -161,11 +165,14 @@ def dflash_inject_context(h: int, stream: int, slots, n_new, hidden_ptrs, debug_
 
 
 def dflash_draft_block(h: int, stream: int, slots, last_token: int, draft: int, topk_ids: int = 0,
-                       topk_logits: int = 0, debug_logits: int = 0, debug_hidden: int = 0) -> None:
+                       topk_logits: int = 0, debug_logits: int = 0, debug_hidden: int = 0,
+                       debug_hidden_in: int = 0) -> None:
     vp = ctypes.c_void_p
+    dbg = None
+    if debug_logits or debug_hidden or debug_hidden_in:
+        dbg = ctypes.byref(DFlashDraftDebug(debug_logits or None, debug_hidden or None, debug_hidden_in or None))
     _check(lib().dflash_draft_block(vp(h), vp(stream), len(slots), _i32s(slots), vp(last_token or None),
-                                    vp(draft or None), vp(topk_ids or None), vp(topk_logits or None),
-                                    vp(debug_logits or None), vp(debug_hidden or None)))
+                                    vp(draft or None), vp(topk_ids or None), vp(topk_logits or None), dbg))
 
 
 def dflash_verify_accept(h: int, stream: int, n_req: int, draft: int, target_greedy: int,

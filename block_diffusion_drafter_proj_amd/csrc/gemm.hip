@@ -22,7 +22,9 @@
 // add; SwiGLU (gate and up tiles processed back to back, silu(gate) * up
 // rounded to the storage dtype); greedy selection (packed logit/id key,
 // running max per row across the workgroup's tiles, one 64-bit atomic max per
-// row and workgroup, ties to the lowest id).
+// row and workgroup, ties to the lowest id); top-16 (the same keys, a sorted
+// list of 16 per row kept across the row's 16 lanes by bitonic sort and merge,
+// one list per row and workgroup merged by k_topk_merge).
 #include "common.h"
 #include "kernels.h"
 
@@ -31,6 +33,42 @@ namespace dflash {
 namespace {
 
 constexpr int kFragElems = 64 * 8;  // elements of one wave fragment
+
+__device__ __forceinline__ unsigned long long kmax(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+__device__ __forceinline__ unsigned long long kmin(unsigned long long a, unsigned long long b) {
+  return a < b ? a : b;
+}
+
+// 16 adjacent lanes hold one key each; sort them descending (bitonic).
+__device__ __forceinline__ unsigned long long sort16_desc(unsigned long long v, int i) {
+#pragma unroll
+  for (int k = 2; k <= 16; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const unsigned long long o = __shfl_xor(v, j, 64);
+      const bool desc = (i & k) == 0;
+      const bool lower = (i & j) == 0;
+      v = (lower == desc) ? kmax(v, o) : kmin(v, o);
+    }
+  }
+  return v;
+}
+
+// cur and nw are sorted descending over the 16 lanes; returns the 16 largest
+// of both, sorted descending (lane i holds rank i).
+__device__ __forceinline__ unsigned long long merge16_desc(unsigned long long cur,
+                                                           unsigned long long nw, int i) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long t = kmax(cur, __shfl(nw, (lane & 48) | (15 - i), 64));
+#pragma unroll
+  for (int j = 8; j > 0; j >>= 1) {
+    const unsigned long long o = __shfl_xor(t, j, 64);
+    t = ((i & j) == 0) ? kmax(t, o) : kmin(t, o);
+  }
+  return t;
+}
 
 template <typename T, int MT>
 struct Shape {
@@ -158,7 +196,7 @@ __global__ __launch_bounds__(1024) void k_gemm(GemmParams p) {
               const float sg = g0 / (1.0f + expf(-g0));
               reinterpret_cast<T*>(p.out_t)[(long long)em * p.ldt + n] = from_f<T>(sg * v);
             }
-          } else {  // EPI_ARGMAX: all 16 columns of a row sit in 16 adjacent lanes
+          } else if (EPI == EPI_ARGMAX) {  // all 16 columns of a row sit in 16 adjacent lanes
             if (ok && p.dbg) p.dbg[(long long)em * p.ld_dbg + n] = v;
             unsigned long long key = ok ? argmax_key(v, n, p.N) : 0ull;
 #pragma unroll
@@ -167,9 +205,22 @@ __global__ __launch_bounds__(1024) void k_gemm(GemmParams p) {
               key = other > key ? other : key;
             }
             best[it] = key > best[it] ? key : best[it];
+          } else {  // EPI_TOPK: running sorted top-16 of the row across its 16 lanes
+            if (ok && p.dbg) p.dbg[(long long)em * p.ld_dbg + n] = v;
+            const unsigned long long key = ok ? argmax_key(v, n, p.N) : 0ull;
+            best[it] = merge16_desc(best[it], sort16_desc(key, ecol), ecol);
           }
         }
       }
+    }
+  }
+  if (EPI == EPI_TOPK) {
+#pragma unroll
+    for (int it = 0; it < EIT; ++it) {
+      const int e = t + it * (int)blockDim.x;
+      if (e >= 256 * MT) break;
+      const int em = m_base + (e >> 8) * 16 + ((e >> 4) & 15);
+      if (em < p.M) p.keys[((long long)em * gridDim.x + blockIdx.x) * 16 + (e & 15)] = best[it];
     }
   }
   if (EPI == EPI_ARGMAX && n_units > 0) {
@@ -213,6 +264,7 @@ void launch_dt(int epi, const GemmPlan& pl, const GemmParams& p, hipStream_t s) 
     case EPI_PARTIAL: launch_t<T, EPI_PARTIAL>(pl, p, s); break;
     case EPI_RESID: launch_t<T, EPI_RESID>(pl, p, s); break;
     case EPI_SWIGLU: launch_t<T, EPI_SWIGLU>(pl, p, s); break;
+    case EPI_TOPK: launch_t<T, EPI_TOPK>(pl, p, s); break;
     default: launch_t<T, EPI_ARGMAX>(pl, p, s); break;
   }
 }

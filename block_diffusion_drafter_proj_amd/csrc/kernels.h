@@ -11,7 +11,7 @@ namespace dflash {
 constexpr int kMaxSeg = DFLASH_MAX_LAYERS;
 constexpr int kMaxChunkReq = 64;  // requests per inject scatter launch
 
-enum Epilogue { EPI_PARTIAL = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
+enum Epilogue { EPI_PARTIAL = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3, EPI_TOPK = 4 };
 
 // Y[M, N] = X[M, K] * W[N, K]^T with a fused epilogue, W packed by launch_pack.
 //  X: virtual concatenation along k of a_parts row-major arrays, each
@@ -33,8 +33,8 @@ struct GemmParams {
   int ldt;
   float* resid;  // EPI_RESID
   int ldr;
-  unsigned long long* keys;  // EPI_ARGMAX, one per row
-  float* dbg;                // EPI_ARGMAX, optional fp32 logits
+  unsigned long long* keys;  // EPI_ARGMAX: one per row; EPI_TOPK: [M][gridDim.x][16] sorted lists
+  float* dbg;                // EPI_ARGMAX / EPI_TOPK, optional fp32 logits
   int ld_dbg;
 };
 
@@ -59,6 +59,35 @@ struct NormParams {
   int d, M;
   float* dbg;  // optional fp32 copy of x [M, d]
   unsigned long long* zero_keys;  // optional: keys[row] = 0
+  // two-tap conv of the normalised rows (DFlash 2): out_i = w0*n_i + w1*n_{i-1}
+  // inside each request's block of B rows; row 0 reads embed[last_token[r]]
+  const void* conv;        // [2][d] taps (w0, w1) or NULL
+  const void* embed;       // [V, d]
+  const int* last_token;   // [n_req]
+  int B, vocab;
+  unsigned int* err;
+};
+
+// h_i += w0*y_i + w1*y_{i-1} with y the sum of a GEMM's split-K partials and
+// y_{-1} = embed[last_token[r]] at the start of each request's block.
+struct ResidConvParams {
+  float* h;  // [M, d]
+  const float* part;
+  int n_part;
+  const void* conv;  // [2][d]
+  const void* embed;
+  const int* last_token;
+  int B, vocab, d, M;
+  unsigned int* err;
+};
+
+// Merge of the per-workgroup top-16 lists of the LM head.
+struct TopkParams {
+  const unsigned long long* lists;  // [M][n_lists][16]
+  int n_lists, M, vocab;
+  int* draft;        // [M] argmax ids
+  int* topk_ids;     // [M][16]
+  float* topk_logits;  // [M][16]
 };
 
 struct SlotArgs {
@@ -153,6 +182,8 @@ __host__ __device__ inline int split_pages(int n_units, int target, int cap) {
 }
 void launch_combine(int dtype, int dh, const CombineParams& p, hipStream_t s);
 void launch_scatter(int dtype, int dh, const ScatterParams& p, hipStream_t s);
+void launch_resid_conv(int dtype, const ResidConvParams& p, hipStream_t s);
+void launch_topk_merge(const TopkParams& p, hipStream_t s);
 void launch_finalize(const unsigned long long* keys, int rows, int vocab, int* draft,
                      hipStream_t s);
 void launch_verify(int n_req, int B, int vocab, const int* draft, const int* greedy,

@@ -20,16 +20,20 @@ template <typename T> struct Out4;
 template <> struct Out4<bf16> { typedef bf16x4 type; };
 template <> struct Out4<float> { typedef f32x4 type; };
 
-// One workgroup of d/4 threads per row; every thread owns 4 consecutive
-// elements, issues all of its loads (residual and every split-K partial)
-// before summing them, and keeps the row in registers across the reduction.
-template <typename T>
-__global__ __launch_bounds__(1024) void k_rmsnorm(NormParams p) {
-  __shared__ float part[16];
-  const int row = blockIdx.x;
+// Sum of 4 values of every thread over the workgroup (fixed order).
+__device__ __forceinline__ float block_sum(float v, float* red, int slot) {
+  v = wave_sum(v);
   const int t = threadIdx.x;
-  const int k = 4 * t;
-  const long long plane = (long long)p.M * p.d;
+  const int nw = blockDim.x >> 6;
+  if ((t & 63) == 0) red[slot * 16 + (t >> 6)] = v;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < nw; ++w) tot += red[slot * 16 + w];
+  return tot;
+}
+
+template <typename T>
+__device__ __forceinline__ f32x4 load_row4(const NormParams& p, int row, int k, long long plane) {
   f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
   if (p.init_row) {
     const T* init = reinterpret_cast<const T*>(p.init_row) + k;
@@ -38,35 +42,117 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(NormParams p) {
   } else if (p.x_in) {
     x = *reinterpret_cast<const f32x4*>(p.x_in + (long long)row * p.ldx + k);
   }
-  const float* pp = p.part + (long long)row * p.d + k;
-  for (int q0 = 0; q0 < p.n_part; q0 += 8) {
-    f32x4 v[8];
+  if (p.n_part) {
+    const float* pp = p.part + (long long)row * p.d + k;
+    for (int q0 = 0; q0 < p.n_part; q0 += 8) {
+      f32x4 v[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (q0 + q < p.n_part) v[q] = *reinterpret_cast<const f32x4*>(pp + (q0 + q) * plane);
+      for (int q = 0; q < 8; ++q)
+        if (q0 + q < p.n_part) v[q] = *reinterpret_cast<const f32x4*>(pp + (q0 + q) * plane);
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (q0 + q < p.n_part) x += v[q];
+      for (int q = 0; q < 8; ++q)
+        if (q0 + q < p.n_part) x += v[q];
+    }
   }
+  return x;
+}
+
+// One workgroup of d/4 threads per row; every thread owns 4 consecutive
+// elements, issues all of its loads (residual and every split-K partial)
+// before summing them, and keeps the row in registers across the reduction.
+// With a conv, the workgroup also normalises the previous row of the block.
+template <typename T>
+__global__ __launch_bounds__(1024) void k_rmsnorm(NormParams p) {
+  __shared__ float red[32];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int k = 4 * t;
+  const long long plane = (long long)p.M * p.d;
+  const f32x4 x = load_row4<T>(p, row, k, plane);
+  const bool first = p.conv && (row % p.B) == 0;
+  f32x4 xp = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (p.conv && !first) xp = load_row4<T>(p, row - 1, k, plane);
   if (p.x_out) *reinterpret_cast<f32x4*>(p.x_out + (long long)row * p.ldx + k) = x;
   if (p.dbg) *reinterpret_cast<f32x4*>(p.dbg + (long long)row * p.d + k) = x;
-  float ss = (x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3]);
-  ss = wave_sum(ss);
-  const int nw = blockDim.x >> 6;
-  if ((t & 63) == 0) part[t >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
-  for (int w = 0; w < nw; ++w) tot += part[w];
+  const float tot = block_sum((x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3]), red, 0);
   const float r = 1.0f / sqrtf(tot / (float)p.d + p.eps);
   const T* gamma = reinterpret_cast<const T*>(p.gamma) + k;
+  f32x4 y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = x[i] * r * to_f(gamma[i]);
+  if (p.conv) {
+    f32x4 prev;
+    if (first) {
+      int tok = p.last_token[row / p.B];
+      if (tok < 0 || tok >= p.vocab) {
+        if (t == 0) atomicOr(p.err, 1u);
+        tok = 0;
+      }
+      const T* e = reinterpret_cast<const T*>(p.embed) + (long long)tok * p.d + k;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) prev[i] = to_f(e[i]);
+    } else {
+      const float totp = block_sum((xp[0] * xp[0] + xp[1] * xp[1]) + (xp[2] * xp[2] + xp[3] * xp[3]), red, 1);
+      const float rp = 1.0f / sqrtf(totp / (float)p.d + p.eps);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) prev[i] = xp[i] * rp * to_f(gamma[i]);
+    }
+    const T* w0 = reinterpret_cast<const T*>(p.conv) + k;
+    const T* w1 = w0 + p.d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = to_f(w0[i]) * y[i] + to_f(w1[i]) * prev[i];
+  }
   typename Out4<T>::type o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = from_f<T>(x[i] * r * to_f(gamma[i]));
+  for (int i = 0; i < 4; ++i) o[i] = from_f<T>(y[i]);
   *reinterpret_cast<typename Out4<T>::type*>(reinterpret_cast<T*>(p.out) + (long long)row * p.ldo + k) = o;
   if (p.zero_keys && t == 0) p.zero_keys[row] = 0ull;
 }
 
+// Residual add of a conv'd GEMM output (DFlash 2): one workgroup per row.
+template <typename T>
+__global__ __launch_bounds__(1024) void k_resid_conv(ResidConvParams p) {
+  const int row = blockIdx.x;
+  const int k = 4 * threadIdx.x;
+  const long long plane = (long long)p.M * p.d;
+  auto sum_parts = [&](int rw) {
+    f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float* pp = p.part + (long long)rw * p.d + k;
+    for (int q = 0; q < p.n_part; ++q) y += *reinterpret_cast<const f32x4*>(pp + q * plane);
+    return y;
+  };
+  const f32x4 y = sum_parts(row);
+  f32x4 prev;
+  if (row % p.B == 0) {
+    int tok = p.last_token[row / p.B];
+    if (tok < 0 || tok >= p.vocab) {
+      if (threadIdx.x == 0) atomicOr(p.err, 1u);
+      tok = 0;
+    }
+    const T* e = reinterpret_cast<const T*>(p.embed) + (long long)tok * p.d + k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) prev[i] = to_f(e[i]);
+  } else {
+    prev = sum_parts(row - 1);
+  }
+  const T* w0 = reinterpret_cast<const T*>(p.conv) + k;
+  const T* w1 = w0 + p.d;
+  f32x4* hp = reinterpret_cast<f32x4*>(p.h + (long long)row * p.d + k);
+  f32x4 h = *hp;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] += to_f(w0[i]) * y[i] + to_f(w1[i]) * prev[i];
+  *hp = h;
+}
+
 }  // namespace
+
+void launch_resid_conv(int dtype, const ResidConvParams& p, hipStream_t s) {
+  if (p.M <= 0) return;
+  if (dtype == DFLASH_BF16)
+    hipLaunchKernelGGL(k_resid_conv<bf16>, dim3(p.M), dim3(p.d / 4), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_resid_conv<float>, dim3(p.M), dim3(p.d / 4), 0, s, p);
+}
 
 void launch_rmsnorm(int dtype, const NormParams& p, hipStream_t s) {
   if (p.M <= 0) return;

@@ -97,7 +97,7 @@ int max_p(const dflash_config& c, GemmPlan Plans::*f) {
 
 struct Layout {
   size_t state, err, page_table, cos_t, sin_t;
-  size_t h, xa, xo, qkv, qb, blk, part_o, part_ml, nsplit, z, keys, opart, dpart;
+  size_t h, xa, xo, qkv, qb, blk, part_o, part_ml, nsplit, z, keys, tlists, opart, dpart;
   size_t u, f, kvo;
   size_t total;
 };
@@ -133,6 +133,7 @@ Layout make_layout(const dflash_config& c) {
   L.nsplit = take(sizeof(int) * c.max_batch);
   L.z = take(e * M * c.ffn);
   L.keys = take(sizeof(unsigned long long) * M);
+  L.tlists = c.topk ? take(sizeof(unsigned long long) * M * 256 * 16) : 0;
   L.opart = take(sizeof(float) * max_p(c, &Plans::o) * M * c.hidden);
   L.dpart = take(sizeof(float) * max_p(c, &Plans::down) * M * c.hidden);
   L.u = take(sizeof(float) * max_p(c, &Plans::fc) * R * c.hidden);
@@ -586,8 +587,11 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
 
 dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
                                  const int32_t* slots, const int32_t* last_token, int32_t* draft,
-                                 int32_t* topk_ids, float* topk_logits, float* debug_logits,
-                                 float* debug_hidden) {
+                                 int32_t* topk_ids, float* topk_logits,
+                                 const dflash_draft_debug* debug) {
+  float* debug_logits = debug ? debug->logits : nullptr;
+  float* debug_hidden = debug ? debug->hidden : nullptr;
+  const float* hidden_in = debug ? debug->hidden_in : nullptr;
   if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
   const dflash_config& c = h->cfg;
   dflash_status st = check_slots(h, n_req, slots);
@@ -595,7 +599,6 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   if (!draft) return fail(DFLASH_E_INVALID, "draft is NULL");
   if (c.conv2 && !last_token) return fail(DFLASH_E_INVALID, "conv2 needs last_token");
   if (c.topk && (!topk_ids || !topk_logits)) return fail(DFLASH_E_INVALID, "topk needs topk_ids and topk_logits");
-  if (c.conv2 || c.topk) return fail(DFLASH_E_UNSUPPORTED, "conv2 / topk are not implemented yet");
   for (int i = 0; i < n_req; ++i) {
     const HostSlot& hs = h->slots[slots[i]];
     if (hs.ctx_len + c.block_size + 1 > c.max_position)
@@ -644,18 +647,53 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     return g;
   };
 
+  // DFlash 2 two-tap conv: taps of point k of layer l, [2][d]
+  auto conv_taps = [&](int l, int k) { return wptr(h->w.layers[l].conv, (size_t)k * 2 * d, e); };
+  // h += conv(sum of partials) for the conv variant, one launch
+  auto resid_conv = [&](const float* part, int n_part, int l, int k) {
+    ResidConvParams rc{};
+    rc.h = hbuf;
+    rc.part = part;
+    rc.n_part = n_part;
+    rc.conv = conv_taps(l, k);
+    rc.embed = h->w.embed;
+    rc.last_token = last_token;
+    rc.B = B;
+    rc.vocab = c.vocab;
+    rc.d = d;
+    rc.M = M;
+    rc.err = at<unsigned int>(h, h->lay.err);
+    ProfScope ps(h, DFLASH_KERNEL_NORM, s);
+    launch_resid_conv(c.dtype, rc, s);
+  };
+  auto set_conv = [&](NormParams& np, int l, int k) {
+    np.conv = conv_taps(l, k);
+    np.embed = h->w.embed;
+    np.last_token = last_token;
+    np.B = B;
+    np.vocab = c.vocab;
+    np.err = at<unsigned int>(h, h->lay.err);
+  };
+
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& lw = h->w.layers[l];
-    // residual: block init (layer 0) or h + previous layer's down-projection partials
+    // residual: block init (layer 0) or h + previous layer's down-projection
+    // partials (with the conv variant folded in by its own launch first)
     NormParams n1{};
-    if (l == 0) {
+    if (hidden_in) {
+      n1.x_in = hidden_in + (size_t)l * M * d;  // teacher forcing
+    } else if (l == 0) {
       n1.init_row = wptr(h->w.embed, (size_t)c.mask_token_id * d, e);
+    } else if (c.conv2) {
+      resid_conv(dpart, pl.down.P, l - 1, 3);
+      n1.x_in = hbuf;
     } else {
       n1.x_in = hbuf;
       n1.part = dpart;
       n1.n_part = pl.down.P;
     }
-    n1.x_out = hbuf;
+    if (c.conv2) set_conv(n1, l, 0);
+    n1.x_out = (hidden_in || l == 0 || !c.conv2) ? hbuf : nullptr;
     n1.ldx = d;
     n1.gamma = lw.attn_norm;
     n1.eps = c.rms_eps;
@@ -736,9 +774,14 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
 
     NormParams n2{};
     n2.x_in = hbuf;
-    n2.part = opart;
-    n2.n_part = pl.o.P;
-    n2.x_out = hbuf;
+    if (c.conv2) {
+      resid_conv(opart, pl.o.P, l, 1);
+      set_conv(n2, l, 2);
+    } else {
+      n2.part = opart;
+      n2.n_part = pl.o.P;
+      n2.x_out = hbuf;
+    }
     n2.ldx = d;
     n2.gamma = lw.mlp_norm;
     n2.eps = c.rms_eps;
@@ -771,9 +814,15 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
 
   NormParams nf{};
   nf.x_in = hbuf;
-  nf.part = dpart;
-  nf.n_part = pl.down.P;
-  nf.x_out = hbuf;
+  if (hidden_in) {
+    nf.x_in = hidden_in + (size_t)c.n_layers * M * d;  // teacher forcing
+  } else if (c.conv2) {
+    resid_conv(dpart, pl.down.P, c.n_layers - 1, 3);
+  } else {
+    nf.part = dpart;
+    nf.n_part = pl.down.P;
+    nf.x_out = hbuf;
+  }
   nf.ldx = d;
   nf.gamma = h->w.final_norm;
   nf.eps = c.rms_eps;
@@ -790,11 +839,25 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   gl.tiles = tiles_of(c.vocab);
   gl.N = c.vocab;
   gl.P = 1;
-  gl.keys = at<unsigned long long>(h, h->lay.keys);
+  gl.keys = at<unsigned long long>(h, c.topk ? h->lay.tlists : h->lay.keys);
   gl.dbg = debug_logits;
   gl.ld_dbg = c.vocab;
-  { ProfScope ps(h, DFLASH_KERNEL_LM_HEAD, s); launch_gemm(c.dtype, EPI_ARGMAX, pl.lm, gl, s); }
   {
+    ProfScope ps(h, DFLASH_KERNEL_LM_HEAD, s);
+    launch_gemm(c.dtype, c.topk ? EPI_TOPK : EPI_ARGMAX, pl.lm, gl, s);
+  }
+  if (c.topk) {
+    TopkParams tp{};
+    tp.lists = gl.keys;
+    tp.n_lists = pl.lm.GP;
+    tp.M = M;
+    tp.vocab = c.vocab;
+    tp.draft = draft;
+    tp.topk_ids = topk_ids;
+    tp.topk_logits = topk_logits;
+    ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
+    launch_topk_merge(tp, s);
+  } else {
     ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
     launch_finalize(at<unsigned long long>(h, h->lay.keys), M, c.vocab, draft, s);
   }

@@ -50,7 +50,56 @@ __global__ __launch_bounds__(64) void k_verify(int B, int vocab, const int* draf
   }
 }
 
+// One workgroup per row: the per-workgroup sorted lists are merged pairwise
+// in LDS (each thread merges two lists of 16 by a sequential merge) until one
+// list remains; rank 0 is the greedy draft token.
+__global__ __launch_bounds__(256) void k_topk_merge(TopkParams p) {
+  __shared__ unsigned long long lst[256 * 16];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const unsigned long long* src = p.lists + (long long)row * p.n_lists * 16;
+  for (int e = t; e < 256 * 16; e += 256) lst[e] = (e / 16) < p.n_lists ? src[e] : 0ull;
+  __syncthreads();
+  for (int half = 128; half >= 1; half >>= 1) {
+    unsigned long long out[16];
+    if (t < half) {
+      const unsigned long long* a = lst + t * 16;
+      const unsigned long long* b = lst + (t + half) * 16;
+      int ia = 0, ib = 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const unsigned long long va = a[ia], vb = b[ib];
+        if (va >= vb) {
+          out[k] = va;
+          ++ia;
+        } else {
+          out[k] = vb;
+          ++ib;
+        }
+      }
+    }
+    __syncthreads();
+    if (t < half) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) lst[t * 16 + k] = out[k];
+    }
+    __syncthreads();
+  }
+  if (t < 16) {
+    const unsigned long long key = lst[t];
+    const int id = p.vocab - 1 - (int)(uint32_t)(key & 0xffffffffull);
+    p.topk_ids[(long long)row * 16 + t] = id;
+    p.topk_logits[(long long)row * 16 + t] = key_float((uint32_t)(key >> 32));
+    if (t == 0) p.draft[row] = id;
+  }
+}
+
 }  // namespace
+
+void launch_topk_merge(const TopkParams& p, hipStream_t s) {
+  if (p.M <= 0) return;
+  hipLaunchKernelGGL(k_topk_merge, dim3(p.M), dim3(256), 0, s, p);
+}
 
 void launch_finalize(const unsigned long long* keys, int rows, int vocab, int* draft,
                      hipStream_t s) {

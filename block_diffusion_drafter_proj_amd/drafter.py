@@ -135,14 +135,16 @@ class Drafter:
                                 debug_f.data_ptr() if debug_f is not None else 0)
 
     def draft(self, slots, last_token: torch.Tensor | None = None, *, out: torch.Tensor | None = None,
-              topk_ids=None, topk_logits=None, debug_logits=None, debug_hidden=None) -> torch.Tensor:
+              topk_ids=None, topk_logits=None, debug_logits=None, debug_hidden=None,
+              hidden_in=None) -> torch.Tensor:
         n = len(slots)
         Bk = self.cfg.block_size
         if out is None:
             out = torch.empty((n, Bk), dtype=torch.int32, device=self.dev)
         ptr = lambda t: t.data_ptr() if t is not None else 0  # noqa: E731
         B.dflash_draft_block(self.h, self.stream, list(slots), ptr(last_token), out.data_ptr(),
-                             ptr(topk_ids), ptr(topk_logits), ptr(debug_logits), ptr(debug_hidden))
+                             ptr(topk_ids), ptr(topk_logits), ptr(debug_logits), ptr(debug_hidden),
+                             ptr(hidden_in))
         return out
 
     def verify(self, draft: torch.Tensor, greedy: torch.Tensor, accept=None, committed=None, last=None):

@@ -200,12 +200,27 @@ dflash_status dflash_inject_context(dflash_handle *h, void *stream, int32_t n_re
                                     const int32_t *slots, const int32_t *n_new,
                                     const void *const *hidden, void *debug_f);
 
+/* Optional validation outputs and inputs of dflash_draft_block (device
+ * buffers; any field may be NULL):
+ *   logits     [n_req, B, V] fp32 logits of every block position
+ *   hidden     [L+1, n_req*B, d] fp32 residual stream entering layer 0..L-1
+ *              and leaving the last layer
+ *   hidden_in  [L+1, n_req*B, d] fp32 teacher forcing: the residual stream
+ *              entering layer l (and the final norm, l = L) is replaced by
+ *              hidden_in[l], so every layer and the head can be checked on
+ *              given inputs.  The same kernels run; only their input changes. */
+typedef struct dflash_draft_debug {
+  float *logits;
+  float *hidden;
+  const float *hidden_in;
+} dflash_draft_debug;
+
 /* Steps 3 and 4 ([guide] 3.1, 3.2, 7): one forward of the draft over B mask
  * positions n .. n+B-1 (n = ctx_len + 1) of each request: pre-norm layers with
  * bidirectional attention over the visible context KV and the block, GQA,
  * SwiGLU; the draft's final RMSNorm; the shared LM head; greedy argmax with
  * ties to the lowest id.
- *   slots        host [n_req] distinct bound slots with ctx_len >= 1
+ *   slots        host [n_req] distinct bound slots
  *   last_token   device [n_req] int32 last verified token (conv2 only, else
  *                may be NULL): the block start of the two-tap conv reads its
  *                embedding
@@ -213,13 +228,11 @@ dflash_status dflash_inject_context(dflash_handle *h, void *stream, int32_t n_re
  *   topk_ids     device [n_req, B, 16] int32, topk_logits [n_req, B, 16] fp32:
  *                top-16 by logit descending then id ascending (topk == 16),
  *                else NULL
- *   debug_logits optional device [n_req, B, V] fp32
- *   debug_hidden optional device [L+1, n_req*B, d] fp32: residual stream
- *                before layer 0 and after every layer */
+ *   debug        optional validation buffers (NULL in timed runs) */
 dflash_status dflash_draft_block(dflash_handle *h, void *stream, int32_t n_req,
                                  const int32_t *slots, const int32_t *last_token,
                                  int32_t *draft, int32_t *topk_ids, float *topk_logits,
-                                 float *debug_logits, float *debug_hidden);
+                                 const dflash_draft_debug *debug);
 
 /* Step 5 ([news] "DFlash 2 的核心：一次写一块"; [guide] 3.3): a = number of
  * leading positions where draft equals the target's greedy token; commits

@@ -171,7 +171,7 @@ def test_null_handle_is_rejected():
     lib = B.lib()
     assert lib.dflash_bind_request(None, 0, None, 0, 0) == B.E_INVALID
     assert lib.dflash_inject_context(None, None, 1, None, None, None, None) == B.E_INVALID
-    assert lib.dflash_draft_block(None, None, 1, None, None, None, None, None, None, None) == B.E_INVALID
+    assert lib.dflash_draft_block(None, None, 1, None, None, None, None, None, None) == B.E_INVALID
     assert lib.dflash_verify_accept(None, None, 1, None, None, None, None, None) == B.E_INVALID
     assert lib.dflash_check(None, None) == B.E_INVALID
     assert lib.dflash_context_length(None, 0) == -1

@@ -137,7 +137,12 @@ def _draft_both(dev, shape, dr, o, states, slots, last_tokens=None, free=False):
     lt = None
     if last_tokens is not None:
         lt = torch.tensor(last_tokens, dtype=torch.int32, device=dev)
-    draft = dr.draft(slots, lt, debug_logits=dbg_logits, debug_hidden=dbg_hidden)
+    tk_ids = tk_val = None
+    if shape.get("topk"):
+        tk_ids = torch.empty((n, B, 16), dtype=torch.int32, device=dev)
+        tk_val = torch.empty((n, B, 16), dtype=torch.float32, device=dev)
+    draft = dr.draft(slots, lt, debug_logits=dbg_logits, debug_hidden=dbg_hidden,
+                     topk_ids=tk_ids, topk_logits=tk_val)
     torch.cuda.synchronize()
     g_draft = draft.cpu().numpy()
     g_logits = dbg_logits.cpu().numpy()
@@ -158,11 +163,34 @@ def _draft_both(dev, shape, dr, o, states, slots, last_tokens=None, free=False):
         else:
             assert_rows_close(g_logits[i], logits, what=f"logits req {r}")
         exempt += assert_tokens_match(g_draft[i], logits, what=f"draft req {r}")
+        if tk_ids is not None:
+            _check_topk(tk_ids[i].cpu().numpy(), tk_val[i].cpu().numpy(), g_logits[i], logits, g_draft[i])
         ref_drafts.append(np.argmax(logits, axis=-1))
     return g_draft, ref_drafts, exempt
 
 
-@pytest.mark.parametrize("name", ["small_bf16", "small_block10", "small_dh64", "small_batch", "small_window"])
+def _check_topk(ids, vals, g_logits, ref_logits, g_draft):
+    """Top-16 per position: ids exact at ranks whose logit gaps to both
+    neighbours (in the oracle) are at least 1e-2; values equal the GPU's own
+    logits at those ids and sit within tolerance of the oracle's; rank 0 is
+    the draft token."""
+    from oracle import select
+
+    _, _, (rid, rval) = select(ref_logits, topk=17)
+    for b in range(ids.shape[0]):
+        assert ids[b, 0] == g_draft[b]
+        np.testing.assert_array_equal(vals[b], g_logits[b, ids[b]])
+        assert np.all(np.diff(vals[b]) <= 0)
+        gaps = np.abs(np.diff(rval[b]))
+        for k in range(16):
+            left = gaps[k - 1] if k > 0 else np.inf
+            if min(left, gaps[k]) >= 1e-2:
+                assert ids[b, k] == rid[b, k], (b, k, ids[b].tolist(), rid[b, :16].tolist())
+        assert_rows_close(vals[b][None], rval[b, :16][None], what="top-16 logits")
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "small_block10", "small_dh64", "small_batch", "small_window",
+                                  "small_conv"])
 def test_draft_parity_lockstep(name):
     dev, shape, w, dr, ctxs, pages = _setup(name)
     o = DraftOracle(shape, w)
@@ -178,8 +206,10 @@ def test_draft_parity_lockstep(name):
     sched = [synth.accept_schedule(shape, 3, r) for r in slots]
     g = synth.rng(shape["seed"], synth.S_ACCEPT, 99)
     exempt = 0
+    last = [int(x) for x in synth.rng(shape["seed"], synth.S_ACCEPT, 98).integers(0, V, size=n)]
     for cyc in range(3):
-        g_draft, ref_drafts, ex = _draft_both(dev, shape, dr, o, states, slots)
+        g_draft, ref_drafts, ex = _draft_both(dev, shape, dr, o, states, slots,
+                                              last if shape.get("conv2") else None)
         exempt += ex
         G = np.stack([synth.synthetic_greedy(ref_drafts[i], int(sched[i][cyc]), V, g) for i in slots])
         acc, com, last = dr.verify(torch.from_numpy(np.stack(ref_drafts).astype(np.int32)).to(dev),
@@ -187,10 +217,13 @@ def test_draft_parity_lockstep(name):
         torch.cuda.synchronize()
         acc = acc.cpu().numpy()
         counts = []
+        lastg = last.cpu().numpy()
         for i in slots:
             a, c, nx = verify_accept(ref_drafts[i], G[i])
             assert acc[i] == a == sched[i][cyc]
+            assert lastg[i] == nx
             counts.append(a + 1)
+        last = [int(x) for x in lastg]
         starts = [states[i].ctx_len for i in slots]
         _inject_both(dev, shape, dr, o, states, slots, starts, counts)
         _check_kv(shape, dr, o, states, pages)
