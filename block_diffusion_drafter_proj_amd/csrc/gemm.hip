@@ -305,6 +305,10 @@ GemmPlan plan_gemm(int tiles, int K, int kblock, bool single_split) {
 
 void launch_gemm(int dtype, int epi, const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
   if (p.M <= 0 || p.tiles <= 0) return;
+  if (gemm_use_big(dtype, p.M)) {
+    launch_gemm_big(epi, p, s);
+    return;
+  }
   if (dtype == DFLASH_BF16)
     launch_dt<bf16>(epi, pl, p, s);
   else

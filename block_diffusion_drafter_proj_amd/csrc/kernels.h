@@ -164,6 +164,11 @@ struct ScatterParams {
 };
 
 int gemm_kblock(int dtype, int M);
+// Tiled MFMA kernel for M >= 64 (bf16): one split, lists of top-16 per row
+// for `tiles` 16-row weight tiles.
+inline bool gemm_use_big(int dtype, int M) { return dtype == DFLASH_BF16 && M >= 64; }
+int gemm_big_lists(int tiles);
+void launch_gemm_big(int epi, const GemmParams& p, hipStream_t s);
 GemmPlan plan_gemm(int tiles, int K, int kblock, bool single_split);
 void launch_gemm(int dtype, int epi, const GemmPlan& pl, const GemmParams& p, hipStream_t s);
 size_t packed_elems(int N, int K);

@@ -75,6 +75,10 @@ struct Plans {
 int tiles_of(int n) { return (n + 15) / 16; }
 
 Plans make_plans(const dflash_config& c, int M) {
+  if (gemm_use_big(c.dtype, M)) {  // tiled kernel: one split everywhere
+    const GemmPlan one{1, 4, 1};
+    return Plans{one, one, one, one, one, one, one};
+  }
   const int kb = gemm_kblock(c.dtype, M);
   const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
@@ -133,7 +137,8 @@ Layout make_layout(const dflash_config& c) {
   L.nsplit = take(sizeof(int) * c.max_batch);
   L.z = take(e * M * c.ffn);
   L.keys = take(sizeof(unsigned long long) * M);
-  L.tlists = c.topk ? take(sizeof(unsigned long long) * M * 256 * 16) : 0;
+  L.tlists = c.topk ? take(sizeof(unsigned long long) * M * 16 *
+                           std::max(256, gemm_big_lists(tiles_of(c.vocab)))) : 0;
   L.opart = take(sizeof(float) * max_p(c, &Plans::o) * M * c.hidden);
   L.dpart = take(sizeof(float) * max_p(c, &Plans::down) * M * c.hidden);
   L.u = take(sizeof(float) * max_p(c, &Plans::fc) * R * c.hidden);
@@ -849,7 +854,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   if (c.topk) {
     TopkParams tp{};
     tp.lists = gl.keys;
-    tp.n_lists = pl.lm.GP;
+    tp.n_lists = gemm_use_big(c.dtype, M) ? gemm_big_lists(gl.tiles) : pl.lm.GP;
     tp.M = M;
     tp.vocab = c.vocab;
     tp.draft = draft;

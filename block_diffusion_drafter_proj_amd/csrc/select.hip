@@ -50,38 +50,50 @@ __global__ __launch_bounds__(64) void k_verify(int B, int vocab, const int* draf
   }
 }
 
-// One workgroup per row: the per-workgroup sorted lists are merged pairwise
-// in LDS (each thread merges two lists of 16 by a sequential merge) until one
-// list remains; rank 0 is the greedy draft token.
+// Merge two lists sorted descending into the 16 largest, sorted descending.
+__device__ __forceinline__ void merge_lists(const unsigned long long* a, const unsigned long long* b,
+                                            unsigned long long* out) {
+  int ia = 0, ib = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const unsigned long long va = a[ia], vb = b[ib];  // ia + ib = k <= 15
+    if (va >= vb) {
+      out[k] = va;
+      ++ia;
+    } else {
+      out[k] = vb;
+      ++ib;
+    }
+  }
+}
+
+// One workgroup per row: every thread first folds lists t, t+256, ... into a
+// running top-16, then the 256 running lists are merged pairwise in LDS until
+// one list remains; rank 0 is the greedy draft token.
 __global__ __launch_bounds__(256) void k_topk_merge(TopkParams p) {
   __shared__ unsigned long long lst[256 * 16];
   const int row = blockIdx.x;
   const int t = threadIdx.x;
   const unsigned long long* src = p.lists + (long long)row * p.n_lists * 16;
-  for (int e = t; e < 256 * 16; e += 256) lst[e] = (e / 16) < p.n_lists ? src[e] : 0ull;
+  unsigned long long run[16], nxt[16], tmp[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) run[k] = 0ull;
+  for (int li = t; li < p.n_lists; li += 256) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) nxt[k] = src[(long long)li * 16 + k];
+    merge_lists(run, nxt, tmp);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) run[k] = tmp[k];
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) lst[t * 16 + k] = run[k];
   __syncthreads();
   for (int half = 128; half >= 1; half >>= 1) {
-    unsigned long long out[16];
-    if (t < half) {
-      const unsigned long long* a = lst + t * 16;
-      const unsigned long long* b = lst + (t + half) * 16;
-      int ia = 0, ib = 0;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const unsigned long long va = a[ia], vb = b[ib];
-        if (va >= vb) {
-          out[k] = va;
-          ++ia;
-        } else {
-          out[k] = vb;
-          ++ib;
-        }
-      }
-    }
+    if (t < half) merge_lists(lst + t * 16, lst + (t + half) * 16, tmp);
     __syncthreads();
     if (t < half) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) lst[t * 16 + k] = out[k];
+      for (int k = 0; k < 16; ++k) lst[t * 16 + k] = tmp[k];
     }
     __syncthreads();
   }
