@@ -2,27 +2,43 @@
 """Throughput of the DFlash drafting hot path on one MI355X.
 
 One step is one speculative cycle of the whole path on a batch of synthetic
-input: the draft forward over a block of mask positions (steps 3-4), prefix
-acceptance against synthetic target tokens (step 5), and injection of the
-accepted rows' target features into the draft KV cache (steps 1-2).
+input.  The cycle has three parts:
+  * the draft forward over a block of mask positions (steps 3-4);
+  * prefix acceptance against synthetic target tokens (step 5);
+  * injection of every request's accepted rows' target features into the
+    draft KV cache (steps 1-2).
 
-Workload (default ``qwen3_8b``): Qwen3-8B-shaped 5-layer draft, bf16, hidden
-4096, 32 q / 8 kv heads, head_dim 128, SwiGLU 12288, vocab 151936 shared LM
-head, 5 target feature layers projected 20480 -> 4096, block 16, batch 1,
-context 4096 injected positions.  Weights N(0, 0.02), target hidden states
-N(0, 1), accept length per block drawn from U{1..16}.  Every input is seeded
-and resident in HBM before the timed region.
+Default workload ``qwen3_8b``:
+  * Qwen3-8B-shaped 5-layer draft, bf16: hidden 4096, 32 q / 8 kv heads,
+    head_dim 128, SwiGLU 12288, vocab 151936 shared LM head;
+  * 5 target feature layers projected 20480 -> 4096;
+  * block 16, batch 1, context 4096 injected positions.
 
-Target tokens must agree with the GPU's own drafts on a prescribed prefix, so
-the cycle sequence is run once untimed to record the drafts and build the
-target tokens, the state is rebuilt from the same context, and the same
-cycles are then timed back to back with no host synchronisation inside.
+``--config`` selects another workload of ``synth.CONFIGS``:
+  * ``llama31_8b``: block 10, context 8192;
+  * ``coder_b64``: 8 layers, 64 requests with ragged contexts U[512, 8192];
+  * ``dflash2_long``: conv taps and top-16, batch 4, context 32768 with a
+    4096-token window.
 
-Output: one JSON line.  ``value`` is draft blocks/s of the full cycle;
-accepted tok/s, the draft-only rate at fixed context, the per-kernel time
-breakdown, the roofline of the dominant kernel (the LM-head GEMM, timed with
-HIP events on the call's stream during the timed region) and the CPU oracle
-timed on the host are reported beside it.
+Inputs:
+  * Weights are N(0, 0.02) and target hidden states are N(0, 1).
+  * The accept length per block and request is drawn from U{1..B}.
+  * Every input is seeded and resident in HBM before the timed region.
+
+Target tokens must agree with the GPU's own drafts on a prescribed prefix.
+So the cycle sequence is first run once, untimed, to record the drafts and
+build the target tokens (and the next cycle's injected rows).  The state is
+then rebuilt from the same context, and the same cycles are timed back to
+back with no host synchronisation inside.
+
+Output is one JSON line:
+  * ``value``: draft blocks/s of the full cycle (requests x cycles / s);
+  * beside it: accepted tok/s, the draft-only rate at fixed context and the
+    per-kernel time breakdown;
+  * the roofline of the dominant kernel class, timed with HIP events on the
+    call's stream during the timed region and priced against HBM or MFMA,
+    whichever bounds it;
+  * the CPU oracle, timed on the host.
 """
 from __future__ import annotations
 
@@ -41,59 +57,99 @@ sys.path.insert(0, ROOT)
 
 METRIC = "draft blocks/s + accepted tok/s, ctx4K block16 bf16; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
-PROFILE_FILE = os.path.join(ROOT, "profiles", "lm_head_gemm_qwen3_8b_ctx4096.md")
-GEMM_SRC = os.path.join(ROOT, "block_diffusion_drafter_proj_amd", "csrc", "gemm.hip")
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense, MI355X published figures
+CSRC = os.path.join(ROOT, "block_diffusion_drafter_proj_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+GEMM_CLASSES = ("qkv_gemm", "o_gemm", "gateup_gemm", "down_gemm", "lm_head")
 
 
 def elt(shape):
     return 2 if shape["dtype"] == "bf16" else 4
 
 
-def draft_bytes(shape, ctx):
-    """Algorithmic HBM bytes of one draft forward of one request at context ``ctx``:
-    every weight the forward multiplies once, the visible context K/V once."""
+def draft_bytes(shape, visible):
+    """Algorithmic HBM bytes of one draft forward of requests with ``visible``
+    context positions each: every weight the forward multiplies once, each
+    request's visible context K/V once."""
     e = elt(shape)
     d, hq, hkv, dh, F, V, L = (shape[k] for k in ("hidden", "n_q_heads", "n_kv_heads", "head_dim",
                                                    "ffn", "vocab", "n_layers"))
     layer = (hq + 2 * hkv) * dh * d + d * hq * dh + 2 * F * d + d * F
-    kv = L * ctx * 2 * hkv * dh
+    kv = L * sum(visible) * 2 * hkv * dh
     return e * (L * layer + V * d + kv)
 
 
 def inject_bytes(shape, rows):
-    """Algorithmic bytes of injecting ``rows`` positions: W_fc and every layer's
-    K/V projection once, the hidden rows in, the K/V rows out."""
+    """Algorithmic bytes of injecting ``rows`` positions.  Covers W_fc and every
+    layer's K/V projection once, the hidden rows in and the K/V rows out."""
     e = elt(shape)
     d, hkv, dh, L, K = (shape[k] for k in ("hidden", "n_kv_heads", "head_dim", "n_layers", "n_feat"))
     return e * (K * d * d + L * 2 * hkv * dh * d + rows * (K * d + L * 2 * hkv * dh))
 
 
-def lm_head_bytes(shape, rows):
+def class_work(shape, cls, M, visible):
+    """(flops, algorithmic bytes) of ONE launch of a draft kernel class.
+
+    M is the number of block rows (requests x block) and ``visible`` the
+    per-request visible context.  GEMM bytes count the weights, the
+    activations in and the outputs (argmax output is negligible).  Attention
+    counts the visible K/V and the block's q/k/v in and o out."""
     e = elt(shape)
-    return e * (shape["vocab"] * shape["hidden"] + rows * shape["hidden"])
+    d, hq, hkv, dh, F, V, B = (shape[k] for k in ("hidden", "n_q_heads", "n_kv_heads", "head_dim",
+                                                   "ffn", "vocab", "block_size"))
+    nk = {"qkv_gemm": ((hq + 2 * hkv) * dh, d), "o_gemm": (d, hq * dh), "gateup_gemm": (2 * F, d),
+          "down_gemm": (d, F), "lm_head": (V, d)}
+    if cls in nk:
+        N, K = nk[cls]
+        n_out = 0 if cls == "lm_head" else (F if cls == "gateup_gemm" else N)
+        return 2.0 * M * N * K, e * (N * K + M * K + M * n_out)
+    if cls == "attn":
+        keys = sum(v + B for v in visible)
+        flops = 4.0 * hq * dh * B * keys
+        return flops, e * (sum(visible) * 2 * hkv * dh + M * (hq + 2 * hkv) * dh + M * hq * dh)
+    return None
 
 
-def file_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def file_sha(*paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(shape):
-    """HBM bytes per LM-head launch from the committed counter summary, or None
-    when it is missing or was taken from a different GEMM source."""
-    if not os.path.exists(PROFILE_FILE):
+def kernel_sources(shape, cls, M):
+    """Source files whose kernels a class launches at this row count."""
+    if cls in GEMM_CLASSES:
+        big = shape["dtype"] == "bf16" and M >= 64
+        return [os.path.join(CSRC, "gemm_big.hip" if big else "gemm.hip")]
+    if cls == "attn":
+        return [os.path.join(CSRC, "attention.hip")]
+    return []
+
+
+def measured_traffic(config, cls, srcs):
+    """HBM bytes per launch from the committed counter summary
+    ``profiles/<class>_<workload>.md``.  None when the summary is missing or
+    was taken from a different kernel source."""
+    path = os.path.join(PROFILES, f"{cls}_{config}.md")
+    if not srcs or not os.path.exists(path):
         return None
-    txt = open(PROFILE_FILE).read()
+    txt = open(path).read()
     m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    s = re.search(r"gemm_source_sha256_16:\s*([0-9a-f]+)", txt)
-    if not m or not s or s.group(1) != file_sha(GEMM_SRC):
+    s = re.search(r"source_sha256_16:\s*([0-9a-f]+)", txt)
+    if not m or not s or s.group(1) != file_sha(*srcs):
         return None
     return float(m.group(1))
 
 
-def cpu_baseline(shape, weights, a_mean):
-    """The oracle on the host: one cycle (inject of a_mean+1 rows, one draft
-    forward at the workload's context, the accept step)."""
+def cpu_baseline(shape, weights, a_mean, visible):
+    """The oracle on the host: one cycle of ONE request.
+
+    The cycle is one draft forward with ``visible`` context positions, the
+    accept step, and the inject of a_mean+1 rows.  Requests are independent,
+    so a batch costs the oracle this once per request."""
     import synth
     from oracle import DraftOracle, select, verify_accept
 
@@ -104,18 +160,18 @@ def cpu_baseline(shape, weights, a_mean):
         threads = os.cpu_count() or 1
     o = DraftOracle(shape, weights)
     st = o.new_request()
-    ctx = shape["ctx"]
-    # the context K/V of the sample: random bf16 values of the workload's shape
+    # the context K/V of the sample: random values of the workload's shape
     g = np.random.default_rng(7)
     for l in range(shape["n_layers"]):
-        st.K[l] = synth.to_storage(g.standard_normal((ctx, shape["n_kv_heads"], shape["head_dim"]), np.float32), shape["dtype"])
-        st.V[l] = synth.to_storage(g.standard_normal((ctx, shape["n_kv_heads"], shape["head_dim"]), np.float32), shape["dtype"])
-    st.ctx_len = ctx
+        st.K[l] = synth.to_storage(g.standard_normal((visible, shape["n_kv_heads"], shape["head_dim"]), np.float32), shape["dtype"])
+        st.V[l] = synth.to_storage(g.standard_normal((visible, shape["n_kv_heads"], shape["head_dim"]), np.float32), shape["dtype"])
+    st.ctx_len = visible
     rows = int(round(a_mean)) + 1
-    H = synth.hidden_rows(shape, 0, ctx, rows)
+    H = synth.hidden_rows(shape, 0, visible, rows)
+    last = 0 if shape.get("conv2") else None
     t0 = time.perf_counter()
-    logits = o.draft_block(st)
-    d, _, _ = select(logits)
+    logits = o.draft_block(st, last)
+    d, _, _ = select(logits, shape.get("topk") or 0)
     G = np.concatenate([d, [0]])
     verify_accept(d, G)
     t1 = time.perf_counter()
@@ -123,9 +179,24 @@ def cpu_baseline(shape, weights, a_mean):
     t2 = time.perf_counter()
     cycle = t2 - t0
     return dict(value=1.0 / cycle, unit="draft blocks/s", cores=int(threads), kind="oracle",
-                sample=f"1 cycle at ctx {ctx}: draft forward {t1 - t0:.2f} s + inject of {rows} rows "
-                       f"{t2 - t1:.2f} s (float64 numpy; context K/V filled with random bf16 values)",
+                sample=f"1 cycle of 1 request at {visible} visible context positions: draft forward "
+                       f"{t1 - t0:.2f} s + inject of {rows} rows {t2 - t1:.2f} s (float64 numpy; "
+                       f"context K/V filled with random values)",
                 draft_s=t1 - t0, inject_s=t2 - t1, accepted_tok_per_s=a_mean / cycle)
+
+
+def plan_requests(shape, n_cycles):
+    """Per request: context length, first injected position (a window keeps
+    only the last W), the accept schedule and the positions the run adds."""
+    import synth
+
+    W = shape.get("window") or 0
+    reqs = []
+    for r, c in enumerate(synth.context_lengths(shape)):
+        sched = synth.accept_schedule(shape, n_cycles, req=r).astype(int)
+        start = max(0, c - W) if W else 0
+        reqs.append(dict(ctx=c, start=start, sched=sched, grow=int(sched.sum()) + n_cycles))
+    return reqs
 
 
 def main():
@@ -159,40 +230,66 @@ def main():
     from block_diffusion_drafter_proj_amd.drafter import Drafter
 
     shape = synth.config(args.config)
-    assert shape["batch"] == 1 and not shape.get("ctx_range"), "bench.py runs the batch-1 workloads"
     dev = torch.device("cuda")
     t_setup = time.perf_counter()
     weights = synth.make_weights(shape)
-    ctx, B, V, d = shape["ctx"], shape["block_size"], shape["vocab"], shape["hidden"]
+    B, V, d = shape["block_size"], shape["vocab"], shape["hidden"]
+    W = shape.get("window") or 0
+    conv, topk = bool(shape.get("conv2")), int(shape.get("topk") or 0)
     n_cycles = args.warmup + args.steps
-    sched = synth.accept_schedule(shape, n_cycles).astype(int)
-    extra = int(sched.sum()) + n_cycles
-    max_pos = ctx + extra + 2 * B + 16
-    pages = (max_pos + 15) // 16 + 1
-    dr = Drafter(shape, weights, max_batch=1, max_pages=pages, max_pages_per_req=pages,
+    reqs = plan_requests(shape, n_cycles)
+    n = len(reqs)
+    slots = list(range(n))
+    M = n * B
+
+    # KV pages: a window keeps a ring of W/16 + 1 pages, else the whole run's positions
+    for q in reqs:
+        q["n_pages"] = W // 16 + 1 if W else (q["ctx"] + q["grow"] + 2 * B + 32) // 16 + 1
+    total_pages = sum(q["n_pages"] for q in reqs)
+    perm = synth.page_permutation(shape, total_pages) if n > 1 else np.arange(total_pages)
+    off = 0
+    for q in reqs:
+        q["pages"] = [int(x) for x in perm[off:off + q["n_pages"]]]
+        off += q["n_pages"]
+    max_pos = max(q["ctx"] + q["grow"] for q in reqs) + 4 * B + 32
+    dr = Drafter(shape, weights, max_batch=n, max_pages=total_pages,
+                 max_pages_per_req=max(q["n_pages"] for q in reqs),
                  max_position=max_pos, max_inject_rows=1024)
     tdt = dr.tdt
-    # all target hidden states the run needs, resident on the device
-    Hall = [torch.from_numpy(h).to(tdt).to(dev) for h in synth.hidden_rows(shape, 0, 0, ctx + extra)]
-    page_ids = list(range(pages))
+    # all target hidden states the run needs (positions start .. ctx + grow), resident on the device
+    for r, q in enumerate(reqs):
+        rows = q["ctx"] - q["start"] + q["grow"]
+        if n == 1:
+            q["H"] = [torch.from_numpy(h).to(tdt).to(dev) for h in synth.hidden_rows(shape, r, q["start"], rows)]
+        else:
+            q["H"] = synth.hidden_rows_device(shape, r, q["start"], rows, dev)
 
     def reset():
-        dr.bind(0, page_ids)
-        dr.inject([0], [ctx], [h[:ctx] for h in Hall])
+        for r, q in enumerate(reqs):
+            dr.bind(r, q["pages"], q["start"])
+            dr.inject([r], [q["ctx"] - q["start"]], [h[:q["ctx"] - q["start"]] for h in q["H"]])
 
     reset()
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
+    out = torch.empty((n, B), dtype=torch.int32, device=dev)
+    tk_ids = torch.empty((n, B, 16), dtype=torch.int32, device=dev) if topk else None
+    tk_val = torch.empty((n, B, 16), dtype=torch.float32, device=dev) if topk else None
+    last0 = [int(x) for x in synth.rng(shape["seed"], synth.S_ACCEPT, 98).integers(0, V, size=n)]
+    last0_dev = torch.tensor(last0, dtype=torch.int32, device=dev)
+
+    def draft(last_dev):
+        return dr.draft(slots, last_dev if conv else None, out=out, topk_ids=tk_ids, topk_logits=tk_val)
+
     # ---- draft-only rate at fixed context (state is unchanged by a draft) ----
-    out = torch.empty((1, B), dtype=torch.int32, device=dev)
     for _ in range(args.warmup):
-        dr.draft([0], out=out)
+        draft(last0_dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(args.steps):
-        dr.draft([0], out=out)
+        draft(last0_dev)
     e1.record()
     torch.cuda.synchronize()
     draft_ms = e0.elapsed_time(e1) / args.steps
@@ -200,41 +297,49 @@ def main():
     # per-kernel breakdown of the draft forward (separate pass, every class timed)
     Bnd.dflash_profile_begin(dr.h, (1 << len(Bnd.KERNELS)) - 1)
     for _ in range(5):
-        dr.draft([0], out=out)
-    breakdown = Bnd.dflash_profile_end(dr.h)
-    breakdown = {k: round(ms / 5, 4) for k, (ms, n) in breakdown.items()}
+        draft(last0_dev)
+    prof = Bnd.dflash_profile_end(dr.h)
+    breakdown = {k: round(ms / 5, 4) for k, (ms, cnt) in prof.items()}
+    launches = {k: cnt // 5 for k, (ms, cnt) in prof.items()}
+    visible0 = [min(q["ctx"] - q["start"], W) if W else q["ctx"] for q in reqs]
+    dominant = max((k for k in breakdown if class_work(shape, k, M, visible0)), key=lambda k: breakdown[k])
 
     # ---- record pass: drafts -> target tokens with the prescribed accept lengths ----
-    gen = synth.rng(shape["seed"], synth.S_ACCEPT, 1)
-    Gs, starts = [], []
-    pos = ctx
+    gens = [synth.rng(shape["seed"], synth.S_ACCEPT, 1, r) for r in range(n)]
+    pos = [q["ctx"] for q in reqs]
+    Gs, Hc, nnew, lasts = [], [], [], []
+    last_dev = last0_dev
     for i in range(n_cycles):
-        dd = dr.draft([0], out=out).cpu().numpy()[0]
-        G = synth.synthetic_greedy(dd, int(sched[i]), V, gen)
-        Gs.append(torch.from_numpy(G[None]).to(dev))
-        a = int(sched[i])
-        starts.append(pos)
-        dr.inject([0], [a + 1], [h[pos:pos + a + 1] for h in Hall])
-        pos += a + 1
+        dd = draft(last_dev).cpu().numpy()
+        a = [int(q["sched"][i]) for q in reqs]
+        G = np.stack([synth.synthetic_greedy(dd[r], a[r], V, gens[r]) for r in range(n)])
+        Gs.append(torch.from_numpy(G).to(dev))
+        hid = [torch.cat([q["H"][k][pos[r] - q["start"]:pos[r] - q["start"] + a[r] + 1]
+                          for r, q in enumerate(reqs)]) for k in range(shape["n_feat"])]
+        Hc.append(hid)
+        nnew.append([x + 1 for x in a])
+        dr.inject(slots, nnew[i], hid)
+        for r in range(n):
+            pos[r] += a[r] + 1
+        lasts.append([int(G[r][a[r]]) for r in range(n)])
+        last_dev = torch.tensor(lasts[i], dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
     # ---- timed cycles ----
     reset()
-    acc = torch.empty((n_cycles, 1), dtype=torch.int32, device=dev)
-    com = torch.empty((n_cycles, 1, B + 1), dtype=torch.int32, device=dev)
-    last = torch.empty((n_cycles, 1), dtype=torch.int32, device=dev)
+    acc = torch.empty((n_cycles, n), dtype=torch.int32, device=dev)
+    com = torch.empty((n_cycles, n, B + 1), dtype=torch.int32, device=dev)
+    lastbuf = torch.empty((n_cycles, n), dtype=torch.int32, device=dev)
 
     def cycle(i):
-        dr.draft([0], out=out)
-        dr.verify(out, Gs[i], acc[i], com[i], last[i])
-        a = int(sched[i])
-        p0 = starts[i]
-        dr.inject([0], [a + 1], [h[p0:p0 + a + 1] for h in Hall])
+        draft(lastbuf[i - 1] if i else last0_dev)
+        dr.verify(out, Gs[i], acc[i], com[i], lastbuf[i])
+        dr.inject(slots, nnew[i], Hc[i])
 
     for i in range(args.warmup):
         cycle(i)
     torch.cuda.synchronize()
-    Bnd.dflash_profile_begin(dr.h, 1 << Bnd.KERNELS.index("lm_head"))
+    Bnd.dflash_profile_begin(dr.h, 1 << Bnd.KERNELS.index(dominant))
     t0 = time.perf_counter()
     e0.record()
     for i in range(args.warmup, n_cycles):
@@ -242,29 +347,56 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    lm = Bnd.dflash_profile_end(dr.h)["lm_head"]
+    dom_ms, dom_n = Bnd.dflash_profile_end(dr.h)[dominant]
     dr.check()
-    got = acc.cpu().numpy()[:, 0]
-    assert np.array_equal(got, sched), "accept lengths differ from the schedule"
+    sched = np.stack([q["sched"] for q in reqs], axis=1)  # [cycles, n]
+    assert np.array_equal(acc.cpu().numpy(), sched), "accept lengths differ from the schedule"
+    assert np.array_equal(lastbuf.cpu().numpy(), np.array(lasts)), "next tokens differ from the record"
     cycle_ms = e0.elapsed_time(e1) / args.steps
     wall_ms = (t1 - t0) * 1e3 / args.steps
     acc_timed = int(sched[args.warmup:].sum())
 
-    # ---- roofline of the dominant kernel ----
-    lm_ms = lm[0] / lm[1]
-    lm_bytes = lm_head_bytes(shape, B)
-    achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
-    traffic = measured_traffic(shape)
-    roofline = dict(bound="hbm", kernel="lm_head (k_gemm bf16 argmax epilogue)", achieved=round(achieved, 1),
-                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=traffic, algorithmic_bytes=lm_bytes, avg_ms=round(lm_ms, 4))
-    db = draft_bytes(shape, ctx)
+    # ---- roofline of the dominant kernel class (per launch, timed in the cycles) ----
+    # the visible context at the middle of the timed cycles
+    mid = (args.warmup + n_cycles) // 2
+    vis_mid = []
+    for r, q in enumerate(reqs):
+        c = q["ctx"] + int(q["sched"][:mid].sum()) + mid
+        vis_mid.append(min(c - q["start"], W) if W else c)
+    flops, nbytes = class_work(shape, dominant, M, vis_mid)
+    launch_ms = dom_ms / dom_n
+    peak_tf = MFMA_PEAK_TFLOPS[shape["dtype"]]
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (peak_tf * 1e12)
+    srcs = kernel_sources(shape, dominant, M)
+    traffic = measured_traffic(args.config, dominant, srcs)
+    if t_mfma > t_hbm:
+        achieved = flops / (launch_ms * 1e-3) / 1e12
+        roofline = dict(bound="mfma", achieved=round(achieved, 1), peak=peak_tf, unit="TFLOP/s",
+                        frac=round(achieved / peak_tf, 4))
+    else:
+        achieved = nbytes / (launch_ms * 1e-3) / 1e9
+        roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBS, 4))
+    roofline.update(traffic=traffic, kernel=dominant, algorithmic_bytes=int(nbytes), flops=flops,
+                    avg_ms=round(launch_ms, 4), launches_timed=dom_n,
+                    kernel_sources=[os.path.basename(s) for s in srcs])
     a_mean = float(sched[args.warmup:].mean())
-    cyc_bytes = draft_bytes(shape, ctx + extra // 2) + inject_bytes(shape, a_mean + 1)
+    db = draft_bytes(shape, visible0)
+    cyc_bytes = draft_bytes(shape, vis_mid) + inject_bytes(shape, n * (a_mean + 1))
+    draft_flops = sum(class_work(shape, k, M, visible0)[0] * launches.get(k, 0)
+                      for k in GEMM_CLASSES + ("attn",))
 
+    ctxs = [q["ctx"] for q in reqs]
+    desc = (f"{args.config}: {shape['n_layers']}-layer draft, hidden {d}, "
+            f"{shape['n_q_heads']}/{shape['n_kv_heads']} heads x {shape['head_dim']}, "
+            f"ffn {shape['ffn']}, vocab {V}, block {B}, batch {n}, ctx "
+            + (f"{ctxs[0]}" if len(set(ctxs)) == 1 else f"ragged {min(ctxs)}..{max(ctxs)} (mean {np.mean(ctxs):.0f})")
+            + (f", window {W}" if W else "") + (", two-tap conv" if conv else "")
+            + (f", top-{topk}" if topk else ""))
     result = {
         "metric": METRIC,
-        "value": round(1e3 / cycle_ms, 2),
+        "value": round(n * 1e3 / cycle_ms, 2),
         "unit": "draft blocks/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -275,25 +407,25 @@ def main():
         "vs_baseline": None,
         "dtype": shape["dtype"],
         "data": "synthetic",
-        "config": {"workload": f"{args.config}: {shape['n_layers']}-layer draft, hidden {d}, "
-                               f"{shape['n_q_heads']}/{shape['n_kv_heads']} heads x {shape['head_dim']}, "
-                               f"ffn {shape['ffn']}, vocab {V}, block {B}, ctx {ctx}, batch 1",
-                   "global_batch": 1, "block": B, "ctx": ctx, "parallelism": "none (1 GPU)"},
+        "config": {"workload": desc, "global_batch": n, "block": B,
+                   "ctx": ctxs[0] if len(set(ctxs)) == 1 else f"U[{shape['ctx_range'][0]},{shape['ctx_range'][1]}]",
+                   "parallelism": "none (1 GPU)"},
         "accepted_tok_per_s": round(acc_timed / (cycle_ms * 1e-3 * args.steps), 1),
-        "committed_tok_per_s": round((acc_timed + args.steps) / (cycle_ms * 1e-3 * args.steps), 1),
+        "committed_tok_per_s": round((acc_timed + n * args.steps) / (cycle_ms * 1e-3 * args.steps), 1),
         "mean_accept": round(a_mean, 3),
         "cycle_ms_events": round(cycle_ms, 4),
-        "draft_only_blocks_per_s": round(1e3 / draft_ms, 2),
+        "draft_only_blocks_per_s": round(n * 1e3 / draft_ms, 2),
         "draft_ms": round(draft_ms, 4),
         "draft_algorithmic_bytes": db,
-        "draft_roofline_frac": round(db / (draft_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "cycle_roofline_frac": round(cyc_bytes / (cycle_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "draft_hbm_frac": round(db / (draft_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "draft_mfma_frac": round(draft_flops / (draft_ms * 1e-3) / 1e12 / peak_tf, 4),
+        "cycle_hbm_frac": round(cyc_bytes / (cycle_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_ms_per_draft": breakdown,
         "roofline": roofline,
         "setup_s": round(setup_s, 1),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(shape, weights, a_mean)
+        result["cpu_baseline"] = cpu_baseline(shape, weights, a_mean, int(np.median(visible0)))
     print(json.dumps(result))
 
 

@@ -235,6 +235,24 @@ def hidden_rows(cfg: dict, req: int, start: int, count: int) -> list[np.ndarray]
     return [to_storage(o, cfg["dtype"]) for o in out]
 
 
+def hidden_rows_device(cfg: dict, req: int, start: int, count: int, device) -> list:
+    """The distribution of ``hidden_rows`` (N(0,1) in the storage dtype) drawn
+    by torch's generator on ``device``, for batched workloads too large to
+    draw on the host (64 requests x ~4.5K positions x 5 features x 4096).
+
+    Values differ from ``hidden_rows``; the same (seed, req, start, count)
+    always gives the same rows.  Returns ``n_feat`` device tensors [count, d].
+    """
+    import torch
+
+    seed = int(rng(cfg["seed"], S_HIDDEN, req, start, count).integers(1 << 62))
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    return [torch.randn((count, cfg["hidden"]), generator=g, device=device, dtype=torch.float32).to(dt)
+            for _ in range(cfg["n_feat"])]
+
+
 def page_permutation(cfg: dict, n_pages_total: int) -> np.ndarray:
     """A seeded random permutation of the physical KV page pool."""
     return rng(cfg["seed"], S_PAGES).permutation(n_pages_total).astype(np.int32)
