@@ -3,21 +3,29 @@
 // by the weight stream.
 //
 // Y[M, N] = X[M, K] * W[N, K]^T, X row-major bf16 (virtual concatenation of
-// a_parts arrays as in the skinny kernel), W packed in MFMA fragment order.
-//  * A workgroup (4 waves, 2 x 2) computes a BM x 128 output tile; each wave
-//    BM/2 x 64 with 16x16x32 bf16 MFMAs (fp32 accumulators in registers).
-//  * K advances 64 at a time through two LDS stages holding both operands in
-//    fragment order (one 1 KB fragment per 16 rows x 32 k), so every wave
-//    reads its fragments with conflict-free 16-byte LDS loads; the next
-//    stage's global loads are in flight while the current stage is consumed.
-//  * Tile order is XCD-aware: workgroups are dealt to the 8 XCDs round-robin,
-//    and the M-tiles that share a weight tile are given to the same XCD at the
-//    same time, so the weight tile comes from HBM once and from L2 after.
-// Epilogues: fp32 store (one split), SwiGLU (the 128 columns are 64 gate and
-// the matching 64 up columns; the up waves hand their tile to the gate waves
-// through LDS), greedy argmax (row maxima of the two column waves combined
-// in LDS, one 64-bit atomic max per row and workgroup) and top-16 (sorted
-// lists of 16 per row and column wave, merged later).
+// a_parts arrays as in the skinny kernel), W packed in MFMA fragment order
+// (16 output rows x 32 k per 1 KB fragment, lane-major).
+//  * A workgroup of 4 waves (2 x 2) computes a BM x BN output tile; each wave
+//    holds a BM/2 x BN/2 tile in 16x16x32 bf16 MFMA accumulators (fp32).
+//  * K advances 64 per pipeline stage.  A stage holds both operands in
+//    fragment order, written by direct global->LDS 16-byte loads (one 1 KB
+//    fragment per wave instruction, no register staging).  ST stages form a
+//    ring, so ST-1 stages are in flight while one is multiplied.
+//  * Waits are explicit: a wave waits until only the loads of later stages
+//    are outstanding, then meets the other waves; its LDS reads of the
+//    previous stage are complete at that point, so that buffer is refilled.
+//  * Split-K (P > 1) for the partial-output products whose tile grid alone
+//    would not fill the chip; each split writes its own fp32 plane and the
+//    consumer sums the planes in a fixed order.
+//  * Tile order is XCD-aware: workgroups are dealt to the 8 XCDs round-robin;
+//    the M-tiles sharing a weight tile go to the same XCD at the same time,
+//    so the 32 tiles resident on an XCD form a compact 2-D block whose A and
+//    W k-slabs are fetched once into that XCD's L2.
+// Epilogues: fp32 partial plane, SwiGLU (a wave's columns are gate columns
+// and the matching up columns, so silu(g) * u is formed in registers),
+// greedy argmax (row maxima of the two column waves combined in LDS, one
+// 64-bit atomic max per row and workgroup) and top-16 (one sorted list of 16
+// per row and column wave, merged later).
 #include "common.h"
 #include "kernels.h"
 
@@ -26,8 +34,23 @@ namespace dflash {
 namespace {
 
 constexpr int kFrag = 64 * 8;  // bf16 elements of one fragment
-constexpr int BN = 128;
-constexpr int BK = 64;
+constexpr int BK = 64;         // k per pipeline stage (two fragment columns)
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// At most N of this wave's vector-memory loads still outstanding and every
+// LDS access of this wave complete, then the workgroup barrier.  The asm
+// clobber keeps the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void dma16(const void* src, bf16* dst_wave_base) {
+  // lane i's 16 bytes land at dst_wave_base + 16 * i
+  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst_wave_base, 16, 0, 0);
+}
 
 __device__ __forceinline__ unsigned long long kmax2(unsigned long long a, unsigned long long b) {
   return a > b ? a : b;
@@ -35,6 +58,7 @@ __device__ __forceinline__ unsigned long long kmax2(unsigned long long a, unsign
 __device__ __forceinline__ unsigned long long kmin2(unsigned long long a, unsigned long long b) {
   return a < b ? a : b;
 }
+// bitonic sort of 16 keys held one per lane of a 16-lane group, descending
 __device__ __forceinline__ unsigned long long sort16(unsigned long long v, int i) {
 #pragma unroll
   for (int k = 2; k <= 16; k <<= 1)
@@ -45,6 +69,7 @@ __device__ __forceinline__ unsigned long long sort16(unsigned long long v, int i
     }
   return v;
 }
+// the 16 largest of two descending 16-lists, descending
 __device__ __forceinline__ unsigned long long merge16(unsigned long long cur, unsigned long long nw,
                                                       int i) {
   const int lane = threadIdx.x & 63;
@@ -57,14 +82,20 @@ __device__ __forceinline__ unsigned long long merge16(unsigned long long cur, un
   return t;
 }
 
-template <int BM, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_big(GemmParams p) {
-  constexpr int TM = BM / 32;  // 16-row tiles per wave (wave rows = BM / 2)
-  constexpr int TN = 4;        // 16-col tiles per wave (64 columns)
-  constexpr int FA = BM / 16 * 2;  // A fragments per stage (BM rows x 64 k)
-  constexpr int FB = BN / 16 * 2;  // B fragments per stage
-  __shared__ __attribute__((aligned(16))) bf16 lds[2][(FA + FB) * kFrag];
-  __shared__ unsigned long long red[BM];
+// Column tiles of the output grid: SwiGLU tiles cover BN/2 gate columns.
+template <int BN, int EPI>
+__host__ __device__ inline int col_tiles(int tiles) {
+  constexpr int per = (EPI == EPI_SWIGLU) ? BN / 32 : BN / 16;
+  return (tiles + per - 1) / per;
+}
+
+template <int BM, int BN, int ST, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_tile(GemmParams p) {
+  constexpr int TM = BM / 32, TN = BN / 32;  // 16x16 tiles per wave
+  constexpr int FA = BM / 16 * 2, FB = BN / 16 * 2, FS = FA + FB;
+  constexpr int LPW = FS / 4;  // fragment loads per wave and stage
+  static_assert(FS % 4 == 0 && (ST - 2) * LPW < 64, "stage shape");
+  __shared__ __attribute__((aligned(1024))) bf16 lds[ST * FS * kFrag];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -72,129 +103,108 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmParams p) {
   const int wm = wave & 1, wn = wave >> 1;
   const int r16 = lane & 15, g = lane >> 4;
 
-  // XCD-aware tile mapping
   const int n_mt = (p.M + BM - 1) / BM;
+  const int n_nt = col_tiles<BN, EPI>(p.tiles);
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
   const int m_tile = slot % n_mt;
-  const int n_tile = (slot / n_mt) * 8 + xcd;  // 128-column tile
-  const int n_tiles = (EPI == EPI_SWIGLU) ? (p.tiles + 3) / 4 : (p.tiles + 7) / 8;
-  if (n_tile >= n_tiles) return;
+  const int col = (slot / n_mt) * 8 + xcd;  // (split, column tile)
+  if (col >= n_nt * p.P) return;
+  const int n_tile = col % n_nt, split = col / n_nt;
   const int m0 = m_tile * BM;
-  const int S = p.K / 32;
+  const int S32 = p.K / 32;
+  const int nk_all = p.K / BK;
+  const int ks0 = (int)((long long)split * nk_all / p.P);
+  const int nk = (int)((long long)(split + 1) * nk_all / p.P) - ks0;
 
-  // 16-row weight tile index of B fragment column j (0..7) of this tile
-  auto wtile = [&](int j) -> int {
-    if (EPI == EPI_SWIGLU) return j < 4 ? n_tile * 4 + j : p.up_tile_off + n_tile * 4 + (j - 4);
-    return n_tile * 8 + j;
+  // weight tile of stage column jb (0 .. BN/16-1), clamped into the matrix
+  auto wtile = [&](int jb) -> int {
+    if (EPI == EPI_SWIGLU) {
+      const int wv = jb / TN, jj = jb % TN;
+      int gt = n_tile * (BN / 32) + wv * (TN / 2) + (jj % (TN / 2));
+      gt = min(gt, p.tiles - 1);
+      return jj < TN / 2 ? gt : p.up_tile_off + gt;
+    }
+    return min(n_tile * (BN / 16) + jb, p.tiles - 1);
   };
-  auto wfrag = [&](int j, int ks) -> const bf16* {
-    int tt = wtile(j);
+
+  // This wave's share of a stage: LA activation and LB weight fragments.
+  // Addresses are fixed per workgroup except for the k offset, so they are
+  // formed once here; the wave index is made scalar so every branch below is
+  // uniform and the weight pointers stay in scalar registers.
+  constexpr int LA = FA / 4, LB = FB / 4;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  int a_off[LA];  // element offset inside a part, without the stage's k
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int fa = wv * LA + i;
+    const int row = min(m0 + (fa >> 1) * 16 + r16, p.M - 1);
+    a_off[i] = row * p.lda + (fa & 1) * 32 + 8 * g;
+  }
+  const bf16* b_src[LB];  // fragment of k-stage 0
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int fb = wv * LB + i;
+    int tt = wtile(fb >> 1);
     int seg = 0;
     if (p.seg_tiles) {
       seg = tt / p.seg_tiles;
       tt -= seg * p.seg_tiles;
     }
-    return reinterpret_cast<const bf16*>(p.w[seg]) + ((long long)tt * S + ks) * kFrag;
-  };
-  const int wtiles_total = (EPI == EPI_SWIGLU) ? p.up_tile_off + p.tiles : p.tiles;
+    b_src[i] = reinterpret_cast<const bf16*>(p.w[seg]) + ((long long)tt * S32 + (fb & 1)) * kFrag;
+  }
 
-  // global -> registers for one stage: (FA + FB) fragments, 4 lanes' worth per thread per round
-  constexpr int RND = (FA + FB) * 64 / 256;
-  bf16x8 stage[RND];
-  auto gload = [&](int k0) {
+  auto load_stage = [&](int kt, int buf) {
+    bf16* dst = lds + buf * FS * kFrag;
+    const int k0 = kt * BK;
+    const int part = k0 / p.a_part_k;  // a_part_k is a multiple of 64
+    const bf16* abase = reinterpret_cast<const bf16*>(p.a[part]) + (k0 - part * p.a_part_k);
 #pragma unroll
-    for (int q = 0; q < RND; ++q) {
-      const int idx = t + 256 * q;
-      const int f = idx >> 6, l = idx & 63;
-      bf16x8 v;
-      if (f < FA) {
-        const int m16 = f >> 1, k32 = f & 1;
-        const int row = m0 + m16 * 16 + (l & 15);
-        const int k = k0 + k32 * 32 + 8 * (l >> 4);
-        const int part = k / p.a_part_k;
-        if (row < p.M) {
-          v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(p.a[part]) +
-                                               (long long)row * p.lda + (k - part * p.a_part_k));
-        } else {
+    for (int i = 0; i < LA; ++i) dma16(abase + a_off[i], dst + (wv * LA + i) * kFrag);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (bf16)0.0f;
-        }
-      } else {
-        const int fb = f - FA;
-        const int j = fb >> 1, k32 = fb & 1;
-        const int tt = wtile(j);
-        if (tt < wtiles_total && (EPI == EPI_SWIGLU ? (j < 4 ? n_tile * 4 + j : n_tile * 4 + j - 4) < p.tiles : true)) {
-          v = *reinterpret_cast<const bf16x8*>(wfrag(j, k0 / 32 + k32) + l * 8);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (bf16)0.0f;
-        }
-      }
-      stage[q] = v;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < RND; ++q) {
-      const int idx = t + 256 * q;
-      *reinterpret_cast<bf16x8*>(&lds[buf][(idx >> 6) * kFrag + (idx & 63) * 8]) = stage[q];
-    }
+    for (int i = 0; i < LB; ++i)
+      dma16(b_src[i] + (long long)kt * 2 * kFrag + lane * 8, dst + (FA + wv * LB + i) * kFrag);
   };
 
-  // chunk accumulators (one 256-wide slice of K) folded into running totals:
-  // the fp32 rounding chain stays short however long K is
-  f32x4 acc[TM][TN], tot[TM][TN];
+  f32x4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      tot[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = p.K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nk) load_stage(ks0 + s, s);
+
+  for (int it = 0; it < nk; ++it) {
+    const int ahead = min(nk - 1 - it, ST - 2);  // later stages allowed in flight
+    if (ahead >= 2)
+      wait_barrier<(ST >= 4 ? 2 * LPW : 0)>();
+    else if (ahead == 1)
+      wait_barrier<(ST >= 3 ? LPW : 0)>();
+    else
+      wait_barrier<0>();
+    if (it + ST - 1 < nk) load_stage(ks0 + it + ST - 1, (it + ST - 1) % ST);
+    const bf16* sb = lds + (it % ST) * FS * kFrag;
 #pragma unroll
     for (int k32 = 0; k32 < 2; ++k32) {
       bf16x8 af[TM], bfr[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(&lds[cur][((wm * TM + i) * 2 + k32) * kFrag + lane * 8]);
+        af[i] = *reinterpret_cast<const bf16x8*>(sb + ((wm * TM + i) * 2 + k32) * kFrag + lane * 8);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&lds[cur][(FA + (wn * TN + j) * 2 + k32) * kFrag + lane * 8]);
+        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + (FA + (wn * TN + j) * 2 + k32) * kFrag + lane * 8);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma_step(af[i], bfr[j], acc[i][j]);
     }
-    if ((kt & 3) == 3 || kt + 1 == nk) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          tot[i][j] += acc[i][j];
-          acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-    if (kt + 1 < nk) {
-      sstore(cur ^ 1);
-      __syncthreads();
-    }
   }
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = tot[i][j];
 
   // ---- epilogues: lane holds rows 4g+q, column r16 of each 16x16 tile ----
-  if (EPI == EPI_PARTIAL || EPI == EPI_RESID) {
+  if (EPI == EPI_PARTIAL) {
+    float* out = p.out_f32 + (long long)split * p.M * p.N;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -203,43 +213,25 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmParams p) {
         for (int q = 0; q < 4; ++q) {
           const int m = m0 + (wm * TM + i) * 16 + 4 * g + q;
           const int n = n_tile * BN + (wn * TN + j) * 16 + r16;
-          if (m < p.M && n < p.N) {
-            if (EPI == EPI_PARTIAL)
-              p.out_f32[(long long)m * p.N + n] = acc[i][j][q];
-            else
-              p.resid[(long long)m * p.ldr + n] += acc[i][j][q];
-          }
+          if (m < p.M && n < p.N) out[(long long)m * p.N + n] = acc[i][j][q];
         }
   } else if (EPI == EPI_SWIGLU) {
-    __syncthreads();  // LDS stages are free now
-    float* up = reinterpret_cast<float*>(&lds[0][0]);  // [2 wm][TM*16 rows][64 cols]
-    if (wn == 1) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+      for (int jj = 0; jj < TN / 2; ++jj)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            up[(wm * TM * 16 + i * 16 + 4 * g + q) * 64 + j * 16 + r16] = acc[i][j][q];
-    }
-    __syncthreads();
-    if (wn == 0) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int m = m0 + (wm * TM + i) * 16 + 4 * g + q;
-            const int n = n_tile * 64 + j * 16 + r16;
-            if (m < p.M && n < p.N) {
-              const float gt = acc[i][j][q];
-              const float u = up[(wm * TM * 16 + i * 16 + 4 * g + q) * 64 + j * 16 + r16];
-              reinterpret_cast<bf16*>(p.out_t)[(long long)m * p.ldt + n] = (bf16)(gt / (1.0f + expf(-gt)) * u);
-            }
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + (wm * TM + i) * 16 + 4 * g + q;
+          const int n = n_tile * (BN / 2) + (wn * (TN / 2) + jj) * 16 + r16;
+          if (m < p.M && n < p.N) {
+            const float gt = acc[i][jj][q], u = acc[i][jj + TN / 2][q];
+            reinterpret_cast<bf16*>(p.out_t)[(long long)m * p.ldt + n] = (bf16)(gt / (1.0f + expf(-gt)) * u);
           }
-    }
+        }
   } else {  // EPI_ARGMAX / EPI_TOPK
+    unsigned long long* red = reinterpret_cast<unsigned long long*>(lds);  // [2][BM]
+    if (EPI == EPI_ARGMAX) wait_barrier<0>();  // every wave is done with the stages
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -253,58 +245,68 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmParams p) {
           const bool ok = m < p.M && n < p.N;
           if (ok && p.dbg) p.dbg[(long long)m * p.ld_dbg + n] = acc[i][j][q];
           const unsigned long long key = ok ? argmax_key(acc[i][j][q], n, p.N) : 0ull;
-          if (EPI == EPI_TOPK) {
+          if (EPI == EPI_TOPK)
             best = merge16(best, sort16(key, r16), r16);
-          } else {
+          else
             best = kmax2(best, key);
-          }
         }
         if (EPI == EPI_TOPK) {
-          // one sorted list per row and column wave
-          if (m < p.M)
-            p.keys[((long long)m * (2 * n_tiles) + 2 * n_tile + wn) * 16 + r16] = best;
+          if (m < p.M) p.keys[((long long)m * (2 * n_nt) + 2 * n_tile + wn) * 16 + r16] = best;
         } else {
 #pragma unroll
           for (int o = 8; o >= 1; o >>= 1) best = kmax2(best, __shfl_xor(best, o, 64));
-          if (wn == 1 && r16 == 0) red[ml] = best;
-          __syncthreads();
-          if (wn == 0 && r16 == 0 && m < p.M) atomicMax(p.keys + m, kmax2(best, red[ml]));
-          __syncthreads();
+          if (r16 == 0) red[wn * BM + ml] = best;
         }
       }
+    }
+    if (EPI == EPI_ARGMAX) {
+      __syncthreads();
+      for (int r = t; r < BM; r += 256)
+        if (m0 + r < p.M) atomicMax(p.keys + m0 + r, kmax2(red[r], red[BM + r]));
     }
   }
 }
 
-template <int BM, int EPI>
-void launch_bm(const GemmParams& p, hipStream_t s) {
+template <int BM, int BN, int ST, int EPI>
+void launch_cfg(const GemmParams& p, hipStream_t s) {
   const int n_mt = (p.M + BM - 1) / BM;
-  const int n_tiles = (EPI == EPI_SWIGLU) ? (p.tiles + 3) / 4 : (p.tiles + 7) / 8;
-  const int groups = (n_tiles + 7) / 8;
-  hipLaunchKernelGGL((k_gemm_big<BM, EPI>), dim3(groups * 8 * n_mt), dim3(256), 0, s, p);
+  const int cols = col_tiles<BN, EPI>(p.tiles) * p.P;
+  const int groups = (cols + 7) / 8;
+  hipLaunchKernelGGL((k_gemm_tile<BM, BN, ST, EPI>), dim3(groups * 8 * n_mt), dim3(256), 0, s, p);
 }
 
-template <int BM>
-void launch_epi(int epi, const GemmParams& p, hipStream_t s) {
-  switch (epi) {
-    case EPI_PARTIAL: launch_bm<BM, EPI_PARTIAL>(p, s); break;
-    case EPI_RESID: launch_bm<BM, EPI_RESID>(p, s); break;
-    case EPI_SWIGLU: launch_bm<BM, EPI_SWIGLU>(p, s); break;
-    case EPI_TOPK: launch_bm<BM, EPI_TOPK>(p, s); break;
-    default: launch_bm<BM, EPI_ARGMAX>(p, s); break;
-  }
+template <int EPI>
+void launch_epi(const GemmParams& p, hipStream_t s) {
+  if (p.M > 128 && EPI != EPI_TOPK)  // the top-16 sort needs the registers of the smaller tile
+    launch_cfg<256, 128, 3, EPI>(p, s);
+  else
+    launch_cfg<128, 128, 3, EPI>(p, s);
 }
 
 }  // namespace
 
-int gemm_big_lists(int tiles) { return 2 * ((tiles + 7) / 8); }
+// Lists per row written by the top-16 epilogue (two per 128-column tile).
+int gemm_big_lists(int tiles) { return 2 * col_tiles<128, EPI_TOPK>(tiles); }
+
+// Split-K factor of a partial-output product: the smallest power of two that
+// gives at least one workgroup per CU while keeping 8 or more k-stages per split.
+int gemm_big_split(int M, int tiles, int K) {
+  const int bm = M > 128 ? 256 : 128;
+  const int wgs = ((M + bm - 1) / bm) * ((tiles + 7) / 8);
+  int P = 1;
+  while (wgs * P < 256 && K / (BK * 2 * P) >= 8) P *= 2;
+  return P;
+}
 
 void launch_gemm_big(int epi, const GemmParams& p, hipStream_t s) {
   if (p.M <= 0 || p.tiles <= 0) return;
-  if (p.M <= 64)
-    launch_epi<64>(epi, p, s);
-  else
-    launch_epi<128>(epi, p, s);
+  switch (epi) {
+    case EPI_PARTIAL: launch_epi<EPI_PARTIAL>(p, s); break;
+    case EPI_SWIGLU: launch_epi<EPI_SWIGLU>(p, s); break;
+    case EPI_TOPK: launch_epi<EPI_TOPK>(p, s); break;
+    case EPI_ARGMAX: launch_epi<EPI_ARGMAX>(p, s); break;
+    default: break;  // EPI_RESID has no tiled form; the runtime never asks for it here
+  }
 }
 
 }  // namespace dflash

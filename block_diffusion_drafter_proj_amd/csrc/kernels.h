@@ -168,6 +168,7 @@ int gemm_kblock(int dtype, int M);
 // for `tiles` 16-row weight tiles.
 inline bool gemm_use_big(int dtype, int M) { return dtype == DFLASH_BF16 && M >= 64; }
 int gemm_big_lists(int tiles);
+int gemm_big_split(int M, int tiles, int K);
 void launch_gemm_big(int epi, const GemmParams& p, hipStream_t s);
 GemmPlan plan_gemm(int tiles, int K, int kblock, bool single_split);
 void launch_gemm(int dtype, int epi, const GemmPlan& pl, const GemmParams& p, hipStream_t s);

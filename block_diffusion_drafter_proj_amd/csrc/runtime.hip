@@ -75,13 +75,22 @@ struct Plans {
 int tiles_of(int n) { return (n + 15) / 16; }
 
 Plans make_plans(const dflash_config& c, int M) {
-  if (gemm_use_big(c.dtype, M)) {  // tiled kernel: one split everywhere
-    const GemmPlan one{1, 4, 1};
-    return Plans{one, one, one, one, one, one, one};
-  }
-  const int kb = gemm_kblock(c.dtype, M);
   const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  if (gemm_use_big(c.dtype, M)) {  // tiled kernel: split-K only for partial outputs
+    auto tiled = [&](int tiles, int K) { return GemmPlan{gemm_big_split(M, tiles, K), 4, 1}; };
+    const GemmPlan one{1, 4, 1};
+    Plans p;
+    p.qkv = tiled(tiles_of(qkvw), d);
+    p.o = tiled(tiles_of(d), qd);
+    p.gateup = one;
+    p.down = tiled(tiles_of(d), c.ffn);
+    p.lm = one;
+    p.fc = tiled(tiles_of(d), c.n_feat * d);
+    p.kv = tiled(c.n_layers * tiles_of(2 * c.n_kv_heads * c.head_dim), d);
+    return p;
+  }
+  const int kb = gemm_kblock(c.dtype, M);
   Plans p;
   p.qkv = plan_gemm(tiles_of(qkvw), d, kb, false);
   p.o = plan_gemm(tiles_of(d), qd, kb, false);
@@ -93,9 +102,11 @@ Plans make_plans(const dflash_config& c, int M) {
   return p;
 }
 
-int max_p(const dflash_config& c, GemmPlan Plans::*f) {
-  int m = 1;
-  for (int M : {1, 1024}) m = std::max(m, (make_plans(c, M).*f).P);
+// Rows of partial planes a product needs at most: max over M <= max_rows of
+// P(M) * M (the split factor depends on the row count).
+size_t part_rows(const dflash_config& c, GemmPlan Plans::*f, int max_rows) {
+  size_t m = 0;
+  for (int M = 1; M <= max_rows; ++M) m = std::max(m, (size_t)(make_plans(c, M).*f).P * M);
   return m;
 }
 
@@ -128,7 +139,7 @@ Layout make_layout(const dflash_config& c) {
   L.h = take(sizeof(float) * M * c.hidden);
   L.xa = take(e * M * c.hidden);
   L.xo = take(e * M * qd);
-  L.qkv = take(sizeof(float) * max_p(c, &Plans::qkv) * M * qkvw);
+  L.qkv = take(sizeof(float) * part_rows(c, &Plans::qkv, (int)M) * qkvw);
   L.qb = take(e * (size_t)c.max_batch * c.n_q_heads * 16 * c.head_dim);
   L.blk = take(e * (size_t)c.max_batch * page_elems);
   const size_t pp = (size_t)part_pairs(c) * c.n_q_heads * 16;
@@ -139,11 +150,11 @@ Layout make_layout(const dflash_config& c) {
   L.keys = take(sizeof(unsigned long long) * M);
   L.tlists = c.topk ? take(sizeof(unsigned long long) * M * 16 *
                            std::max(256, gemm_big_lists(tiles_of(c.vocab)))) : 0;
-  L.opart = take(sizeof(float) * max_p(c, &Plans::o) * M * c.hidden);
-  L.dpart = take(sizeof(float) * max_p(c, &Plans::down) * M * c.hidden);
-  L.u = take(sizeof(float) * max_p(c, &Plans::fc) * R * c.hidden);
+  L.opart = take(sizeof(float) * part_rows(c, &Plans::o, (int)M) * c.hidden);
+  L.dpart = take(sizeof(float) * part_rows(c, &Plans::down, (int)M) * c.hidden);
+  L.u = take(sizeof(float) * part_rows(c, &Plans::fc, (int)R) * c.hidden);
   L.f = take(e * R * c.hidden);
-  L.kvo = take(sizeof(float) * max_p(c, &Plans::kv) * R * (size_t)c.n_layers * 2 * c.n_kv_heads * c.head_dim);
+  L.kvo = take(sizeof(float) * part_rows(c, &Plans::kv, (int)R) * (size_t)c.n_layers * 2 * c.n_kv_heads * c.head_dim);
   L.total = off;
   return L;
 }

@@ -258,9 +258,14 @@ def test_empty_context_and_subset_of_slots():
     _draft_both(dev, shape, dr, o, states, [3, 0, 1])
 
 
-def test_repeatable_and_batch_invariant():
-    """Bit-identical drafts and logits on repeated calls, and the same result
-    for a request whether it is drafted alone or in a batch."""
+def test_repeatable_and_independent_of_other_requests():
+    """Bit-identical drafts and logits on repeated calls.  A request's result
+    is bit-identical when the other requests of the call change, since rows
+    never mix and attention splits depend on the request's own context only.
+    Across call sizes the GEMM reduction order differs: a request alone is 16
+    rows on the skinny split-K kernel, five requests are 80 rows on the tiled
+    kernel.  There the result agrees to the bf16 bar and the tokens match
+    outside near-ties."""
     dev, shape, w, dr, ctxs, pages = _setup("small_batch")
     o = DraftOracle(shape, w)
     n = shape["batch"]
@@ -275,11 +280,20 @@ def test_repeatable_and_batch_invariant():
         outs.append((d.cpu().numpy().copy(), lg.cpu().numpy().copy()))
     for d, lg in outs[1:]:
         assert np.array_equal(d, outs[0][0]) and np.array_equal(lg, outs[0][1])
+    # request 0 grows by 7 positions: the other requests are unchanged bit for bit
+    _inject_both(dev, shape, dr, o, states, [0], [ctxs[0]], [7])
+    lg = torch.empty((n, B, V), dtype=torch.float32, device=dev)
+    d = dr.draft(list(range(n)), debug_logits=lg)
+    torch.cuda.synchronize()
+    d, lg = d.cpu().numpy(), lg.cpu().numpy()
+    assert not np.array_equal(lg[0], outs[0][1][0])
+    for r in range(1, n):
+        assert np.array_equal(lg[r], outs[0][1][r]) and np.array_equal(d[r], outs[0][0][r]), r
     lg1 = torch.empty((1, B, V), dtype=torch.float32, device=dev)
     d1 = dr.draft([2], debug_logits=lg1)
     torch.cuda.synchronize()
-    assert_rows_close(lg1.cpu().numpy()[0], outs[0][1][2], tol=1e-5, what="batch invariance")
-    assert_tokens_match(d1.cpu().numpy()[0], outs[0][1][2], what="batch invariance")
+    assert_rows_close(lg1.cpu().numpy()[0], outs[0][1][2], what="request alone vs in a batch")
+    assert_tokens_match(d1.cpu().numpy()[0], outs[0][1][2], what="request alone vs in a batch")
 
 
 @pytest.mark.parametrize("name", ["small_bf16", "small_batch"])
