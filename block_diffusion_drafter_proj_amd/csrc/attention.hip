@@ -36,8 +36,7 @@ namespace dflash {
 
 namespace {
 
-template <typename T> constexpr bool kSplitP = false;
-template <> constexpr bool kSplitP<bf16> = true;
+template <typename T> constexpr bool kSplitP = sizeof(T) == 2;  // bf16: P as hi + lo
 
 template <typename T> struct Vec4;
 template <> struct Vec4<bf16> { typedef bf16x4 type; };
@@ -337,6 +336,264 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams p, SlotArgs sl) {
   }
 }
 
+// bf16 attention with the split's K/V streamed through an LDS ring.
+//
+// A workgroup takes one request, one KV head and a run of context units
+// (pages, then the block's own page).  Wave w computes query head gkv*G + w
+// over every key of the run, so each K/V byte comes from HBM once per
+// workgroup and the G waves read it from LDS.  Units are staged in pairs (32
+// keys, one MFMA reduction step) by direct global->LDS copies, kRing pairs
+// deep; every wave makes the same number of copies per stage (a wave with
+// nothing left repeats another wave's copy), so the per-wave count of
+// outstanding copies fixes how far each wait lets the ring run ahead.  A
+// missing unit is copied from the request's block page and fully masked.
+// K rows are stored with their 16-byte chunks permuted (chunk c of key k at
+// slot c ^ swz(k)) so that the 16 keys of one fragment read fall on distinct
+// LDS banks; V^T rows (16 positions, 32 bytes) are read as stored.
+constexpr int kRing = 4;
+
+template <int DH>
+__device__ __forceinline__ int swz(int key) {
+  constexpr int CH = DH / 8;
+  return (key * CH / 16) & (CH - 1);
+}
+
+template <int DH, int G>
+__global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl) {
+  constexpr int NJ = DH / 32;             // k32 steps of S^T = K Q^T
+  constexpr int ND = DH / 16;             // 16-row tiles of O^T
+  constexpr int CH = DH / 8;              // 16-byte chunks per K row
+  constexpr int HEAD = 16 * DH;           // elements of one head's K (or V) in a unit
+  constexpr int KI = HEAD * 2 / 1024;     // 1 KB copies per head block
+  constexpr int NCOPY = 2 * 2 * KI;       // per stage: 2 units x (K, V)
+  constexpr int NI = (NCOPY + G - 1) / G; // copies per wave and stage
+  constexpr int STAGE = 2 * 2 * HEAD;     // elements per stage
+  static_assert((kRing - 2) * NI < 64 && NCOPY >= G, "ring shape");
+  __shared__ __attribute__((aligned(1024))) bf16 ring[kRing * STAGE];
+  const float NEG = -INFINITY;
+
+  const int s = blockIdx.x, gkv = blockIdx.y, r = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = gkv * G + wave;
+  const int lane = lane_id(), l16 = lane & 15, g4 = lane >> 4;
+  const int slot = sl.slots[r];
+  const SlotState st = p.state[slot];
+  const int hi = st.ctx_len;
+  int lo = st.kv_begin;
+  if (p.window > 0) lo = max(lo, hi - p.window);
+  const int lp0 = lo / 16;
+  const int n_lp = hi > lo ? (hi - 1) / 16 - lp0 + 1 : 0;
+  const int n_units = n_lp + 1;
+  const int pps = split_pages(n_units, p.split_target, p.pps_cap);
+  const int n_split = (n_units + pps - 1) / pps;
+  if (s == 0 && gkv == 0 && threadIdx.x == 0) p.n_split[r] = n_split;
+  if (s >= n_split) return;
+  const int u_begin = s * pps;
+  const int u_end = min(u_begin + pps, n_units);
+  const int n_pairs = (u_end - u_begin + 1) / 2;
+  const long long page_elems = 2LL * p.Hkv * 16 * DH;
+  const bf16* pool = reinterpret_cast<const bf16*>(p.pool);
+  const bf16* blk = reinterpret_cast<const bf16*>(p.blk) + (long long)r * page_elems;
+
+  bf16x8 qf[NJ];
+  {
+    const bf16* qrow = reinterpret_cast<const bf16*>(p.qb) + ((long long)(r * p.Hq + h) * 16 + l16) * DH;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) qf[j] = load8<bf16>(qrow + 32 * j + 8 * g4);
+  }
+  // page ids of the split's context units, one per lane (pps <= 64)
+  int my_page = -1;
+  {
+    const int uu = u_begin + lane;
+    if (uu < u_end && uu < n_lp) {
+      const int lp = lp0 + uu;
+      const int idx = p.window > 0 ? lp % st.n_pages : lp;
+      my_page = p.page_table[(long long)slot * p.pt_stride + idx];
+      if (my_page < 0 || my_page >= p.max_pages) {
+        atomicOr(p.err, 2u);
+        my_page = -1;
+      }
+    }
+  }
+  // unit uu (wave-uniform): its base, or nullptr when nothing there is valid
+  auto unit_base = [&](int uu) -> const bf16* {
+    if (uu >= u_end) return nullptr;
+    if (uu < n_lp) {
+      const int page = __builtin_amdgcn_readlane(my_page, uu - u_begin);
+      return page >= 0 ? pool + (long long)page * page_elems : nullptr;
+    }
+    return blk;
+  };
+  // this wave's copies: source offset inside a unit (per lane) and LDS offset
+  int c_src[NI], c_dst[NI], c_unit[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    int q = wave + G * i;
+    if (q >= NCOPY) q -= NCOPY;  // nothing left: repeat another wave's copy
+    const int t = q / (2 * KI), kv = (q / KI) & 1, j = q % KI;
+    int chunk = j * 64 + lane;  // 16-byte chunk of the head block landing at this LDS slot
+    if (!kv) {
+      const int key = chunk / CH;
+      chunk = key * CH + ((chunk % CH) ^ swz<DH>(key));
+    }
+    c_src[i] = ((kv ? p.Hkv : 0) + gkv) * HEAD + chunk * 8;
+    c_dst[i] = (t * 2 + kv) * HEAD + j * 512;
+    c_unit[i] = t;
+  }
+  auto issue = [&](int pair, int buf) {
+    const bf16* b[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      b[t] = unit_base(u_begin + 2 * pair + t);
+      if (!b[t]) b[t] = blk;  // any readable unit; its keys are masked
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16((c_unit[i] ? b[1] : b[0]) + c_src[i], ring + buf * STAGE + c_dst[i]);
+  };
+
+  // Scores are kept in log2 units.  The reference max m_run of a query is
+  // only raised when a score exceeds it by more than 8 (p <= 2^8 stays exact
+  // in fp32 and in the hi + lo bf16 pair), so the rescale of O is skipped for
+  // nearly every pair of a long context; softmax does not depend on the
+  // reference.
+  const float sl2 = p.scale * 1.44269504088896341f;
+  float m_run = NEG, l_run = 0.f;
+  f32x4 o[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int i = 0; i < kRing - 1; ++i)
+    if (i < n_pairs) issue(i, i);
+  for (int it = 0; it < n_pairs; ++it) {
+    const int ahead = min(n_pairs - 1 - it, kRing - 2);
+    if (ahead >= 2)
+      wait_barrier<2 * NI>();
+    else if (ahead == 1)
+      wait_barrier<NI>();
+    else
+      wait_barrier<0>();
+    if (it + kRing - 1 < n_pairs) issue(it + kRing - 1, (it + kRing - 1) % kRing);
+    const bf16* sb = ring + (it % kRing) * STAGE;
+
+    // which keys of the pair are valid (wave-uniform per unit, then per key)
+    bool has[2], full[2];
+    int pos0[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int uu = u_begin + 2 * it + t;
+      has[t] = unit_base(uu) != nullptr;
+      pos0[t] = (lp0 + uu) * 16;
+      full[t] = has[t] && (uu < n_lp ? (pos0[t] >= lo && pos0[t] + 16 <= hi) : p.B == 16);
+    }
+    const bool fast = full[0] && full[1];
+
+    float sv[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (has[t]) {
+        const bf16* kb = sb + (t * 2) * HEAD + l16 * DH;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + ((4 * j + g4) ^ swz<DH>(l16)) * 8);
+          sacc = mfma_step(kf, qf[j], sacc);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[4 * t + i] = sacc[i] * sl2;
+    }
+    // Lane-dependent masking is written as selects: a divergent branch that
+    // stores into one element of the score vector lost that store in code
+    // generation (the exec-masked block kept only the mask itself).
+    bool valid[2][4];
+    if (!fast) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bool is_blk = u_begin + 2 * it + t >= n_lp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 4 * g4 + i;
+          valid[t][i] = has[t] && (is_blk ? key < p.B : (pos0[t] + key >= lo && pos0[t] + key < hi));
+          sv[4 * t + i] = valid[t][i] ? sv[4 * t + i] : NEG;
+        }
+      }
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool grow = mx > m_run + 8.0f;  // false while both are -inf
+    if (__ballot(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float corr = (m_run == NEG) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) o[dt] = o[dt] * corr;
+      l_run *= corr;
+      m_run = m_new;
+    }
+    float pe[8];
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pe[e] = fast ? __builtin_amdgcn_exp2f(sv[e] - m_run)
+                   : (sv[e] == NEG ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m_run));
+      ls += pe[e];
+    }
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    l_run += ls;
+    // P at fp32 accuracy in the bf16 MFMA: an exact hi + lo pair
+    bf16x8 pf, pf_lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pf[e] = (bf16)pe[e];
+      pf_lo[e] = (bf16)(pe[e] - (float)pf[e]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      const bf16* vb = sb + (dt * 16 + l16) * 16 + 4 * g4;
+      const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vb + HEAD);
+      const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vb + 3 * HEAD);
+      bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      if (!fast) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vf[4 * t + i] = valid[t][i] ? vf[4 * t + i] : (bf16)0.0f;
+      }
+      o[dt] = mfma_step(vf, pf, o[dt]);
+      o[dt] = mfma_step(vf, pf_lo, o[dt]);
+    }
+  }
+
+  // lane holds query row l16, dims dt*16 + 4*g4 + i
+  if (n_split == 1) {
+    if (l16 < p.B) {
+      const float inv = 1.0f / l_run;
+      bf16* out = reinterpret_cast<bf16*>(p.out) + (long long)(r * p.B + l16) * p.ldo + h * DH + 4 * g4;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (bf16)(o[dt][i] * inv);
+        *reinterpret_cast<bf16x4*>(out + dt * 16) = v;
+      }
+    }
+    return;
+  }
+  // split partial; the merge works in natural-log units
+  const long long pb = ((long long)(r * p.Hq + h) * p.n_splits + s) * 16 + l16;
+  if (g4 == 0) {
+    p.part_ml[pb * 2 + 0] = m_run == NEG ? NEG : m_run * 0.693147180559945309f;
+    p.part_ml[pb * 2 + 1] = l_run;
+  }
+  float* po = p.part_o + pb * DH + 4 * g4;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
+}
+
 // One wave per (request, query head, block row): the split partials of the
 // row are merged in split order (max, rescaled sums), each lane owning DH/64
 // output columns, so every partial is read once and all loads of a lane are
@@ -459,6 +716,21 @@ void attn_t(int dh, int n_req, const AttnParams& p, const SlotArgs& sl, hipStrea
     hipLaunchKernelGGL((k_attn<T, 64>), grid, block, lds, s, p, sl);
 }
 
+template <int DH>
+void attn_ring_t(int n_req, const AttnParams& p, const SlotArgs& sl, hipStream_t s) {
+  dim3 grid(p.n_splits, p.Hkv, n_req);
+  switch (p.Hq / p.Hkv) {
+    case 1: hipLaunchKernelGGL((k_attn_ring<DH, 1>), grid, dim3(64), 0, s, p, sl); break;
+    case 2: hipLaunchKernelGGL((k_attn_ring<DH, 2>), grid, dim3(128), 0, s, p, sl); break;
+    case 3: hipLaunchKernelGGL((k_attn_ring<DH, 3>), grid, dim3(192), 0, s, p, sl); break;
+    case 4: hipLaunchKernelGGL((k_attn_ring<DH, 4>), grid, dim3(256), 0, s, p, sl); break;
+    case 5: hipLaunchKernelGGL((k_attn_ring<DH, 5>), grid, dim3(320), 0, s, p, sl); break;
+    case 6: hipLaunchKernelGGL((k_attn_ring<DH, 6>), grid, dim3(384), 0, s, p, sl); break;
+    case 7: hipLaunchKernelGGL((k_attn_ring<DH, 7>), grid, dim3(448), 0, s, p, sl); break;
+    default: hipLaunchKernelGGL((k_attn_ring<DH, 8>), grid, dim3(512), 0, s, p, sl); break;
+  }
+}
+
 template <typename T>
 void combine_t(int dh, const CombineParams& p, hipStream_t s) {
   dim3 grid((p.n_rh * 16 + 3) / 4);
@@ -494,10 +766,14 @@ void launch_qkv_post(int dtype, int dh, int n_req, const QkvPostParams& p, const
 
 void launch_attention(int dtype, int dh, int n_req, const AttnParams& p, const SlotArgs& sl,
                       hipStream_t s) {
-  if (dtype == DFLASH_BF16)
-    attn_t<bf16>(dh, n_req, p, sl, s);
-  else
+  if (dtype == DFLASH_BF16) {
+    if (dh == 128)
+      attn_ring_t<128>(n_req, p, sl, s);
+    else
+      attn_ring_t<64>(n_req, p, sl, s);
+  } else {
     attn_t<float>(dh, n_req, p, sl, s);
+  }
 }
 
 void launch_combine(int dtype, int dh, const CombineParams& p, hipStream_t s) {

@@ -62,6 +62,22 @@ __device__ __forceinline__ f32x4 mfma_step(f32x8 a, f32x8 b, f32x4 acc) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Direct global -> LDS copy of 16 bytes per lane (no register staging): lane
+// i's bytes land at lds_wave_base + 16 * i; the LDS address is wave-uniform.
+// The copy counts as an outstanding vector-memory load until it has landed.
+__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// At most N of this wave's vector-memory loads still outstanding and every
+// LDS access of this wave complete, then the workgroup barrier.  The asm
+// clobber keeps the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // Sum over the 64 lanes of a wave (butterfly; every lane gets the result).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

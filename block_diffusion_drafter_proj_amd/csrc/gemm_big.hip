@@ -36,22 +36,6 @@ namespace {
 constexpr int kFrag = 64 * 8;  // bf16 elements of one fragment
 constexpr int BK = 64;         // k per pipeline stage (two fragment columns)
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-
-// At most N of this wave's vector-memory loads still outstanding and every
-// LDS access of this wave complete, then the workgroup barrier.  The asm
-// clobber keeps the compiler from moving memory accesses across it.
-template <int N>
-__device__ __forceinline__ void wait_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void dma16(const void* src, bf16* dst_wave_base) {
-  // lane i's 16 bytes land at dst_wave_base + 16 * i
-  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst_wave_base, 16, 0, 0);
-}
-
 __device__ __forceinline__ unsigned long long kmax2(unsigned long long a, unsigned long long b) {
   return a > b ? a : b;
 }
