@@ -76,8 +76,8 @@ struct Shape {
   static constexpr int NBUF = (sizeof(T) == 2 ? 16 : 8) / KS;     // tiles in the W ring
 };
 
-template <typename T, int MT, int EPI>
-__global__ __launch_bounds__(1024) void k_gemm(GemmParams p) {
+template <typename T, int MT, int EPI, bool FEW>
+__global__ __launch_bounds__(FEW ? 256 : 1024) void k_gemm(GemmParams p) {
   constexpr int KS = Shape<T, MT>::KS;
   constexpr int NBUF = Shape<T, MT>::NBUF;
   constexpr int NSUB = (EPI == EPI_SWIGLU) ? 2 : 1;
@@ -137,9 +137,11 @@ __global__ __launch_bounds__(1024) void k_gemm(GemmParams p) {
   }
 
   // epilogue: element e = t + it * blockDim of the 16 x 16 tile (per m-tile);
-  // workgroups with fewer than 4 waves take several elements per thread
+  // workgroups with fewer than 4 waves (FEW) take several elements per thread,
+  // the others one element per thread and m-tile, which keeps the per-thread
+  // epilogue state out of the register budget of the weight ring
   const int t = threadIdx.x;
-  constexpr int EIT = 4 * MT;  // iterations for the smallest workgroup (one wave)
+  constexpr int EIT = (FEW ? 4 : 1) * MT;
   float gate_v[EIT];
   unsigned long long best[EIT];
 #pragma unroll
@@ -255,7 +257,10 @@ void launch_t(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
   // 16-row m-blocks; rows beyond 16 re-stream W (a batched kernel would not)
   dim3 grid(pl.GP * p.P, (p.M + 15) / 16);
   dim3 block(64 * pl.NW);
-  hipLaunchKernelGGL((k_gemm<T, 1, EPI>), grid, block, 0, s, p);
+  if (pl.NW < 4)
+    hipLaunchKernelGGL((k_gemm<T, 1, EPI, true>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((k_gemm<T, 1, EPI, false>), grid, block, 0, s, p);
 }
 
 template <typename T>

@@ -261,10 +261,14 @@ void launch_cfg(const GemmParams& p, hipStream_t s) {
 
 template <int EPI>
 void launch_epi(const GemmParams& p, hipStream_t s) {
-  if (p.M > 128 && EPI != EPI_TOPK)  // the top-16 sort needs the registers of the smaller tile
-    launch_cfg<256, 128, 3, EPI>(p, s);
-  else
+  if constexpr (EPI == EPI_TOPK) {  // the top-16 sort needs the registers of the smaller tile
     launch_cfg<128, 128, 3, EPI>(p, s);
+  } else {
+    if (p.M > 128)
+      launch_cfg<256, 128, 3, EPI>(p, s);
+    else
+      launch_cfg<128, 128, 3, EPI>(p, s);
+  }
 }
 
 }  // namespace
