@@ -33,8 +33,11 @@ back with no host synchronisation inside.
 
 Output is one JSON line:
   * ``value``: draft blocks/s of the full cycle (requests x cycles / s);
-  * beside it: accepted tok/s, the draft-only rate at fixed context and the
-    per-kernel time breakdown;
+  * beside it: accepted tok/s, the draft-only rate at fixed context, the
+    per-kernel time breakdown, the GEMM kernels' share of the MFMA peak
+    (their flops over their summed time), and accepted tok/s at a fixed
+    accept length of 5 and 6 (the pages' DFlash-2 range), taken from the
+    measured cycle time;
   * the roofline of the dominant kernel class, timed with HIP events on the
     call's stream during the timed region and priced against HBM or MFMA,
     whichever bounds it;
@@ -386,6 +389,9 @@ def main():
     cyc_bytes = draft_bytes(shape, vis_mid) + inject_bytes(shape, n * (a_mean + 1))
     draft_flops = sum(class_work(shape, k, M, visible0)[0] * launches.get(k, 0)
                       for k in GEMM_CLASSES + ("attn",))
+    # GEMM kernels alone: their flops over their summed time in the breakdown pass
+    gemm_flops = sum(class_work(shape, k, M, visible0)[0] * launches.get(k, 0) for k in GEMM_CLASSES)
+    gemm_ms = sum(breakdown.get(k, 0.0) for k in GEMM_CLASSES)
 
     ctxs = [q["ctx"] for q in reqs]
     desc = (f"{args.config}: {shape['n_layers']}-layer draft, hidden {d}, "
@@ -419,6 +425,9 @@ def main():
         "draft_algorithmic_bytes": db,
         "draft_hbm_frac": round(db / (draft_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "draft_mfma_frac": round(draft_flops / (draft_ms * 1e-3) / 1e12 / peak_tf, 4),
+        "gemm_mfma_frac": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak_tf, 4) if gemm_ms else None,
+        "accepted_tok_per_s_at_a5": round(5 * n * 1e3 / cycle_ms, 1),
+        "accepted_tok_per_s_at_a6": round(6 * n * 1e3 / cycle_ms, 1),
         "cycle_hbm_frac": round(cyc_bytes / (cycle_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_ms_per_draft": breakdown,
         "roofline": roofline,
