@@ -34,7 +34,6 @@ namespace dflash {
 namespace {
 
 constexpr int kFrag = 64 * 8;  // bf16 elements of one fragment
-constexpr int BK = 64;         // k per pipeline stage (two fragment columns)
 
 __device__ __forceinline__ unsigned long long kmax2(unsigned long long a, unsigned long long b) {
   return a > b ? a : b;
@@ -67,24 +66,38 @@ __device__ __forceinline__ unsigned long long merge16(unsigned long long cur, un
 }
 
 // Column tiles of the output grid: SwiGLU tiles cover BN/2 gate columns.
+// A tile configuration: BM x BN output tile, WM x WN waves (each holding a
+// BM/WM x BN/WN tile), KF 32-wide k steps per pipeline stage, ST stages.
+template <int BM_, int BN_, int WM_, int WN_, int KF_, int ST_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, KF = KF_, ST = ST_;
+  static constexpr int NW = WM * WN;
+  static constexpr int TM = BM / WM / 16, TN = BN / WN / 16;  // 16x16 tiles per wave
+  static constexpr int FA = BM / 16 * KF, FB = BN / 16 * KF, FS = FA + FB;  // fragments per stage
+  static constexpr int LA = FA / NW, LB = FB / NW, LPW = LA + LB;          // loads per wave and stage
+  static constexpr int BKS = 32 * KF;                                       // k per stage
+  static_assert(FA % NW == 0 && FB % NW == 0 && (ST - 2) * LPW < 64 && TN % 2 == 0, "tile shape");
+};
+
+// Column tiles of the output grid: SwiGLU tiles cover BN/2 gate columns.
 template <int BN, int EPI>
 __host__ __device__ inline int col_tiles(int tiles) {
   constexpr int per = (EPI == EPI_SWIGLU) ? BN / 32 : BN / 16;
   return (tiles + per - 1) / per;
 }
 
-template <int BM, int BN, int ST, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_tile(GemmParams p) {
-  constexpr int TM = BM / 32, TN = BN / 32;  // 16x16 tiles per wave
-  constexpr int FA = BM / 16 * 2, FB = BN / 16 * 2, FS = FA + FB;
-  constexpr int LPW = FS / 4;  // fragment loads per wave and stage
-  static_assert(FS % 4 == 0 && (ST - 2) * LPW < 64, "stage shape");
+template <typename C, int EPI>
+__global__ __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
+void k_gemm_tile(GemmParams p) {
+  constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, KF = C::KF, ST = C::ST;
+  constexpr int TM = C::TM, TN = C::TN, FA = C::FA, FS = C::FS, LA = C::LA, LB = C::LB, LPW = C::LPW;
+  constexpr int NT = C::NW * 64;
   __shared__ __attribute__((aligned(1024))) bf16 lds[ST * FS * kFrag];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, scalar
+  const int wm = wv % WM, wn = wv / WM;
   const int r16 = lane & 15, g = lane >> 4;
 
   const int n_mt = (p.M + BM - 1) / BM;
@@ -97,57 +110,66 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmParams p) {
   const int n_tile = col % n_nt, split = col / n_nt;
   const int m0 = m_tile * BM;
   const int S32 = p.K / 32;
-  const int nk_all = p.K / BK;
+  const int nk_all = p.K / C::BKS;
   const int ks0 = (int)((long long)split * nk_all / p.P);
   const int nk = (int)((long long)(split + 1) * nk_all / p.P) - ks0;
 
-  // weight tile of stage column jb (0 .. BN/16-1), clamped into the matrix
+  // weight tile of stage column jb (0 .. BN/16-1), clamped into the matrix;
+  // with SwiGLU each wave's TN columns are TN/2 gate tiles and the matching up tiles
   auto wtile = [&](int jb) -> int {
     if (EPI == EPI_SWIGLU) {
-      const int wv = jb / TN, jj = jb % TN;
-      int gt = n_tile * (BN / 32) + wv * (TN / 2) + (jj % (TN / 2));
+      const int w_ = jb / TN, jj = jb % TN;
+      int gt = n_tile * (BN / 32) + w_ * (TN / 2) + (jj % (TN / 2));
       gt = min(gt, p.tiles - 1);
       return jj < TN / 2 ? gt : p.up_tile_off + gt;
     }
     return min(n_tile * (BN / 16) + jb, p.tiles - 1);
   };
 
-  // This wave's share of a stage: LA activation and LB weight fragments.
-  // Addresses are fixed per workgroup except for the k offset, so they are
-  // formed once here; the wave index is made scalar so every branch below is
-  // uniform and the weight pointers stay in scalar registers.
-  constexpr int LA = FA / 4, LB = FB / 4;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // This wave's share of a stage: LA activation and LB weight fragments
+  // (fragment (row or column block r, k step s) sits at r * KF + s).  Their
+  // addresses are fixed per workgroup except for the k offset, so they are
+  // formed once; the wave index is scalar, so the weight pointers stay in
+  // scalar registers and no branch below diverges.
   int a_off[LA];  // element offset inside a part, without the stage's k
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
     const int fa = wv * LA + i;
-    const int row = min(m0 + (fa >> 1) * 16 + r16, p.M - 1);
-    a_off[i] = row * p.lda + (fa & 1) * 32 + 8 * g;
+    const int row = min(m0 + (fa / KF) * 16 + r16, p.M - 1);
+    a_off[i] = row * p.lda + (fa % KF) * 32 + 8 * g;
   }
   const bf16* b_src[LB];  // fragment of k-stage 0
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
     const int fb = wv * LB + i;
-    int tt = wtile(fb >> 1);
+    int tt = wtile(fb / KF);
     int seg = 0;
     if (p.seg_tiles) {
       seg = tt / p.seg_tiles;
       tt -= seg * p.seg_tiles;
     }
-    b_src[i] = reinterpret_cast<const bf16*>(p.w[seg]) + ((long long)tt * S32 + (fb & 1)) * kFrag;
+    b_src[i] = reinterpret_cast<const bf16*>(p.w[seg]) + ((long long)tt * S32 + (fb % KF)) * kFrag;
   }
 
+  // activation part of the next stage to load (stages are loaded in k order;
+  // a_part_k is a multiple of the stage's k, so a stage never straddles parts)
+  int part = ks0 * C::BKS / p.a_part_k;
+  int part_k0 = part * p.a_part_k;
+  const bf16* apart = reinterpret_cast<const bf16*>(p.a[part]);
   auto load_stage = [&](int kt, int buf) {
     bf16* dst = lds + buf * FS * kFrag;
-    const int k0 = kt * BK;
-    const int part = k0 / p.a_part_k;  // a_part_k is a multiple of 64
-    const bf16* abase = reinterpret_cast<const bf16*>(p.a[part]) + (k0 - part * p.a_part_k);
+    const int k0 = kt * C::BKS;
+    if (k0 >= part_k0 + p.a_part_k) {
+      ++part;
+      part_k0 += p.a_part_k;
+      apart = reinterpret_cast<const bf16*>(p.a[part]);
+    }
+    const bf16* abase = apart + (k0 - part_k0);
 #pragma unroll
     for (int i = 0; i < LA; ++i) dma16(abase + a_off[i], dst + (wv * LA + i) * kFrag);
 #pragma unroll
     for (int i = 0; i < LB; ++i)
-      dma16(b_src[i] + (long long)kt * 2 * kFrag + lane * 8, dst + (FA + wv * LB + i) * kFrag);
+      dma16(b_src[i] + (long long)kt * KF * kFrag + lane * 8, dst + (FA + wv * LB + i) * kFrag);
   };
 
   f32x4 acc[TM][TN];
@@ -170,19 +192,27 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmParams p) {
       wait_barrier<0>();
     if (it + ST - 1 < nk) load_stage(ks0 + it + ST - 1, (it + ST - 1) % ST);
     const bf16* sb = lds + (it % ST) * FS * kFrag;
+    // All of the stage's fragments are read before any product, in a fixed
+    // order (the scheduling barriers keep the compiler from sinking each read
+    // next to its first use), so later reads complete under earlier MFMAs.
+    bf16x8 af[KF][TM], bfr[KF][TN];
 #pragma unroll
-    for (int k32 = 0; k32 < 2; ++k32) {
-      bf16x8 af[TM], bfr[TN];
+    for (int k32 = 0; k32 < KF; ++k32) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(sb + ((wm * TM + i) * 2 + k32) * kFrag + lane * 8);
+        af[k32][i] = *reinterpret_cast<const bf16x8*>(sb + ((wm * TM + i) * KF + k32) * kFrag + lane * 8);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + (FA + (wn * TN + j) * 2 + k32) * kFrag + lane * 8);
+        bfr[k32][j] = *reinterpret_cast<const bf16x8*>(sb + (FA + (wn * TN + j) * KF + k32) * kFrag + lane * 8);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int k32 = 0; k32 < KF; ++k32) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_step(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_step(af[k32][i], bfr[k32][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -213,9 +243,44 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmParams p) {
             reinterpret_cast<bf16*>(p.out_t)[(long long)m * p.ldt + n] = (bf16)(gt / (1.0f + expf(-gt)) * u);
           }
         }
-  } else {  // EPI_ARGMAX / EPI_TOPK
-    unsigned long long* red = reinterpret_cast<unsigned long long*>(lds);  // [2][BM]
-    if (EPI == EPI_ARGMAX) wait_barrier<0>();  // every wave is done with the stages
+  } else if (EPI == EPI_ARGMAX) {
+    // per lane and row: a running 32-bit order key of the logit (strict > keeps
+    // the lowest column on ties, the lane's columns increase with j); the 64-bit
+    // (key, id) pair is formed once per row for the reduction across lanes
+    unsigned long long* red = reinterpret_cast<unsigned long long*>(lds);  // [WN][BM]
+    wait_barrier<0>();  // every wave is done with the stages
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ml = (wm * TM + i) * 16 + 4 * g + q;  // row within the tile
+        const int m = m0 + ml;
+        uint32_t bk = 0;
+        int bn = -1;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = n_tile * BN + (wn * TN + j) * 16 + r16;
+          const bool ok = m < p.M && n < p.N;
+          if (ok && p.dbg) p.dbg[(long long)m * p.ld_dbg + n] = acc[i][j][q];
+          const uint32_t k = float_key(acc[i][j][q]);
+          const bool better = ok && (bn < 0 || k > bk);
+          bk = better ? k : bk;
+          bn = better ? n : bn;
+        }
+        unsigned long long best = bn < 0 ? 0ull : (((unsigned long long)bk << 32) | (uint32_t)(p.N - 1 - bn));
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) best = kmax2(best, __shfl_xor(best, o, 64));
+        if (r16 == 0) red[wn * BM + ml] = best;
+      }
+    }
+    __syncthreads();
+    for (int r = t; r < BM; r += NT) {
+      unsigned long long v = red[r];
+#pragma unroll
+      for (int w_ = 1; w_ < WN; ++w_) v = kmax2(v, red[w_ * BM + r]);
+      if (m0 + r < p.M) atomicMax(p.keys + m0 + r, v);
+    }
+  } else {  // EPI_TOPK
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -229,60 +294,59 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmParams p) {
           const bool ok = m < p.M && n < p.N;
           if (ok && p.dbg) p.dbg[(long long)m * p.ld_dbg + n] = acc[i][j][q];
           const unsigned long long key = ok ? argmax_key(acc[i][j][q], n, p.N) : 0ull;
-          if (EPI == EPI_TOPK)
-            best = merge16(best, sort16(key, r16), r16);
-          else
-            best = kmax2(best, key);
+          best = merge16(best, sort16(key, r16), r16);
         }
-        if (EPI == EPI_TOPK) {
-          if (m < p.M) p.keys[((long long)m * (2 * n_nt) + 2 * n_tile + wn) * 16 + r16] = best;
-        } else {
-#pragma unroll
-          for (int o = 8; o >= 1; o >>= 1) best = kmax2(best, __shfl_xor(best, o, 64));
-          if (r16 == 0) red[wn * BM + ml] = best;
-        }
+        if (m < p.M) p.keys[((long long)m * (WN * n_nt) + WN * n_tile + wn) * 16 + r16] = best;
       }
-    }
-    if (EPI == EPI_ARGMAX) {
-      __syncthreads();
-      for (int r = t; r < BM; r += 256)
-        if (m0 + r < p.M) atomicMax(p.keys + m0 + r, kmax2(red[r], red[BM + r]));
     }
   }
 }
 
-template <int BM, int BN, int ST, int EPI>
+template <typename C, int EPI>
 void launch_cfg(const GemmParams& p, hipStream_t s) {
-  const int n_mt = (p.M + BM - 1) / BM;
-  const int cols = col_tiles<BN, EPI>(p.tiles) * p.P;
+  const int n_mt = (p.M + C::BM - 1) / C::BM;
+  const int cols = col_tiles<C::BN, EPI>(p.tiles) * p.P;
   const int groups = (cols + 7) / 8;
-  hipLaunchKernelGGL((k_gemm_tile<BM, BN, ST, EPI>), dim3(groups * 8 * n_mt), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_gemm_tile<C, EPI>), dim3(groups * 8 * n_mt), dim3(C::NW * 64), 0, s, p);
 }
+
+// Above 128 rows: 256x256 tiles, 8 waves of 128x64 (two per SIMD), one
+// 32-wide k step per stage and a 4-stage ring (128 KB of LDS).  Operand bytes
+// per flop set the speed here: the direct loads are bounded by the requests a
+// CU keeps in flight, and this tile needs 0.68x the bytes per flop of 256x128.
+// Up to 128 rows (and for top-16, whose sort needs the registers): 128x128
+// tiles, 4 waves of 64x64, two k steps per stage, 3 stages.
+typedef TileCfg<128, 128, 2, 2, 2, 3> CfgSmall;
+typedef TileCfg<256, 256, 2, 4, 1, 4> CfgBig;
+
+bool use_big_cfg(int epi, int M) { return epi != EPI_TOPK && M > 128; }
 
 template <int EPI>
 void launch_epi(const GemmParams& p, hipStream_t s) {
-  if constexpr (EPI == EPI_TOPK) {  // the top-16 sort needs the registers of the smaller tile
-    launch_cfg<128, 128, 3, EPI>(p, s);
+  if constexpr (EPI == EPI_TOPK) {
+    launch_cfg<CfgSmall, EPI>(p, s);
   } else {
-    if (p.M > 128)
-      launch_cfg<256, 128, 3, EPI>(p, s);
+    if (use_big_cfg(EPI, p.M))
+      launch_cfg<CfgBig, EPI>(p, s);
     else
-      launch_cfg<128, 128, 3, EPI>(p, s);
+      launch_cfg<CfgSmall, EPI>(p, s);
   }
 }
 
 }  // namespace
 
-// Lists per row written by the top-16 epilogue (two per 128-column tile).
-int gemm_big_lists(int tiles) { return 2 * col_tiles<128, EPI_TOPK>(tiles); }
+// Lists per row written by the top-16 epilogue (one per column wave and tile).
+int gemm_big_lists(int tiles) { return CfgSmall::WN * col_tiles<CfgSmall::BN, EPI_TOPK>(tiles); }
 
 // Split-K factor of a partial-output product: the smallest power of two that
-// gives at least one workgroup per CU while keeping 8 or more k-stages per split.
+// gives at least one workgroup per CU while keeping 8 or more 64-wide k blocks
+// per split.
 int gemm_big_split(int M, int tiles, int K) {
-  const int bm = M > 128 ? 256 : 128;
-  const int wgs = ((M + bm - 1) / bm) * ((tiles + 7) / 8);
+  const bool big = use_big_cfg(EPI_PARTIAL, M);
+  const int bm = big ? CfgBig::BM : CfgSmall::BM, bn = big ? CfgBig::BN : CfgSmall::BN;
+  const int wgs = ((M + bm - 1) / bm) * ((tiles + bn / 16 - 1) / (bn / 16));
   int P = 1;
-  while (wgs * P < 256 && K / (BK * 2 * P) >= 8) P *= 2;
+  while (wgs * P < 256 && K / (64 * 2 * P) >= 8) P *= 2;
   return P;
 }
 
