@@ -451,16 +451,24 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
     for (int i = 0; i < NI; ++i) dma16((c_unit[i] ? b[1] : b[0]) + c_src[i], ring + buf * STAGE + c_dst[i]);
   };
 
-  // Scores are kept in log2 units.  The reference max m_run of a query is
-  // only raised when a score exceeds it by more than 8 (p <= 2^8 stays exact
-  // in fp32 and in the hi + lo bf16 pair), so the rescale of O is skipped for
-  // nearly every pair of a long context; softmax does not depend on the
-  // reference.
+  // Softmax in log2 units with a lazily raised reference max: p = 2^(s*c - m)
+  // with c = scale*log2(e).  The reference m of a query is only raised when
+  // one of its scores exceeds it by more than 8 (so p <= 2^8, exact in fp32
+  // and in the hi + lo bf16 pair); each lane checks its own scores and the
+  // cross-lane reduction and rescale of O run only when some lane of the wave
+  // needs it, which after the first pair of a long context is rare.  Softmax
+  // does not depend on the reference.  The row sums l come from the matrix
+  // cores: a tile of ones joins the PV product as a ninth O tile.
   const float sl2 = p.scale * 1.44269504088896341f;
-  float m_run = NEG, l_run = 0.f;
-  f32x4 o[ND];
+  float m_run = NEG;
+  f32x4 o[ND], o_l = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
+  // context units [uf0, uf1) are pages whose 16 positions are all visible
+  const int uf0 = (lo & 15) ? 1 : 0, uf1 = hi / 16 - lp0;
 
 #pragma unroll
   for (int i = 0; i < kRing - 1; ++i)
@@ -477,16 +485,15 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
     const bf16* sb = ring + (it % kRing) * STAGE;
 
     // which keys of the pair are valid (wave-uniform per unit, then per key)
-    bool has[2], full[2];
-    int pos0[2];
+    const int u0 = u_begin + 2 * it;
+    bool has[2];
+    bool fast = true;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int uu = u_begin + 2 * it + t;
+      const int uu = u0 + t;
       has[t] = unit_base(uu) != nullptr;
-      pos0[t] = (lp0 + uu) * 16;
-      full[t] = has[t] && (uu < n_lp ? (pos0[t] >= lo && pos0[t] + 16 <= hi) : p.B == 16);
+      fast = fast && has[t] && (uu < n_lp ? (uu >= uf0 && uu < uf1) : p.B == 16);
     }
-    const bool fast = full[0] && full[1];
 
     float sv[8];
 #pragma unroll
@@ -501,7 +508,7 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[4 * t + i] = sacc[i] * sl2;
+      for (int i = 0; i < 4; ++i) sv[4 * t + i] = sacc[i];
     }
     // Lane-dependent masking is written as selects: a divergent branch that
     // stores into one element of the score vector lost that store in code
@@ -510,40 +517,35 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
     if (!fast) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bool is_blk = u_begin + 2 * it + t >= n_lp;
+        const int uu = u0 + t;
+        const bool is_blk = uu >= n_lp;
+        const int pos0 = (lp0 + uu) * 16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = 4 * g4 + i;
-          valid[t][i] = has[t] && (is_blk ? key < p.B : (pos0[t] + key >= lo && pos0[t] + key < hi));
+          valid[t][i] = has[t] && (is_blk ? key < p.B : (pos0 + key >= lo && pos0 + key < hi));
           sv[4 * t + i] = valid[t][i] ? sv[4 * t + i] : NEG;
         }
       }
     }
-    float mx = sv[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const bool grow = mx > m_run + 8.0f;  // false while both are -inf
-    if (__ballot(grow)) {
+    float lmx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    if (__ballot(lmx * sl2 > m_run + 8.0f)) {  // false while both are -inf
+      float mx = fmaxf(lmx, __shfl_xor(lmx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;  // the query's max in log2 units
+      const bool grow = mx > m_run + 8.0f;
       const float m_new = grow ? mx : m_run;
       const float corr = (m_run == NEG) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) o[dt] = o[dt] * corr;
-      l_run *= corr;
+      o_l = o_l * corr;
       m_run = m_new;
     }
     float pe[8];
-    float ls = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pe[e] = fast ? __builtin_amdgcn_exp2f(sv[e] - m_run)
-                   : (sv[e] == NEG ? 0.f : __builtin_amdgcn_exp2f(sv[e] - m_run));
-      ls += pe[e];
+      const float x = __builtin_amdgcn_exp2f(fmaf(sv[e], sl2, -m_run));
+      pe[e] = fast ? x : (sv[e] == NEG ? 0.f : x);
     }
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
-    l_run += ls;
     // P at fp32 accuracy in the bf16 MFMA: an exact hi + lo pair
     bf16x8 pf, pf_lo;
 #pragma unroll
@@ -551,6 +553,8 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
       pf[e] = (bf16)pe[e];
       pf_lo[e] = (bf16)(pe[e] - (float)pf[e]);
     }
+    o_l = mfma_step(ones, pf, o_l);
+    o_l = mfma_step(ones, pf_lo, o_l);
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
       const bf16* vb = sb + (dt * 16 + l16) * 16 + 4 * g4;
@@ -567,6 +571,7 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
       o[dt] = mfma_step(vf, pf_lo, o[dt]);
     }
   }
+  const float l_run = o_l[0];  // every row of the ones tile holds the query's sum
 
   // lane holds query row l16, dims dt*16 + 4*g4 + i
   if (n_split == 1) {
