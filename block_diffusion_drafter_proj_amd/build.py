@@ -29,13 +29,20 @@ CFLAGS = [
 ]
 
 
+# Per-source flags.  The attention kernel keeps its MFMA accumulators in
+# ordinary VGPRs (gfx950 allows either register file): its O tiles are also
+# rescaled by plain float code, and with AGPR accumulators the compiler copies
+# every tile between the two files on each step.
+FILE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

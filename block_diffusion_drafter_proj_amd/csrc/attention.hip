@@ -347,27 +347,25 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams p, SlotArgs sl) {
 // nothing left repeats another wave's copy), so the per-wave count of
 // outstanding copies fixes how far each wait lets the ring run ahead.  A
 // missing unit is copied from the request's block page and fully masked.
-// K rows are stored with their 16-byte chunks permuted (chunk c of key k at
-// slot c ^ swz(k)) so that the 16 keys of one fragment read fall on distinct
-// LDS banks; V^T rows (16 positions, 32 bytes) are read as stored.
+// A stage holds the pair's K and V already in MFMA fragment order (each 1 KB
+// fragment is lane-major, so every LDS read is a sequential 16-byte-per-lane
+// read with no bank conflict); the copies gather the 16 bytes each lane needs.
+// Inside the pair, keys are ordered so that both products gather whole
+// 16-byte pieces: row 4g+i of score tile t is unit g/2, position
+// 8(g%2)+4t+i.  Then a lane of group g holds, across its two score tiles,
+// exactly the 8 keys that its PV operand spans (unit g/2, positions
+// 8(g%2)..+7: one contiguous 16-byte piece of a V^T row), so P never moves
+// between lanes.
 constexpr int kRing = 4;
-
-template <int DH>
-__device__ __forceinline__ int swz(int key) {
-  constexpr int CH = DH / 8;
-  return (key * CH / 16) & (CH - 1);
-}
 
 template <int DH, int G>
 __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl) {
   constexpr int NJ = DH / 32;             // k32 steps of S^T = K Q^T
   constexpr int ND = DH / 16;             // 16-row tiles of O^T
-  constexpr int CH = DH / 8;              // 16-byte chunks per K row
   constexpr int HEAD = 16 * DH;           // elements of one head's K (or V) in a unit
-  constexpr int KI = HEAD * 2 / 1024;     // 1 KB copies per head block
-  constexpr int NCOPY = 2 * 2 * KI;       // per stage: 2 units x (K, V)
+  constexpr int NCOPY = 2 * NJ + ND;      // fragments per stage: K (2 tiles x NJ), V (ND)
   constexpr int NI = (NCOPY + G - 1) / G; // copies per wave and stage
-  constexpr int STAGE = 2 * 2 * HEAD;     // elements per stage
+  constexpr int STAGE = NCOPY * 512;      // elements per stage
   static_assert((kRing - 2) * NI < 64 && NCOPY >= G, "ring shape");
   __shared__ __attribute__((aligned(1024))) bf16 ring[kRing * STAGE];
   const float NEG = -INFINITY;
@@ -401,54 +399,66 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) qf[j] = load8<bf16>(qrow + 32 * j + 8 * g4);
   }
-  // page ids of the split's context units, one per lane (pps <= 64)
-  int my_page = -1;
+  // Per-unit tables, lane L describing unit u_begin + L of the split (pps <=
+  // 64): its base (the block page stands in for a missing unit, whose keys
+  // are masked) and its visible positions as a 16-bit mask.
+  const bf16* my_base = blk;
+  unsigned my_vis = 0;
   {
     const int uu = u_begin + lane;
-    if (uu < u_end && uu < n_lp) {
-      const int lp = lp0 + uu;
-      const int idx = p.window > 0 ? lp % st.n_pages : lp;
-      my_page = p.page_table[(long long)slot * p.pt_stride + idx];
-      if (my_page < 0 || my_page >= p.max_pages) {
-        atomicOr(p.err, 2u);
-        my_page = -1;
+    if (uu < u_end) {
+      if (uu < n_lp) {
+        const int lp = lp0 + uu;
+        const int idx = p.window > 0 ? lp % st.n_pages : lp;
+        const int page = p.page_table[(long long)slot * p.pt_stride + idx];
+        if (page < 0 || page >= p.max_pages) {
+          atomicOr(p.err, 2u);
+        } else {
+          my_base = pool + (long long)page * page_elems;
+          const int pos0 = lp * 16;
+          const int a0 = max(lo - pos0, 0), a1 = min(hi - pos0, 16);
+          my_vis = ((1u << a1) - 1u) & ~((1u << a0) - 1u);
+        }
+      } else {
+        my_vis = (1u << p.B) - 1u;
       }
     }
   }
-  // unit uu (wave-uniform): its base, or nullptr when nothing there is valid
-  auto unit_base = [&](int uu) -> const bf16* {
-    if (uu >= u_end) return nullptr;
-    if (uu < n_lp) {
-      const int page = __builtin_amdgcn_readlane(my_page, uu - u_begin);
-      return page >= 0 ? pool + (long long)page * page_elems : nullptr;
-    }
-    return blk;
+  // units whose 16 positions are all visible: those pairs skip masking
+  const unsigned long long full_mask = __ballot(my_vis == 0xffffu);
+  const unsigned long long base_lo = reinterpret_cast<unsigned long long>(my_base);
+  const unsigned b_lo32 = (unsigned)base_lo, b_hi32 = (unsigned)(base_lo >> 32);
+  auto unit_ptr = [&](int lane_idx) -> const bf16* {
+    const unsigned long long lo32 = (unsigned)__builtin_amdgcn_readlane((int)b_lo32, lane_idx);
+    const unsigned long long hi32 = (unsigned)__builtin_amdgcn_readlane((int)b_hi32, lane_idx);
+    return reinterpret_cast<const bf16*>(lo32 | (hi32 << 32));
   };
-  // this wave's copies: source offset inside a unit (per lane) and LDS offset
-  int c_src[NI], c_dst[NI], c_unit[NI];
+  // this wave's copies: fragment q of the stage is K fragment (tile q / NJ,
+  // k step q % NJ) for q < 2 NJ, else V fragment q - 2 NJ; per lane, the unit
+  // (0 or 1 of the pair) and the element offset inside it of its 16 bytes
+  int c_src[NI], c_dst[NI];
+  bool c_u1[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     int q = wave + G * i;
     if (q >= NCOPY) q -= NCOPY;  // nothing left: repeat another wave's copy
-    const int t = q / (2 * KI), kv = (q / KI) & 1, j = q % KI;
-    int chunk = j * 64 + lane;  // 16-byte chunk of the head block landing at this LDS slot
-    if (!kv) {
-      const int key = chunk / CH;
-      chunk = key * CH + ((chunk % CH) ^ swz<DH>(key));
+    const int fr = lane & 15, fc = lane >> 4;  // fragment row and 8-element column group
+    if (q < 2 * NJ) {  // K: row fr of tile t = key (unit g/2, position 8(g%2)+4t+i), g = fr/4, i = fr%4
+      const int t = q / NJ, j = q % NJ, gg = fr >> 2;
+      c_u1[i] = gg >= 2;
+      c_src[i] = gkv * HEAD + (8 * (gg & 1) + 4 * t + (fr & 3)) * DH + 32 * j + 8 * fc;
+    } else {  // V^T: dh row dt*16 + fr, keys 8(fc%2)..+7 of unit fc/2
+      const int dt = q - 2 * NJ;
+      c_u1[i] = fc >= 2;
+      c_src[i] = (p.Hkv + gkv) * HEAD + (dt * 16 + fr) * 16 + 8 * (fc & 1);
     }
-    c_src[i] = ((kv ? p.Hkv : 0) + gkv) * HEAD + chunk * 8;
-    c_dst[i] = (t * 2 + kv) * HEAD + j * 512;
-    c_unit[i] = t;
+    c_dst[i] = q * 512;
   }
   auto issue = [&](int pair, int buf) {
-    const bf16* b[2];
+    const bf16* b0 = unit_ptr(2 * pair);
+    const bf16* b1 = unit_ptr(2 * pair + 1);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      b[t] = unit_base(u_begin + 2 * pair + t);
-      if (!b[t]) b[t] = blk;  // any readable unit; its keys are masked
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) dma16((c_unit[i] ? b[1] : b[0]) + c_src[i], ring + buf * STAGE + c_dst[i]);
+    for (int i = 0; i < NI; ++i) dma16((c_u1[i] ? b1 : b0) + c_src[i], ring + buf * STAGE + c_dst[i]);
   };
 
   // Softmax in log2 units with a lazily raised reference max: p = 2^(s*c - m)
@@ -457,18 +467,19 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
   // and in the hi + lo bf16 pair); each lane checks its own scores and the
   // cross-lane reduction and rescale of O run only when some lane of the wave
   // needs it, which after the first pair of a long context is rare.  Softmax
-  // does not depend on the reference.  The row sums l come from the matrix
-  // cores: a tile of ones joins the PV product as a ninth O tile.
+  // does not depend on the reference.  m starts at a finite -1e30, so a
+  // masked score (-inf) gives p = 2^-inf = 0 with no select, and the first
+  // visible score always raises it (the rescale factor 2^(-1e30 - m) is 0).
+  // The row sums l come from the matrix cores: a tile of ones joins the PV
+  // product as a ninth O tile.
   const float sl2 = p.scale * 1.44269504088896341f;
-  float m_run = NEG;
+  float m_run = -1e30f;
   f32x4 o[ND], o_l = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
-  // context units [uf0, uf1) are pages whose 16 positions are all visible
-  const int uf0 = (lo & 15) ? 1 : 0, uf1 = hi / 16 - lp0;
 
 #pragma unroll
   for (int i = 0; i < kRing - 1; ++i)
@@ -483,58 +494,39 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
       wait_barrier<0>();
     if (it + kRing - 1 < n_pairs) issue(it + kRing - 1, (it + kRing - 1) % kRing);
     const bf16* sb = ring + (it % kRing) * STAGE;
+    const bool fast = ((full_mask >> (2 * it)) & 3ull) == 3ull;
 
-    // which keys of the pair are valid (wave-uniform per unit, then per key)
-    const int u0 = u_begin + 2 * it;
-    bool has[2];
-    bool fast = true;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int uu = u0 + t;
-      has[t] = unit_base(uu) != nullptr;
-      fast = fast && has[t] && (uu < n_lp ? (uu >= uf0 && uu < uf1) : p.B == 16);
-    }
-
+    // score tiles: sv[4t+i] of a lane in group g4 is key (unit g4/2, position 8(g4%2)+4t+i)
     float sv[8];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (has[t]) {
-        const bf16* kb = sb + (t * 2) * HEAD + l16 * DH;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + ((4 * j + g4) ^ swz<DH>(l16)) * 8);
-          sacc = mfma_step(kf, qf[j], sacc);
-        }
+      for (int j = 0; j < NJ; ++j) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sb + (t * NJ + j) * 512 + lane * 8);
+        sacc = mfma_step(kf, qf[j], sacc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[4 * t + i] = sacc[i];
     }
-    // Lane-dependent masking is written as selects: a divergent branch that
-    // stores into one element of the score vector lost that store in code
-    // generation (the exec-masked block kept only the mask itself).
-    bool valid[2][4];
+    // Partly visible pair: the lane's 8 keys are bits 8(g4%2)..+7 of its
+    // unit's visibility mask.  Masking is written as selects: a divergent
+    // branch that stored into one element of the score vector lost that store
+    // in code generation.
+    unsigned vbits = 0xffu;
     if (!fast) {
+      const unsigned m0 = __builtin_amdgcn_readlane(my_vis, 2 * it);
+      const unsigned m1 = __builtin_amdgcn_readlane(my_vis, 2 * it + 1);
+      vbits = (((g4 >> 1) ? m1 : m0) >> (8 * (g4 & 1))) & 0xffu;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int uu = u0 + t;
-        const bool is_blk = uu >= n_lp;
-        const int pos0 = (lp0 + uu) * 16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 4 * g4 + i;
-          valid[t][i] = has[t] && (is_blk ? key < p.B : (pos0 + key >= lo && pos0 + key < hi));
-          sv[4 * t + i] = valid[t][i] ? sv[4 * t + i] : NEG;
-        }
-      }
+      for (int e = 0; e < 8; ++e) sv[e] = ((vbits >> e) & 1u) ? sv[e] : NEG;
     }
     float lmx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    if (__ballot(lmx * sl2 > m_run + 8.0f)) {  // false while both are -inf
+    if (__ballot(lmx * sl2 > m_run + 8.0f)) {  // false for a lane whose keys are all masked
       float mx = fmaxf(lmx, __shfl_xor(lmx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;  // the query's max in log2 units
-      const bool grow = mx > m_run + 8.0f;
-      const float m_new = grow ? mx : m_run;
-      const float corr = (m_run == NEG) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float m_new = mx > m_run + 8.0f ? mx : m_run;
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) o[dt] = o[dt] * corr;
       o_l = o_l * corr;
@@ -542,31 +534,35 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
     }
     float pe[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = __builtin_amdgcn_exp2f(fmaf(sv[e], sl2, -m_run));
-      pe[e] = fast ? x : (sv[e] == NEG ? 0.f : x);
-    }
-    // P at fp32 accuracy in the bf16 MFMA: an exact hi + lo pair
+    for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], sl2, -m_run));
+    // P at fp32 accuracy in the bf16 MFMA: an exact hi + lo pair (the hi
+    // halves are widened back to fp32 by moving their bits, not converted)
     bf16x8 pf, pf_lo;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pf[e] = (bf16)pe[e];
-      pf_lo[e] = (bf16)(pe[e] - (float)pf[e]);
+    for (int e = 0; e < 8; ++e) pf[e] = (bf16)pe[e];
+    {
+      const u32x4 w = __builtin_bit_cast(u32x4, pf);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        pf_lo[2 * k] = (bf16)(pe[2 * k] - __uint_as_float(w[k] << 16));
+        pf_lo[2 * k + 1] = (bf16)(pe[2 * k + 1] - __uint_as_float(w[k] & 0xffff0000u));
+      }
     }
     o_l = mfma_step(ones, pf, o_l);
     o_l = mfma_step(ones, pf_lo, o_l);
+    // V of masked keys is zeroed too: a stale or unwritten position may hold
+    // a non-finite pattern, and 0 * inf would poison O
+    u32x4 vkeep = u32x4{~0u, ~0u, ~0u, ~0u};
+    if (!fast) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        vkeep[k] = (((vbits >> (2 * k)) & 1u) ? 0xffffu : 0u) | (((vbits >> (2 * k + 1)) & 1u) ? 0xffff0000u : 0u);
+    }
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
-      const bf16* vb = sb + (dt * 16 + l16) * 16 + 4 * g4;
-      const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vb + HEAD);
-      const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vb + 3 * HEAD);
-      bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      if (!fast) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) vf[4 * t + i] = valid[t][i] ? vf[4 * t + i] : (bf16)0.0f;
-      }
+      u32x4 vr = *reinterpret_cast<const u32x4*>(sb + (2 * NJ + dt) * 512 + lane * 8);
+      if (!fast) vr &= vkeep;
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, vr);
       o[dt] = mfma_step(vf, pf, o[dt]);
       o[dt] = mfma_step(vf, pf_lo, o[dt]);
     }
@@ -591,7 +587,7 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
   // split partial; the merge works in natural-log units
   const long long pb = ((long long)(r * p.Hq + h) * p.n_splits + s) * 16 + l16;
   if (g4 == 0) {
-    p.part_ml[pb * 2 + 0] = m_run == NEG ? NEG : m_run * 0.693147180559945309f;
+    p.part_ml[pb * 2 + 0] = l_run > 0.f ? m_run * 0.693147180559945309f : NEG;
     p.part_ml[pb * 2 + 1] = l_run;
   }
   float* po = p.part_o + pb * DH + 4 * g4;
