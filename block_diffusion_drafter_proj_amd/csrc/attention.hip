@@ -100,8 +100,8 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams p, SlotArgs sl) {
   const float NEG = -INFINITY;
   extern __shared__ float smem[];
 
-  const int s = blockIdx.x;
-  const int gkv = blockIdx.y;
+  const int gkv = blockIdx.x;
+  const int s = blockIdx.y;
   const int r = blockIdx.z;
   const int G = p.Hq / p.Hkv;
   const int KQ = p.KQ;
@@ -358,6 +358,20 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams p, SlotArgs sl) {
 // between lanes.
 constexpr int kRing = 4;
 
+// Waits until at most `ahead` stages of this wave's copies (NI each) are
+// still in flight, then joins the workgroup barrier.
+template <int NI, int A>
+__device__ __forceinline__ void wait_ring(int ahead) {
+  if constexpr (A == 0) {
+    wait_barrier<0>();
+  } else {
+    if (ahead >= A)
+      wait_barrier<A * NI>();
+    else
+      wait_ring<NI, A - 1>(ahead);
+  }
+}
+
 template <int DH, int G>
 __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl) {
   constexpr int NJ = DH / 32;             // k32 steps of S^T = K Q^T
@@ -370,7 +384,7 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
   __shared__ __attribute__((aligned(1024))) bf16 ring[kRing * STAGE];
   const float NEG = -INFINITY;
 
-  const int s = blockIdx.x, gkv = blockIdx.y, r = blockIdx.z;
+  const int gkv = blockIdx.x, s = blockIdx.y, r = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = gkv * G + wave;
   const int lane = lane_id(), l16 = lane & 15, g4 = lane >> 4;
@@ -485,13 +499,7 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
   for (int i = 0; i < kRing - 1; ++i)
     if (i < n_pairs) issue(i, i);
   for (int it = 0; it < n_pairs; ++it) {
-    const int ahead = min(n_pairs - 1 - it, kRing - 2);
-    if (ahead >= 2)
-      wait_barrier<2 * NI>();
-    else if (ahead == 1)
-      wait_barrier<NI>();
-    else
-      wait_barrier<0>();
+    wait_ring<NI, kRing - 2>(n_pairs - 1 - it);
     if (it + kRing - 1 < n_pairs) issue(it + kRing - 1, (it + kRing - 1) % kRing);
     const bf16* sb = ring + (it % kRing) * STAGE;
     const bool fast = ((full_mask >> (2 * it)) & 3ull) == 3ull;
@@ -707,7 +715,7 @@ void qkv_post_t(int dh, int n_req, const QkvPostParams& p, const SlotArgs& sl, h
 
 template <typename T>
 void attn_t(int dh, int n_req, const AttnParams& p, const SlotArgs& sl, hipStream_t s) {
-  dim3 grid(p.n_splits, p.Hkv, n_req);
+  dim3 grid(p.Hkv, p.n_splits, n_req);  // KV head fastest: see attn_ring_t
   const int G = p.Hq / p.Hkv;
   dim3 block(64 * G * p.KQ);
   const size_t lds = attn_lds_bytes(p.Hq, p.Hkv, dh, p.KQ);
@@ -719,7 +727,11 @@ void attn_t(int dh, int n_req, const AttnParams& p, const SlotArgs& sl, hipStrea
 
 template <int DH>
 void attn_ring_t(int n_req, const AttnParams& p, const SlotArgs& sl, hipStream_t s) {
-  dim3 grid(p.n_splits, p.Hkv, n_req);
+  // KV head fastest: workgroups go to the eight XCDs round-robin by linear
+  // id, so with eight KV heads each XCD takes one head of every (request,
+  // split) and all XCDs get the same work.  (Split fastest sent split s of
+  // every request to XCD s, and the first XCDs carried most of the load.)
+  dim3 grid(p.Hkv, p.n_splits, n_req);
   switch (p.Hq / p.Hkv) {
     case 1: hipLaunchKernelGGL((k_attn_ring<DH, 1>), grid, dim3(64), 0, s, p, sl); break;
     case 2: hipLaunchKernelGGL((k_attn_ring<DH, 2>), grid, dim3(128), 0, s, p, sl); break;

@@ -181,10 +181,15 @@ void launch_attention(int dtype, int dh, int n_req, const AttnParams& p, const S
                       hipStream_t s);
 size_t attn_lds_bytes(int Hq, int Hkv, int dh, int KQ);
 // Pages per attention split of a request with n_units pages (the block counts
-// as one): about `target` splits, at most `cap` pages each.  Host and device.
+// as one): `target` splits (fewer if there are fewer pages, more if a split
+// would exceed `cap` pages), cut into runs of equal length so that the
+// workgroups of one request finish together.  Host and device.
 __host__ __device__ inline int split_pages(int n_units, int target, int cap) {
-  const int pps = (n_units + target - 1) / target;
-  return pps < 1 ? 1 : (pps > cap ? cap : pps);
+  if (n_units <= 1) return 1;
+  int n = (n_units + cap - 1) / cap;
+  const int want = target < n_units ? target : n_units;
+  if (n < want) n = want;
+  return (n_units + n - 1) / n;
 }
 void launch_combine(int dtype, int dh, const CombineParams& p, hipStream_t s);
 void launch_scatter(int dtype, int dh, const ScatterParams& p, hipStream_t s);
