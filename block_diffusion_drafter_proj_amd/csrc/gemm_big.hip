@@ -316,20 +316,65 @@ void launch_cfg(const GemmParams& p, hipStream_t s) {
 // CU keeps in flight, and this tile needs 0.68x the bytes per flop of 256x128.
 // Up to 128 rows (and for top-16, whose sort needs the registers): 128x128
 // tiles, 4 waves of 64x64, two k steps per stage, 3 stages.
+// 256x192 tiles (8 waves of 64x96, 64-deep k stages, double buffered in
+// 112 KB of LDS) are taken where their workgroup count fills the CUs better
+// than 256x256: the 24576-wide SwiGLU product gets 512 workgroups (two full
+// rounds) instead of 384, whose second round would leave half the CUs idle.
 typedef TileCfg<128, 128, 2, 2, 2, 3> CfgSmall;
 typedef TileCfg<256, 256, 2, 4, 1, 4> CfgBig;
+typedef TileCfg<256, 192, 4, 2, 2, 2> CfgWide;
 
-bool use_big_cfg(int epi, int M) { return epi != EPI_TOPK && M > 128; }
+enum { CFG_SMALL, CFG_BIG, CFG_WIDE };
+
+// Workgroups with real work and the split-K factor of a partial-output
+// product: the smallest power of two that gives at least one workgroup per CU
+// while keeping 8 or more 64-wide k blocks per split.
+template <typename C, int EPI>
+int cfg_work(int M, int tiles, int P) {
+  return ((M + C::BM - 1) / C::BM) * col_tiles<C::BN, EPI>(tiles) * P;
+}
+template <typename C>
+int cfg_split(int M, int tiles, int K) {
+  const int wgs = cfg_work<C, EPI_PARTIAL>(M, tiles, 1);
+  int P = 1;
+  while (wgs * P < 256 && K / (64 * 2 * P) >= 8) P *= 2;
+  return P;
+}
+// share of the CU slots of the last round that has work (one workgroup per CU)
+double round_fill(int w) { return (double)w / (256.0 * ((w + 255) / 256)); }
+
+template <int EPI>
+int tile_cfg_t(int M, int tiles, int K) {
+  if (EPI == EPI_TOPK || M <= 128) return CFG_SMALL;
+  if (EPI == EPI_ARGMAX) return CFG_BIG;  // the vocabulary-wide product fills the CUs either way
+  const int pb = EPI == EPI_PARTIAL ? cfg_split<CfgBig>(M, tiles, K) : 1;
+  const int pw = EPI == EPI_PARTIAL ? cfg_split<CfgWide>(M, tiles, K) : 1;
+  const double fb = round_fill(cfg_work<CfgBig, EPI>(M, tiles, pb));
+  const double fw = round_fill(cfg_work<CfgWide, EPI>(M, tiles, pw));
+  return fw > fb + 0.05 ? CFG_WIDE : CFG_BIG;
+}
+
+int tile_cfg(int epi, int M, int tiles, int K) {
+  switch (epi) {
+    case EPI_PARTIAL: return tile_cfg_t<EPI_PARTIAL>(M, tiles, K);
+    case EPI_SWIGLU: return tile_cfg_t<EPI_SWIGLU>(M, tiles, K);
+    case EPI_ARGMAX: return tile_cfg_t<EPI_ARGMAX>(M, tiles, K);
+    default: return CFG_SMALL;
+  }
+}
 
 template <int EPI>
 void launch_epi(const GemmParams& p, hipStream_t s) {
   if constexpr (EPI == EPI_TOPK) {
     launch_cfg<CfgSmall, EPI>(p, s);
   } else {
-    if (use_big_cfg(EPI, p.M))
-      launch_cfg<CfgBig, EPI>(p, s);
-    else
-      launch_cfg<CfgSmall, EPI>(p, s);
+    switch (tile_cfg_t<EPI>(p.M, p.tiles, p.K)) {
+      case CFG_WIDE:
+        if constexpr (EPI != EPI_ARGMAX) launch_cfg<CfgWide, EPI>(p, s);
+        break;
+      case CFG_BIG: launch_cfg<CfgBig, EPI>(p, s); break;
+      default: launch_cfg<CfgSmall, EPI>(p, s); break;
+    }
   }
 }
 
@@ -338,16 +383,14 @@ void launch_epi(const GemmParams& p, hipStream_t s) {
 // Lists per row written by the top-16 epilogue (one per column wave and tile).
 int gemm_big_lists(int tiles) { return CfgSmall::WN * col_tiles<CfgSmall::BN, EPI_TOPK>(tiles); }
 
-// Split-K factor of a partial-output product: the smallest power of two that
-// gives at least one workgroup per CU while keeping 8 or more 64-wide k blocks
-// per split.
+// Split-K factor of a partial-output product, for the tile shape the launch
+// will pick.
 int gemm_big_split(int M, int tiles, int K) {
-  const bool big = use_big_cfg(EPI_PARTIAL, M);
-  const int bm = big ? CfgBig::BM : CfgSmall::BM, bn = big ? CfgBig::BN : CfgSmall::BN;
-  const int wgs = ((M + bm - 1) / bm) * ((tiles + bn / 16 - 1) / (bn / 16));
-  int P = 1;
-  while (wgs * P < 256 && K / (64 * 2 * P) >= 8) P *= 2;
-  return P;
+  switch (tile_cfg(EPI_PARTIAL, M, tiles, K)) {
+    case CFG_WIDE: return cfg_split<CfgWide>(M, tiles, K);
+    case CFG_BIG: return cfg_split<CfgBig>(M, tiles, K);
+    default: return cfg_split<CfgSmall>(M, tiles, K);
+  }
 }
 
 void launch_gemm_big(int epi, const GemmParams& p, hipStream_t s) {
