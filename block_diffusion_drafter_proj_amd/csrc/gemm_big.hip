@@ -320,11 +320,17 @@ void launch_cfg(const GemmParams& p, hipStream_t s) {
 // 112 KB of LDS) are taken where their workgroup count fills the CUs better
 // than 256x256: the 24576-wide SwiGLU product gets 512 workgroups (two full
 // rounds) instead of 384, whose second round would leave half the CUs idle.
+// At 64 rows (4 requests of 16), 64x128 tiles: 4 waves of 32x64 and a
+// 72 KB ring, so two workgroups share a CU and no MFMA row is empty; the
+// product streams its weights once and is bound by that stream.  Two waves
+// across N keep the top-16 list count per row equal to CfgSmall's.
+typedef TileCfg<64, 128, 2, 2, 2, 3> Cfg64;
 typedef TileCfg<128, 128, 2, 2, 2, 3> CfgSmall;
 typedef TileCfg<256, 256, 2, 4, 1, 4> CfgBig;
 typedef TileCfg<256, 192, 4, 2, 2, 2> CfgWide;
+static_assert(Cfg64::WN == CfgSmall::WN && Cfg64::BN == CfgSmall::BN, "top-16 lists per row");
 
-enum { CFG_SMALL, CFG_BIG, CFG_WIDE };
+enum { CFG_SMALL, CFG_BIG, CFG_WIDE, CFG_64 };
 
 // Workgroups with real work and the split-K factor of a partial-output
 // product: the smallest power of two that gives at least one workgroup per CU
@@ -345,6 +351,7 @@ double round_fill(int w) { return (double)w / (256.0 * ((w + 255) / 256)); }
 
 template <int EPI>
 int tile_cfg_t(int M, int tiles, int K) {
+  if (M <= 64) return CFG_64;
   if (EPI == EPI_TOPK || M <= 128) return CFG_SMALL;
   if (EPI == EPI_ARGMAX) return CFG_BIG;  // the vocabulary-wide product fills the CUs either way
   const int pb = EPI == EPI_PARTIAL ? cfg_split<CfgBig>(M, tiles, K) : 1;
@@ -359,22 +366,22 @@ int tile_cfg(int epi, int M, int tiles, int K) {
     case EPI_PARTIAL: return tile_cfg_t<EPI_PARTIAL>(M, tiles, K);
     case EPI_SWIGLU: return tile_cfg_t<EPI_SWIGLU>(M, tiles, K);
     case EPI_ARGMAX: return tile_cfg_t<EPI_ARGMAX>(M, tiles, K);
+    case EPI_TOPK: return tile_cfg_t<EPI_TOPK>(M, tiles, K);
     default: return CFG_SMALL;
   }
 }
 
 template <int EPI>
 void launch_epi(const GemmParams& p, hipStream_t s) {
-  if constexpr (EPI == EPI_TOPK) {
-    launch_cfg<CfgSmall, EPI>(p, s);
-  } else {
-    switch (tile_cfg_t<EPI>(p.M, p.tiles, p.K)) {
-      case CFG_WIDE:
-        if constexpr (EPI != EPI_ARGMAX) launch_cfg<CfgWide, EPI>(p, s);
-        break;
-      case CFG_BIG: launch_cfg<CfgBig, EPI>(p, s); break;
-      default: launch_cfg<CfgSmall, EPI>(p, s); break;
-    }
+  switch (tile_cfg_t<EPI>(p.M, p.tiles, p.K)) {
+    case CFG_64: launch_cfg<Cfg64, EPI>(p, s); break;
+    case CFG_WIDE:
+      if constexpr (EPI != EPI_ARGMAX && EPI != EPI_TOPK) launch_cfg<CfgWide, EPI>(p, s);
+      break;
+    case CFG_BIG:
+      if constexpr (EPI != EPI_TOPK) launch_cfg<CfgBig, EPI>(p, s);
+      break;
+    default: launch_cfg<CfgSmall, EPI>(p, s); break;
   }
 }
 
@@ -389,6 +396,7 @@ int gemm_big_split(int M, int tiles, int K) {
   switch (tile_cfg(EPI_PARTIAL, M, tiles, K)) {
     case CFG_WIDE: return cfg_split<CfgWide>(M, tiles, K);
     case CFG_BIG: return cfg_split<CfgBig>(M, tiles, K);
+    case CFG_64: return cfg_split<Cfg64>(M, tiles, K);
     default: return cfg_split<CfgSmall>(M, tiles, K);
   }
 }
