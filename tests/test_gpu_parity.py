@@ -308,6 +308,18 @@ def test_free_running_within_tolerance(name):
     _draft_both(dev, shape, dr, o, states, list(range(n)), free=True)
 
 
+@pytest.mark.parametrize("batch", [4, 12])
+def test_tile_shapes_within_tolerance(batch):
+    """Row counts that select the other tiled GEMM shapes: 64 rows (64x128
+    tiles) and 192 rows (one ragged 256-row tile of the large shapes), whole
+    path free-running against the oracle."""
+    dev, shape, w, dr, ctxs, pages = _setup("small_batch", batch=batch, seed=40 + batch)
+    o = DraftOracle(shape, w)
+    states = [o.new_request() for _ in range(batch)]
+    _inject_both(dev, shape, dr, o, states, list(range(batch)), [0] * batch, ctxs)
+    _draft_both(dev, shape, dr, o, states, list(range(batch)), free=True)
+
+
 def test_window_ring_wraps_and_starts_late():
     """Sliding window: the ring of W/16 + 1 pages wraps several times over
     chunked injects; a request bound with a start position beyond 0 only ever
