@@ -358,20 +358,6 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams p, SlotArgs sl) {
 // between lanes.
 constexpr int kRing = 4;
 
-// Waits until at most `ahead` stages of this wave's copies (NI each) are
-// still in flight, then joins the workgroup barrier.
-template <int NI, int A>
-__device__ __forceinline__ void wait_ring(int ahead) {
-  if constexpr (A == 0) {
-    wait_barrier<0>();
-  } else {
-    if (ahead >= A)
-      wait_barrier<A * NI>();
-    else
-      wait_ring<NI, A - 1>(ahead);
-  }
-}
-
 template <int DH, int G>
 __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl) {
   constexpr int NJ = DH / 32;             // k32 steps of S^T = K Q^T

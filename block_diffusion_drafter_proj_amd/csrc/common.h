@@ -79,6 +79,21 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Stage ring of direct loads, NI per wave and stage: waits until at most
+// min(ahead, A) later stages of this wave are still in flight, then joins the
+// workgroup barrier.
+template <int NI, int A>
+__device__ __forceinline__ void wait_ring(int ahead) {
+  if constexpr (A <= 0) {
+    wait_barrier<0>();
+  } else {
+    if (ahead >= A)
+      wait_barrier<A * NI>();
+    else
+      wait_ring<NI, A - 1>(ahead);
+  }
+}
+
 // Sum over the 64 lanes of a wave (butterfly; every lane gets the result).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -183,13 +183,7 @@ void k_gemm_tile(GemmParams p) {
     if (s < nk) load_stage(ks0 + s, s);
 
   for (int it = 0; it < nk; ++it) {
-    const int ahead = min(nk - 1 - it, ST - 2);  // later stages allowed in flight
-    if (ahead >= 2)
-      wait_barrier<(ST >= 4 ? 2 * LPW : 0)>();
-    else if (ahead == 1)
-      wait_barrier<(ST >= 3 ? LPW : 0)>();
-    else
-      wait_barrier<0>();
+    wait_ring<LPW, ST - 2>(nk - 1 - it);  // later stages allowed in flight
     if (it + ST - 1 < nk) load_stage(ks0 + it + ST - 1, (it + ST - 1) % ST);
     const bf16* sb = lds + (it % ST) * FS * kFrag;
     // All of the stage's fragments are read before any product, in a fixed
@@ -311,7 +305,8 @@ void launch_cfg(const GemmParams& p, hipStream_t s) {
 }
 
 // Above 128 rows: 256x256 tiles, 8 waves of 128x64 (two per SIMD), one
-// 32-wide k step per stage and a 4-stage ring (128 KB of LDS).  Operand bytes
+// 32-wide k step per stage and a 5-stage ring (all 160 KB of LDS; three
+// stages in flight while one is multiplied).  Operand bytes
 // per flop set the speed here: the direct loads are bounded by the requests a
 // CU keeps in flight, and this tile needs 0.68x the bytes per flop of 256x128.
 // Up to 128 rows (and for top-16, whose sort needs the registers): 128x128
@@ -326,7 +321,7 @@ void launch_cfg(const GemmParams& p, hipStream_t s) {
 // across N keep the top-16 list count per row equal to CfgSmall's.
 typedef TileCfg<64, 128, 2, 2, 2, 3> Cfg64;
 typedef TileCfg<128, 128, 2, 2, 2, 3> CfgSmall;
-typedef TileCfg<256, 256, 2, 4, 1, 4> CfgBig;
+typedef TileCfg<256, 256, 2, 4, 1, 5> CfgBig;
 typedef TileCfg<256, 192, 4, 2, 2, 2> CfgWide;
 static_assert(Cfg64::WN == CfgSmall::WN && Cfg64::BN == CfgSmall::BN, "top-16 lists per row");
 
