@@ -51,10 +51,27 @@ __global__ __launch_bounds__(1024) void k_qkv_post(QkvPostParams p, SlotArgs sl)
   const int n = p.state[sl.slots[r]].ctx_len + 1;
   const float* src = p.qkv + (long long)r * p.B * ld + hh * DH;
   const long long plane = (long long)gridDim.x * p.B * ld;
-  auto rd = [&](long long off) {
-    float x = 0.f;
-    for (int q = 0; q < p.n_part; ++q) x += src[q * plane + off];
-    return x;
+  // sums of the split-K partials at two offsets; every load of a chunk of 4
+  // partials is issued before any is added (same order of addition)
+  auto rd2 = [&](long long off1, long long off2, float& x1, float& x2) {
+    x1 = 0.f;
+    x2 = 0.f;
+    for (int q0 = 0; q0 < p.n_part; q0 += 4) {
+      float a[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool ok = q0 + q < p.n_part;
+        a[q] = ok ? src[(q0 + q) * plane + off1] : 0.f;
+        b[q] = ok ? src[(q0 + q) * plane + off2] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q0 + q < p.n_part) {
+          x1 += a[q];
+          x2 += b[q];
+        }
+      }
+    }
   };
   constexpr int H2 = DH / 2;
   const long long page_elems = 2LL * p.Hkv * 16 * DH;
@@ -69,8 +86,8 @@ __global__ __launch_bounds__(1024) void k_qkv_post(QkvPostParams p, SlotArgs sl)
       const int j = e - i * H2;
       float y1 = 0.f, y2 = 0.f;
       if (i < p.B) {
-        const float x1 = rd((long long)i * ld + j);
-        const float x2 = rd((long long)i * ld + j + H2);
+        float x1, x2;
+        rd2((long long)i * ld + j, (long long)i * ld + j + H2, x1, x2);
         const long long ti = (long long)(n + i) * H2 + j;
         const float c = p.cos_t[ti], s = p.sin_t[ti];
         y1 = x1 * c - x2 * s;
@@ -85,7 +102,8 @@ __global__ __launch_bounds__(1024) void k_qkv_post(QkvPostParams p, SlotArgs sl)
     for (int e = t; e < 16 * DH; e += blockDim.x) {
       const int i = e & 15;
       const int d = e >> 4;
-      const float x = i < p.B ? rd((long long)i * ld + d) : 0.f;
+      float x = 0.f, unused;
+      if (i < p.B) rd2((long long)i * ld + d, (long long)i * ld + d, x, unused);
       dst[d * 16 + i] = from_f<T>(x);
     }
   }
@@ -611,8 +629,16 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p) {
   if (ns <= 1) return;  // written by the attention kernel
   const long long pb = (long long)rh * S * 16 + q;
   const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + pb;
-  // lane s holds split s's (max, sum); weights are broadcast by shuffles
+  const float* po = p.part_o + pb * DH + lane * C;
+  // lane s holds split s's (max, sum); weights are broadcast by shuffles.  The
+  // first 16 partial rows are requested together with the (max, sum) pairs,
+  // so the merge waits for one memory round trip, not two.
   const float2 mine = lane < ns ? ml[lane * 16] : make_float2(-INFINITY, 0.f);
+  float v[16][C];
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+#pragma unroll
+    for (int c = 0; c < C; ++c) v[k][c] = k < ns ? po[(long long)k * 16 * DH + c] : 0.f;
   float mx = mine.x;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
@@ -622,13 +648,13 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p) {
   float acc[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) acc[c] = 0.f;
-  const float* po = p.part_o + pb * DH + lane * C;
   for (int s0 = 0; s0 < ns; s0 += 16) {
-    float v[16][C];
+    if (s0 > 0) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+      for (int k = 0; k < 16; ++k)
 #pragma unroll
-      for (int c = 0; c < C; ++c) v[k][c] = s0 + k < ns ? po[(long long)(s0 + k) * 16 * DH + c] : 0.f;
+        for (int c = 0; c < C; ++c) v[k][c] = s0 + k < ns ? po[(long long)(s0 + k) * 16 * DH + c] : 0.f;
+    }
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const float w = __shfl(w_mine, (s0 + k) & 63, 64);
@@ -653,8 +679,15 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterParams p) {
     const InjectReq q = p.req[t];
     p.state[q.slot].ctx_len = q.pos0 + q.count;
   }
-  int ri = 0;
-  while (ri + 1 < p.n_req && row >= p.req[ri + 1].row_start) ++ri;
+  // the request owning this row: binary search over the row starts
+  int ri = 0, rhi = p.n_req - 1;
+  while (ri < rhi) {
+    const int mid = (ri + rhi + 1) >> 1;
+    if (row >= p.req[mid].row_start)
+      ri = mid;
+    else
+      rhi = mid - 1;
+  }
   const InjectReq rq = p.req[ri];
   const int pos = rq.pos0 + (row - rq.row_start);
   if (p.window > 0 && pos < rq.final_ctx - p.window) return;
@@ -670,17 +703,34 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterParams p) {
   T* pg = reinterpret_cast<T*>(p.pool) + l * p.layer_stride + page * page_elems;
   const float* src = p.kv + (long long)row * (p.L * 2 * p.Hkv * DH) + (long long)l * 2 * p.Hkv * DH;
   const long long plane = (long long)p.rows * p.L * 2 * p.Hkv * DH;
-  auto rd = [&](int off) {
-    float x = 0.f;
-    for (int q = 0; q < p.n_part; ++q) x += src[q * plane + off];
-    return x;
+  // sums of the split-K partials at two offsets; every load of a chunk of 4
+  // partials is issued before any is added (same order of addition)
+  auto rd2 = [&](int off1, int off2, float& x1, float& x2) {
+    x1 = 0.f;
+    x2 = 0.f;
+    for (int q0 = 0; q0 < p.n_part; q0 += 4) {
+      float a[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool ok = q0 + q < p.n_part;
+        a[q] = ok ? src[(q0 + q) * plane + off1] : 0.f;
+        b[q] = ok ? src[(q0 + q) * plane + off2] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q0 + q < p.n_part) {
+          x1 += a[q];
+          x2 += b[q];
+        }
+      }
+    }
   };
   const int slotpos = pos & 15;
   for (int e = t; e < p.Hkv * H2; e += 256) {
     const int g = e / H2;
     const int j = e - g * H2;
-    const float x1 = rd(g * DH + j);
-    const float x2 = rd(g * DH + j + H2);
+    float x1, x2;
+    rd2(g * DH + j, g * DH + j + H2, x1, x2);
     const long long ti = (long long)pos * H2 + j;
     const float c = p.cos_t[ti], s = p.sin_t[ti];
     T* kd = pg + (long long)(g * 16 + slotpos) * DH;
@@ -690,7 +740,9 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterParams p) {
   for (int e = t; e < p.Hkv * DH; e += 256) {
     const int g = e / DH;
     const int d = e - g * DH;
-    pg[(long long)(p.Hkv + g) * 16 * DH + d * 16 + slotpos] = from_f<T>(rd((p.Hkv + g) * DH + d));
+    float x, unused;
+    rd2((p.Hkv + g) * DH + d, (p.Hkv + g) * DH + d, x, unused);
+    pg[(long long)(p.Hkv + g) * 16 * DH + d * 16 + slotpos] = from_f<T>(x);
   }
 }
 

@@ -72,14 +72,29 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(NormParams p) {
   const bool first = p.conv && (row % p.B) == 0;
   f32x4 xp = f32x4{0.f, 0.f, 0.f, 0.f};
   if (p.conv && !first) xp = load_row4<T>(p, row - 1, k, plane);
+  // the row-independent operands are requested with the row: the reduction's
+  // barrier below would otherwise hold their loads back for a second round trip
+  f32x4 gm, cw0 = f32x4{0.f, 0.f, 0.f, 0.f}, cw1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    const T* gamma = reinterpret_cast<const T*>(p.gamma) + k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gm[i] = to_f(gamma[i]);
+    if (p.conv) {
+      const T* w0 = reinterpret_cast<const T*>(p.conv) + k;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        cw0[i] = to_f(w0[i]);
+        cw1[i] = to_f(w0[p.d + i]);
+      }
+    }
+  }
   if (p.x_out) *reinterpret_cast<f32x4*>(p.x_out + (long long)row * p.ldx + k) = x;
   if (p.dbg) *reinterpret_cast<f32x4*>(p.dbg + (long long)row * p.d + k) = x;
   const float tot = block_sum((x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3]), red, 0);
   const float r = 1.0f / sqrtf(tot / (float)p.d + p.eps);
-  const T* gamma = reinterpret_cast<const T*>(p.gamma) + k;
   f32x4 y;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) y[i] = x[i] * r * to_f(gamma[i]);
+  for (int i = 0; i < 4; ++i) y[i] = x[i] * r * gm[i];
   if (p.conv) {
     f32x4 prev;
     if (first) {
@@ -95,12 +110,10 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(NormParams p) {
       const float totp = block_sum((xp[0] * xp[0] + xp[1] * xp[1]) + (xp[2] * xp[2] + xp[3] * xp[3]), red, 1);
       const float rp = 1.0f / sqrtf(totp / (float)p.d + p.eps);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) prev[i] = xp[i] * rp * to_f(gamma[i]);
+      for (int i = 0; i < 4; ++i) prev[i] = xp[i] * rp * gm[i];
     }
-    const T* w0 = reinterpret_cast<const T*>(p.conv) + k;
-    const T* w1 = w0 + p.d;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = to_f(w0[i]) * y[i] + to_f(w1[i]) * prev[i];
+    for (int i = 0; i < 4; ++i) y[i] = cw0[i] * y[i] + cw1[i] * prev[i];
   }
   typename Out4<T>::type o;
 #pragma unroll
