@@ -65,7 +65,6 @@ __device__ __forceinline__ unsigned long long merge16(unsigned long long cur, un
   return t;
 }
 
-// Column tiles of the output grid: SwiGLU tiles cover BN/2 gate columns.
 // A tile configuration: BM x BN output tile, WM x WN waves (each holding a
 // BM/WM x BN/WN tile), KF 32-wide k steps per pipeline stage, ST stages.
 template <int BM_, int BN_, int WM_, int WN_, int KF_, int ST_>
@@ -138,17 +137,20 @@ void k_gemm_tile(GemmParams p) {
     const int row = min(m0 + (fa / KF) * 16 + r16, p.M - 1);
     a_off[i] = row * p.lda + (fa % KF) * 32 + 8 * g;
   }
-  const bf16* b_src[LB];  // fragment of k-stage 0
-#pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int fb = wv * LB + i;
-    int tt = wtile(fb / KF);
+  auto wsrc = [&](int jb) -> const bf16* {  // weight column block jb at k-stage 0
+    int tt = wtile(jb);
     int seg = 0;
     if (p.seg_tiles) {
       seg = tt / p.seg_tiles;
       tt -= seg * p.seg_tiles;
     }
-    b_src[i] = reinterpret_cast<const bf16*>(p.w[seg]) + ((long long)tt * S32 + (fb % KF)) * kFrag;
+    return reinterpret_cast<const bf16*>(p.w[seg]) + (long long)tt * S32 * kFrag;
+  };
+  const bf16* b_src[LB];  // fragment of k-stage 0
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int fb = wv * LB + i;
+    b_src[i] = wsrc(fb / KF) + (fb % KF) * kFrag;
   }
 
   // activation part of the next stage to load (stages are loaded in k order;
@@ -172,6 +174,7 @@ void k_gemm_tile(GemmParams p) {
       dma16(b_src[i] + (long long)kt * KF * kFrag + lane * 8, dst + (FA + wv * LB + i) * kFrag);
   };
 
+
   f32x4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -182,10 +185,10 @@ void k_gemm_tile(GemmParams p) {
   for (int s = 0; s < ST - 1; ++s)
     if (s < nk) load_stage(ks0 + s, s);
 
-  for (int it = 0; it < nk; ++it) {
-    wait_ring<LPW, ST - 2>(nk - 1 - it);  // later stages allowed in flight
-    if (it + ST - 1 < nk) load_stage(ks0 + it + ST - 1, (it + ST - 1) % ST);
-    const bf16* sb = lds + (it % ST) * FS * kFrag;
+  // Stage it sits in LDS buffer it % ST; the loops are unrolled by ST, so the
+  // buffer of each pass is a constant.
+  auto compute = [&](int u) {
+    const bf16* sb = lds + u * FS * kFrag;
     // All of the stage's fragments are read before any product, in a fixed
     // order (the scheduling barriers keep the compiler from sinking each read
     // next to its first use), so later reads complete under earlier MFMAs.
@@ -207,6 +210,29 @@ void k_gemm_tile(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma_step(af[k32][i], bfr[k32][j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto issue = [&](int it, int u) { load_stage(ks0 + it + ST - 1, (u + ST - 1) % ST); };
+  int it0 = 0;
+  // steady state: every pass waits for the full ring depth and starts a stage
+  for (; it0 + 2 * ST - 2 < nk; it0 += ST) {
+#pragma unroll
+    for (int u = 0; u < ST; ++u) {
+      wait_ring<LPW, ST - 2>(ST - 2);
+      issue(it0 + u, u);
+      compute(u);
+    }
+  }
+  // the last stages: fewer ahead
+  for (; it0 < nk; it0 += ST) {
+#pragma unroll
+    for (int u = 0; u < ST; ++u) {
+      const int it = it0 + u;
+      if (it < nk) {
+        wait_ring<LPW, ST - 2>(nk - 1 - it);
+        if (it + ST - 1 < nk) issue(it, u);
+        compute(u);
+      }
     }
   }
 
