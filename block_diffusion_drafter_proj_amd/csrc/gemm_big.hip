@@ -332,9 +332,11 @@ void launch_cfg(const GemmParams& p, hipStream_t s) {
 
 // Above 128 rows: 256x256 tiles, 8 waves of 128x64 (two per SIMD), one
 // 32-wide k step per stage and a 5-stage ring (all 160 KB of LDS; three
-// stages in flight while one is multiplied).  Operand bytes
-// per flop set the speed here: the direct loads are bounded by the requests a
-// CU keeps in flight, and this tile needs 0.68x the bytes per flop of 256x128.
+// stages in flight while one is multiplied).  Per stage a CU moves 96
+// fragment reads and 32 KB of direct loads through LDS against 1024 MFMA
+// cycles per SIMD, so operand bytes per flop set the speed; two waves per
+// SIMD keep the matrix cores busy across each stage's barrier, which one
+// larger wave per SIMD does not.
 // Up to 128 rows (and for top-16, whose sort needs the registers): 128x128
 // tiles, 4 waves of 64x64, two k steps per stage, 3 stages.
 // 256x192 tiles (8 waves of 64x96, 64-deep k stages, double buffered in
