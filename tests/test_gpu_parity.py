@@ -342,3 +342,35 @@ def test_window_ring_wraps_and_starts_late():
         assert dr.context_length(r) == states[r].ctx_len
     _check_kv(shape, dr, o, states, pages)
     _draft_both(dev, shape, dr, o, states, [0, 1])
+
+
+@pytest.mark.parametrize("name", ["small_batch", "small_dh64"])
+def test_request_alone_equals_request_in_a_pair(name):
+    """A request alone (16 rows) and the same request beside another (32 rows)
+    run the same skinny kernels: the GEMM split plan does not depend on the
+    row count, norms and attention work per row, and the attention splits
+    depend on the request's own context only.  So its logits, every layer's
+    hidden state and its drafts are identical bit for bit, call after call."""
+    dev, shape, w, dr, ctxs, pages = _setup(name, batch=2, ctx_range=(300, 700), ctx=None)
+    o = DraftOracle(shape, w)
+    states = [o.new_request() for _ in range(2)]
+    _inject_both(dev, shape, dr, o, states, [0, 1], [0, 0], ctxs)
+    B, V, d, L = shape["block_size"], shape["vocab"], shape["hidden"], shape["n_layers"]
+
+    def run(slots):
+        lg = torch.empty((len(slots), B, V), dtype=torch.float32, device=dev)
+        hd = torch.empty((L + 1, len(slots) * B, d), dtype=torch.float32, device=dev)
+        dd = dr.draft(slots, debug_logits=lg, debug_hidden=hd)
+        torch.cuda.synchronize()
+        return dd.cpu().numpy(), lg.cpu().numpy(), hd.cpu().numpy().reshape(L + 1, len(slots), B, d)
+
+    pair = run([0, 1])
+    for _ in range(3):
+        for i, r in enumerate([0, 1]):
+            alone = run([r])
+            assert np.array_equal(alone[0][0], pair[0][i]), r
+            assert np.array_equal(alone[1][0], pair[1][i]), r
+            assert np.array_equal(alone[2][:, 0], pair[2][:, i]), r
+    logits = o.draft_block(states[0])
+    assert_rows_close(pair[1][0], logits, what="request 0 vs oracle")
+    dr.check()
