@@ -20,7 +20,8 @@
 //
 // Epilogues: split-K partials (fp32, summed by the consuming kernel); residual
 // add; SwiGLU (gate and up tiles processed back to back, silu(gate) * up
-// rounded to the storage dtype); greedy selection (packed logit/id key,
+// rounded to the storage dtype); RoPE (the two halves of a head processed back
+// to back, rotated and written in the attention layouts); greedy selection (packed logit/id key,
 // running max per row across the workgroup's tiles, one 64-bit atomic max per
 // row and workgroup, ties to the lowest id); top-16 (the same keys, a sorted
 // list of 16 per row kept across the row's 16 lanes by bitonic sort and merge,
@@ -80,9 +81,12 @@ template <typename T, int MT, int EPI, bool FEW>
 __global__ __launch_bounds__(FEW ? 256 : 1024) void k_gemm(GemmParams p) {
   constexpr int KS = Shape<T, MT>::KS;
   constexpr int NBUF = Shape<T, MT>::NBUF;
-  constexpr int NSUB = (EPI == EPI_SWIGLU) ? 2 : 1;
+  constexpr int NSUB = (EPI == EPI_SWIGLU || EPI == EPI_ROPE) ? 2 : 1;
   typedef typename Frag8<T>::type Frag;
   __shared__ float red[2][16][MT][256];
+  // EPI_ROPE: tiles per head and the tile distance of a rotate-half pair
+  const int rope_tph = EPI == EPI_ROPE ? p.rope.dh / 16 : 0;
+  const int rope_half = rope_tph / 2;
 
   const int NW = blockDim.x >> 6;
   const int lane = lane_id();
@@ -114,10 +118,16 @@ __global__ __launch_bounds__(FEW ? 256 : 1024) void k_gemm(GemmParams p) {
     }
   }
 
-  auto wsrc = [&](int sub) -> const T* {
+  // weight tile of sub-unit `sub` of this workgroup
+  auto tile_of = [&](int sub) {
     const int u = sub / NSUB;
     int t = bl + u * GP;
     if (EPI == EPI_SWIGLU && (sub & 1)) t += p.up_tile_off;
+    if (EPI == EPI_ROPE) t = (t / rope_half) * rope_tph + t % rope_half + (sub & 1) * rope_half;
+    return t;
+  };
+  auto wsrc = [&](int sub) -> const T* {
+    int t = tile_of(sub);
     int seg = 0, lt = t;
     if (p.seg_tiles) {
       seg = t / p.seg_tiles;
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(FEW ? 256 : 1024) void k_gemm(GemmParams p) {
           float v = 0.f;
           for (int w2 = 0; w2 < NW; ++w2) v += red[rb][w2][emt][e & 255];
           const int u = sub / NSUB;
-          const int tile = bl + u * GP;
+          const int tile = EPI == EPI_ROPE ? tile_of(sub) : bl + u * GP;
           const int n = tile * 16 + ecol;
           const bool ok = em < p.M && n < p.N;
           if (EPI == EPI_PARTIAL) {
@@ -197,6 +207,32 @@ __global__ __launch_bounds__(FEW ? 256 : 1024) void k_gemm(GemmParams p) {
               const float g0 = gate_v[it];
               const float sg = g0 / (1.0f + expf(-g0));
               reinterpret_cast<T*>(p.out_t)[(long long)em * p.ldt + n] = from_f<T>(sg * v);
+            }
+          } else if (EPI == EPI_ROPE) {
+            if (!(sub & 1)) {
+              gate_v[it] = v;  // column j of the head; v below is column j + dh/2
+            } else if (ok) {
+              const RopeOut& ro = p.rope;
+              const int dh = ro.dh, h2 = dh >> 1;
+              const int head = (n - h2) / dh;
+              const int j = n - h2 - head * dh;
+              const int r = em / ro.B, i = em - r * ro.B;
+              const float x1 = gate_v[it];
+              T* o;
+              if (head < ro.Hq + ro.Hkv) {
+                const long long ti = (long long)(ro.state[ro.slots[r]].ctx_len + 1 + i) * h2 + j;
+                const float c = ro.cos_t[ti], sn = ro.sin_t[ti];
+                if (head < ro.Hq)
+                  o = reinterpret_cast<T*>(ro.qb) + ((long long)(r * ro.Hq + head) * 16 + i) * dh;
+                else
+                  o = reinterpret_cast<T*>(ro.blk) + ((long long)(r * 2 + 0) * ro.Hkv + head - ro.Hq) * 16 * dh + i * dh;
+                o[j] = from_f<T>(x1 * c - v * sn);
+                o[j + h2] = from_f<T>(v * c + x1 * sn);
+              } else {
+                o = reinterpret_cast<T*>(ro.blk) + ((long long)(r * 2 + 1) * ro.Hkv + head - ro.Hq - ro.Hkv) * 16 * dh;
+                o[j * 16 + i] = from_f<T>(x1);
+                o[(j + h2) * 16 + i] = from_f<T>(v);
+              }
             }
           } else if (EPI == EPI_ARGMAX) {  // all 16 columns of a row sit in 16 adjacent lanes
             if (ok && p.dbg) p.dbg[(long long)em * p.ld_dbg + n] = v;
@@ -269,6 +305,7 @@ void launch_dt(int epi, const GemmPlan& pl, const GemmParams& p, hipStream_t s) 
     case EPI_PARTIAL: launch_t<T, EPI_PARTIAL>(pl, p, s); break;
     case EPI_RESID: launch_t<T, EPI_RESID>(pl, p, s); break;
     case EPI_SWIGLU: launch_t<T, EPI_SWIGLU>(pl, p, s); break;
+    case EPI_ROPE: launch_t<T, EPI_ROPE>(pl, p, s); break;
     case EPI_TOPK: launch_t<T, EPI_TOPK>(pl, p, s); break;
     default: launch_t<T, EPI_ARGMAX>(pl, p, s); break;
   }

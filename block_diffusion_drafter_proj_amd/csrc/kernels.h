@@ -11,7 +11,29 @@ namespace dflash {
 constexpr int kMaxSeg = DFLASH_MAX_LAYERS;
 constexpr int kMaxChunkReq = 64;  // requests per inject scatter launch
 
-enum Epilogue { EPI_PARTIAL = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3, EPI_TOPK = 4 };
+enum Epilogue { EPI_PARTIAL = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3, EPI_TOPK = 4, EPI_ROPE = 5 };
+
+constexpr int kMaxRopeReq = 64;  // requests of one EPI_ROPE launch (skinny sizes: under 64 rows)
+
+struct SlotState;
+
+// EPI_ROPE: the QKV product of the block rows written straight into the
+// attention layouts.  Units are pairs of 16-column tiles half a head apart
+// (columns j and j + dh/2 of one head), so one thread holds both halves of a
+// rotate-half pair: q and k heads are rotated at the block positions
+// n .. n+B-1 (n = ctx_len + 1 of the row's request), q goes to
+// qb [r][head][16][dh], k to the request's block page [head][16][dh] and v to
+// it transposed [head][dh][16].  Rows B..15 of each 16-row tile are never
+// written (zero from the handle's set-up).
+struct RopeOut {
+  const SlotState* state;
+  const float* cos_t;  // [max_position, dh/2]
+  const float* sin_t;
+  void* qb;
+  void* blk;
+  int B, Hq, Hkv, dh;
+  int slots[kMaxRopeReq];
+};
 
 // Y[M, N] = X[M, K] * W[N, K]^T with a fused epilogue, W packed by launch_pack.
 //  X: virtual concatenation along k of a_parts row-major arrays, each
@@ -36,6 +58,7 @@ struct GemmParams {
   unsigned long long* keys;  // EPI_ARGMAX: one per row; EPI_TOPK: [M][gridDim.x][16] sorted lists
   float* dbg;                // EPI_ARGMAX / EPI_TOPK, optional fp32 logits
   int ld_dbg;
+  RopeOut rope;              // EPI_ROPE (tiles counts column-tile pairs)
 };
 
 struct GemmPlan {

@@ -74,6 +74,12 @@ struct Plans {
 
 int tiles_of(int n) { return (n + 15) / 16; }
 
+// The skinny QKV product writes q and the block K/V itself (RoPE epilogue,
+// no split-K); the tiled one writes split-K partials for k_qkv_post.
+bool qkv_rope(const dflash_config& c, int M) {
+  return !gemm_use_big(c.dtype, M) && (M + c.block_size - 1) / c.block_size <= kMaxRopeReq;
+}
+
 Plans make_plans(const dflash_config& c, int M) {
   const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
@@ -92,7 +98,7 @@ Plans make_plans(const dflash_config& c, int M) {
   }
   const int kb = gemm_kblock(c.dtype, M);
   Plans p;
-  p.qkv = plan_gemm(tiles_of(qkvw), d, kb, false);
+  p.qkv = qkv_rope(c, M) ? plan_gemm(tiles_of(qkvw) / 2, d, kb, true) : plan_gemm(tiles_of(qkvw), d, kb, false);
   p.o = plan_gemm(tiles_of(d), qd, kb, false);
   p.gateup = plan_gemm(tiles_of(c.ffn), d, kb, true);
   p.down = plan_gemm(tiles_of(d), c.ffn, kb, false);
@@ -282,6 +288,11 @@ dflash_status ensure_device(dflash_handle* h) {
   if ((e = hipMemset(h->ws + h->lay.state, 0, sizeof(SlotState) * c.max_batch)))
     return hip_fail(e, "state init");
   if ((e = hipMemset(h->ws + h->lay.err, 0, 16))) return hip_fail(e, "state init");
+  // rows B..15 of the block's q / K / V tiles stay zero (the RoPE epilogue
+  // writes rows 0..B-1 only)
+  if ((e = hipMemset(h->ws + h->lay.qb, 0, h->lay.blk - h->lay.qb))) return hip_fail(e, "state init");
+  if ((e = hipMemset(h->ws + h->lay.blk, 0, elt(c) * (size_t)c.max_batch * 2 * c.n_kv_heads * 16 * c.head_dim)))
+    return hip_fail(e, "state init");
   if ((e = hipMemset(h->ws + h->lay.page_table, 0xff,
                      sizeof(int32_t) * c.max_batch * (size_t)c.max_pages_per_req)))
     return hip_fail(e, "page table init");
@@ -647,6 +658,21 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     splits = std::max(splits, (u + pps - 1) / pps);
   }
 
+  const bool rope = qkv_rope(c, M);
+  RopeOut rope_out{};
+  if (rope) {
+    rope_out.state = at<SlotState>(h, h->lay.state);
+    rope_out.cos_t = at<float>(h, h->lay.cos_t);
+    rope_out.sin_t = at<float>(h, h->lay.sin_t);
+    rope_out.qb = h->ws + h->lay.qb;
+    rope_out.blk = h->ws + h->lay.blk;
+    rope_out.B = B;
+    rope_out.Hq = c.n_q_heads;
+    rope_out.Hkv = c.n_kv_heads;
+    rope_out.dh = c.head_dim;
+    for (int i = 0; i < n_req; ++i) rope_out.slots[i] = slots[i];
+  }
+
   float* hbuf = at<float>(h, h->lay.h);
   float* dpart = at<float>(h, h->lay.dpart);
   float* opart = at<float>(h, h->lay.opart);
@@ -722,11 +748,19 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
 
     GemmParams g = gemm_in(h->ws + h->lay.xa, d);
     g.w[0] = h->packed + h->pk.wqkv[l];
-    g.tiles = tiles_of(qkvw);
     g.N = qkvw;
     g.P = pl.qkv.P;
-    g.out_f32 = at<float>(h, h->lay.qkv);
-    { ProfScope ps(h, DFLASH_KERNEL_QKV_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.qkv, g, s); }
+    if (rope) {
+      g.tiles = tiles_of(qkvw) / 2;
+      g.rope = rope_out;
+      ProfScope ps(h, DFLASH_KERNEL_QKV_GEMM, s);
+      launch_gemm(c.dtype, EPI_ROPE, pl.qkv, g, s);
+    } else {
+      g.tiles = tiles_of(qkvw);
+      g.out_f32 = at<float>(h, h->lay.qkv);
+      ProfScope ps(h, DFLASH_KERNEL_QKV_GEMM, s);
+      launch_gemm(c.dtype, EPI_PARTIAL, pl.qkv, g, s);
+    }
 
     QkvPostParams qp{};
     qp.qkv = at<float>(h, h->lay.qkv);
@@ -739,7 +773,10 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     qp.sin_t = at<float>(h, h->lay.sin_t);
     qp.qb = h->ws + h->lay.qb;
     qp.blk = h->ws + h->lay.blk;
-    { ProfScope ps(h, DFLASH_KERNEL_QKV_POST, s); launch_qkv_post(c.dtype, c.head_dim, n_req, qp, sl, s); }
+    if (!rope) {
+      ProfScope ps(h, DFLASH_KERNEL_QKV_POST, s);
+      launch_qkv_post(c.dtype, c.head_dim, n_req, qp, sl, s);
+    }
 
     AttnParams ap{};
     ap.qb = h->ws + h->lay.qb;
