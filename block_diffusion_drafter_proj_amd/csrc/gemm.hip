@@ -77,13 +77,15 @@ struct Shape {
   static constexpr int NBUF = (sizeof(T) == 2 ? 16 : 8) / KS;     // tiles in the W ring
 };
 
+// Workgroups of MT > 1 have at most 8 waves (their activation and weight
+// registers need two waves per SIMD at most).
 template <typename T, int MT, int EPI, bool FEW>
-__global__ __launch_bounds__(FEW ? 256 : 1024) void k_gemm(GemmParams p) {
+__global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(GemmParams p) {
   constexpr int KS = Shape<T, MT>::KS;
   constexpr int NBUF = Shape<T, MT>::NBUF;
   constexpr int NSUB = (EPI == EPI_SWIGLU || EPI == EPI_ROPE) ? 2 : 1;
   typedef typename Frag8<T>::type Frag;
-  __shared__ float red[2][16][MT][256];
+  __shared__ float red[2][MT > 1 ? 8 : 16][MT][256];
   // EPI_ROPE: tiles per head and the tile distance of a rotate-half pair
   const int rope_tph = EPI == EPI_ROPE ? p.rope.dh / 16 : 0;
   const int rope_half = rope_tph / 2;
@@ -290,7 +292,17 @@ __global__ __launch_bounds__(256) void k_pack(const T* src, T* dst, int N, int K
 
 template <typename T, int EPI>
 void launch_t(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
-  // 16-row m-blocks; rows beyond 16 re-stream W (a batched kernel would not)
+  if constexpr (sizeof(T) == 2 && EPI == EPI_PARTIAL) {
+    if (pl.mt == 4) {  // one block of up to 64 rows: W streamed once
+      const dim3 grid(pl.GP * p.P, (p.M + 63) / 64);
+      if (pl.NW < 4)
+        hipLaunchKernelGGL((k_gemm<T, 4, EPI, true>), grid, dim3(64 * pl.NW), 0, s, p);
+      else
+        hipLaunchKernelGGL((k_gemm<T, 4, EPI, false>), grid, dim3(64 * pl.NW), 0, s, p);
+      return;
+    }
+  }
+  // 16-row m-blocks; rows beyond 16 re-stream W
   dim3 grid(pl.GP * p.P, (p.M + 15) / 16);
   dim3 block(64 * pl.NW);
   if (pl.NW < 4)
@@ -313,8 +325,8 @@ void launch_dt(int epi, const GemmPlan& pl, const GemmParams& p, hipStream_t s) 
 
 }  // namespace
 
-int gemm_kblock(int dtype, int M) {
-  (void)M;
+int gemm_kblock(int dtype, int mt) {
+  if (mt == 4) return 32 * Shape<bf16, 4>::KS;
   return 32 * (dtype == DFLASH_BF16 ? Shape<bf16, 1>::KS : Shape<float, 1>::KS);
 }
 
@@ -322,14 +334,14 @@ int gemm_kblock(int dtype, int M) {
 // GEMM of `tiles` 16-row output tiles over K.  Minimises the per-workgroup
 // stream (units per workgroup x K / P) with at most 256 workgroups (one per
 // CU), penalising fewer than 8 waves per workgroup.
-GemmPlan plan_gemm(int tiles, int K, int kblock, bool single_split) {
-  GemmPlan best{0, 0, 0};
+GemmPlan plan_gemm(int tiles, int K, int kblock, bool single_split, int max_nw) {
+  GemmPlan best{0, 0, 0, 1};
   double best_cost = 1e300;
   const int kb = K / kblock;
   for (int P = 1; P <= kb; ++P) {
     if (kb % P) continue;
     const int NW = kb / P;
-    if (NW > 16) continue;
+    if (NW > max_nw) continue;
     if (single_split && P != 1) break;
     const int gp_max = 256 / P;
     if (gp_max < 1) break;
@@ -339,7 +351,7 @@ GemmPlan plan_gemm(int tiles, int K, int kblock, bool single_split) {
     const double cost = (double)units * K / P / eff;
     if (cost < best_cost * 0.999) {
       best_cost = cost;
-      best = GemmPlan{P, NW, GP};
+      best = GemmPlan{P, NW, GP, 1};
     }
   }
   return best;
@@ -347,7 +359,7 @@ GemmPlan plan_gemm(int tiles, int K, int kblock, bool single_split) {
 
 void launch_gemm(int dtype, int epi, const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
   if (p.M <= 0 || p.tiles <= 0) return;
-  if (gemm_use_big(dtype, p.M)) {
+  if (pl.mt == 0) {
     launch_gemm_big(epi, p, s);
     return;
   }

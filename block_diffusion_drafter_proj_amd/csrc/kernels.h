@@ -63,6 +63,9 @@ struct GemmParams {
 
 struct GemmPlan {
   int P, NW, GP;  // split-K factor, waves per workgroup, workgroups per split
+  // kernel: 0 = tiled (gemm_big.hip); 1 = skinny, one 16-row block per grid
+  // row; 4 = skinny, up to 64 rows in one block (split-K products only)
+  int mt;
 };
 
 // Row-wise RMSNorm of fp32 rows into the storage dtype.  The input row is
@@ -186,14 +189,17 @@ struct ScatterParams {
   unsigned int* err;
 };
 
-int gemm_kblock(int dtype, int M);
+// k per wave and weight tile of the skinny kernel with mt 16-row tiles
+int gemm_kblock(int dtype, int mt);
+// The skinny kernel holds up to 64 rows at once for split-K (partial) products.
+inline bool gemm_use_mt4(int dtype, int M) { return dtype == DFLASH_BF16 && M > 16 && M <= 64; }
 // Tiled MFMA kernel for M >= 64 (bf16): one split, lists of top-16 per row
 // for `tiles` 16-row weight tiles.
 inline bool gemm_use_big(int dtype, int M) { return dtype == DFLASH_BF16 && M >= 64; }
 int gemm_big_lists(int tiles);
 int gemm_big_split(int M, int tiles, int K);
 void launch_gemm_big(int epi, const GemmParams& p, hipStream_t s);
-GemmPlan plan_gemm(int tiles, int K, int kblock, bool single_split);
+GemmPlan plan_gemm(int tiles, int K, int kblock, bool single_split, int max_nw = 16);
 void launch_gemm(int dtype, int epi, const GemmPlan& pl, const GemmParams& p, hipStream_t s);
 size_t packed_elems(int N, int K);
 void launch_pack(int dtype, const void* src, void* dst, int N, int K, hipStream_t s);

@@ -77,15 +77,42 @@ int tiles_of(int n) { return (n + 15) / 16; }
 // The skinny QKV product writes q and the block K/V itself (RoPE epilogue,
 // no split-K); the tiled one writes split-K partials for k_qkv_post.
 bool qkv_rope(const dflash_config& c, int M) {
-  return !gemm_use_big(c.dtype, M) && (M + c.block_size - 1) / c.block_size <= kMaxRopeReq;
+  return !gemm_use_big(c.dtype, M) && !gemm_use_mt4(c.dtype, M) &&
+         (M + c.block_size - 1) / c.block_size <= kMaxRopeReq;
 }
 
 Plans make_plans(const dflash_config& c, int M) {
   const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  // 17..64 rows: the split-K products stream their weights once for all
+  // rows (skinny kernel, 64-row block); the others keep their kernel below.
+  // At exactly 64 rows the tiled kernel (split-K 8 and 12) streams the O and
+  // down weights faster than the 64-row block (measured 13 vs 15.5 us per O
+  // launch at 33.6 MB), and the QKV and injection products slower.
+  if (gemm_use_mt4(c.dtype, M)) {
+    const int kb4 = gemm_kblock(c.dtype, 4);
+    auto mt4 = [&](int tiles, int K) {
+      GemmPlan g = plan_gemm(tiles, K, kb4, false, 8);
+      g.mt = 4;
+      return g;
+    };
+    const int kb = gemm_kblock(c.dtype, 1);
+    const GemmPlan one{1, 4, 1, 0};
+    Plans p;
+    p.qkv = mt4(tiles_of(qkvw), d);
+    const bool tiled_ok = gemm_use_big(c.dtype, M);
+    auto tiled = [&](int tiles, int K) { return GemmPlan{gemm_big_split(M, tiles, K), 4, 1, 0}; };
+    p.o = tiled_ok ? tiled(tiles_of(d), qd) : mt4(tiles_of(d), qd);
+    p.gateup = gemm_use_big(c.dtype, M) ? one : plan_gemm(tiles_of(c.ffn), d, kb, true);
+    p.down = tiled_ok ? tiled(tiles_of(d), c.ffn) : mt4(tiles_of(d), c.ffn);
+    p.lm = gemm_use_big(c.dtype, M) ? one : plan_gemm(tiles_of(c.vocab), d, kb, true);
+    p.fc = mt4(tiles_of(d), c.n_feat * d);
+    p.kv = mt4(c.n_layers * tiles_of(2 * c.n_kv_heads * c.head_dim), d);
+    return p;
+  }
   if (gemm_use_big(c.dtype, M)) {  // tiled kernel: split-K only for partial outputs
-    auto tiled = [&](int tiles, int K) { return GemmPlan{gemm_big_split(M, tiles, K), 4, 1}; };
-    const GemmPlan one{1, 4, 1};
+    auto tiled = [&](int tiles, int K) { return GemmPlan{gemm_big_split(M, tiles, K), 4, 1, 0}; };
+    const GemmPlan one{1, 4, 1, 0};
     Plans p;
     p.qkv = tiled(tiles_of(qkvw), d);
     p.o = tiled(tiles_of(d), qd);
@@ -96,7 +123,7 @@ Plans make_plans(const dflash_config& c, int M) {
     p.kv = tiled(c.n_layers * tiles_of(2 * c.n_kv_heads * c.head_dim), d);
     return p;
   }
-  const int kb = gemm_kblock(c.dtype, M);
+  const int kb = gemm_kblock(c.dtype, 1);
   Plans p;
   p.qkv = qkv_rope(c, M) ? plan_gemm(tiles_of(qkvw) / 2, d, kb, true) : plan_gemm(tiles_of(qkvw), d, kb, false);
   p.o = plan_gemm(tiles_of(d), qd, kb, false);
@@ -902,7 +929,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   if (c.topk) {
     TopkParams tp{};
     tp.lists = gl.keys;
-    tp.n_lists = gemm_use_big(c.dtype, M) ? gemm_big_lists(gl.tiles) : pl.lm.GP;
+    tp.n_lists = pl.lm.mt == 0 ? gemm_big_lists(gl.tiles) : pl.lm.GP;
     tp.M = M;
     tp.vocab = c.vocab;
     tp.draft = draft;
