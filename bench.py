@@ -126,8 +126,8 @@ def kernel_sources(shape, cls, M):
     """Source files whose kernels a class launches at this row count."""
     if cls in GEMM_CLASSES:
         big = shape["dtype"] == "bf16" and M >= 64
-        if cls == "qkv_gemm" and M == 64:
-            big = False  # the QKV product of 64 rows runs on the skinny kernel's 64-row block
+        if cls in ("qkv_gemm", "lm_head") and M == 64:
+            big = False  # these products of 64 rows run on the skinny kernel's 64-row block
         return [os.path.join(CSRC, "gemm_big.hip" if big else "gemm.hip")]
     if cls == "attn":
         return [os.path.join(CSRC, "attention.hip")]

@@ -116,4 +116,41 @@ __device__ __forceinline__ uint64_t argmax_key(float logit, int id, int vocab) {
   return ((uint64_t)float_key(logit) << 32) | (uint32_t)(vocab - 1 - id);
 }
 
+__device__ __forceinline__ unsigned long long key_max(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+__device__ __forceinline__ unsigned long long key_min(unsigned long long a, unsigned long long b) {
+  return a < b ? a : b;
+}
+
+// 16 adjacent lanes hold one key each (lane i of the group: index i); sort
+// them descending (bitonic network over the group).
+__device__ __forceinline__ unsigned long long sort16_desc(unsigned long long v, int i) {
+#pragma unroll
+  for (int k = 2; k <= 16; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const unsigned long long o = __shfl_xor(v, j, 64);
+      const bool desc = (i & k) == 0;
+      const bool lower = (i & j) == 0;
+      v = (lower == desc) ? key_max(v, o) : key_min(v, o);
+    }
+  }
+  return v;
+}
+
+// cur and nw are sorted descending over the same 16 lanes; returns the 16
+// largest of both, sorted descending (lane i holds rank i).
+__device__ __forceinline__ unsigned long long merge16_desc(unsigned long long cur, unsigned long long nw,
+                                                           int i) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long t = key_max(cur, __shfl(nw, (lane & 48) | (15 - i), 64));
+#pragma unroll
+  for (int j = 8; j > 0; j >>= 1) {
+    const unsigned long long o = __shfl_xor(t, j, 64);
+    t = ((i & j) == 0) ? key_max(t, o) : key_min(t, o);
+  }
+  return t;
+}
+
 }  // namespace dflash

@@ -35,42 +35,6 @@ namespace {
 
 constexpr int kFragElems = 64 * 8;  // elements of one wave fragment
 
-__device__ __forceinline__ unsigned long long kmax(unsigned long long a, unsigned long long b) {
-  return a > b ? a : b;
-}
-__device__ __forceinline__ unsigned long long kmin(unsigned long long a, unsigned long long b) {
-  return a < b ? a : b;
-}
-
-// 16 adjacent lanes hold one key each; sort them descending (bitonic).
-__device__ __forceinline__ unsigned long long sort16_desc(unsigned long long v, int i) {
-#pragma unroll
-  for (int k = 2; k <= 16; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const unsigned long long o = __shfl_xor(v, j, 64);
-      const bool desc = (i & k) == 0;
-      const bool lower = (i & j) == 0;
-      v = (lower == desc) ? kmax(v, o) : kmin(v, o);
-    }
-  }
-  return v;
-}
-
-// cur and nw are sorted descending over the 16 lanes; returns the 16 largest
-// of both, sorted descending (lane i holds rank i).
-__device__ __forceinline__ unsigned long long merge16_desc(unsigned long long cur,
-                                                           unsigned long long nw, int i) {
-  const int lane = threadIdx.x & 63;
-  unsigned long long t = kmax(cur, __shfl(nw, (lane & 48) | (15 - i), 64));
-#pragma unroll
-  for (int j = 8; j > 0; j >>= 1) {
-    const unsigned long long o = __shfl_xor(t, j, 64);
-    t = ((i & j) == 0) ? kmax(t, o) : kmin(t, o);
-  }
-  return t;
-}
-
 template <typename T, int MT>
 struct Shape {
   static constexpr int KS = (sizeof(T) == 2 && MT == 1) ? 8 : 4;  // k-steps per wave per tile

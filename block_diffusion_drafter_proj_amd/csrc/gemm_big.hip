@@ -35,36 +35,6 @@ namespace {
 
 constexpr int kFrag = 64 * 8;  // bf16 elements of one fragment
 
-__device__ __forceinline__ unsigned long long kmax2(unsigned long long a, unsigned long long b) {
-  return a > b ? a : b;
-}
-__device__ __forceinline__ unsigned long long kmin2(unsigned long long a, unsigned long long b) {
-  return a < b ? a : b;
-}
-// bitonic sort of 16 keys held one per lane of a 16-lane group, descending
-__device__ __forceinline__ unsigned long long sort16(unsigned long long v, int i) {
-#pragma unroll
-  for (int k = 2; k <= 16; k <<= 1)
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const unsigned long long o = __shfl_xor(v, j, 64);
-      v = (((i & j) == 0) == ((i & k) == 0)) ? kmax2(v, o) : kmin2(v, o);
-    }
-  return v;
-}
-// the 16 largest of two descending 16-lists, descending
-__device__ __forceinline__ unsigned long long merge16(unsigned long long cur, unsigned long long nw,
-                                                      int i) {
-  const int lane = threadIdx.x & 63;
-  unsigned long long t = kmax2(cur, __shfl(nw, (lane & 48) | (15 - i), 64));
-#pragma unroll
-  for (int j = 8; j > 0; j >>= 1) {
-    const unsigned long long o = __shfl_xor(t, j, 64);
-    t = ((i & j) == 0) ? kmax2(t, o) : kmin2(t, o);
-  }
-  return t;
-}
-
 // A tile configuration: BM x BN output tile, WM x WN waves (each holding a
 // BM/WM x BN/WN tile), KF 32-wide k steps per pipeline stage, ST stages.
 template <int BM_, int BN_, int WM_, int WN_, int KF_, int ST_>
@@ -289,7 +259,7 @@ void k_gemm_tile(GemmParams p) {
         }
         unsigned long long best = bn < 0 ? 0ull : (((unsigned long long)bk << 32) | (uint32_t)(p.N - 1 - bn));
 #pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) best = kmax2(best, __shfl_xor(best, o, 64));
+        for (int o = 8; o >= 1; o >>= 1) best = key_max(best, __shfl_xor(best, o, 64));
         if (r16 == 0) red[wn * BM + ml] = best;
       }
     }
@@ -297,7 +267,7 @@ void k_gemm_tile(GemmParams p) {
     for (int r = t; r < BM; r += NT) {
       unsigned long long v = red[r];
 #pragma unroll
-      for (int w_ = 1; w_ < WN; ++w_) v = kmax2(v, red[w_ * BM + r]);
+      for (int w_ = 1; w_ < WN; ++w_) v = key_max(v, red[w_ * BM + r]);
       if (m0 + r < p.M) atomicMax(p.keys + m0 + r, v);
     }
   } else {  // EPI_TOPK
@@ -314,7 +284,7 @@ void k_gemm_tile(GemmParams p) {
           const bool ok = m < p.M && n < p.N;
           if (ok && p.dbg) p.dbg[(long long)m * p.ld_dbg + n] = acc[i][j][q];
           const unsigned long long key = ok ? argmax_key(acc[i][j][q], n, p.N) : 0ull;
-          best = merge16(best, sort16(key, r16), r16);
+          best = merge16_desc(best, sort16_desc(key, r16), r16);
         }
         if (m < p.M) p.keys[((long long)m * (WN * n_nt) + WN * n_tile + wn) * 16 + r16] = best;
       }

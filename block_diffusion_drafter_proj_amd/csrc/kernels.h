@@ -107,6 +107,24 @@ struct ResidConvParams {
   unsigned int* err;
 };
 
+// Greedy selection over split-K partial logits (the vocabulary product of
+// 17..64 rows): one workgroup of 4 waves per (chunk of kSelChunk columns,
+// row) sums the planes in split order and leaves its best packed key
+// (atomic max into keys[row]) or one sorted top-16 list per wave
+// (lists[row][chunk * 4 + wave]).
+constexpr int kSelChunk = 4096;
+struct LogitSelParams {
+  const float* part;  // [n_part][M][N] fp32
+  int n_part, M, N;
+  float* dbg;  // optional fp32 logits [M][ld_dbg]
+  int ld_dbg;
+  unsigned long long* keys;   // argmax: one per row (zero on entry)
+  unsigned long long* lists;  // top-16: [M][n_lists][16]
+  int n_lists;                // 4 * chunks
+};
+inline int logit_sel_lists(int N) { return 4 * ((N + kSelChunk - 1) / kSelChunk); }
+void launch_logit_select(bool topk, const LogitSelParams& p, hipStream_t s);
+
 // Merge of the per-workgroup top-16 lists of the LM head.
 struct TopkParams {
   const unsigned long long* lists;  // [M][n_lists][16]

@@ -105,7 +105,7 @@ Plans make_plans(const dflash_config& c, int M) {
     p.o = tiled_ok ? tiled(tiles_of(d), qd) : mt4(tiles_of(d), qd);
     p.gateup = gemm_use_big(c.dtype, M) ? one : plan_gemm(tiles_of(c.ffn), d, kb, true);
     p.down = tiled_ok ? tiled(tiles_of(d), c.ffn) : mt4(tiles_of(d), c.ffn);
-    p.lm = gemm_use_big(c.dtype, M) ? one : plan_gemm(tiles_of(c.vocab), d, kb, true);
+    p.lm = mt4(tiles_of(c.vocab), d);  // partial logits, then k_logit_select
     p.fc = mt4(tiles_of(d), c.n_feat * d);
     p.kv = mt4(c.n_layers * tiles_of(2 * c.n_kv_heads * c.head_dim), d);
     return p;
@@ -145,7 +145,7 @@ size_t part_rows(const dflash_config& c, GemmPlan Plans::*f, int max_rows) {
 
 struct Layout {
   size_t state, err, page_table, cos_t, sin_t;
-  size_t h, xa, xo, qkv, qb, blk, part_o, part_ml, nsplit, z, keys, tlists, opart, dpart;
+  size_t h, xa, xo, qkv, qb, blk, part_o, part_ml, nsplit, z, keys, tlists, lpart, opart, dpart;
   size_t u, f, kvo;
   size_t total;
 };
@@ -182,7 +182,16 @@ Layout make_layout(const dflash_config& c) {
   L.z = take(e * M * c.ffn);
   L.keys = take(sizeof(unsigned long long) * M);
   L.tlists = c.topk ? take(sizeof(unsigned long long) * M * 16 *
-                           std::max(256, gemm_big_lists(tiles_of(c.vocab)))) : 0;
+                           std::max({256, gemm_big_lists(tiles_of(c.vocab)), logit_sel_lists(c.vocab)}))
+                    : 0;
+  {  // split-K partial logits of the 64-row vocabulary product
+    size_t lrows = 0;
+    for (int m = 1; m <= (int)M; ++m) {
+      const GemmPlan g = make_plans(c, m).lm;
+      if (g.mt == 4) lrows = std::max(lrows, (size_t)g.P * m);
+    }
+    L.lpart = lrows ? take(sizeof(float) * lrows * c.vocab) : 0;
+  }
   L.opart = take(sizeof(float) * part_rows(c, &Plans::o, (int)M) * c.hidden);
   L.dpart = take(sizeof(float) * part_rows(c, &Plans::down, (int)M) * c.hidden);
   L.u = take(sizeof(float) * part_rows(c, &Plans::fc, (int)R) * c.hidden);
@@ -919,6 +928,40 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   gl.tiles = tiles_of(c.vocab);
   gl.N = c.vocab;
   gl.P = 1;
+  if (pl.lm.mt == 4) {  // 17..64 rows: split-K partial logits, then the selection pass
+    gl.P = pl.lm.P;
+    gl.out_f32 = at<float>(h, h->lay.lpart);
+    {
+      ProfScope ps(h, DFLASH_KERNEL_LM_HEAD, s);
+      launch_gemm(c.dtype, EPI_PARTIAL, pl.lm, gl, s);
+    }
+    LogitSelParams lp{};
+    lp.part = gl.out_f32;
+    lp.n_part = pl.lm.P;
+    lp.M = M;
+    lp.N = c.vocab;
+    lp.dbg = debug_logits;
+    lp.ld_dbg = c.vocab;
+    lp.keys = at<unsigned long long>(h, h->lay.keys);
+    lp.lists = at<unsigned long long>(h, h->lay.tlists);
+    lp.n_lists = logit_sel_lists(c.vocab);
+    ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
+    launch_logit_select(c.topk != 0, lp, s);
+    if (c.topk) {
+      TopkParams tp{};
+      tp.lists = lp.lists;
+      tp.n_lists = lp.n_lists;
+      tp.M = M;
+      tp.vocab = c.vocab;
+      tp.draft = draft;
+      tp.topk_ids = topk_ids;
+      tp.topk_logits = topk_logits;
+      launch_topk_merge(tp, s);
+    } else {
+      launch_finalize(lp.keys, M, c.vocab, draft, s);
+    }
+    return launched("draft head");
+  }
   gl.keys = at<unsigned long long>(h, c.topk ? h->lay.tlists : h->lay.keys);
   gl.dbg = debug_logits;
   gl.ld_dbg = c.vocab;

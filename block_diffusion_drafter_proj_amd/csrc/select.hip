@@ -50,6 +50,59 @@ __global__ __launch_bounds__(64) void k_verify(int B, int vocab, const int* draf
   }
 }
 
+// Sums the split-K partial logits of one row over one chunk of the
+// vocabulary (planes in split order, so the result does not depend on
+// scheduling).  Wave w takes the 64-column blocks w, w+4, ... of the chunk;
+// every lane requests all of its partial values before the first sum, then
+// argmax keeps a running maximum key per lane and top-16 a running sorted
+// list per 16-lane group, merged across the wave's four groups at the end.
+template <bool TOPK>
+__global__ __launch_bounds__(256) void k_logit_select(LogitSelParams p) {
+  constexpr int NB = kSelChunk / 256;  // column blocks per wave
+  __shared__ unsigned long long red[4];
+  const int chunk = blockIdx.x, row = blockIdx.y;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, i16 = lane & 15;
+  const long long plane = (long long)p.M * p.N;
+  const float* src = p.part + (long long)row * p.N;
+  const int c0 = chunk * kSelChunk + wave * 64 + lane;
+  float v[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) v[b] = 0.f;
+  for (int q = 0; q < p.n_part; ++q) {
+    float x[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int n = c0 + 256 * b;
+      x[b] = n < p.N ? src[q * plane + n] : 0.f;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) v[b] += x[b];
+  }
+  unsigned long long best = 0ull;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int n = c0 + 256 * b;
+    const bool ok = n < p.N;
+    if (ok && p.dbg) p.dbg[(long long)row * p.ld_dbg + n] = v[b];
+    const unsigned long long key = ok ? argmax_key(v[b], n, p.N) : 0ull;
+    if (TOPK)
+      best = merge16_desc(best, sort16_desc(key, i16), i16);
+    else
+      best = key_max(best, key);
+  }
+  if (TOPK) {
+    best = merge16_desc(best, __shfl_xor(best, 16, 64), i16);
+    best = merge16_desc(best, __shfl_xor(best, 32, 64), i16);
+    if (lane < 16) p.lists[((long long)row * p.n_lists + chunk * 4 + wave) * 16 + lane] = best;
+  } else {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) best = key_max(best, __shfl_xor(best, o, 64));
+    if (lane == 0) red[wave] = best;
+    __syncthreads();
+    if (t == 0) atomicMax(p.keys + row, key_max(key_max(red[0], red[1]), key_max(red[2], red[3])));
+  }
+}
+
 // Merge two lists sorted descending into the 16 largest, sorted descending.
 __device__ __forceinline__ void merge_lists(const unsigned long long* a, const unsigned long long* b,
                                             unsigned long long* out) {
@@ -107,6 +160,15 @@ __global__ __launch_bounds__(256) void k_topk_merge(TopkParams p) {
 }
 
 }  // namespace
+
+void launch_logit_select(bool topk, const LogitSelParams& p, hipStream_t s) {
+  if (p.M <= 0) return;
+  const dim3 grid((p.N + kSelChunk - 1) / kSelChunk, p.M);
+  if (topk)
+    hipLaunchKernelGGL(k_logit_select<true>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_logit_select<false>, grid, dim3(256), 0, s, p);
+}
 
 void launch_topk_merge(const TopkParams& p, hipStream_t s) {
   if (p.M <= 0) return;
