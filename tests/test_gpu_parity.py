@@ -197,7 +197,21 @@ def _check_topk(ids, vals, g_logits, ref_logits, g_draft):
 @pytest.mark.parametrize("name", ["small_bf16", "small_block10", "small_dh64", "small_batch", "small_window",
                                   "small_conv"])
 def test_draft_parity_lockstep(name):
-    dev, shape, w, dr, ctxs, pages = _setup(name)
+    _lockstep(name)
+
+
+@pytest.mark.parametrize("name,over", [
+    ("small_bf16", {"block_size": 1}),                 # one drafted position per block
+    ("small_batch", {"block_size": 1}),                # 5 rows: one per request
+    ("small_batch", {"batch": 4}),                     # exactly 64 rows: skinny 64-row block and tiled kernel
+    ("small_conv", {"batch": 3, "ctx": None, "ctx_range": (60, 300)}),  # 48 rows: split-K logits, top-16
+], ids=["block1", "batch5_block1", "rows64", "conv_rows48"])
+def test_draft_parity_lockstep_shapes(name, over):
+    _lockstep(name, **over)
+
+
+def _lockstep(name, **over):
+    dev, shape, w, dr, ctxs, pages = _setup(name, **over)
     o = DraftOracle(shape, w)
     n = shape["batch"]
     slots = list(range(n))
