@@ -589,13 +589,15 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
   if (n_split == 1) {
     if (l16 < p.B) {
       const float inv = 1.0f / l_run;
-      bf16* out = reinterpret_cast<bf16*>(p.out) + (long long)(r * p.B + l16) * p.ldo + h * DH + 4 * g4;
+      const int m = r * p.B + l16;
+      bf16* out = reinterpret_cast<bf16*>(p.out);
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
         bf16x4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = (bf16)(o[dt][i] * inv);
-        *reinterpret_cast<bf16x4*>(out + dt * 16) = v;
+        const int k = h * DH + 4 * g4 + dt * 16;
+        *reinterpret_cast<bf16x4*>(out + (p.out_packed ? frag_index(m, k, p.ldo) : (long long)m * p.ldo + k)) = v;
       }
     }
     return;
@@ -664,7 +666,8 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p) {
     }
   }
   const float inv = 1.0f / L;
-  T* out = reinterpret_cast<T*>(p.out) + (long long)(r * p.B + q) * p.ldo + h * DH + lane * C;
+  const int m = r * p.B + q, k = h * DH + lane * C;  // C consecutive k stay contiguous
+  T* out = reinterpret_cast<T*>(p.out) + (p.out_packed ? frag_index(m, k, p.ldo) : (long long)m * p.ldo + k);
 #pragma unroll
   for (int c = 0; c < C; ++c) out[c] = from_f<T>(acc[c] * inv);
 }

@@ -63,6 +63,15 @@ __device__ __forceinline__ f32x4 mfma_step(f32x8 a, f32x8 b, f32x4 acc) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Element (m, k) of an activation matrix with K columns stored in MFMA
+// fragment order, the order the tiled GEMM stages its operands in:
+// [m / 16][k / 32][lane = m % 16 + 16 * (k % 32 / 8)][k % 8], so one
+// fragment (16 rows x 32 k) is 1 KB of contiguous memory.  Four consecutive
+// k from a multiple of 4 stay contiguous.
+__device__ __forceinline__ long long frag_index(int m, int k, int K) {
+  return ((((long long)(m >> 4) * (K >> 5) + (k >> 5)) * 64 + (m & 15) + 16 * ((k & 31) >> 3)) << 3) + (k & 7);
+}
+
 // Direct global -> LDS copy of 16 bytes per lane (no register staging): lane
 // i's bytes land at lds_wave_base + 16 * i; the LDS address is wave-uniform.
 // The copy counts as an outstanding vector-memory load until it has landed.

@@ -104,8 +104,13 @@ void k_gemm_tile(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
     const int fa = wv * LA + i;
-    const int row = min(m0 + (fa / KF) * 16 + r16, p.M - 1);
-    a_off[i] = row * p.lda + (fa % KF) * 32 + 8 * g;
+    if (p.a_packed) {  // fragment order: the fragment is 1 KB at (row block, k step)
+      const int rb = min(m0 / 16 + fa / KF, (p.M - 1) / 16);
+      a_off[i] = (rb * S32 + fa % KF) * kFrag + lane * 8;
+    } else {
+      const int row = min(m0 + (fa / KF) * 16 + r16, p.M - 1);
+      a_off[i] = row * p.lda + (fa % KF) * 32 + 8 * g;
+    }
   }
   auto wsrc = [&](int jb) -> const bf16* {  // weight column block jb at k-stage 0
     int tt = wtile(jb);
@@ -136,7 +141,8 @@ void k_gemm_tile(GemmParams p) {
       part_k0 += p.a_part_k;
       apart = reinterpret_cast<const bf16*>(p.a[part]);
     }
-    const bf16* abase = apart + (k0 - part_k0);
+    // row-major: k advances along the row; fragment order: 32 k per fragment
+    const bf16* abase = apart + (long long)(k0 - part_k0) * (p.a_packed ? 16 : 1);
 #pragma unroll
     for (int i = 0; i < LA; ++i) dma16(abase + a_off[i], dst + (wv * LA + i) * kFrag);
 #pragma unroll
@@ -230,7 +236,8 @@ void k_gemm_tile(GemmParams p) {
           const int n = n_tile * (BN / 2) + (wn * (TN / 2) + jj) * 16 + r16;
           if (m < p.M && n < p.N) {
             const float gt = acc[i][jj][q], u = acc[i][jj + TN / 2][q];
-            reinterpret_cast<bf16*>(p.out_t)[(long long)m * p.ldt + n] = (bf16)(gt / (1.0f + expf(-gt)) * u);
+            reinterpret_cast<bf16*>(p.out_t)[p.out_packed ? frag_index(m, n, p.ldt) : (long long)m * p.ldt + n] =
+                (bf16)(gt / (1.0f + expf(-gt)) * u);
           }
         }
   } else if (EPI == EPI_ARGMAX) {

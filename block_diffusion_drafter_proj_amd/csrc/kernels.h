@@ -59,6 +59,9 @@ struct GemmParams {
   float* dbg;                // EPI_ARGMAX / EPI_TOPK, optional fp32 logits
   int ld_dbg;
   RopeOut rope;              // EPI_ROPE (tiles counts column-tile pairs)
+  // tiled kernel only: A (one part) and the SwiGLU output stored in fragment
+  // order (frag_index) instead of row-major
+  int a_packed, out_packed;
 };
 
 struct GemmPlan {
@@ -80,8 +83,9 @@ struct NormParams {
   int ldx;
   const void* gamma;  // storage dtype [d]
   float eps;
-  void* out;  // storage dtype [M, d]
+  void* out;  // storage dtype [M, d] (row stride ldo), or fragment order (out_packed)
   int ldo;
+  int out_packed;
   int d, M;
   float* dbg;  // optional fp32 copy of x [M, d]
   unsigned long long* zero_keys;  // optional: keys[row] = 0
@@ -174,6 +178,7 @@ struct AttnParams {
   float* part_ml;  // [n_req, Hq, n_splits, 16, 2]
   void* out;       // storage dtype [n_req*B, Hq*dh] (written here when n_splits == 1)
   int ldo;
+  int out_packed;  // out in fragment order with ldo columns
   unsigned int* err;
 };
 
@@ -184,6 +189,7 @@ struct CombineParams {
   int n_splits, n_rh, Hq, B;  // n_rh = n_req * Hq
   void* out;  // storage dtype [n_req*B, Hq*dh]
   int ldo;
+  int out_packed;  // out in fragment order with ldo columns
 };
 
 struct InjectReq {

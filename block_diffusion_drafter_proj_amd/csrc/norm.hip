@@ -9,6 +9,8 @@
 // section 3.1: the block is recovered from noise in one forward; the noise is
 // read as mask tokens).  The final norm clears the per-row argmax keys that
 // the LM head accumulates into.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -118,8 +120,91 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(NormParams p) {
   typename Out4<T>::type o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = from_f<T>(y[i]);
-  *reinterpret_cast<typename Out4<T>::type*>(reinterpret_cast<T*>(p.out) + (long long)row * p.ldo + k) = o;
+  const long long oi = p.out_packed ? frag_index(row, k, p.d) : (long long)row * p.ldo + k;
+  *reinterpret_cast<typename Out4<T>::type*>(reinterpret_cast<T*>(p.out) + oi) = o;
   if (p.zero_keys && t == 0) p.zero_keys[row] = 0ull;
+}
+
+// RMSNorm into fragment order (the tiled GEMM's operand layout), ROWS rows
+// per workgroup (ROWS divides 16, so they sit in one 16-row block).  Output
+// chunk c (8 consecutive k of one row, 16 bytes in bf16) is row c mod ROWS,
+// k group (c / ROWS) mod 4 and k step c / (4 ROWS), and belongs to thread
+// c mod blockDim: the ROWS rows' chunks of one fragment lane group are
+// adjacent in memory, so a wave writes whole 64-byte runs and reads 512
+// contiguous bytes of each of its rows.  blockDim is a multiple of 64, so
+// thread t only ever holds row t mod ROWS; its chunks stay in registers, their
+// squares are summed in chunk order, then over the row's lanes of the wave
+// (butterfly) and over the waves in order.  Gamma waits in LDS.  No conv taps (those need the previous row of the
+// request's block).
+constexpr int kNormRows = 4;  // rows per workgroup of the fragment-order norm
+
+template <typename T, int ROWS>
+__global__ __launch_bounds__(1024) void k_rmsnorm_frag(NormParams p) {
+  constexpr int CMAX = 8;  // chunks per thread: ROWS * d / 8 over blockDim
+  __shared__ float red[16 * ROWS];
+  __shared__ float rs[ROWS];
+  __shared__ float gs[4096];  // gamma, staged while the rows load
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int row = blockIdx.x * ROWS + t % ROWS;
+  const bool live = row < p.M;
+  const int cpt = ROWS * p.d / 8 / nt;
+  const int S = p.d / 32;
+  const long long plane = (long long)p.M * p.d;
+  for (int k = t; k < p.d; k += nt) gs[k] = to_f(reinterpret_cast<const T*>(p.gamma)[k]);
+  f32x4 x[CMAX][2];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < CMAX; ++j) {
+    if (j < cpt) {
+      const int q = (t + j * nt) / ROWS;
+      const int k = 32 * (q >> 2) + 8 * (q & 3);
+      x[j][0] = live ? load_row4<T>(p, row, k, plane) : f32x4{0.f, 0.f, 0.f, 0.f};
+      x[j][1] = live ? load_row4<T>(p, row, k + 4, plane) : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (live && p.x_out) {
+        *reinterpret_cast<f32x4*>(p.x_out + (long long)row * p.ldx + k) = x[j][0];
+        *reinterpret_cast<f32x4*>(p.x_out + (long long)row * p.ldx + k + 4) = x[j][1];
+      }
+      if (live && p.dbg) {
+        *reinterpret_cast<f32x4*>(p.dbg + (long long)row * p.d + k) = x[j][0];
+        *reinterpret_cast<f32x4*>(p.dbg + (long long)row * p.d + k + 4) = x[j][1];
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        ss += (x[j][h][0] * x[j][h][0] + x[j][h][1] * x[j][h][1]) + (x[j][h][2] * x[j][h][2] + x[j][h][3] * x[j][h][3]);
+    }
+  }
+  // a row's lanes in a wave are ROWS apart: butterfly over them, then the
+  // waves in order
+#pragma unroll
+  for (int o = 32; o >= ROWS; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((t & 63) < ROWS) red[(t >> 6) * ROWS + (t & 63)] = ss;
+  __syncthreads();
+  if (t < ROWS) {
+    float tot = 0.f;
+    for (int w = 0; w < nt / 64; ++w) tot += red[w * ROWS + t];
+    rs[t] = 1.0f / sqrtf(tot / (float)p.d + p.eps);
+  }
+  __syncthreads();
+  const float r = rs[t % ROWS];
+  T* out = reinterpret_cast<T*>(p.out);
+  const long long rb = row >> 4;
+  const int lane0 = row & 15;
+#pragma unroll
+  for (int j = 0; j < CMAX; ++j) {
+    if (j < cpt) {
+      const int q = (t + j * nt) / ROWS;
+      const int k = 32 * (q >> 2) + 8 * (q & 3);
+      typename Out4<T>::type o[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[h][i] = from_f<T>(live ? x[j][h][i] * r * gs[k + 4 * h + i] : 0.f);
+      T* dst = out + (((rb * S + (q >> 2)) * 64 + lane0 + 16 * (q & 3)) << 3);  // frag_index(row, k, d)
+      *reinterpret_cast<typename Out4<T>::type*>(dst) = o[0];
+      *reinterpret_cast<typename Out4<T>::type*>(dst + 4) = o[1];
+    }
+  }
+  if (p.zero_keys && t < ROWS && live) p.zero_keys[row] = 0ull;
 }
 
 // Residual add of a conv'd GEMM output (DFlash 2): one workgroup per row.
@@ -169,6 +254,15 @@ void launch_resid_conv(int dtype, const ResidConvParams& p, hipStream_t s) {
 
 void launch_rmsnorm(int dtype, const NormParams& p, hipStream_t s) {
   if (p.M <= 0) return;
+  if (p.out_packed && !p.conv && p.d % 256 == 0 && p.d <= 4096) {
+    constexpr int R = kNormRows;
+    const int nt = std::min(1024, R * p.d / 8);  // R * d / 8 chunks, at most 8 per thread
+    if (dtype == DFLASH_BF16)
+      hipLaunchKernelGGL((k_rmsnorm_frag<bf16, R>), dim3((p.M + R - 1) / R), dim3(nt), 0, s, p);
+    else
+      hipLaunchKernelGGL((k_rmsnorm_frag<float, R>), dim3((p.M + R - 1) / R), dim3(nt), 0, s, p);
+    return;
+  }
   if (dtype == DFLASH_BF16)
     hipLaunchKernelGGL(k_rmsnorm<bf16>, dim3(p.M), dim3(p.d / 4), 0, s, p);
   else

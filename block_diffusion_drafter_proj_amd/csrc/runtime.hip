@@ -170,8 +170,10 @@ Layout make_layout(const dflash_config& c) {
   L.cos_t = take(sizeof(float) * (size_t)c.max_position * (c.head_dim / 2));
   L.sin_t = take(sizeof(float) * (size_t)c.max_position * (c.head_dim / 2));
   L.h = take(sizeof(float) * M * c.hidden);
-  L.xa = take(e * M * c.hidden);
-  L.xo = take(e * M * qd);
+  // GEMM inputs: rows rounded up to whole 16-row fragments (fragment order)
+  const size_t M16 = (M + 15) / 16 * 16;
+  L.xa = take(e * M16 * c.hidden);
+  L.xo = take(e * M16 * qd);
   L.qkv = take(sizeof(float) * part_rows(c, &Plans::qkv, (int)M) * qkvw);
   L.qb = take(e * (size_t)c.max_batch * c.n_q_heads * 16 * c.head_dim);
   L.blk = take(e * (size_t)c.max_batch * page_elems);
@@ -179,7 +181,7 @@ Layout make_layout(const dflash_config& c) {
   L.part_o = take(sizeof(float) * pp * c.head_dim);
   L.part_ml = take(sizeof(float) * pp * 2);
   L.nsplit = take(sizeof(int) * c.max_batch);
-  L.z = take(e * M * c.ffn);
+  L.z = take(e * M16 * c.ffn);
   L.keys = take(sizeof(unsigned long long) * M);
   L.tlists = c.topk ? take(sizeof(unsigned long long) * M * 16 *
                            std::max({256, gemm_big_lists(tiles_of(c.vocab)), logit_sel_lists(c.vocab)}))
@@ -777,12 +779,14 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     n1.eps = c.rms_eps;
     n1.out = h->ws + h->lay.xa;
     n1.ldo = d;
+    n1.out_packed = pl.qkv.mt == 0;  // the tiled QKV product reads fragment order
     n1.d = d;
     n1.M = M;
     n1.dbg = debug_hidden ? debug_hidden + (size_t)l * M * d : nullptr;
     { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, n1, s); }
 
     GemmParams g = gemm_in(h->ws + h->lay.xa, d);
+    g.a_packed = n1.out_packed;
     g.w[0] = h->packed + h->pk.wqkv[l];
     g.N = qkvw;
     g.P = pl.qkv.P;
@@ -836,6 +840,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     ap.part_ml = at<float>(h, h->lay.part_ml);
     ap.out = h->ws + h->lay.xo;
     ap.ldo = qd;
+    ap.out_packed = pl.o.mt == 0;
     ap.err = at<unsigned int>(h, h->lay.err);
     { ProfScope ps(h, DFLASH_KERNEL_ATTN, s); launch_attention(c.dtype, c.head_dim, n_req, ap, sl, s); }
     if (splits > 1) {
@@ -849,11 +854,13 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
       cp.B = B;
       cp.out = ap.out;
       cp.ldo = qd;
+      cp.out_packed = ap.out_packed;
       ProfScope ps(h, DFLASH_KERNEL_COMBINE, s);
       launch_combine(c.dtype, c.head_dim, cp, s);
     }
 
     GemmParams go = gemm_in(h->ws + h->lay.xo, qd);
+    go.a_packed = ap.out_packed;
     go.w[0] = h->packed + h->pk.wo[l];
     go.tiles = tiles_of(d);
     go.N = d;
@@ -876,11 +883,14 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     n2.eps = c.rms_eps;
     n2.out = h->ws + h->lay.xa;
     n2.ldo = d;
+    n2.out_packed = pl.gateup.mt == 0;
     n2.d = d;
     n2.M = M;
     { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, n2, s); }
 
     GemmParams gu = gemm_in(h->ws + h->lay.xa, d);
+    gu.a_packed = n2.out_packed;
+    gu.out_packed = pl.gateup.mt == 0 && pl.down.mt == 0;  // z for a tiled down product
     gu.w[0] = h->packed + h->pk.wgateup[l];
     gu.tiles = tiles_of(c.ffn);
     gu.up_tile_off = tiles_of(c.ffn);
@@ -891,6 +901,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     { ProfScope ps(h, DFLASH_KERNEL_GATEUP_GEMM, s); launch_gemm(c.dtype, EPI_SWIGLU, pl.gateup, gu, s); }
 
     GemmParams gd = gemm_in(h->ws + h->lay.z, c.ffn);
+    gd.a_packed = gu.out_packed;
     gd.w[0] = h->packed + h->pk.wdown[l];
     gd.tiles = tiles_of(d);
     gd.N = d;
@@ -917,6 +928,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   nf.eps = c.rms_eps;
   nf.out = h->ws + h->lay.xa;
   nf.ldo = d;
+  nf.out_packed = pl.lm.mt == 0;
   nf.d = d;
   nf.M = M;
   nf.dbg = debug_hidden ? debug_hidden + (size_t)c.n_layers * M * d : nullptr;
@@ -924,6 +936,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, nf, s); }
 
   GemmParams gl = gemm_in(h->ws + h->lay.xa, d);
+  gl.a_packed = nf.out_packed;
   gl.w[0] = h->packed + h->pk.lm_head;
   gl.tiles = tiles_of(c.vocab);
   gl.N = c.vocab;
