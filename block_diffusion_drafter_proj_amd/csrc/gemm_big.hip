@@ -226,20 +226,33 @@ void k_gemm_tile(GemmParams p) {
           if (m < p.M && n < p.N) out[(long long)m * p.N + n] = acc[i][j][q];
         }
   } else if (EPI == EPI_SWIGLU) {
+    // silu(gate) * up per element into the wave's slice of the (now free)
+    // stage ring, then 8 consecutive columns of one row per lane and store:
+    // 16-byte writes instead of one element per lane
+    constexpr int WR = TM * 16, WC = TN / 2 * 16;  // the wave's output rows and columns
+    static_assert(C::NW * WR * WC <= ST * FS * kFrag, "SwiGLU staging fits the ring");
+    bf16* stage = lds + wv * WR * WC;
+    wait_barrier<0>();  // every wave is done with the stages
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int jj = 0; jj < TN / 2; ++jj)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int m = m0 + (wm * TM + i) * 16 + 4 * g + q;
-          const int n = n_tile * (BN / 2) + (wn * (TN / 2) + jj) * 16 + r16;
-          if (m < p.M && n < p.N) {
-            const float gt = acc[i][jj][q], u = acc[i][jj + TN / 2][q];
-            reinterpret_cast<bf16*>(p.out_t)[p.out_packed ? frag_index(m, n, p.ldt) : (long long)m * p.ldt + n] =
-                (bf16)(gt / (1.0f + expf(-gt)) * u);
-          }
+          const float gt = acc[i][jj][q], u = acc[i][jj + TN / 2][q];
+          stage[(i * 16 + 4 * g + q) * WC + jj * 16 + r16] = (bf16)(gt / (1.0f + expf(-gt)) * u);
         }
+    __syncthreads();
+    for (int c = lane; c < WR * WC / 8; c += 64) {
+      const int rl = c / (WC / 8), cl = (c % (WC / 8)) * 8;
+      const int m = m0 + wm * WR + rl;
+      const int n = n_tile * (BN / 2) + wn * WC + cl;
+      if (m < p.M && n < p.N) {  // N is a multiple of 8: a chunk is all in or all out
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(stage + rl * WC + cl);
+        *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(p.out_t) +
+                                   (p.out_packed ? frag_index(m, n, p.ldt) : (long long)m * p.ldt + n)) = v;
+      }
+    }
   } else if (EPI == EPI_ARGMAX) {
     // per lane and row: a running 32-bit order key of the logit (strict > keeps
     // the lowest column on ties, the lane's columns increase with j); the 64-bit
