@@ -96,14 +96,13 @@ Plans make_plans(const dflash_config& c, int M) {
       g.mt = 4;
       return g;
     };
-    const int kb = gemm_kblock(c.dtype, 1);
+    auto tiled = [&](int tiles, int K) { return GemmPlan{gemm_big_split(M, tiles, K), 4, 1, 0}; };
+    const bool tiled_ok = gemm_use_big(c.dtype, M);  // exactly 64 rows
     const GemmPlan one{1, 4, 1, 0};
     Plans p;
     p.qkv = mt4(tiles_of(qkvw), d);
-    const bool tiled_ok = gemm_use_big(c.dtype, M);
-    auto tiled = [&](int tiles, int K) { return GemmPlan{gemm_big_split(M, tiles, K), 4, 1, 0}; };
     p.o = tiled_ok ? tiled(tiles_of(d), qd) : mt4(tiles_of(d), qd);
-    p.gateup = gemm_use_big(c.dtype, M) ? one : plan_gemm(tiles_of(c.ffn), d, kb, true);
+    p.gateup = tiled_ok ? one : plan_gemm(tiles_of(c.ffn), d, gemm_kblock(c.dtype, 1), true);
     p.down = tiled_ok ? tiled(tiles_of(d), c.ffn) : mt4(tiles_of(d), c.ffn);
     p.lm = mt4(tiles_of(c.vocab), d);  // partial logits, then k_logit_select
     p.fc = mt4(tiles_of(d), c.n_feat * d);
