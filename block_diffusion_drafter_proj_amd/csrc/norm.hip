@@ -150,9 +150,9 @@ __global__ __launch_bounds__(1024) void k_rmsnorm_frag(NormParams p) {
   const int cpt = ROWS * p.d / 8 / nt;
   const int S = p.d / 32;
   const long long plane = (long long)p.M * p.d;
-  for (int k = t; k < p.d; k += nt) gs[k] = to_f(reinterpret_cast<const T*>(p.gamma)[k]);
+  // every row and partial load of the thread is issued before any is used,
+  // and gamma is staged after them, so the pass waits for one round trip
   f32x4 x[CMAX][2];
-  float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < CMAX; ++j) {
     if (j < cpt) {
@@ -160,6 +160,15 @@ __global__ __launch_bounds__(1024) void k_rmsnorm_frag(NormParams p) {
       const int k = 32 * (q >> 2) + 8 * (q & 3);
       x[j][0] = live ? load_row4<T>(p, row, k, plane) : f32x4{0.f, 0.f, 0.f, 0.f};
       x[j][1] = live ? load_row4<T>(p, row, k + 4, plane) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  for (int k = t; k < p.d; k += nt) gs[k] = to_f(reinterpret_cast<const T*>(p.gamma)[k]);
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < CMAX; ++j) {
+    if (j < cpt) {
+      const int q = (t + j * nt) / ROWS;
+      const int k = 32 * (q >> 2) + 8 * (q & 3);
       if (live && p.x_out) {
         *reinterpret_cast<f32x4*>(p.x_out + (long long)row * p.ldx + k) = x[j][0];
         *reinterpret_cast<f32x4*>(p.x_out + (long long)row * p.ldx + k + 4) = x[j][1];
