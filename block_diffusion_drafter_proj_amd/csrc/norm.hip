@@ -136,7 +136,8 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(NormParams p) {
 // squares are summed in chunk order, then over the row's lanes of the wave
 // (butterfly) and over the waves in order.  Gamma waits in LDS.  No conv taps (those need the previous row of the
 // request's block).
-constexpr int kNormRows = 4;  // rows per workgroup of the fragment-order norm
+constexpr int kNormRows = 4;       // rows per workgroup of the fragment-order norm
+constexpr int kNormThreads = 1024;  // its workgroup size at most
 
 template <typename T, int ROWS>
 __global__ __launch_bounds__(1024) void k_rmsnorm_frag(NormParams p) {
@@ -265,7 +266,7 @@ void launch_rmsnorm(int dtype, const NormParams& p, hipStream_t s) {
   if (p.M <= 0) return;
   if (p.out_packed && !p.conv && p.d % 256 == 0 && p.d <= 4096) {
     constexpr int R = kNormRows;
-    const int nt = std::min(1024, R * p.d / 8);  // R * d / 8 chunks, at most 8 per thread
+    const int nt = std::min(kNormThreads, R * p.d / 8);  // R * d / 8 chunks, at most 8 per thread
     if (dtype == DFLASH_BF16)
       hipLaunchKernelGGL((k_rmsnorm_frag<bf16, R>), dim3((p.M + R - 1) / R), dim3(nt), 0, s, p);
     else
