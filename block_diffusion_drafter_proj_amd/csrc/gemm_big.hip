@@ -341,9 +341,14 @@ typedef TileCfg<64, 128, 2, 2, 2, 3> Cfg64;
 typedef TileCfg<128, 128, 2, 2, 2, 3> CfgSmall;
 typedef TileCfg<256, 256, 2, 4, 1, 5> CfgBig;
 typedef TileCfg<256, 192, 4, 2, 2, 2> CfgWide;
+// 256x128 (8 waves of 128x32, 24 KB stages, 6-deep ring): for a split-K
+// product whose K is short and whose columns fit 256 tiles, this grid fills
+// the CUs with half the split of 256x256, so the consumer sums half as many
+// fp32 planes (the O product at 1,024 rows: its norm reads 2 planes, not 4).
+typedef TileCfg<256, 128, 2, 4, 1, 6> CfgTall;
 static_assert(Cfg64::WN == CfgSmall::WN && Cfg64::BN == CfgSmall::BN, "top-16 lists per row");
 
-enum { CFG_SMALL, CFG_BIG, CFG_WIDE, CFG_64 };
+enum { CFG_SMALL, CFG_BIG, CFG_WIDE, CFG_64, CFG_TALL };
 
 // Workgroups with real work and the split-K factor of a partial-output
 // product: the smallest power of two that gives at least one workgroup per CU
@@ -367,6 +372,7 @@ int tile_cfg_t(int M, int tiles, int K) {
   if (M <= 64) return CFG_64;
   if (EPI == EPI_TOPK || M <= 128) return CFG_SMALL;
   if (EPI == EPI_ARGMAX) return CFG_BIG;  // the vocabulary-wide product fills the CUs either way
+  if (EPI == EPI_PARTIAL && M >= 256 && tiles <= 256 && K <= 4096) return CFG_TALL;
   const int pb = EPI == EPI_PARTIAL ? cfg_split<CfgBig>(M, tiles, K) : 1;
   const int pw = EPI == EPI_PARTIAL ? cfg_split<CfgWide>(M, tiles, K) : 1;
   const double fb = round_fill(cfg_work<CfgBig, EPI>(M, tiles, pb));
@@ -388,6 +394,9 @@ template <int EPI>
 void launch_epi(const GemmParams& p, hipStream_t s) {
   switch (tile_cfg_t<EPI>(p.M, p.tiles, p.K)) {
     case CFG_64: launch_cfg<Cfg64, EPI>(p, s); break;
+    case CFG_TALL:
+      if constexpr (EPI == EPI_PARTIAL) launch_cfg<CfgTall, EPI>(p, s);
+      break;
     case CFG_WIDE:
       if constexpr (EPI != EPI_ARGMAX && EPI != EPI_TOPK) launch_cfg<CfgWide, EPI>(p, s);
       break;
@@ -410,6 +419,7 @@ int gemm_big_split(int M, int tiles, int K) {
     case CFG_WIDE: return cfg_split<CfgWide>(M, tiles, K);
     case CFG_BIG: return cfg_split<CfgBig>(M, tiles, K);
     case CFG_64: return cfg_split<Cfg64>(M, tiles, K);
+    case CFG_TALL: return cfg_split<CfgTall>(M, tiles, K);
     default: return cfg_split<CfgSmall>(M, tiles, K);
   }
 }
