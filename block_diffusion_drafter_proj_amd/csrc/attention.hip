@@ -42,8 +42,13 @@ template <typename T> struct Vec4;
 template <> struct Vec4<bf16> { typedef bf16x4 type; };
 template <> struct Vec4<float> { typedef f32x4 type; };
 
+// One workgroup of 256 threads per (request, head).  q and k heads: a thread
+// takes one block row and four consecutive rotate-half pairs (columns j..j+3
+// and their partners j+dh/2..), so every partial, cos and sin read is 16
+// bytes; V heads: a thread takes one row and dh/16 consecutive dims, written
+// transposed.
 template <typename T, int DH>
-__global__ __launch_bounds__(1024) void k_qkv_post(QkvPostParams p, SlotArgs sl) {
+__global__ __launch_bounds__(256) void k_qkv_post(QkvPostParams p, SlotArgs sl) {
   const int r = blockIdx.x;
   const int hh = blockIdx.y;
   const int t = threadIdx.x;
@@ -51,18 +56,19 @@ __global__ __launch_bounds__(1024) void k_qkv_post(QkvPostParams p, SlotArgs sl)
   const int n = p.state[sl.slots[r]].ctx_len + 1;
   const float* src = p.qkv + (long long)r * p.B * ld + hh * DH;
   const long long plane = (long long)gridDim.x * p.B * ld;
-  // sums of the split-K partials at two offsets; every load of a chunk of 4
-  // partials is issued before any is added (same order of addition)
-  auto rd2 = [&](long long off1, long long off2, float& x1, float& x2) {
-    x1 = 0.f;
-    x2 = 0.f;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // sums of the split-K partials of 4 columns at two offsets, in part order;
+  // every load of a chunk of 4 parts is issued before any is added
+  auto rd2 = [&](long long off1, long long off2, f32x4& x1, f32x4& x2) {
+    x1 = zero;
+    x2 = zero;
     for (int q0 = 0; q0 < p.n_part; q0 += 4) {
-      float a[4], b[4];
+      f32x4 a[4], b[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const bool ok = q0 + q < p.n_part;
-        a[q] = ok ? src[(q0 + q) * plane + off1] : 0.f;
-        b[q] = ok ? src[(q0 + q) * plane + off2] : 0.f;
+        a[q] = ok ? *reinterpret_cast<const f32x4*>(src + (q0 + q) * plane + off1) : zero;
+        b[q] = ok ? *reinterpret_cast<const f32x4*>(src + (q0 + q) * plane + off2) : zero;
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -73,7 +79,13 @@ __global__ __launch_bounds__(1024) void k_qkv_post(QkvPostParams p, SlotArgs sl)
       }
     }
   };
-  constexpr int H2 = DH / 2;
+  auto st4 = [](T* d, f32x4 v) {
+    typename Vec4<T>::type o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = from_f<T>(v[k]);
+    *reinterpret_cast<typename Vec4<T>::type*>(d) = o;
+  };
+  constexpr int H2 = DH / 2, QUADS = H2 / 4;
   const long long page_elems = 2LL * p.Hkv * 16 * DH;
   if (hh < p.Hq + p.Hkv) {
     T* dst;
@@ -81,31 +93,35 @@ __global__ __launch_bounds__(1024) void k_qkv_post(QkvPostParams p, SlotArgs sl)
       dst = reinterpret_cast<T*>(p.qb) + (long long)(r * p.Hq + hh) * 16 * DH;
     else
       dst = reinterpret_cast<T*>(p.blk) + r * page_elems + (long long)(hh - p.Hq) * 16 * DH;
-    for (int e = t; e < 16 * H2; e += blockDim.x) {
-      const int i = e / H2;
-      const int j = e - i * H2;
-      float y1 = 0.f, y2 = 0.f;
+    for (int e = t; e < 16 * QUADS; e += blockDim.x) {
+      const int i = e / QUADS;
+      const int j = (e - i * QUADS) * 4;
+      f32x4 y1 = zero, y2 = zero;
       if (i < p.B) {
-        float x1, x2;
+        f32x4 x1, x2;
         rd2((long long)i * ld + j, (long long)i * ld + j + H2, x1, x2);
         const long long ti = (long long)(n + i) * H2 + j;
-        const float c = p.cos_t[ti], s = p.sin_t[ti];
-        y1 = x1 * c - x2 * s;
-        y2 = x2 * c + x1 * s;
+        const f32x4 c = *reinterpret_cast<const f32x4*>(p.cos_t + ti);
+        const f32x4 sn = *reinterpret_cast<const f32x4*>(p.sin_t + ti);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          y1[k] = x1[k] * c[k] - x2[k] * sn[k];
+          y2[k] = x2[k] * c[k] + x1[k] * sn[k];
+        }
       }
-      dst[i * DH + j] = from_f<T>(y1);
-      dst[i * DH + j + H2] = from_f<T>(y2);
+      st4(dst + i * DH + j, y1);
+      st4(dst + i * DH + j + H2, y2);
     }
   } else {
+    constexpr int DPT = DH / 16;  // dims per thread
     const int g = hh - p.Hq - p.Hkv;
     T* dst = reinterpret_cast<T*>(p.blk) + r * page_elems + (long long)(p.Hkv + g) * 16 * DH;
-    for (int e = t; e < 16 * DH; e += blockDim.x) {
-      const int i = e & 15;
-      const int d = e >> 4;
-      float x = 0.f, unused;
-      if (i < p.B) rd2((long long)i * ld + d, (long long)i * ld + d, x, unused);
-      dst[d * 16 + i] = from_f<T>(x);
-    }
+    const int i = t & 15;
+    const int d0 = (t >> 4) * DPT;
+    f32x4 x1 = zero, x2 = zero;
+    if (i < p.B) rd2((long long)i * ld + d0, (long long)i * ld + d0 + (DPT > 4 ? 4 : 0), x1, x2);
+#pragma unroll
+    for (int k = 0; k < DPT; ++k) dst[(d0 + k) * 16 + i] = from_f<T>(k < 4 ? x1[k] : x2[k - 4]);
   }
 }
 
@@ -753,9 +769,9 @@ template <typename T>
 void qkv_post_t(int dh, int n_req, const QkvPostParams& p, const SlotArgs& sl, hipStream_t s) {
   dim3 grid(n_req, p.Hq + 2 * p.Hkv);
   if (dh == 128)
-    hipLaunchKernelGGL((k_qkv_post<T, 128>), grid, dim3(1024), 0, s, p, sl);
+    hipLaunchKernelGGL((k_qkv_post<T, 128>), grid, dim3(256), 0, s, p, sl);
   else
-    hipLaunchKernelGGL((k_qkv_post<T, 64>), grid, dim3(512), 0, s, p, sl);
+    hipLaunchKernelGGL((k_qkv_post<T, 64>), grid, dim3(256), 0, s, p, sl);
 }
 
 template <typename T>
