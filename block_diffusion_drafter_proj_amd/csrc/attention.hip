@@ -688,6 +688,65 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p) {
   for (int c = 0; c < C; ++c) out[c] = from_f<T>(acc[c] * inv);
 }
 
+// The same merge with two rows per wave (lanes 0-31 row q, lanes 32-63 row
+// q + 1 of the same request and head) and 4 consecutive output columns per
+// lane, so every partial read is 16 bytes; a half-wave holds the (max, sum)
+// of up to 32 splits.  Each output element sees the same operations in the
+// same order as in k_combine.
+template <typename T>
+__global__ __launch_bounds__(256) void k_combine2(CombineParams p) {
+  constexpr int DH = 128;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int half = lane >> 5, hl = lane & 31;
+  const int q = (wid & 7) * 2 + half;
+  const int rh = wid >> 3;  // r * Hq + h
+  if (rh >= p.n_rh) return;
+  const bool live = q < p.B;
+  const int r = rh / p.Hq, h = rh - r * p.Hq;
+  const int S = p.n_splits;
+  const int ns = p.n_split[r];
+  if (ns <= 1) return;  // written by the attention kernel
+  const long long pb = (long long)rh * S * 16 + q;
+  const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + pb;
+  const float* po = p.part_o + pb * DH + hl * 4;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const float2 mine = live && hl < ns ? ml[hl * 16] : make_float2(-INFINITY, 0.f);
+  f32x4 v[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] = live && k < ns ? *reinterpret_cast<const f32x4*>(po + (long long)k * 16 * DH) : zero;
+  float mx = mine.x;
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  const float w_mine = mine.x == -INFINITY ? 0.f : expf(mine.x - mx);
+  const int base = half * 32;
+  float L = 0.f;
+  for (int s = 0; s < ns; ++s) L += __shfl(mine.y, base + s, 64) * __shfl(w_mine, base + s, 64);
+  f32x4 acc = zero;
+  for (int s0 = 0; s0 < ns; s0 += 16) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        v[k] = live && s0 + k < ns ? *reinterpret_cast<const f32x4*>(po + (long long)(s0 + k) * 16 * DH) : zero;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float w = __shfl(w_mine, base + ((s0 + k) & 31), 64);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (s0 + k < ns) acc[c] += w * v[k][c];
+    }
+  }
+  if (!live) return;
+  const float inv = 1.0f / L;
+  const int m = r * p.B + q, k = h * DH + hl * 4;  // 4 consecutive k stay contiguous
+  typename Vec4<T>::type o;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o[c] = from_f<T>(acc[c] * inv);
+  T* out = reinterpret_cast<T*>(p.out) + (p.out_packed ? frag_index(m, k, p.ldo) : (long long)m * p.ldo + k);
+  *reinterpret_cast<typename Vec4<T>::type*>(out) = o;
+}
+
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_scatter(ScatterParams p) {
   const int row = blockIdx.x;
@@ -808,7 +867,12 @@ void attn_ring_t(int n_req, const AttnParams& p, const SlotArgs& sl, hipStream_t
 template <typename T>
 void combine_t(int dh, const CombineParams& p, hipStream_t s) {
   dim3 grid((p.n_rh * 16 + 3) / 4);
-  if (dh == 128)
+  // two rows per wave pays where the merge streams many partials; a small
+  // merge (one request: 32 rows of heads) is latency-bound and keeps one row
+  // per wave, which spreads it over twice the workgroups
+  if (dh == 128 && p.n_splits <= 32 && p.n_rh >= 256)
+    hipLaunchKernelGGL((k_combine2<T>), dim3(p.n_rh * 2), dim3(256), 0, s, p);
+  else if (dh == 128)
     hipLaunchKernelGGL((k_combine<T, 128>), grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((k_combine<T, 64>), grid, dim3(256), 0, s, p);
