@@ -320,13 +320,14 @@ void launch_cfg(const GemmParams& p, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm_tile<C, EPI>), dim3(groups * 8 * n_mt), dim3(C::NW * 64), 0, s, p);
 }
 
-// Above 128 rows: 256x256 tiles, 8 waves of 128x64 (two per SIMD), one
-// 32-wide k step per stage and a 5-stage ring (all 160 KB of LDS; three
-// stages in flight while one is multiplied).  Per stage a CU moves 96
-// fragment reads and 32 KB of direct loads through LDS against 1024 MFMA
-// cycles per SIMD, so operand bytes per flop set the speed; two waves per
-// SIMD keep the matrix cores busy across each stage's barrier, which one
-// larger wave per SIMD does not.
+// Above 128 rows: 256x256 tiles, 16 waves of 64x64 (four per SIMD, 128
+// VGPRs each), one 32-wide k step per stage and a 5-stage ring (all 160 KB
+// of LDS; three stages in flight while one is multiplied).  Per stage a CU
+// moves 128 fragment reads and 32 KB of direct loads through LDS against
+// 1024 MFMA cycles per SIMD.  More waves per SIMD keep the matrix cores busy
+// across each stage's barrier: one wave of 128x128 per SIMD lost 15-30 %
+// against two of 128x64, and four of 64x64 run the vocabulary product 5 %
+// faster than two.
 // Up to 128 rows (and for top-16, whose sort needs the registers): 128x128
 // tiles, 4 waves of 64x64, two k steps per stage, 3 stages.
 // 256x192 tiles (8 waves of 64x96, 64-deep k stages, double buffered in
@@ -339,7 +340,7 @@ void launch_cfg(const GemmParams& p, hipStream_t s) {
 // across N keep the top-16 list count per row equal to CfgSmall's.
 typedef TileCfg<64, 128, 2, 2, 2, 3> Cfg64;
 typedef TileCfg<128, 128, 2, 2, 2, 3> CfgSmall;
-typedef TileCfg<256, 256, 2, 4, 1, 5> CfgBig;
+typedef TileCfg<256, 256, 4, 4, 1, 5> CfgBig;
 typedef TileCfg<256, 192, 4, 2, 2, 2> CfgWide;
 // 256x128 (8 waves of 128x32, 24 KB stages, 6-deep ring): for a split-K
 // product whose K is short and whose columns fit 256 tiles, this grid fills
