@@ -39,8 +39,9 @@ Output is one JSON line:
     accept length of 5 and 6 (the pages' DFlash-2 range), taken from the
     measured cycle time;
   * the roofline of the dominant kernel class, timed with HIP events on the
-    call's stream during the timed region and priced against HBM or MFMA,
-    whichever bounds it;
+    call's stream in one timed cycle of every four (each event record idles
+    the stream for a few microseconds, so the other cycles run without
+    them) and priced against HBM or MFMA, whichever bounds it;
   * the CPU oracle, timed on the host.
 """
 from __future__ import annotations
@@ -63,6 +64,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense, MI355X published figures
 CSRC = os.path.join(ROOT, "block_diffusion_drafter_proj_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
+TIME_EVERY = 4  # the dominant kernel class is timed in one timed cycle of this many
 
 GEMM_CLASSES = ("qkv_gemm", "o_gemm", "gateup_gemm", "down_gemm", "lm_head")
 
@@ -344,10 +346,12 @@ def main():
     for i in range(args.warmup):
         cycle(i)
     torch.cuda.synchronize()
-    Bnd.dflash_profile_begin(dr.h, 1 << Bnd.KERNELS.index(dominant))
+    dom_bit = 1 << Bnd.KERNELS.index(dominant)
+    Bnd.dflash_profile_begin(dr.h, dom_bit)
     t0 = time.perf_counter()
     e0.record()
     for i in range(args.warmup, n_cycles):
+        Bnd.dflash_profile_mask(dr.h, dom_bit if (i - args.warmup) % TIME_EVERY == 0 else 0)
         cycle(i)
     e1.record()
     torch.cuda.synchronize()

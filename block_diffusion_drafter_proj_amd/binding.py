@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
             "dflash_check": (i32, [vp, vp]),
             "dflash_profile_begin": (i32, [vp, ctypes.c_uint32]),
             "dflash_profile_end": (i32, [vp, ctypes.POINTER(ctypes.c_float), pi32]),
+            "dflash_profile_mask": (i32, [vp, ctypes.c_uint32]),
         }
         for name, (res, args) in sigs.items():
             f = getattr(L, name)
@@ -193,6 +194,10 @@ KERNELS = ["fc_gemm", "norm", "kv_gemm", "scatter", "qkv_gemm", "qkv_post", "att
 
 def dflash_profile_begin(h: int, mask: int) -> None:
     _check(lib().dflash_profile_begin(ctypes.c_void_p(h), mask))
+
+
+def dflash_profile_mask(h: int, mask: int) -> None:
+    _check(lib().dflash_profile_mask(ctypes.c_void_p(h), mask))
 
 
 def dflash_profile_end(h: int) -> dict:

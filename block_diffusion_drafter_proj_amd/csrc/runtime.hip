@@ -1028,6 +1028,12 @@ dflash_status dflash_profile_begin(dflash_handle* h, uint32_t mask) {
   return DFLASH_OK;
 }
 
+dflash_status dflash_profile_mask(dflash_handle* h, uint32_t mask) {
+  if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
+  h->prof.mask = mask & ((1u << DFLASH_KERNEL_COUNT) - 1);
+  return DFLASH_OK;
+}
+
 dflash_status dflash_profile_end(dflash_handle* h, float* total_ms, int32_t* launches) {
   if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
   if (!total_ms || !launches) return fail(DFLASH_E_INVALID, "output arrays are NULL");

@@ -279,6 +279,13 @@ typedef enum {
 dflash_status dflash_profile_begin(dflash_handle *h, uint32_t mask);
 dflash_status dflash_profile_end(dflash_handle *h, float *total_ms, int32_t *launches);
 
+/* Replaces the set of timed classes of a running measurement without
+ * discarding the events recorded since dflash_profile_begin, so a run can
+ * time one call in n (mask 0 in between) and keep the events' own cost
+ * (each record briefly idles the stream) off the other calls.  Returns
+ * DFLASH_E_INVALID for a NULL handle; bits of unknown classes are ignored. */
+dflash_status dflash_profile_mask(dflash_handle *h, uint32_t mask);
+
 /* Synchronises `stream` and reads the sticky device error word; returns
  * DFLASH_E_DEVICE (and clears the word) if a kernel recorded an
  * out-of-range token id, else DFLASH_OK. */

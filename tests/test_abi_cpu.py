@@ -177,3 +177,17 @@ def test_null_handle_is_rejected():
     assert lib.dflash_context_length(None, 0) == -1
     out = ctypes.c_void_p()
     assert lib.dflash_create(None, None, None, None, None, ctypes.byref(out)) == B.E_INVALID
+
+
+def test_profiling_calls_without_launches(handle):
+    """The timing calls validate their handle and, with no launch bracketed
+    in between, report no class (nothing to synchronise on)."""
+    h, _ = handle
+    lib = B.lib()
+    assert lib.dflash_profile_begin(None, 1) == B.E_INVALID
+    assert lib.dflash_profile_mask(None, 1) == B.E_INVALID
+    assert lib.dflash_profile_end(None, None, None) == B.E_INVALID
+    B.dflash_profile_begin(h, 1 << B.KERNELS.index("lm_head"))
+    B.dflash_profile_mask(h, 0)
+    B.dflash_profile_mask(h, 0xFFFFFFFF)  # bits of unknown classes are ignored
+    assert B.dflash_profile_end(h) == {}
