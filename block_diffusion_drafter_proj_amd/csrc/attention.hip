@@ -644,19 +644,22 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p) {
   const int r = rh / p.Hq, h = rh - r * p.Hq;
   const int S = p.n_splits;
   const int ns = p.n_split[r];
-  if (ns <= 1) return;  // written by the attention kernel
   const long long pb = (long long)rh * S * 16 + q;
   const float2* ml = reinterpret_cast<const float2*>(p.part_ml) + pb;
   const float* po = p.part_o + pb * DH + lane * C;
   // lane s holds split s's (max, sum); weights are broadcast by shuffles.  The
-  // first 16 partial rows are requested together with the (max, sum) pairs,
-  // so the merge waits for one memory round trip, not two.
-  const float2 mine = lane < ns ? ml[lane * 16] : make_float2(-INFINITY, 0.f);
+  // pairs and the first 16 partial rows are requested together with the
+  // split count (bounded by the allocated count S, which needs no load), so
+  // the merge waits for one memory round trip; entries past the request's
+  // own count are masked once it arrives.
+  const float2 raw = lane < S ? ml[lane * 16] : make_float2(-INFINITY, 0.f);
   float v[16][C];
 #pragma unroll
   for (int k = 0; k < 16; ++k)
 #pragma unroll
-    for (int c = 0; c < C; ++c) v[k][c] = k < ns ? po[(long long)k * 16 * DH + c] : 0.f;
+    for (int c = 0; c < C; ++c) v[k][c] = k < S ? po[(long long)k * 16 * DH + c] : 0.f;
+  if (ns <= 1) return;  // written by the attention kernel
+  const float2 mine = lane < ns ? raw : make_float2(-INFINITY, 0.f);
   float mx = mine.x;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
