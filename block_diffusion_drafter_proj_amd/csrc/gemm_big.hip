@@ -352,8 +352,9 @@ static_assert(Cfg64::WN == CfgSmall::WN && Cfg64::BN == CfgSmall::BN, "top-16 li
 enum { CFG_SMALL, CFG_BIG, CFG_WIDE, CFG_64, CFG_TALL };
 
 // Workgroups with real work and the split-K factor of a partial-output
-// product: the smallest power of two that gives at least one workgroup per CU
-// while keeping 8 or more 64-wide k blocks per split.
+// product: the largest split whose grid still fits one round of the CUs (a
+// grid of more than one round only adds a partly idle round and fp32 planes
+// for the consumer to sum), keeping 8 or more 64-wide k blocks per split.
 template <typename C, int EPI>
 int cfg_work(int M, int tiles, int P) {
   return ((M + C::BM - 1) / C::BM) * col_tiles<C::BN, EPI>(tiles) * P;
@@ -361,8 +362,8 @@ int cfg_work(int M, int tiles, int P) {
 template <typename C>
 int cfg_split(int M, int tiles, int K) {
   const int wgs = cfg_work<C, EPI_PARTIAL>(M, tiles, 1);
-  int P = 1;
-  while (wgs * P < 256 && K / (64 * 2 * P) >= 8) P *= 2;
+  int P = wgs >= 256 ? 1 : 256 / wgs;
+  while (P > 1 && K / (64 * P) < 8) --P;
   return P;
 }
 // share of the CU slots of the last round that has work (one workgroup per CU)
