@@ -755,75 +755,96 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterParams p) {
   const int row = blockIdx.x;
   const int l = blockIdx.y;
   const int t = threadIdx.x;
-  constexpr int H2 = DH / 2;
+  constexpr int H2 = DH / 2, KQ = H2 / 4, VQ = DH / 4;  // 4-element groups per K half-head and V head
   if (row == 0 && l == 0 && t < p.n_req) {
     const InjectReq q = p.req[t];
     p.state[q.slot].ctx_len = q.pos0 + q.count;
   }
-  // the request owning this row: binary search over the row starts
-  int ri = 0, rhi = p.n_req - 1;
-  while (ri < rhi) {
-    const int mid = (ri + rhi + 1) >> 1;
-    if (row >= p.req[mid].row_start)
-      ri = mid;
-    else
-      rhi = mid - 1;
-  }
-  const InjectReq rq = p.req[ri];
-  const int pos = rq.pos0 + (row - rq.row_start);
-  if (p.window > 0 && pos < rq.final_ctx - p.window) return;
-  const int n_pages = p.state[rq.slot].n_pages;
-  const int lp = pos / 16;
-  const int idx = p.window > 0 ? lp % n_pages : lp;
-  const int page = p.page_table[(long long)rq.slot * p.pt_stride + idx];
-  if (page < 0 || page >= p.max_pages) {
-    if (t == 0) atomicOr(p.err, 4u);
-    return;
-  }
-  const long long page_elems = 2LL * p.Hkv * 16 * DH;
-  T* pg = reinterpret_cast<T*>(p.pool) + l * p.layer_stride + page * page_elems;
   const float* src = p.kv + (long long)row * (p.L * 2 * p.Hkv * DH) + (long long)l * 2 * p.Hkv * DH;
   const long long plane = (long long)p.rows * p.L * 2 * p.Hkv * DH;
-  // sums of the split-K partials at two offsets; every load of a chunk of 4
-  // partials is issued before any is added (same order of addition)
-  auto rd2 = [&](int off1, int off2, float& x1, float& x2) {
-    x1 = 0.f;
-    x2 = 0.f;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const int nk = p.Hkv * KQ, nv = p.Hkv * VQ;
+  // Rounds of 2 groups per thread and kind.  The row's K/V sums depend on the
+  // row alone, so their 16-byte loads are issued before the request lookup
+  // and the page-table read, which then overlap them; split-K parts are
+  // summed in order, every load of a chunk of 4 parts before any addition.
+  for (int e0 = 0; e0 < nv; e0 += 512) {
+    f32x4 k1[2], k2[2], v[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) k1[i] = k2[i] = v[i] = zero;
     for (int q0 = 0; q0 < p.n_part; q0 += 4) {
-      float a[4], b[4];
+      f32x4 a[4][2], b[4][2], c[4][2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool ok = q0 + q < p.n_part;
-        a[q] = ok ? src[(q0 + q) * plane + off1] : 0.f;
-        b[q] = ok ? src[(q0 + q) * plane + off2] : 0.f;
-      }
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (q0 + q < p.n_part) {
-          x1 += a[q];
-          x2 += b[q];
+        for (int i = 0; i < 2; ++i) {
+          const bool ok = q0 + q < p.n_part;
+          const float* sp = src + (q0 + q) * plane;
+          const int e = e0 + t + 256 * i;
+          const int gk = e / KQ, jk = (e - gk * KQ) * 4;
+          const int gv = e / VQ, dv = (e - gv * VQ) * 4;
+          a[q][i] = ok && e < nk ? *reinterpret_cast<const f32x4*>(sp + gk * DH + jk) : zero;
+          b[q][i] = ok && e < nk ? *reinterpret_cast<const f32x4*>(sp + gk * DH + jk + H2) : zero;
+          c[q][i] = ok && e < nv ? *reinterpret_cast<const f32x4*>(sp + (p.Hkv + gv) * DH + dv) : zero;
         }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (q0 + q < p.n_part) {
+            k1[i] += a[q][i];
+            k2[i] += b[q][i];
+            v[i] += c[q][i];
+          }
+    }
+    // the request owning this row: binary search over the row starts
+    int ri = 0, rhi = p.n_req - 1;
+    while (ri < rhi) {
+      const int mid = (ri + rhi + 1) >> 1;
+      if (row >= p.req[mid].row_start)
+        ri = mid;
+      else
+        rhi = mid - 1;
+    }
+    const InjectReq rq = p.req[ri];
+    const int pos = rq.pos0 + (row - rq.row_start);
+    if (p.window > 0 && pos < rq.final_ctx - p.window) return;
+    const int n_pages = p.state[rq.slot].n_pages;
+    const int lp = pos / 16;
+    const int idx = p.window > 0 ? lp % n_pages : lp;
+    const int page = p.page_table[(long long)rq.slot * p.pt_stride + idx];
+    if (page < 0 || page >= p.max_pages) {
+      if (t == 0 && e0 == 0) atomicOr(p.err, 4u);
+      return;
+    }
+    const long long page_elems = 2LL * p.Hkv * 16 * DH;
+    T* pg = reinterpret_cast<T*>(p.pool) + l * p.layer_stride + page * page_elems;
+    const int slotpos = pos & 15;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = e0 + t + 256 * i;
+      if (e < nk) {  // K with RoPE at the row's position, [16 positions][dh] per head
+        const int g = e / KQ, j = (e - g * KQ) * 4;
+        const long long ti = (long long)pos * H2 + j;
+        const f32x4 cs = *reinterpret_cast<const f32x4*>(p.cos_t + ti);
+        const f32x4 sn = *reinterpret_cast<const f32x4*>(p.sin_t + ti);
+        typename Vec4<T>::type o1, o2;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          o1[k] = from_f<T>(k1[i][k] * cs[k] - k2[i][k] * sn[k]);
+          o2[k] = from_f<T>(k2[i][k] * cs[k] + k1[i][k] * sn[k]);
+        }
+        T* kd = pg + (long long)(g * 16 + slotpos) * DH + j;
+        *reinterpret_cast<typename Vec4<T>::type*>(kd) = o1;
+        *reinterpret_cast<typename Vec4<T>::type*>(kd + H2) = o2;
+      }
+      if (e < nv) {  // V transposed, [dh][16 positions] per head
+        const int g = e / VQ, d = (e - g * VQ) * 4;
+        T* vd = pg + (long long)(p.Hkv + g) * 16 * DH + slotpos;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vd[(d + k) * 16] = from_f<T>(v[i][k]);
       }
     }
-  };
-  const int slotpos = pos & 15;
-  for (int e = t; e < p.Hkv * H2; e += 256) {
-    const int g = e / H2;
-    const int j = e - g * H2;
-    float x1, x2;
-    rd2(g * DH + j, g * DH + j + H2, x1, x2);
-    const long long ti = (long long)pos * H2 + j;
-    const float c = p.cos_t[ti], s = p.sin_t[ti];
-    T* kd = pg + (long long)(g * 16 + slotpos) * DH;
-    kd[j] = from_f<T>(x1 * c - x2 * s);
-    kd[j + H2] = from_f<T>(x2 * c + x1 * s);
-  }
-  for (int e = t; e < p.Hkv * DH; e += 256) {
-    const int g = e / DH;
-    const int d = e - g * DH;
-    float x, unused;
-    rd2((p.Hkv + g) * DH + d, (p.Hkv + g) * DH + d, x, unused);
-    pg[(long long)(p.Hkv + g) * 16 * DH + d * 16 + slotpos] = from_f<T>(x);
   }
 }
 
