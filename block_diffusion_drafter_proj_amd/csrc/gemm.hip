@@ -125,6 +125,19 @@ __global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(Gemm
     gate_v[it] = 0.f;
     best[it] = 0ull;
   }
+  // EPI_ROPE: position of block row 0 of each epilogue element's request,
+  // requested while the weights stream so the epilogue does not wait for the
+  // slot and state reads after the reduction
+  int rope_n[EIT];
+#pragma unroll
+  for (int it = 0; it < EIT; ++it) {
+    rope_n[it] = 0;
+    if (EPI == EPI_ROPE) {
+      const int e = t + it * (int)blockDim.x;
+      const int em = m_base + (e >> 8) * 16 + ((e >> 4) & 15);
+      if (e < 256 * MT && em < p.M) rope_n[it] = p.rope.state[p.rope.slots[em / p.rope.B]].ctx_len + 1;
+    }
+  }
 
   for (int i = 0; i < n_sub; i += NBUF) {
 #pragma unroll
@@ -186,7 +199,7 @@ __global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(Gemm
               const float x1 = gate_v[it];
               T* o;
               if (head < ro.Hq + ro.Hkv) {
-                const long long ti = (long long)(ro.state[ro.slots[r]].ctx_len + 1 + i) * h2 + j;
+                const long long ti = (long long)(rope_n[it] + i) * h2 + j;
                 const float c = ro.cos_t[ti], sn = ro.sin_t[ti];
                 if (head < ro.Hq)
                   o = reinterpret_cast<T*>(ro.qb) + ((long long)(r * ro.Hq + head) * 16 + i) * dh;
