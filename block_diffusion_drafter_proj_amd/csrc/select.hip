@@ -103,6 +103,67 @@ __global__ __launch_bounds__(256) void k_logit_select(LogitSelParams p) {
   }
 }
 
+// The same selection with 16-byte reads, for a vocabulary that is a multiple
+// of 4 (every row then starts 16-byte aligned): wave w takes the 256-column
+// blocks w, w+4, ... of the chunk, each lane 4 consecutive columns of a
+// block, and the loads of up to 4 planes are all issued before any sum.  The
+// selected keys do not depend on the order in which columns are visited.
+template <bool TOPK>
+__global__ __launch_bounds__(256) void k_logit_select4(LogitSelParams p) {
+  constexpr int NB = kSelChunk / 1024;  // 256-column blocks per wave
+  __shared__ unsigned long long red[4];
+  const int chunk = blockIdx.x, row = blockIdx.y;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, i16 = lane & 15;
+  const long long plane = (long long)p.M * p.N;
+  const float* src = p.part + (long long)row * p.N;
+  const int c0 = chunk * kSelChunk + wave * 256 + lane * 4;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 v[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) v[b] = zero;
+  for (int q0 = 0; q0 < p.n_part; q0 += 4) {
+    f32x4 x[4][NB];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int n = c0 + 1024 * b;
+        x[q][b] = q0 + q < p.n_part && n < p.N ? *reinterpret_cast<const f32x4*>(src + (q0 + q) * plane + n) : zero;
+      }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (q0 + q < p.n_part) v[b] += x[q][b];
+  }
+  unsigned long long best = 0ull;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int n = c0 + 1024 * b + k;
+      const bool ok = n < p.N;
+      if (ok && p.dbg) p.dbg[(long long)row * p.ld_dbg + n] = v[b][k];
+      const unsigned long long key = ok ? argmax_key(v[b][k], n, p.N) : 0ull;
+      if (TOPK)
+        best = merge16_desc(best, sort16_desc(key, i16), i16);
+      else
+        best = key_max(best, key);
+    }
+  }
+  if (TOPK) {
+    best = merge16_desc(best, __shfl_xor(best, 16, 64), i16);
+    best = merge16_desc(best, __shfl_xor(best, 32, 64), i16);
+    if (lane < 16) p.lists[((long long)row * p.n_lists + chunk * 4 + wave) * 16 + lane] = best;
+  } else {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) best = key_max(best, __shfl_xor(best, o, 64));
+    if (lane == 0) red[wave] = best;
+    __syncthreads();
+    if (t == 0) atomicMax(p.keys + row, key_max(key_max(red[0], red[1]), key_max(red[2], red[3])));
+  }
+}
+
 // Merge two lists sorted descending into the 16 largest, sorted descending.
 __device__ __forceinline__ void merge_lists(const unsigned long long* a, const unsigned long long* b,
                                             unsigned long long* out) {
@@ -164,10 +225,16 @@ __global__ __launch_bounds__(256) void k_topk_merge(TopkParams p) {
 void launch_logit_select(bool topk, const LogitSelParams& p, hipStream_t s) {
   if (p.M <= 0) return;
   const dim3 grid((p.N + kSelChunk - 1) / kSelChunk, p.M);
-  if (topk)
+  if (p.N % 4 == 0) {
+    if (topk)
+      hipLaunchKernelGGL(k_logit_select4<true>, grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_logit_select4<false>, grid, dim3(256), 0, s, p);
+  } else if (topk) {
     hipLaunchKernelGGL(k_logit_select<true>, grid, dim3(256), 0, s, p);
-  else
+  } else {
     hipLaunchKernelGGL(k_logit_select<false>, grid, dim3(256), 0, s, p);
+  }
 }
 
 void launch_topk_merge(const TopkParams& p, hipStream_t s) {

@@ -210,7 +210,11 @@ def test_draft_parity_lockstep(name):
     ("small_batch", {"batch": 4}),                     # exactly 64 rows: skinny 64-row block and tiled kernel
     ("small_conv", {"batch": 3, "ctx": None, "ctx_range": (60, 300)}),  # 48 rows: split-K logits, top-16
     ("small_block10", {"batch": 7, "ctx": None, "ctx_range": (40, 400)}),  # 70 rows: tiled, last 16-row tile partial
-], ids=["block1", "batch5_block1", "rows64", "conv_rows48", "block10_rows70"])
+    # a vocabulary that is a multiple of 4: the selection pass over split-K
+    # partial logits reads 16 bytes per lane (argmax, then top-16)
+    ("small_batch", {"batch": 4, "vocab": 3000}),
+    ("small_conv", {"batch": 3, "ctx": None, "ctx_range": (60, 300), "vocab": 3000}),
+], ids=["block1", "batch5_block1", "rows64", "conv_rows48", "block10_rows70", "rows64_vocab4", "conv_rows48_vocab4"])
 def test_draft_parity_lockstep_shapes(name, over):
     _lockstep(name, **over)
 
