@@ -6,8 +6,8 @@
 //   inject : per chunk of rows  fc GEMM (virtual concat of the n_feat hidden
 //            arrays) -> RMSNorm -> all-layer K/V GEMM -> RoPE + page scatter
 //   draft  : per layer  RMSNorm (+ residual) -> QKV GEMM -> q/k RoPE ->
-//            attention (split over pages, splits merged by the last
-//            workgroup) -> O GEMM -> RMSNorm (+ residual) -> gate/up GEMM +
+//            attention (split over pages; a separate k_combine launch merges
+//            the splits of requests that have more than one) -> O GEMM -> RMSNorm (+ residual) -> gate/up GEMM +
 //            SwiGLU -> down GEMM; then RMSNorm (+ residual) -> LM head GEMM
 //            + argmax -> decode ids.  GEMMs split over K leave fp32 partials
 //            that the next kernel adds in a fixed order.

@@ -179,10 +179,12 @@ def test_full_size_coder_b64_sampled():
     1024 rows (tiled GEMMs, batched attention).  Every request is injected
     from hidden states drawn on the device by synth's seeded generator (the
     same generator bench.py uses); the oracle gets the host copies of the
-    sampled requests' rows.  Sampled outputs: the two shortest requests in
-    full (K/V of every position and layer, the free-running forward, and exact
-    tokens under per-layer teacher forcing), and the K/V of 16 positions in
-    the middle of the longest request."""
+    sampled requests' rows.  Sampled outputs, each in full (K/V of every
+    position and layer, the free-running forward, and exact tokens under
+    per-layer teacher forcing): the two shortest requests (one attention
+    split each, whose output skips the split merge) and the longest (about
+    8,100 positions in 8 splits of at most 64 pages, merged by the
+    two-rows-per-wave merge that most of this batch goes through)."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from block_diffusion_drafter_proj_amd.drafter import Drafter
@@ -203,8 +205,7 @@ def test_full_size_coder_b64_sampled():
     dr = Drafter(shape, w, max_batch=n, max_pages=total, max_pages_per_req=max(ppr),
                  max_position=max(ctxs) + 4 * B + 32, max_inject_rows=1024, poison_kv=True)
     order = np.argsort(ctxs)
-    sampled = [int(order[0]), int(order[1])]
-    longest = int(order[-1])
+    sampled = [int(order[0]), int(order[1]), int(order[-1])]
     H = {}
     for r in range(n):
         dr.bind(r, pages[r])
@@ -212,23 +213,11 @@ def test_full_size_coder_b64_sampled():
         dr.inject([r], [ctxs[r]], h)
         if r in sampled:
             H[r] = [x.float().cpu().numpy() for x in h]
-        if r == longest:
-            p0 = (ctxs[r] // 32) * 16
-            H[r] = (p0, [x[p0:p0 + 16].float().cpu().numpy() for x in h])
         del h
     torch.cuda.synchronize()
     print(f"[coder_b64] gpu inject done; sampled {sampled} ctx {[ctxs[r] for r in sampled]}", flush=True)
     view = dr.kv_view()
     o = DraftOracle(shape, w)
-    # the longest request: 16 positions from a request bound at that position
-    p0, rows = H[longest]
-    st = o.new_request(p0)
-    o.inject(st, rows)
-    for l in range(L):
-        kg, vg = unpack_kv(view, l, pages[longest], list(range(p0, p0 + 16)))
-        kr, vr = o.visible(st, l)
-        assert_rows_close(kg, kr, what=f"K layer {l} req {longest}")
-        assert_rows_close(vg, vr, what=f"V layer {l} req {longest}")
     states = {}
     for r in sampled:
         st = o.new_request()

@@ -214,9 +214,33 @@ def test_draft_parity_lockstep(name):
     # partial logits reads 16 bytes per lane (argmax, then top-16)
     ("small_batch", {"batch": 4, "vocab": 3000}),
     ("small_conv", {"batch": 3, "ctx": None, "ctx_range": (60, 300), "vocab": 3000}),
-], ids=["block1", "batch5_block1", "rows64", "conv_rows48", "block10_rows70", "rows64_vocab4", "conv_rows48_vocab4"])
+    # 80 rows with top-16: the tiled LM head's top-16 epilogue and the merge
+    # of its per-workgroup lists
+    ("small_conv", {"batch": 5, "ctx": None, "ctx_range": (60, 300)}),
+    # 32 requests x 8 query heads = 256 (request, head) pairs, 4 attention
+    # splits per request: the two-rows-per-wave split merge with up to 4 splits
+    ("small_batch", {"batch": 32, "ctx": None, "ctx_range": (200, 900)}),
+], ids=["block1", "batch5_block1", "rows64", "conv_rows48", "block10_rows70", "rows64_vocab4", "conv_rows48_vocab4",
+        "conv_rows80_topk_tiled", "batch32_merge_splits"])
 def test_draft_parity_lockstep_shapes(name, over):
+    if over.get("batch") == 32:
+        # premise: every request has several splits (target 256 / (32 * 2) = 4)
+        shape = synth.config(name, **over)
+        assert min(_attn_splits(shape, c) for c in synth.context_lengths(shape)) >= 2
     _lockstep(name, **over)
+
+
+def _attn_splits(shape, ctx):
+    """Attention splits of a request with `ctx` visible positions (the
+    library's plan: about 256 / (batch * Hkv) splits per request, at most 64
+    pages each, the block page counted as one)."""
+    target = min(64, max(1, 256 // (shape["batch"] * shape["n_kv_heads"])))
+    units = (ctx - 1) // 16 + 1 + 1 if ctx > 0 else 1
+    if units <= 1:
+        return 1
+    n = max((units + 63) // 64, min(target, units))
+    pps = (units + n - 1) // n
+    return (units + pps - 1) // pps
 
 
 def _lockstep(name, **over):

@@ -167,6 +167,43 @@ def test_rope_is_complex_rotation():
                                np.linalg.norm(x, axis=-1), rtol=1e-12)
 
 
+def test_rope_frequency_schedule_by_hand():
+    """The frequency of pair j is theta^(-2j/dh), checked on angles worked out
+    by hand, with textbook values of cos(1) and sin(1):
+
+    * dh 4, theta 1e4: pair 1 turns at 1e4^(-2/4) = 1/100 rad per position, so
+      position 100 turns it by 1 rad; pair 0 turns at 1 rad per position.
+    * dh 128, theta 1e6 (the Qwen3-8B-shaped draft): pair 32 turns at
+      1e6^(-64/128) = 1e-3 rad per position, so position 1000 turns it by 1 rad.
+
+    A slip in the exponent (theta^(-j/dh), theta^(-2j/(dh-2)), or pairs of
+    adjacent channels instead of halves) moves these off the unit circle
+    points below."""
+    cos1, sin1 = 0.5403023058681398, 0.8414709848078965  # cos(1), sin(1)
+    # dh 4: x = e_1 (real part of pair 1) at position 100 -> (cos 1, sin 1) on channels 1, 3
+    x = np.zeros((1, 1, 4))
+    x[0, 0, 1] = 1.0
+    y = rope(x, np.array([100]), 1.0e4)[0, 0]
+    np.testing.assert_allclose(y, [0.0, cos1, 0.0, sin1], rtol=0, atol=1e-13)
+    # the imaginary part turns the other way round: e_3 -> (-sin 1, cos 1) on channels 1, 3
+    x = np.zeros((1, 1, 4))
+    x[0, 0, 3] = 1.0
+    y = rope(x, np.array([100]), 1.0e4)[0, 0]
+    np.testing.assert_allclose(y, [0.0, -sin1, 0.0, cos1], rtol=0, atol=1e-13)
+    # pair 0 at position 1 turns by 1 rad as well
+    x = np.zeros((1, 1, 4))
+    x[0, 0, 0] = 1.0
+    y = rope(x, np.array([1]), 1.0e4)[0, 0]
+    np.testing.assert_allclose(y, [cos1, 0.0, sin1, 0.0], rtol=0, atol=1e-13)
+    # dh 128, theta 1e6: pair 32 (channels 32 and 96) at position 1000
+    x = np.zeros((1, 1, 128))
+    x[0, 0, 32] = 1.0
+    y = rope(x, np.array([1000]), 1.0e6)[0, 0]
+    expect = np.zeros(128)
+    expect[32], expect[96] = cos1, sin1
+    np.testing.assert_allclose(y, expect, rtol=0, atol=1e-12)
+
+
 def test_rope_relative_position():
     rng = np.random.default_rng(4)
     q = rng.standard_normal((1, 1, 128))
