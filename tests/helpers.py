@@ -2,16 +2,17 @@
 
 Comparison rules for floating point (GPU vs the float64 oracle): per row the
 relative L2 error is at most ``tol`` = 2e-2, and no element is an outlier:
-|gpu - ref| <= elem_tol * (|ref| + rms(ref row)) with elem_tol = 0.1 (a single
-wrong column or a dropped term shows up there even when the row norm hides
-it).  Both pipelines round to bf16 at the same storage points, but once they
-differ by fp32 noise every later rounding turns a perturbation d << ulp into
-an rms difference of about sqrt(d * ulp), so after a few layers the two sides
-differ at the bf16 ulp level (~5e-3 relative on logits); the elementwise
-maximum over tens of thousands of logits then sits near 4 sigma of that.  Integer
-outputs are compared exactly; a draft position is exempt when the oracle's
-top-1 / top-2 logit margin is below 1e-2 (a near tie that fp32 rounding may
-flip).
+|gpu - ref| <= elem_tol * (|ref| + rms(ref row)).  elem_tol is ELEM_TOL = 3e-2
+for one-step and teacher-forced comparisons (f, K/V, each layer's output on
+the oracle's input, logits in lock step) and FREE_ELEM_TOL = 6e-2 for whole
+free-running forwards at full size, where one-ulp bf16 re-roundings cascade
+through 5-8 layers.  Measured worst ratios on an MI355X: 2.2e-2 for lock-step
+logits at the small shapes, 6.1e-3 for the full-size K/V and forced checks,
+4.4e-2 for the full-size free-running forwards (coder_b64, 8 layers); the
+conftest prints them per test.  A single wrong column or a dropped term
+still shows up there when the row norm hides it.  Integer outputs are
+compared exactly; a draft position is exempt when the oracle's top-1 / top-2
+logit margin is below 1e-2 (a near tie that fp32 rounding may flip).
 """
 from __future__ import annotations
 
@@ -20,7 +21,8 @@ import math
 import numpy as np
 
 TOL = 2e-2
-ELEM_TOL = 0.1
+ELEM_TOL = 3e-2
+FREE_ELEM_TOL = 6e-2
 MARGIN = 1e-2
 
 # Worst ratios seen by assert_rows_close in the running test (conftest prints
