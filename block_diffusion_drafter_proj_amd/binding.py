@@ -23,6 +23,7 @@ MAX_FEAT = 8
 MAX_BATCH = 256
 PAGE = 16
 TOPK = 16
+DFLASH_STATIC_SCRATCH_BYTES = 64 << 20  # static scratch of dflash_draft_block_static
 
 BF16 = 0
 F32 = 1
@@ -86,6 +87,9 @@ def lib() -> ctypes.CDLL:
             "dflash_context_length": (i32, [vp, i32]),
             "dflash_inject_context": (i32, [vp, vp, i32, pi32, pi32, ctypes.POINTER(vp), vp]),
             "dflash_draft_block": (i32, [vp, vp, i32, pi32, vp, vp, vp, vp, ctypes.POINTER(DFlashDraftDebug)]),
+            "dflash_draft_block_static": (i32, [vp, vp, i32, pi32, vp, vp, vp, vp,
+                                                ctypes.POINTER(DFlashDraftDebug)]),
+            "dflash_draft_static_bytes": (sz, [ctypes.POINTER(DFlashConfig), i32]),
             "dflash_verify_accept": (i32, [vp, vp, i32, vp, vp, vp, vp, vp]),
             "dflash_check": (i32, [vp, vp]),
             "dflash_profile_begin": (i32, [vp, ctypes.c_uint32]),
@@ -174,6 +178,21 @@ def dflash_draft_block(h: int, stream: int, slots, last_token: int, draft: int, 
         dbg = ctypes.byref(DFlashDraftDebug(debug_logits or None, debug_hidden or None, debug_hidden_in or None))
     _check(lib().dflash_draft_block(vp(h), vp(stream), len(slots), _i32s(slots), vp(last_token or None),
                                     vp(draft or None), vp(topk_ids or None), vp(topk_logits or None), dbg))
+
+
+def dflash_draft_block_static(h: int, stream: int, slots, last_token: int, draft: int, topk_ids: int = 0,
+                              topk_logits: int = 0, debug_logits: int = 0, debug_hidden: int = 0,
+                              debug_hidden_in: int = 0) -> None:
+    vp = ctypes.c_void_p
+    dbg = None
+    if debug_logits or debug_hidden or debug_hidden_in:
+        dbg = ctypes.byref(DFlashDraftDebug(debug_logits or None, debug_hidden or None, debug_hidden_in or None))
+    _check(lib().dflash_draft_block_static(vp(h), vp(stream), len(slots), _i32s(slots), vp(last_token or None),
+                                           vp(draft or None), vp(topk_ids or None), vp(topk_logits or None), dbg))
+
+
+def dflash_draft_static_bytes(cfg: DFlashConfig, n_req: int) -> int:
+    return int(lib().dflash_draft_static_bytes(ctypes.byref(cfg), n_req))
 
 
 def dflash_verify_accept(h: int, stream: int, n_req: int, draft: int, target_greedy: int,

@@ -1,6 +1,7 @@
 // Host runtime behind the C ABI in include/dflash.h: argument validation,
 // the host mirror of every request slot, the workspace carve-up and the
-// launch sequence of each call.  Contains no device code.
+// launch sequence of each call.  Contains no kernels; its one device object
+// is the static scratch array of dflash_draft_block_static.
 //
 // Call sequences (all kernels on the caller's stream, no synchronisation):
 //   inject : per chunk of rows  fc GEMM (virtual concat of the n_feat hidden
@@ -12,12 +13,15 @@
 //            + argmax -> decode ids.  GEMMs split over K leave fp32 partials
 //            that the next kernel adds in a fixed order.
 //   verify : one kernel
+// dflash_draft_block_static runs the same draft sequence with its scratch
+// buffers in a static device array instead of the handle's workspace.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -142,12 +146,73 @@ size_t part_rows(const dflash_config& c, GemmPlan Plans::*f, int max_rows) {
   return m;
 }
 
-struct Layout {
-  size_t state, err, page_table, cos_t, sin_t;
-  size_t h, xa, xo, qkv, qb, blk, part_o, part_ml, nsplit, z, keys, tlists, lpart, opart, dpart;
-  size_t u, f, kvo;
+// Device memory of a handle, in two parts.  State (kept across calls): slot
+// state, error word, page table, RoPE tables, and the block's q / K / V tiles
+// whose rows B..15 stay zero.  Scratch (rewritten by every call before it is
+// read): the residual stream, GEMM inputs, split-K partial planes, attention
+// split partials, selection keys and lists, inject staging.
+struct Scratch {
+  size_t h, xa, xo, qkv, part_o, part_ml, nsplit, z, keys, tlists, lpart, opart, dpart;
+  size_t u, f, kvo;  // inject only (0 when not laid out)
   size_t total;
 };
+
+struct Layout {
+  size_t state, err, page_table, cos_t, sin_t, qb, blk;
+  size_t scratch;  // offset of the scratch part in the workspace
+  Scratch sc;
+  size_t total;
+};
+
+// Scratch of a draft call of up to n_req requests (and, with inject, of an
+// inject chunk of max_inject_rows rows), offsets from a 256-byte aligned base.
+Scratch make_scratch(const dflash_config& c, int n_req, bool inject) {
+  Scratch S{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t e = elt(c);
+  const size_t M = (size_t)n_req * c.block_size;
+  const size_t qd = (size_t)c.n_q_heads * c.head_dim;
+  const size_t qkvw = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  S.h = take(sizeof(float) * M * c.hidden);
+  // GEMM inputs: rows rounded up to whole 16-row fragments (fragment order)
+  const size_t M16 = (M + 15) / 16 * 16;
+  S.xa = take(e * M16 * c.hidden);
+  S.xo = take(e * M16 * qd);
+  S.qkv = take(sizeof(float) * part_rows(c, &Plans::qkv, (int)M) * qkvw);
+  const size_t pp = (size_t)n_req * max_splits(c) * c.n_q_heads * 16;
+  S.part_o = take(sizeof(float) * pp * c.head_dim);
+  S.part_ml = take(sizeof(float) * pp * 2);
+  S.nsplit = take(sizeof(int) * n_req);
+  S.z = take(e * M16 * c.ffn);
+  S.keys = take(sizeof(unsigned long long) * M);
+  S.tlists = c.topk ? take(sizeof(unsigned long long) * M * 16 *
+                           std::max({256, gemm_big_lists(tiles_of(c.vocab)), logit_sel_lists(c.vocab)}))
+                    : 0;
+  {  // split-K partial logits of the 64-row vocabulary product
+    size_t lrows = 0;
+    for (int m = 1; m <= (int)M; ++m) {
+      const GemmPlan g = make_plans(c, m).lm;
+      if (g.mt == 4) lrows = std::max(lrows, (size_t)g.P * m);
+    }
+    S.lpart = lrows ? take(sizeof(float) * lrows * c.vocab) : 0;
+  }
+  S.opart = take(sizeof(float) * part_rows(c, &Plans::o, (int)M) * c.hidden);
+  S.dpart = take(sizeof(float) * part_rows(c, &Plans::down, (int)M) * c.hidden);
+  if (inject) {
+    const size_t R = c.max_inject_rows;
+    S.u = take(sizeof(float) * part_rows(c, &Plans::fc, (int)R) * c.hidden);
+    S.f = take(e * R * c.hidden);
+    S.kvo = take(sizeof(float) * part_rows(c, &Plans::kv, (int)R) * (size_t)c.n_layers * 2 * c.n_kv_heads *
+                 c.head_dim);
+  }
+  S.total = off;
+  return S;
+}
 
 Layout make_layout(const dflash_config& c) {
   Layout L{};
@@ -158,46 +223,16 @@ Layout make_layout(const dflash_config& c) {
     return o;
   };
   const size_t e = elt(c);
-  const size_t M = (size_t)c.max_batch * c.block_size;
-  const size_t qd = (size_t)c.n_q_heads * c.head_dim;
-  const size_t qkvw = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   const size_t page_elems = 2ull * c.n_kv_heads * 16 * c.head_dim;
-  const size_t R = c.max_inject_rows;
   L.state = take(sizeof(SlotState) * c.max_batch);
   L.err = take(16);
   L.page_table = take(sizeof(int32_t) * c.max_batch * (size_t)c.max_pages_per_req);
   L.cos_t = take(sizeof(float) * (size_t)c.max_position * (c.head_dim / 2));
   L.sin_t = take(sizeof(float) * (size_t)c.max_position * (c.head_dim / 2));
-  L.h = take(sizeof(float) * M * c.hidden);
-  // GEMM inputs: rows rounded up to whole 16-row fragments (fragment order)
-  const size_t M16 = (M + 15) / 16 * 16;
-  L.xa = take(e * M16 * c.hidden);
-  L.xo = take(e * M16 * qd);
-  L.qkv = take(sizeof(float) * part_rows(c, &Plans::qkv, (int)M) * qkvw);
   L.qb = take(e * (size_t)c.max_batch * c.n_q_heads * 16 * c.head_dim);
   L.blk = take(e * (size_t)c.max_batch * page_elems);
-  const size_t pp = (size_t)part_pairs(c) * c.n_q_heads * 16;
-  L.part_o = take(sizeof(float) * pp * c.head_dim);
-  L.part_ml = take(sizeof(float) * pp * 2);
-  L.nsplit = take(sizeof(int) * c.max_batch);
-  L.z = take(e * M16 * c.ffn);
-  L.keys = take(sizeof(unsigned long long) * M);
-  L.tlists = c.topk ? take(sizeof(unsigned long long) * M * 16 *
-                           std::max({256, gemm_big_lists(tiles_of(c.vocab)), logit_sel_lists(c.vocab)}))
-                    : 0;
-  {  // split-K partial logits of the 64-row vocabulary product
-    size_t lrows = 0;
-    for (int m = 1; m <= (int)M; ++m) {
-      const GemmPlan g = make_plans(c, m).lm;
-      if (g.mt == 4) lrows = std::max(lrows, (size_t)g.P * m);
-    }
-    L.lpart = lrows ? take(sizeof(float) * lrows * c.vocab) : 0;
-  }
-  L.opart = take(sizeof(float) * part_rows(c, &Plans::o, (int)M) * c.hidden);
-  L.dpart = take(sizeof(float) * part_rows(c, &Plans::down, (int)M) * c.hidden);
-  L.u = take(sizeof(float) * part_rows(c, &Plans::fc, (int)R) * c.hidden);
-  L.f = take(e * R * c.hidden);
-  L.kvo = take(sizeof(float) * part_rows(c, &Plans::kv, (int)R) * (size_t)c.n_layers * 2 * c.n_kv_heads * c.head_dim);
+  L.sc = make_scratch(c, c.max_batch, true);
+  L.scratch = take(L.sc.total);
   L.total = off;
   return L;
 }
@@ -296,6 +331,7 @@ struct dflash_handle {
   std::vector<HostSlot> slots;
   bool dev_init = false;
   Profiler prof;
+  std::vector<Scratch> static_sc;  // scratch layouts of static-scratch calls, by request count
 };
 
 namespace {
@@ -303,6 +339,12 @@ namespace {
 template <typename P>
 P* at(dflash_handle* h, size_t off) {
   return reinterpret_cast<P*>(h->ws + off);
+}
+
+// a buffer of the scratch part at base sb
+template <typename P>
+P* sat(char* sb, size_t off) {
+  return reinterpret_cast<P*>(sb + off);
 }
 
 dflash_status ensure_device(dflash_handle* h) {
@@ -390,6 +432,40 @@ dflash_status check_slots(dflash_handle* h, int32_t n_req, const int32_t* slots)
     seen[s] = 1;
     if (!h->slots[s].bound) return fail(DFLASH_E_INVALID, "slot %d is not bound", s);
   }
+  return DFLASH_OK;
+}
+
+// Scratch for callers that cannot allocate (dflash_draft_block_static): one
+// static device array per GPU, shared by every handle and call on that GPU.
+// Host code never uses the array's name as an address: the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device with
+// that device current.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];
+
+dflash_status static_scratch(dflash_handle* h, int n_req, char** base, const Scratch** sc) {
+  if ((int)h->static_sc.size() <= n_req) h->static_sc.resize(n_req + 1, Scratch{});
+  Scratch& S = h->static_sc[n_req];
+  if (S.total == 0) S = make_scratch(h->cfg, n_req, false);
+  if (S.total > kStaticScratchBytes)
+    return fail(DFLASH_E_CAPACITY, "static scratch: %d requests need %zu bytes, above the %zu-byte array", n_req,
+                S.total, kStaticScratchBytes);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e) return hip_fail(e, "static scratch: current device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DFLASH_E_UNSUPPORTED, "static scratch: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e) return hip_fail(e, "static scratch: symbol address");
+    g_scratch_ptr[dev] = reinterpret_cast<char*>(p);
+  }
+  *base = g_scratch_ptr[dev];
+  *sc = &S;
   return DFLASH_OK;
 }
 
@@ -547,6 +623,8 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
   const int kvw = c.n_layers * 2 * c.n_kv_heads * c.head_dim;
   const int R = c.max_inject_rows;
   const int kv_seg_tiles = tiles_of(2 * c.n_kv_heads * c.head_dim);
+  char* sb = h->ws + h->lay.scratch;
+  const Scratch& sc = h->lay.sc;
 
   // walk requests in call order, cutting chunks of <= R rows and <= kMaxChunkReq requests
   int req = 0, used = 0;  // current request and rows of it already emitted
@@ -590,29 +668,29 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
     g.N = d;
     g.K = c.n_feat * d;
     g.P = pl.fc.P;
-    g.out_f32 = at<float>(h, h->lay.u);
+    g.out_f32 = sat<float>(sb, sc.u);
     { ProfScope ps(h, DFLASH_KERNEL_FC_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.fc, g, s); }
 
     NormParams np{};
-    np.part = at<float>(h, h->lay.u);
+    np.part = sat<float>(sb, sc.u);
     np.n_part = pl.fc.P;
     np.ldx = d;
     np.gamma = h->w.fc_norm;
     np.eps = c.rms_eps;
-    np.out = h->ws + h->lay.f;
+    np.out = sb + sc.f;
     np.ldo = d;
     np.d = d;
     np.M = rows;
     { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, np, s); }
     if (debug_f) {
       hipError_t err = hipMemcpyAsync(reinterpret_cast<char*>(debug_f) + (size_t)row0 * d * e,
-                                      h->ws + h->lay.f, (size_t)rows * d * e,
+                                      sb + sc.f, (size_t)rows * d * e,
                                       hipMemcpyDeviceToDevice, s);
       if (err) return hip_fail(err, "debug_f copy");
     }
 
     GemmParams kv{};
-    kv.a[0] = h->ws + h->lay.f;
+    kv.a[0] = sb + sc.f;
     kv.a_parts = 1;
     kv.a_part_k = d;
     kv.lda = d;
@@ -625,10 +703,10 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
     kv.N = kvw;
     kv.K = d;
     kv.P = pl.kv.P;
-    kv.out_f32 = at<float>(h, h->lay.kvo);
+    kv.out_f32 = sat<float>(sb, sc.kvo);
     { ProfScope ps(h, DFLASH_KERNEL_KV_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.kv, kv, s); }
 
-    sp.kv = at<float>(h, h->lay.kvo);
+    sp.kv = sat<float>(sb, sc.kvo);
     sp.n_part = pl.kv.P;
     sp.rows = rows;
     sp.L = c.n_layers;
@@ -652,10 +730,11 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
   return DFLASH_OK;
 }
 
-dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
-                                 const int32_t* slots, const int32_t* last_token, int32_t* draft,
-                                 int32_t* topk_ids, float* topk_logits,
-                                 const dflash_draft_debug* debug) {
+// Steps 3 and 4 with the scratch part at the handle's workspace or, with
+// from_static, in the library's static device array.
+static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots,
+                                const int32_t* last_token, int32_t* draft, int32_t* topk_ids,
+                                float* topk_logits, const dflash_draft_debug* debug, bool from_static) {
   float* debug_logits = debug ? debug->logits : nullptr;
   float* debug_hidden = debug ? debug->hidden : nullptr;
   const float* hidden_in = debug ? debug->hidden_in : nullptr;
@@ -673,6 +752,13 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   }
   st = ensure_device(h);
   if (st) return st;
+  char* sb = h->ws + h->lay.scratch;
+  const Scratch* scp = &h->lay.sc;
+  if (from_static) {
+    st = static_scratch(h, n_req, &sb, &scp);
+    if (st) return st;
+  }
+  const Scratch& sc = *scp;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const size_t e = elt(c);
@@ -713,9 +799,9 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     for (int i = 0; i < n_req; ++i) rope_out.slots[i] = slots[i];
   }
 
-  float* hbuf = at<float>(h, h->lay.h);
-  float* dpart = at<float>(h, h->lay.dpart);
-  float* opart = at<float>(h, h->lay.opart);
+  float* hbuf = sat<float>(sb, sc.h);
+  float* dpart = sat<float>(sb, sc.dpart);
+  float* opart = sat<float>(sb, sc.opart);
   const size_t page_layer = (size_t)c.max_pages * 2 * c.n_kv_heads * 16 * c.head_dim;
 
   auto gemm_in = [&](const void* a, int K) {
@@ -779,7 +865,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     n1.ldx = d;
     n1.gamma = lw.attn_norm;
     n1.eps = c.rms_eps;
-    n1.out = h->ws + h->lay.xa;
+    n1.out = sb + sc.xa;
     n1.ldo = d;
     n1.out_packed = pl.qkv.mt == 0;  // the tiled QKV product reads fragment order
     n1.d = d;
@@ -787,7 +873,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     n1.dbg = debug_hidden ? debug_hidden + (size_t)l * M * d : nullptr;
     { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, n1, s); }
 
-    GemmParams g = gemm_in(h->ws + h->lay.xa, d);
+    GemmParams g = gemm_in(sb + sc.xa, d);
     g.a_packed = n1.out_packed;
     g.w[0] = h->packed + h->pk.wqkv[l];
     g.N = qkvw;
@@ -799,13 +885,13 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
       launch_gemm(c.dtype, EPI_ROPE, pl.qkv, g, s);
     } else {
       g.tiles = tiles_of(qkvw);
-      g.out_f32 = at<float>(h, h->lay.qkv);
+      g.out_f32 = sat<float>(sb, sc.qkv);
       ProfScope ps(h, DFLASH_KERNEL_QKV_GEMM, s);
       launch_gemm(c.dtype, EPI_PARTIAL, pl.qkv, g, s);
     }
 
     QkvPostParams qp{};
-    qp.qkv = at<float>(h, h->lay.qkv);
+    qp.qkv = sat<float>(sb, sc.qkv);
     qp.n_part = pl.qkv.P;
     qp.B = B;
     qp.Hq = c.n_q_heads;
@@ -834,13 +920,13 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     ap.B = B;
     ap.split_target = target;
     ap.pps_cap = kPpsCap;
-    ap.n_split = at<int>(h, h->lay.nsplit);
+    ap.n_split = sat<int>(sb, sc.nsplit);
     ap.n_splits = splits;
     ap.KQ = KQ;
     ap.scale = (float)(1.0 / sqrt((double)c.head_dim));
-    ap.part_o = at<float>(h, h->lay.part_o);
-    ap.part_ml = at<float>(h, h->lay.part_ml);
-    ap.out = h->ws + h->lay.xo;
+    ap.part_o = sat<float>(sb, sc.part_o);
+    ap.part_ml = sat<float>(sb, sc.part_ml);
+    ap.out = sb + sc.xo;
     ap.ldo = qd;
     ap.out_packed = pl.o.mt == 0;
     ap.err = at<unsigned int>(h, h->lay.err);
@@ -861,7 +947,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
       launch_combine(c.dtype, c.head_dim, cp, s);
     }
 
-    GemmParams go = gemm_in(h->ws + h->lay.xo, qd);
+    GemmParams go = gemm_in(sb + sc.xo, qd);
     go.a_packed = ap.out_packed;
     go.w[0] = h->packed + h->pk.wo[l];
     go.tiles = tiles_of(d);
@@ -883,14 +969,14 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     n2.ldx = d;
     n2.gamma = lw.mlp_norm;
     n2.eps = c.rms_eps;
-    n2.out = h->ws + h->lay.xa;
+    n2.out = sb + sc.xa;
     n2.ldo = d;
     n2.out_packed = pl.gateup.mt == 0;
     n2.d = d;
     n2.M = M;
     { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, n2, s); }
 
-    GemmParams gu = gemm_in(h->ws + h->lay.xa, d);
+    GemmParams gu = gemm_in(sb + sc.xa, d);
     gu.a_packed = n2.out_packed;
     gu.out_packed = pl.gateup.mt == 0 && pl.down.mt == 0;  // z for a tiled down product
     gu.w[0] = h->packed + h->pk.wgateup[l];
@@ -898,11 +984,11 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     gu.up_tile_off = tiles_of(c.ffn);
     gu.N = c.ffn;
     gu.P = 1;
-    gu.out_t = h->ws + h->lay.z;
+    gu.out_t = sb + sc.z;
     gu.ldt = c.ffn;
     { ProfScope ps(h, DFLASH_KERNEL_GATEUP_GEMM, s); launch_gemm(c.dtype, EPI_SWIGLU, pl.gateup, gu, s); }
 
-    GemmParams gd = gemm_in(h->ws + h->lay.z, c.ffn);
+    GemmParams gd = gemm_in(sb + sc.z, c.ffn);
     gd.a_packed = gu.out_packed;
     gd.w[0] = h->packed + h->pk.wdown[l];
     gd.tiles = tiles_of(d);
@@ -928,16 +1014,16 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   nf.ldx = d;
   nf.gamma = h->w.final_norm;
   nf.eps = c.rms_eps;
-  nf.out = h->ws + h->lay.xa;
+  nf.out = sb + sc.xa;
   nf.ldo = d;
   nf.out_packed = pl.lm.mt == 0;
   nf.d = d;
   nf.M = M;
   nf.dbg = debug_hidden ? debug_hidden + (size_t)c.n_layers * M * d : nullptr;
-  nf.zero_keys = at<unsigned long long>(h, h->lay.keys);
+  nf.zero_keys = sat<unsigned long long>(sb, sc.keys);
   { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, nf, s); }
 
-  GemmParams gl = gemm_in(h->ws + h->lay.xa, d);
+  GemmParams gl = gemm_in(sb + sc.xa, d);
   gl.a_packed = nf.out_packed;
   gl.w[0] = h->packed + h->pk.lm_head;
   gl.tiles = tiles_of(c.vocab);
@@ -945,7 +1031,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
   gl.P = 1;
   if (pl.lm.mt == 4) {  // 17..64 rows: split-K partial logits, then the selection pass
     gl.P = pl.lm.P;
-    gl.out_f32 = at<float>(h, h->lay.lpart);
+    gl.out_f32 = sat<float>(sb, sc.lpart);
     {
       ProfScope ps(h, DFLASH_KERNEL_LM_HEAD, s);
       launch_gemm(c.dtype, EPI_PARTIAL, pl.lm, gl, s);
@@ -957,8 +1043,8 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     lp.N = c.vocab;
     lp.dbg = debug_logits;
     lp.ld_dbg = c.vocab;
-    lp.keys = at<unsigned long long>(h, h->lay.keys);
-    lp.lists = at<unsigned long long>(h, h->lay.tlists);
+    lp.keys = sat<unsigned long long>(sb, sc.keys);
+    lp.lists = sat<unsigned long long>(sb, sc.tlists);
     lp.n_lists = logit_sel_lists(c.vocab);
     ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
     launch_logit_select(c.topk != 0, lp, s);
@@ -977,7 +1063,7 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     }
     return launched("draft head");
   }
-  gl.keys = at<unsigned long long>(h, c.topk ? h->lay.tlists : h->lay.keys);
+  gl.keys = sat<unsigned long long>(sb, c.topk ? sc.tlists : sc.keys);
   gl.dbg = debug_logits;
   gl.ld_dbg = c.vocab;
   {
@@ -997,9 +1083,28 @@ dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
     launch_topk_merge(tp, s);
   } else {
     ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
-    launch_finalize(at<unsigned long long>(h, h->lay.keys), M, c.vocab, draft, s);
+    launch_finalize(sat<unsigned long long>(sb, sc.keys), M, c.vocab, draft, s);
   }
   return launched("draft head");
+}
+
+dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
+                                 const int32_t* slots, const int32_t* last_token, int32_t* draft,
+                                 int32_t* topk_ids, float* topk_logits,
+                                 const dflash_draft_debug* debug) {
+  return draft_impl(h, stream, n_req, slots, last_token, draft, topk_ids, topk_logits, debug, false);
+}
+
+dflash_status dflash_draft_block_static(dflash_handle* h, void* stream, int32_t n_req,
+                                        const int32_t* slots, const int32_t* last_token, int32_t* draft,
+                                        int32_t* topk_ids, float* topk_logits,
+                                        const dflash_draft_debug* debug) {
+  return draft_impl(h, stream, n_req, slots, last_token, draft, topk_ids, topk_logits, debug, true);
+}
+
+size_t dflash_draft_static_bytes(const dflash_config* cfg, int32_t n_req) {
+  if (validate(cfg) != DFLASH_OK || n_req < 1 || n_req > cfg->max_batch) return 0;
+  return make_scratch(*cfg, n_req, false).total;
 }
 
 dflash_status dflash_verify_accept(dflash_handle* h, void* stream, int32_t n_req,

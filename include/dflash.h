@@ -234,6 +234,30 @@ dflash_status dflash_draft_block(dflash_handle *h, void *stream, int32_t n_req,
                                  int32_t *draft, int32_t *topk_ids, float *topk_logits,
                                  const dflash_draft_debug *debug);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * draft as dflash_draft_block, same arguments, outputs and kernels, with its
+ * scratch (residual stream, GEMM inputs, split-K partial planes, attention
+ * split partials, selection keys and lists) taken from a static device array
+ * of DFLASH_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on every GPU
+ * it runs on until the process ends, instead of the handle's workspace.  The
+ * handle's workspace still holds the request state.  Allocates nothing.
+ * Every call on a GPU, from any handle, uses that GPU's one array and leaves
+ * its contents behind; calls that overlap on one GPU (two streams, two
+ * threads) race and must be serialised by the caller.  Returns
+ * DFLASH_E_CAPACITY when n_req requests need more scratch than the array
+ * holds (dflash_draft_static_bytes tells), else as dflash_draft_block. */
+#define DFLASH_STATIC_SCRATCH_BYTES (64u << 20)
+dflash_status dflash_draft_block_static(dflash_handle *h, void *stream, int32_t n_req,
+                                        const int32_t *slots, const int32_t *last_token,
+                                        int32_t *draft, int32_t *topk_ids, float *topk_logits,
+                                        const dflash_draft_debug *debug);
+
+/* Scratch bytes dflash_draft_block_static needs for a call of n_req requests
+ * with this config (0 for an invalid config or n_req outside [1, max_batch]).
+ * Host only. */
+size_t dflash_draft_static_bytes(const dflash_config *cfg, int32_t n_req);
+
 /* Step 5 ([news] "DFlash 2 的核心：一次写一块"; [guide] 3.3): a = number of
  * leading positions where draft equals the target's greedy token; commits
  * draft[0..a) followed by target_greedy[a], which becomes the next pending
