@@ -33,6 +33,9 @@ back with no host synchronisation inside.
 
 Output is one JSON line:
   * ``value``: draft blocks/s of the full cycle (requests x cycles / s);
+  * the draft call's p10/p50/p90/p95 time, the handle's device memory
+    (weights, packed weights, KV pool, workspace) and each GEMM class's
+    TFLOP/s;
   * beside it: accepted tok/s, the draft-only rate at fixed context, the
     per-kernel time breakdown, the GEMM kernels' share of the MFMA peak
     (their flops over their summed time), and accepted tok/s at a fixed
@@ -42,7 +45,12 @@ Output is one JSON line:
     call's stream in one timed cycle of every four (each event record idles
     the stream for a few microseconds, so the other cycles run without
     them) and priced against HBM or MFMA, whichever bounds it;
-  * the CPU oracle, timed on the host.
+  * the CPU oracle, timed on the host (prefill inject, median of 3 drafts,
+    3 steady-state cycles of one request);
+  * by default (``--config qwen3_8b`` without ``--single``), a ``workloads``
+    object with the same figures for llama31_8b, coder_b64 (batch 64: the
+    GEMMs' share of the bf16 MFMA peak) and dflash2_long (with the conv's
+    and the top-16 selection's share of the cycle), each in its own handle.
 """
 from __future__ import annotations
 
@@ -151,45 +159,78 @@ def measured_traffic(config, cls, srcs):
     return float(m.group(1))
 
 
-def cpu_baseline(shape, weights, a_mean, visible):
-    """The oracle on the host: one cycle of ONE request.
+def blas_info():
+    """BLAS library, vendor and thread count numpy runs on."""
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            i = info[0]
+            return dict(library=i.get("internal_api"), vendor=i.get("prefix"), threads=int(i.get("num_threads", 1)))
+    except Exception:  # pragma: no cover
+        pass
+    return dict(library=None, vendor=None, threads=os.cpu_count() or 1)
 
-    The cycle is one draft forward with ``visible`` context positions, the
-    accept step, and the inject of a_mean+1 rows.  Requests are independent,
-    so a batch costs the oracle this once per request."""
+
+def cpu_baseline(shape, weights, a_mean, visible, n_drafts=3, n_cycles=3):
+    """The oracle on the host, on a bounded sample of ONE request.
+
+    The request's context is injected by the oracle itself (the prefill: the
+    projection and every layer's K/V of ``visible`` positions), then
+    ``n_drafts`` draft forwards at that context are timed (median), then
+    ``n_cycles`` speculative cycles: draft, accept against target tokens
+    that agree with the draft on round(a_mean) positions, and the inject of
+    the a+1 accepted rows (the steady-state inject).  Requests are
+    independent, so a batch costs the oracle this once per request."""
     import synth
     from oracle import DraftOracle, select, verify_accept
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    blas = blas_info()
     o = DraftOracle(shape, weights)
-    st = o.new_request()
-    # the context K/V of the sample: random values of the workload's shape
-    g = np.random.default_rng(7)
-    for l in range(shape["n_layers"]):
-        st.K[l] = synth.to_storage(g.standard_normal((visible, shape["n_kv_heads"], shape["head_dim"]), np.float32), shape["dtype"])
-        st.V[l] = synth.to_storage(g.standard_normal((visible, shape["n_kv_heads"], shape["head_dim"]), np.float32), shape["dtype"])
-    st.ctx_len = visible
-    rows = int(round(a_mean)) + 1
-    H = synth.hidden_rows(shape, 0, visible, rows)
-    last = 0 if shape.get("conv2") else None
+    start = max(0, shape["ctx"] - visible) if shape.get("window") else 0
+    st = o.new_request(start)
+    H = synth.hidden_rows(shape, 0, start, visible)
     t0 = time.perf_counter()
-    logits = o.draft_block(st, last)
-    d, _, _ = select(logits, shape.get("topk") or 0)
-    G = np.concatenate([d, [0]])
-    verify_accept(d, G)
-    t1 = time.perf_counter()
     o.inject(st, H)
-    t2 = time.perf_counter()
-    cycle = t2 - t0
-    return dict(value=1.0 / cycle, unit="draft blocks/s", cores=int(threads), kind="oracle",
-                sample=f"1 cycle of 1 request at {visible} visible context positions: draft forward "
-                       f"{t1 - t0:.2f} s + inject of {rows} rows {t2 - t1:.2f} s (float64 numpy; "
-                       f"context K/V filled with random values)",
-                draft_s=t1 - t0, inject_s=t2 - t1, accepted_tok_per_s=a_mean / cycle)
+    prefill_s = time.perf_counter() - t0
+    last = 0 if shape.get("conv2") else None
+    d_times = []
+    for _ in range(n_drafts):
+        t0 = time.perf_counter()
+        logits = o.draft_block(st, last)
+        select(logits, shape.get("topk") or 0)
+        d_times.append(time.perf_counter() - t0)
+    a_fixed = int(round(a_mean))
+    V = shape["vocab"]
+    g = synth.rng(shape["seed"], synth.S_ACCEPT, 77)
+    c_times, i_times, accepted = [], [], 0
+    pos = start + visible
+    for _ in range(n_cycles):
+        t0 = time.perf_counter()
+        logits = o.draft_block(st, last)
+        d, _, _ = select(logits, shape.get("topk") or 0)
+        G = synth.synthetic_greedy(d, a_fixed, V, g)
+        a, _, nxt = verify_accept(d, G)
+        t1 = time.perf_counter()
+        o.inject(st, synth.hidden_rows(shape, 0, pos, a + 1))
+        t2 = time.perf_counter()
+        pos += a + 1
+        last = nxt if last is not None else None
+        accepted += a
+        c_times.append(t2 - t0)
+        i_times.append(t2 - t1)
+    cycle = float(np.median(c_times))
+    return dict(value=round(1.0 / cycle, 4), unit="draft blocks/s", cores=blas["threads"],
+                cores_affine=len(os.sched_getaffinity(0)), cpu_count=os.cpu_count(),
+                blas=blas, kind="oracle",
+                sample=(f"1 request: oracle prefill inject of {visible} positions ({prefill_s:.2f} s), "
+                        f"{n_drafts} draft forwards at that context (median {np.median(d_times):.2f} s), "
+                        f"then {n_cycles} cycles of draft + accept (a = {a_fixed}) + inject of a+1 rows "
+                        f"(median cycle {cycle:.2f} s, median steady inject {np.median(i_times):.3f} s); "
+                        f"float64 numpy"),
+                prefill_inject_s=round(prefill_s, 3), draft_s_median=round(float(np.median(d_times)), 3),
+                steady_inject_s_median=round(float(np.median(i_times)), 4),
+                accepted_tok_per_s=round(accepted / sum(c_times), 4))
 
 
 def plan_requests(shape, n_cycles):
@@ -212,6 +253,8 @@ def main():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="qwen3_8b")
+    ap.add_argument("--single", action="store_true",
+                    help="run only --config (the default run adds the other measured workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (counter calibration)")
@@ -232,18 +275,42 @@ def main():
         print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30}))
         return
 
+    result = run_workload(args.config, args.steps, args.warmup, cpu=not args.no_cpu_baseline)
+    if not args.single and args.config == "qwen3_8b":
+        # the other measured workloads, each in its own handle, reported beside the headline
+        result["workloads"] = {}
+        for name in ("llama31_8b", "coder_b64", "dflash2_long"):
+            r = run_workload(name, args.steps, args.warmup, cpu=False)
+            result["workloads"][name] = {k: r[k] for k in SUMMARY_KEYS if k in r}
+    print(json.dumps(result))
+
+
+SUMMARY_KEYS = ("value", "unit", "config", "dtype", "ms_per_step", "accepted_tok_per_s", "mean_accept",
+                "draft_ms", "draft_ms_percentiles", "draft_only_blocks_per_s", "draft_hbm_frac",
+                "gemm_mfma_frac", "gemm_tflops", "cycle_hbm_frac", "kernel_ms_per_draft", "roofline",
+                "memory_bytes", "shares_of_cycle")
+
+
+def run_workload(config, steps, warmup, cpu=False):
+    """One workload in its own handle: draft-only rate (with per-call
+    percentiles), kernel breakdown, the timed speculative cycles and the
+    roofline of the dominant kernel class; for the DFlash-2 workload, the
+    conv taps' and the top-16 selection's kernel time as shares of the
+    cycle."""
+    import torch
+
     import synth
     from block_diffusion_drafter_proj_amd import binding as Bnd
     from block_diffusion_drafter_proj_amd.drafter import Drafter
 
-    shape = synth.config(args.config)
+    shape = synth.config(config)
     dev = torch.device("cuda")
     t_setup = time.perf_counter()
     weights = synth.make_weights(shape)
     B, V, d = shape["block_size"], shape["vocab"], shape["hidden"]
     W = shape.get("window") or 0
     conv, topk = bool(shape.get("conv2")), int(shape.get("topk") or 0)
-    n_cycles = args.warmup + args.steps
+    n_cycles = warmup + steps
     reqs = plan_requests(shape, n_cycles)
     n = len(reqs)
     slots = list(range(n))
@@ -290,16 +357,28 @@ def main():
         return dr.draft(slots, last_dev if conv else None, out=out, topk_ids=tk_ids, topk_logits=tk_val)
 
     # ---- draft-only rate at fixed context (state is unchanged by a draft) ----
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         draft(last0_dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         draft(last0_dev)
     e1.record()
     torch.cuda.synchronize()
-    draft_ms = e0.elapsed_time(e1) / args.steps
+    draft_ms = e0.elapsed_time(e1) / steps
+    # per-call times (one event at every call boundary; each record adds a few
+    # microseconds, so these sit slightly above the back-to-back rate)
+    n_pct = max(steps, 100)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_pct + 1)]
+    evs[0].record()
+    for i in range(n_pct):
+        draft(last0_dev)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_call = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(n_pct)])
+    draft_pct = {f"p{q}": round(float(np.percentile(per_call, q)), 4) for q in (10, 50, 90, 95)}
+    draft_pct["calls"] = n_pct
 
     # per-kernel breakdown of the draft forward (separate pass, every class timed)
     Bnd.dflash_profile_begin(dr.h, (1 << len(Bnd.KERNELS)) - 1)
@@ -343,15 +422,15 @@ def main():
         dr.verify(out, Gs[i], acc[i], com[i], lastbuf[i])
         dr.inject(slots, nnew[i], Hc[i])
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         cycle(i)
     torch.cuda.synchronize()
     dom_bit = 1 << Bnd.KERNELS.index(dominant)
     Bnd.dflash_profile_begin(dr.h, dom_bit)
     t0 = time.perf_counter()
     e0.record()
-    for i in range(args.warmup, n_cycles):
-        Bnd.dflash_profile_mask(dr.h, dom_bit if (i - args.warmup) % TIME_EVERY == 0 else 0)
+    for i in range(warmup, n_cycles):
+        Bnd.dflash_profile_mask(dr.h, dom_bit if (i - warmup) % TIME_EVERY == 0 else 0)
         cycle(i)
     e1.record()
     torch.cuda.synchronize()
@@ -361,13 +440,13 @@ def main():
     sched = np.stack([q["sched"] for q in reqs], axis=1)  # [cycles, n]
     assert np.array_equal(acc.cpu().numpy(), sched), "accept lengths differ from the schedule"
     assert np.array_equal(lastbuf.cpu().numpy(), np.array(lasts)), "next tokens differ from the record"
-    cycle_ms = e0.elapsed_time(e1) / args.steps
-    wall_ms = (t1 - t0) * 1e3 / args.steps
-    acc_timed = int(sched[args.warmup:].sum())
+    cycle_ms = e0.elapsed_time(e1) / steps
+    wall_ms = (t1 - t0) * 1e3 / steps
+    acc_timed = int(sched[warmup:].sum())
 
     # ---- roofline of the dominant kernel class (per launch, timed in the cycles) ----
     # the visible context at the middle of the timed cycles
-    mid = (args.warmup + n_cycles) // 2
+    mid = (warmup + n_cycles) // 2
     vis_mid = []
     for r, q in enumerate(reqs):
         c = q["ctx"] + int(q["sched"][:mid].sum()) + mid
@@ -378,7 +457,7 @@ def main():
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = flops / (peak_tf * 1e12)
     srcs = kernel_sources(shape, dominant, M)
-    traffic = measured_traffic(args.config, dominant, srcs)
+    traffic = measured_traffic(config, dominant, srcs)
     if t_mfma > t_hbm:
         achieved = flops / (launch_ms * 1e-3) / 1e12
         roofline = dict(bound="mfma", achieved=round(achieved, 1), peak=peak_tf, unit="TFLOP/s",
@@ -390,7 +469,7 @@ def main():
     roofline.update(traffic=traffic, kernel=dominant, algorithmic_bytes=int(nbytes), flops=flops,
                     avg_ms=round(launch_ms, 4), launches_timed=dom_n,
                     kernel_sources=[os.path.basename(s) for s in srcs])
-    a_mean = float(sched[args.warmup:].mean())
+    a_mean = float(sched[warmup:].mean())
     db = draft_bytes(shape, visible0)
     cyc_bytes = draft_bytes(shape, vis_mid) + inject_bytes(shape, n * (a_mean + 1))
     draft_flops = sum(class_work(shape, k, M, visible0)[0] * launches.get(k, 0)
@@ -400,7 +479,7 @@ def main():
     gemm_ms = sum(breakdown.get(k, 0.0) for k in GEMM_CLASSES)
 
     ctxs = [q["ctx"] for q in reqs]
-    desc = (f"{args.config}: {shape['n_layers']}-layer draft, hidden {d}, "
+    desc = (f"{config}: {shape['n_layers']}-layer draft, hidden {d}, "
             f"{shape['n_q_heads']}/{shape['n_kv_heads']} heads x {shape['head_dim']}, "
             f"ffn {shape['ffn']}, vocab {V}, block {B}, batch {n}, ctx "
             + (f"{ctxs[0]}" if len(set(ctxs)) == 1 else f"ragged {min(ctxs)}..{max(ctxs)} (mean {np.mean(ctxs):.0f})")
@@ -411,8 +490,8 @@ def main():
         "value": round(n * 1e3 / cycle_ms, 2),
         "unit": "draft blocks/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(wall_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -422,8 +501,8 @@ def main():
         "config": {"workload": desc, "global_batch": n, "block": B,
                    "ctx": ctxs[0] if len(set(ctxs)) == 1 else f"U[{shape['ctx_range'][0]},{shape['ctx_range'][1]}]",
                    "parallelism": "none (1 GPU)"},
-        "accepted_tok_per_s": round(acc_timed / (cycle_ms * 1e-3 * args.steps), 1),
-        "committed_tok_per_s": round((acc_timed + n * args.steps) / (cycle_ms * 1e-3 * args.steps), 1),
+        "accepted_tok_per_s": round(acc_timed / (cycle_ms * 1e-3 * steps), 1),
+        "committed_tok_per_s": round((acc_timed + n * steps) / (cycle_ms * 1e-3 * steps), 1),
         "mean_accept": round(a_mean, 3),
         "cycle_ms_events": round(cycle_ms, 4),
         "draft_only_blocks_per_s": round(n * 1e3 / draft_ms, 2),
@@ -439,9 +518,39 @@ def main():
         "roofline": roofline,
         "setup_s": round(setup_s, 1),
     }
-    if not args.no_cpu_baseline:
+    result["draft_ms_percentiles"] = draft_pct
+    result["gemm_tflops"] = {k: round(class_work(shape, k, M, visible0)[0] * launches[k] / (breakdown[k] * 1e-3) / 1e12, 1)
+                             for k in GEMM_CLASSES if breakdown.get(k)}
+    weight_bytes = sum(t.numel() * t.element_size() for t in dr._keep)
+    result["memory_bytes"] = {"weights": int(weight_bytes), "packed_weights": int(dr.packed.numel()),
+                              "kv_pool": int(dr.kv_pool.numel()), "workspace": int(dr.workspace.numel()),
+                              "total": int(weight_bytes + dr.packed.numel() + dr.kv_pool.numel()
+                                           + dr.workspace.numel())}
+    if conv or topk:
+        # the DFlash-2 components' kernels, timed in the breakdown pass, over the cycle
+        shares = {}
+        if conv:
+            shares["two_tap_conv"] = {
+                "ms_per_cycle": breakdown.get("conv", 0.0),
+                "share": round(breakdown.get("conv", 0.0) / cycle_ms, 4),
+                "counted": "the conv-tap launches at the O and down outputs; the taps at the attention "
+                           "and MLP inputs run inside the norms and are not counted"}
+        if topk:
+            sel = breakdown.get("select", 0.0) + breakdown.get("topk", 0.0)
+            shares["top16_selection"] = {
+                "ms_per_cycle": round(sel, 4),
+                "share": round(sel / cycle_ms, 4),
+                "counted": "the selection pass that keeps sorted top-16 lists from the split-K logits, and "
+                           "the merge of the lists (at more than 64 rows the lists come from the LM head's "
+                           "epilogue and only the merge is counted)"}
+        shares["pages"] = "0.7 % (conv) and 0.6 % (path selector) of the cycle, hardware not stated"
+        result["shares_of_cycle"] = shares
+    if cpu:
         result["cpu_baseline"] = cpu_baseline(shape, weights, a_mean, int(np.median(visible0)))
-    print(json.dumps(result))
+    dr.close()
+    del dr, reqs, Gs, Hc
+    torch.cuda.empty_cache()
+    return result
 
 
 if __name__ == "__main__":

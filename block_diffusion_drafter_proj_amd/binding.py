@@ -208,7 +208,7 @@ def dflash_check(h: int, stream: int) -> None:
 
 
 KERNELS = ["fc_gemm", "norm", "kv_gemm", "scatter", "qkv_gemm", "qkv_post", "attn", "combine",
-           "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "finalize", "verify"]
+           "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "finalize", "verify", "select", "conv", "topk"]
 
 
 def dflash_profile_begin(h: int, mask: int) -> None:

@@ -831,7 +831,7 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     rc.d = d;
     rc.M = M;
     rc.err = at<unsigned int>(h, h->lay.err);
-    ProfScope ps(h, DFLASH_KERNEL_NORM, s);
+    ProfScope ps(h, DFLASH_KERNEL_CONV, s);
     launch_resid_conv(c.dtype, rc, s);
   };
   auto set_conv = [&](NormParams& np, int l, int k) {
@@ -1046,8 +1046,10 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     lp.keys = sat<unsigned long long>(sb, sc.keys);
     lp.lists = sat<unsigned long long>(sb, sc.tlists);
     lp.n_lists = logit_sel_lists(c.vocab);
-    ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
-    launch_logit_select(c.topk != 0, lp, s);
+    {
+      ProfScope ps(h, DFLASH_KERNEL_SELECT, s);
+      launch_logit_select(c.topk != 0, lp, s);
+    }
     if (c.topk) {
       TopkParams tp{};
       tp.lists = lp.lists;
@@ -1057,8 +1059,10 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
       tp.draft = draft;
       tp.topk_ids = topk_ids;
       tp.topk_logits = topk_logits;
+      ProfScope ps(h, DFLASH_KERNEL_TOPK, s);
       launch_topk_merge(tp, s);
     } else {
+      ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
       launch_finalize(lp.keys, M, c.vocab, draft, s);
     }
     return launched("draft head");
@@ -1079,7 +1083,7 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     tp.draft = draft;
     tp.topk_ids = topk_ids;
     tp.topk_logits = topk_logits;
-    ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
+    ProfScope ps(h, DFLASH_KERNEL_TOPK, s);
     launch_topk_merge(tp, s);
   } else {
     ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
