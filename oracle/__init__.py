@@ -28,6 +28,9 @@ Parity status per function (what pins it, see ``tests/test_oracle_*.py``):
                        through the decomposition and invariants: batch /
                        window / conv-identity / GQA-to-MHA reductions.
 * ``spec_generate``    pinned: equals ``greedy_ar`` exactly (lossless).
+* ``dflash2.select_path`` (DFlash-2 path selector) pinned: zero bilinear form
+                       gives the argmax chain; a hand-worked 3-position case
+                       with an asymmetric form; per-position logit shifts.
 """
 from .dflash_oracle import (  # noqa: F401
     DraftOracle,
@@ -43,4 +46,5 @@ from .dflash_oracle import (  # noqa: F401
     to_f32,
     verify_accept,
 )
+from .dflash2 import pair_scores, select_path, selector_vectors  # noqa: F401
 from .tiny_target import OracleDrafter, TinyTarget, greedy_ar, spec_generate  # noqa: F401
