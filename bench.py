@@ -17,7 +17,8 @@ Default workload ``qwen3_8b``:
 ``--config`` selects another workload of ``synth.CONFIGS``:
   * ``llama31_8b``: block 10, context 8192;
   * ``coder_b64``: 8 layers, 64 requests with ragged contexts U[512, 8192];
-  * ``dflash2_long``: conv taps and top-16, batch 4, context 32768 with a
+  * ``dflash2_long``: conv taps, top-16 and the path selector (rank 256;
+    the target verifies the path), batch 4, context 32768 with a
     4096-token window.
 
 Inputs:
@@ -353,8 +354,13 @@ def run_workload(config, steps, warmup, cpu=False):
     last0 = [int(x) for x in synth.rng(shape["seed"], synth.S_ACCEPT, 98).integers(0, V, size=n)]
     last0_dev = torch.tensor(last0, dtype=torch.int32, device=dev)
 
+    # with a path selector (DFlash 2) the path through the top-16 lists is what the target verifies
+    sel = bool(shape.get("selector_rank"))
+    path_out = torch.empty((n, B), dtype=torch.int32, device=dev) if sel else None
+
     def draft(last_dev):
-        return dr.draft(slots, last_dev if conv else None, out=out, topk_ids=tk_ids, topk_logits=tk_val)
+        d_ = dr.draft(slots, last_dev if conv else None, out=out, topk_ids=tk_ids, topk_logits=tk_val)
+        return dr.select_path(tk_ids, tk_val, path=path_out) if sel else d_
 
     # ---- draft-only rate at fixed context (state is unchanged by a draft) ----
     for _ in range(warmup):
@@ -418,8 +424,8 @@ def run_workload(config, steps, warmup, cpu=False):
     lastbuf = torch.empty((n_cycles, n), dtype=torch.int32, device=dev)
 
     def cycle(i):
-        draft(lastbuf[i - 1] if i else last0_dev)
-        dr.verify(out, Gs[i], acc[i], com[i], lastbuf[i])
+        toks = draft(lastbuf[i - 1] if i else last0_dev)
+        dr.verify(toks, Gs[i], acc[i], com[i], lastbuf[i])
         dr.inject(slots, nnew[i], Hc[i])
 
     for i in range(warmup):
@@ -543,6 +549,11 @@ def run_workload(config, steps, warmup, cpu=False):
                 "counted": "the selection pass that keeps sorted top-16 lists from the split-K logits, and "
                            "the merge of the lists (at more than 64 rows the lists come from the LM head's "
                            "epilogue and only the merge is counted)"}
+        if sel:
+            shares["path_selector"] = {
+                "ms_per_cycle": breakdown.get("path", 0.0),
+                "share": round(breakdown.get("path", 0.0) / cycle_ms, 4),
+                "counted": "the path walk through the top-16 lists (pair scores on the matrix cores)"}
         shares["pages"] = "0.7 % (conv) and 0.6 % (path selector) of the cycle, hardware not stated"
         result["shares_of_cycle"] = shares
     if cpu:

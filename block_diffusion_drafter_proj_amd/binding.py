@@ -43,7 +43,8 @@ class DFlashConfig(ctypes.Structure):
         "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "vocab", "n_layers",
         "block_size", "n_feat", "dtype", "mask_token_id", "page_size", "window", "conv2",
         "topk", "max_batch", "max_pages", "max_pages_per_req", "max_position",
-        "max_inject_rows")] + [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+        "max_inject_rows")] + [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                               ("selector_rank", ctypes.c_int32)]
 
 
 class DFlashLayerWeights(ctypes.Structure):
@@ -57,7 +58,7 @@ class DFlashDraftDebug(ctypes.Structure):
 
 class DFlashWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("embed", "lm_head", "fc", "fc_norm", "final_norm")] + [
-        ("layers", DFlashLayerWeights * MAX_LAYERS)]
+        ("layers", DFlashLayerWeights * MAX_LAYERS), ("sel_u", ctypes.c_void_p), ("sel_v", ctypes.c_void_p)]
 
 
 _lib = None
@@ -90,6 +91,7 @@ def lib() -> ctypes.CDLL:
             "dflash_draft_block_static": (i32, [vp, vp, i32, pi32, vp, vp, vp, vp,
                                                 ctypes.POINTER(DFlashDraftDebug)]),
             "dflash_draft_static_bytes": (sz, [ctypes.POINTER(DFlashConfig), i32]),
+            "dflash_select_path": (i32, [vp, vp, i32, vp, vp, vp, vp]),
             "dflash_verify_accept": (i32, [vp, vp, i32, vp, vp, vp, vp, vp]),
             "dflash_check": (i32, [vp, vp]),
             "dflash_profile_begin": (i32, [vp, ctypes.c_uint32]),
@@ -195,6 +197,13 @@ def dflash_draft_static_bytes(cfg: DFlashConfig, n_req: int) -> int:
     return int(lib().dflash_draft_static_bytes(ctypes.byref(cfg), n_req))
 
 
+def dflash_select_path(h: int, stream: int, n_req: int, topk_ids: int, topk_logits: int, path: int,
+                       step_scores: int = 0) -> None:
+    vp = ctypes.c_void_p
+    _check(lib().dflash_select_path(vp(h), vp(stream), n_req, vp(topk_ids or None), vp(topk_logits or None),
+                                    vp(path or None), vp(step_scores or None)))
+
+
 def dflash_verify_accept(h: int, stream: int, n_req: int, draft: int, target_greedy: int,
                          accept_len: int, committed: int, last_token: int) -> None:
     vp = ctypes.c_void_p
@@ -208,7 +217,8 @@ def dflash_check(h: int, stream: int) -> None:
 
 
 KERNELS = ["fc_gemm", "norm", "kv_gemm", "scatter", "qkv_gemm", "qkv_post", "attn", "combine",
-           "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "finalize", "verify", "select", "conv", "topk"]
+           "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "finalize", "verify", "select", "conv", "topk",
+           "path"]
 
 
 def dflash_profile_begin(h: int, mask: int) -> None:

@@ -250,6 +250,21 @@ void launch_resid_conv(int dtype, const ResidConvParams& p, hipStream_t s);
 void launch_topk_merge(const TopkParams& p, hipStream_t s);
 void launch_finalize(const unsigned long long* keys, int rows, int vocab, int* draft,
                      hipStream_t s);
+// DFlash-2 path selector: projected embedding tables (once) and the greedy
+// path per request over its top-16 lists.
+struct PathParams {
+  const int* topk_ids;       // [n_req][B][16]
+  const float* topk_logits;  // [n_req][B][16]
+  const float* tu;           // [V][r] = E W_u^T
+  const float* tv;           // [V][r] = E W_v^T
+  int B, r, vocab;
+  int* path;           // [n_req][B]
+  float* step_scores;  // [n_req][B] or NULL
+  unsigned int* err;
+};
+void launch_sel_table(int dtype, const void* embed, const void* wu, const void* wv, float* tu, float* tv, int V,
+                      int d, int r, hipStream_t s);
+void launch_select_path(const PathParams& p, int n_req, hipStream_t s);
 void launch_verify(int n_req, int B, int vocab, const int* draft, const int* greedy,
                    int* accept, int* committed, int* last, unsigned int* err, hipStream_t s);
 

@@ -238,9 +238,11 @@ Layout make_layout(const dflash_config& c) {
 }
 
 // Packed (MFMA fragment order) copies of every weight matrix.
+// With a path selector, also the projected embedding tables (fp32 [V, r]).
 struct PackedLayout {
   size_t lm_head, fc, wqkv[DFLASH_MAX_LAYERS], wo[DFLASH_MAX_LAYERS], wgateup[DFLASH_MAX_LAYERS],
       wdown[DFLASH_MAX_LAYERS];
+  size_t sel_u, sel_v;
   size_t total;
 };
 
@@ -262,6 +264,13 @@ PackedLayout make_packed(const dflash_config& c) {
     P.wo[l] = take(d, qd);
     P.wgateup[l] = take(2 * c.ffn, d);
     P.wdown[l] = take(d, c.ffn);
+  }
+  if (c.selector_rank) {
+    const size_t tb = sizeof(float) * (size_t)c.vocab * c.selector_rank;
+    P.sel_u = off;
+    off = align_up(off + tb);
+    P.sel_v = off;
+    off = align_up(off + tb);
   }
   P.total = off;
   return P;
@@ -298,6 +307,9 @@ dflash_status validate(const dflash_config* c) {
   if (c->max_position < c->block_size + 2) return bad("max_position too small");
   if (c->max_inject_rows < 1) return bad("max_inject_rows must be positive");
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) return bad("rms_eps and rope_theta must be positive");
+  if (c->selector_rank < 0 || c->selector_rank > 512 || c->selector_rank % 64)
+    return bad("selector_rank must be 0 or a multiple of 64 up to 512");
+  if (c->selector_rank && c->topk != DFLASH_MAX_TOPK) return bad("the path selector needs topk 16");
   // the LM head and SwiGLU GEMMs run unsplit: K = hidden must fit 16 waves
   const int max_d = 16 * gemm_kblock(c->dtype, 1);
   if (c->hidden > max_d)
@@ -387,6 +399,9 @@ dflash_status ensure_device(dflash_handle* h) {
     launch_pack(c.dtype, lw.wgateup, h->packed + h->pk.wgateup[l], 2 * c.ffn, d, nullptr);
     launch_pack(c.dtype, lw.wdown, h->packed + h->pk.wdown[l], d, c.ffn, nullptr);
   }
+  if (c.selector_rank)
+    launch_sel_table(c.dtype, h->w.embed, h->w.sel_u, h->w.sel_v, reinterpret_cast<float*>(h->packed + h->pk.sel_u),
+                     reinterpret_cast<float*>(h->packed + h->pk.sel_v), c.vocab, d, c.selector_rank, nullptr);
   if ((e = hipGetLastError())) return hip_fail(e, "weight packing");
   if ((e = hipDeviceSynchronize())) return hip_fail(e, "device init");
   h->dev_init = true;
@@ -532,6 +547,8 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
       return fail(DFLASH_E_INVALID, "layer %d: a weight pointer is NULL", l);
     if (cfg->conv2 && !lw.conv) return fail(DFLASH_E_INVALID, "layer %d: conv taps are NULL", l);
   }
+  if (cfg->selector_rank && (!w->sel_u || !w->sel_v))
+    return fail(DFLASH_E_INVALID, "selector_rank is set but sel_u / sel_v are NULL");
   dflash_handle* h = new dflash_handle();
   h->cfg = *cfg;
   h->w = *w;
@@ -1109,6 +1126,34 @@ dflash_status dflash_draft_block_static(dflash_handle* h, void* stream, int32_t 
 size_t dflash_draft_static_bytes(const dflash_config* cfg, int32_t n_req) {
   if (validate(cfg) != DFLASH_OK || n_req < 1 || n_req > cfg->max_batch) return 0;
   return make_scratch(*cfg, n_req, false).total;
+}
+
+dflash_status dflash_select_path(dflash_handle* h, void* stream, int32_t n_req, const int32_t* topk_ids,
+                                 const float* topk_logits, int32_t* path, float* step_scores) {
+  if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
+  const dflash_config& c = h->cfg;
+  if (!c.selector_rank) return fail(DFLASH_E_UNSUPPORTED, "the handle has no path selector (selector_rank 0)");
+  if (n_req < 1 || n_req > c.max_batch) return fail(DFLASH_E_INVALID, "n_req %d out of [1, %d]", n_req, c.max_batch);
+  if (!topk_ids || !topk_logits || !path) return fail(DFLASH_E_INVALID, "a path selector pointer is NULL");
+  dflash_status st = ensure_device(h);
+  if (st) return st;
+  PathParams pp{};
+  pp.topk_ids = topk_ids;
+  pp.topk_logits = topk_logits;
+  pp.tu = reinterpret_cast<const float*>(h->packed + h->pk.sel_u);
+  pp.tv = reinterpret_cast<const float*>(h->packed + h->pk.sel_v);
+  pp.B = c.block_size;
+  pp.r = c.selector_rank;
+  pp.vocab = c.vocab;
+  pp.path = path;
+  pp.step_scores = step_scores;
+  pp.err = at<unsigned int>(h, h->lay.err);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  {
+    ProfScope ps(h, DFLASH_KERNEL_PATH, s);
+    launch_select_path(pp, n_req, s);
+  }
+  return launched("path selector");
 }
 
 dflash_status dflash_verify_accept(dflash_handle* h, void* stream, int32_t n_req,

@@ -46,6 +46,7 @@ def make_config(shape: dict, *, max_batch: int, max_pages: int, max_pages_per_re
     c.max_inject_rows = max_inject_rows
     c.rms_eps = shape["rms_eps"]
     c.rope_theta = shape["rope_theta"]
+    c.selector_rank = int(shape.get("selector_rank") or 0)
     return c
 
 
@@ -87,6 +88,9 @@ class Drafter:
             L.attn_norm = up(lw["attn_norm"])
             L.mlp_norm = up(lw["mlp_norm"])
             L.conv = up(lw["conv"]) if "conv" in lw else None
+        if self.cfg.selector_rank:
+            w.sel_u = up(weights["sel_u"])
+            w.sel_v = up(weights["sel_v"])
         self.w = w
         kvb = B.dflash_kv_pool_bytes(self.cfg)
         wsb = B.dflash_workspace_bytes(self.cfg)
@@ -146,6 +150,15 @@ class Drafter:
                              ptr(topk_ids), ptr(topk_logits), ptr(debug_logits), ptr(debug_hidden),
                              ptr(hidden_in))
         return out
+
+    def select_path(self, topk_ids: torch.Tensor, topk_logits: torch.Tensor, path=None, step_scores=None):
+        """DFlash-2 path through the top-16 lists [n, B, 16] -> path [n, B]."""
+        n = topk_ids.shape[0]
+        path = path if path is not None else torch.empty((n, self.cfg.block_size), dtype=torch.int32,
+                                                          device=self.dev)
+        B.dflash_select_path(self.h, self.stream, n, topk_ids.data_ptr(), topk_logits.data_ptr(), path.data_ptr(),
+                             step_scores.data_ptr() if step_scores is not None else 0)
+        return path
 
     def verify(self, draft: torch.Tensor, greedy: torch.Tensor, accept=None, committed=None, last=None):
         n = draft.shape[0]

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define DFLASH_ABI_VERSION 1
+#define DFLASH_ABI_VERSION 2
 #define DFLASH_MAX_LAYERS 16
 #define DFLASH_MAX_FEAT 8
 #define DFLASH_MAX_BATCH 256
@@ -80,7 +80,8 @@ typedef enum { DFLASH_BF16 = 0, DFLASH_F32 = 1 } dflash_dtype;
  *   n_q_heads/n_kv_heads <= 8; 1 <= block_size <= 16; page_size == 16;
  *   1 <= n_layers <= DFLASH_MAX_LAYERS; 1 <= n_feat <= DFLASH_MAX_FEAT;
  *   0 <= mask_token_id < vocab; window 0 (unbounded) or a positive multiple
- *   of 16; topk 0 or 16; max_batch <= DFLASH_MAX_BATCH. */
+ *   of 16; topk 0 or 16; max_batch <= DFLASH_MAX_BATCH; selector_rank 0,
+ *   or a multiple of 64 up to 512 with topk 16. */
 typedef struct dflash_config {
   int32_t hidden;            /* d */
   int32_t n_q_heads;         /* Hq */
@@ -104,6 +105,7 @@ typedef struct dflash_config {
   int32_t max_inject_rows;   /* rows per internal inject chunk (workspace size) */
   float rms_eps;             /* RMSNorm epsilon */
   float rope_theta;          /* RoPE base */
+  int32_t selector_rank;     /* DFlash-2 path selector rank r ([guide] 7); 0 = none */
 } dflash_config;
 
 /* Per-layer weights (device pointers, dtype of the config).
@@ -121,10 +123,14 @@ typedef struct dflash_layer_weights {
 /* Model weights (device pointers).
  *   embed [V, d] and lm_head [V, d] are the target's, shared by the draft
  *   ([guide] 3.1); fc [d, n_feat*d] and fc_norm [d] form the context
- *   projection ([guide] 3.2); final_norm [d] is the draft's last RMSNorm. */
+ *   projection ([guide] 3.2); final_norm [d] is the draft's last RMSNorm.
+ *   sel_u, sel_v [r, d]: the path selector's low-rank bilinear form
+ *   s(a, b) = (sel_u E[a]) . (sel_v E[b]) over shared-embedding rows
+ *   ([guide] 7), NULL when selector_rank == 0. */
 typedef struct dflash_weights {
   const void *embed, *lm_head, *fc, *fc_norm, *final_norm;
   dflash_layer_weights layers[DFLASH_MAX_LAYERS];
+  const void *sel_u, *sel_v;
 } dflash_weights;
 
 typedef struct dflash_handle dflash_handle;
@@ -258,6 +264,26 @@ dflash_status dflash_draft_block_static(dflash_handle *h, void *stream, int32_t 
  * Host only. */
 size_t dflash_draft_static_bytes(const dflash_config *cfg, int32_t n_req);
 
+/* DFlash-2 path selector ([guide] section 7, path selector bullet): from
+ * the top-16 candidates of every block position (dflash_draft_block's
+ * topk_ids / topk_logits), one path per request: position 0 takes its top-1
+ * candidate; position i+1 takes the candidate b maximising
+ *   topk_logits[i+1][b] + (sel_u E[c_i]) . (sel_v E[b])
+ * with c_i the candidate chosen at position i (ties to the lower candidate
+ * index).  The path replaces the argmax drafts in dflash_verify_accept.
+ *   topk_ids     device [n_req, B, 16] int32 (ids outside [0, vocab) are
+ *                clamped and set the sticky error word)
+ *   topk_logits  device [n_req, B, 16] fp32
+ *   path         device [n_req, B] int32 output
+ *   step_scores  device [n_req, B] fp32 output (the chosen step's score; for
+ *                position 0 its logit), or NULL
+ * DFLASH_E_UNSUPPORTED when the handle has no selector (selector_rank 0).
+ * The projected embedding rows sel_u E and sel_v E (fp32 [V, r] each) are
+ * computed once at device initialisation into the packed-weights buffer. */
+dflash_status dflash_select_path(dflash_handle *h, void *stream, int32_t n_req,
+                                 const int32_t *topk_ids, const float *topk_logits,
+                                 int32_t *path, float *step_scores);
+
 /* Step 5 ([news] "DFlash 2 的核心：一次写一块"; [guide] 3.3): a = number of
  * leading positions where draft equals the target's greedy token; commits
  * draft[0..a) followed by target_greedy[a], which becomes the next pending
@@ -291,7 +317,8 @@ typedef enum {
   DFLASH_KERNEL_SELECT = 14,     /* selection pass over split-K partial logits */
   DFLASH_KERNEL_CONV = 15,       /* conv taps of the output points */
   DFLASH_KERNEL_TOPK = 16,       /* merge of the top-16 lists */
-  DFLASH_KERNEL_COUNT = 17
+  DFLASH_KERNEL_PATH = 17,       /* DFlash-2 path selector */
+  DFLASH_KERNEL_COUNT = 18
 } dflash_kernel;
 
 /* Launch timing for measurement runs.  After dflash_profile_begin(h, mask),

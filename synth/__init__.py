@@ -41,7 +41,7 @@ S_TARGET = 6
 _BASE = dict(
     hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn=12288,
     vocab=151936, n_layers=5, block_size=16, n_feat=5, dtype="bf16",
-    rope_theta=1.0e6, rms_eps=1.0e-6, window=0, conv2=0, topk=0,
+    rope_theta=1.0e6, rms_eps=1.0e-6, window=0, conv2=0, topk=0, selector_rank=0,
     batch=1, ctx=4096, ctx_range=None, target_layers=36, page_size=16,
     seed=2,
 )
@@ -62,7 +62,7 @@ CONFIGS = {
         n_layers=8, batch=64, ctx=None, ctx_range=(512, 8192), seed=4,
     ),
     "dflash2_long": dict(
-        conv2=1, topk=16, ctx=32768, window=4096, batch=4, seed=5,
+        conv2=1, topk=16, ctx=32768, window=4096, batch=4, seed=5, selector_rank=256,
     ),
     # parity cases
     "small_bf16": dict(
@@ -91,7 +91,7 @@ CONFIGS = {
     "small_conv": dict(
         hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1536,
         vocab=3001, n_layers=2, conv2=1, topk=16, window=128, batch=2,
-        ctx=500, seed=15,
+        ctx=500, seed=15, selector_rank=64, sel_std=0.3,
     ),
 }
 
@@ -152,7 +152,7 @@ def _normal(seed, stream, keys, shape, std, mean=0.0):
 
 # tensor ids for weight streams
 _TID = dict(embed=0, lm_head=1, fc=2, fc_norm=3, final_norm=4, wqkv=10,
-            wo=11, wgateup=12, wdown=13, attn_norm=14, mlp_norm=15, conv=16)
+            wo=11, wgateup=12, wdown=13, attn_norm=14, mlp_norm=15, conv=16, sel_u=20, sel_v=21)
 
 
 def make_weights(cfg: dict, seed: int | None = None, norm_std: float = 0.0,
@@ -165,6 +165,8 @@ def make_weights(cfg: dict, seed: int | None = None, norm_std: float = 0.0,
     Every matrix is N(0, 0.02).  RMSNorm gains are 1 (``norm_std`` > 0 draws
     them as 1 + N(0, norm_std) instead, to make the gain visible in tests).
     Conv taps (when ``conv2``) are w0 = 1 + N(0, 0.02), w1 = N(0, 0.02).
+    The path selector's forms (when ``selector_rank``) are [r, d] matrices of
+    N(0, cfg["sel_std"]) (0.02 unless the shape says otherwise).
     """
     seed = cfg["seed"] if seed is None else seed
     d, hq, hkv, dh = cfg["hidden"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
@@ -201,7 +203,22 @@ def make_weights(cfg: dict, seed: int | None = None, norm_std: float = 0.0,
             c[:, 0, :] += 1.0
             lw["conv"] = to_storage(c, dt)
         w["layers"].append(lw)
+    r = int(cfg.get("selector_rank") or 0)
+    if r:
+        sd = float(cfg.get("sel_std", 0.02))
+        w["sel_u"] = to_storage(_normal(seed, S_WEIGHTS, (_TID["sel_u"], 0), (r, d), sd), dt)
+        w["sel_v"] = to_storage(_normal(seed, S_WEIGHTS, (_TID["sel_v"], 0), (r, d), sd), dt)
     return w
+
+
+def candidate_lists(cfg: dict, n_req: int, key: int = 0):
+    """Synthetic top-16 lists for the path selector: per request and block
+    position 16 distinct token ids and logits sorted descending, N(0, 2)."""
+    g = rng(cfg["seed"], S_TARGET, 31, key)
+    B, V = cfg["block_size"], cfg["vocab"]
+    ids = np.stack([np.stack([g.choice(V, size=16, replace=False) for _ in range(B)]) for _ in range(n_req)])
+    lg = -np.sort(-g.standard_normal((n_req, B, 16)) * 2.0, axis=-1)
+    return ids.astype(np.int32), lg.astype(np.float32)
 
 
 def context_lengths(cfg: dict) -> list[int]:

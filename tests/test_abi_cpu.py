@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function():
     assert len(names) >= 14
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/dflash.h but not exported"
-    assert B.dflash_abi_version() == 1
+    assert B.dflash_abi_version() == 2
 
 
 def test_feature_layers_entry_point_matches_rule():
@@ -191,3 +191,40 @@ def test_profiling_calls_without_launches(handle):
     B.dflash_profile_mask(h, 0)
     B.dflash_profile_mask(h, 0xFFFFFFFF)  # bits of unknown classes are ignored
     assert B.dflash_profile_end(h) == {}
+
+
+def test_selector_config_rules_and_entry_validation():
+    """The path selector needs topk 16 and a rank that is a multiple of 64 up
+    to 512; its entry point refuses a handle without one before any device
+    work (DFLASH_E_UNSUPPORTED)."""
+    for r, topk, ok in ((64, 16, True), (256, 16, True), (512, 16, True), (32, 16, False), (576, 16, False),
+                        (-64, 16, False), (64, 0, False)):
+        c = _cfg("small_conv", max_batch=2)
+        c.selector_rank = r
+        c.topk = topk
+        if ok:
+            B.dflash_validate_config(c)
+        else:
+            with pytest.raises(B.DFlashError) as e:
+                B.dflash_validate_config(c)
+            assert e.value.status == B.E_INVALID
+    # packed bytes grow by the two fp32 [V, r] tables
+    c0 = _cfg("small_conv", max_batch=2)
+    c0.selector_rank = 0
+    c1 = _cfg("small_conv", max_batch=2)
+    c1.selector_rank = 64
+    grow = B.dflash_packed_weights_bytes(c1) - B.dflash_packed_weights_bytes(c0)
+    assert 2 * 3001 * 64 * 4 <= grow < 2 * 3001 * 64 * 4 + 512
+    # a handle without a selector: refused on the host
+    h = B.dflash_create(c0, _fake_weights(c0.n_layers, conv=True), 1 << 30, 2 << 30, 3 << 30)
+    try:
+        with pytest.raises(B.DFlashError) as e:
+            B.dflash_select_path(h, 0, 1, 1 << 20, 1 << 20, 1 << 20)
+        assert e.value.status == B.E_UNSUPPORTED
+    finally:
+        B.dflash_destroy(h)
+    # a selector handle needs both forms
+    w = _fake_weights(c1.n_layers, conv=True)
+    with pytest.raises(B.DFlashError) as e:
+        B.dflash_create(c1, w, 1 << 30, 2 << 30, 3 << 30)
+    assert e.value.status == B.E_INVALID
