@@ -539,8 +539,8 @@ def run_workload(config, steps, warmup, cpu=False):
             shares["two_tap_conv"] = {
                 "ms_per_cycle": breakdown.get("conv", 0.0),
                 "share": round(breakdown.get("conv", 0.0) / cycle_ms, 4),
-                "counted": "the conv-tap launches at the O and down outputs; the taps at the attention "
-                           "and MLP inputs run inside the norms and are not counted"}
+                "counted": "the norm launches that apply the conv taps (all four points run inside them); "
+                           "an upper bound, since the RMSNorm work of those launches is included"}
         if topk:
             sel = breakdown.get("select", 0.0) + breakdown.get("topk", 0.0)
             shares["top16_selection"] = {

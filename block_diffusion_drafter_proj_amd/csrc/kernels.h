@@ -73,7 +73,11 @@ struct GemmPlan {
 
 // Row-wise RMSNorm of fp32 rows into the storage dtype.  The input row is
 //   x = (init_row ? init_row : x_in ? x_in[row] : 0) + sum_p part[p][row]
-// and is written back to x_out[row] when x_out is set.
+// or, with oconv (the DFlash-2 conv at the producing GEMM's output),
+//   x = x_in[row] + w0 * y[row] + w1 * y[row-1],  y[r] = sum_p part[p][r],
+// with y[row-1] = embed[last_token] at the start of each request's block;
+// x is written to x_out[row] when x_out is set (x_out must differ from x_in
+// with oconv and the input conv, whose previous row re-reads x_in).
 struct NormParams {
   const float* x_in;       // [M, ld] fp32 residual, or NULL
   const void* init_row;    // storage dtype [d]: every row starts from it, or NULL
@@ -92,22 +96,10 @@ struct NormParams {
   // two-tap conv of the normalised rows (DFlash 2): out_i = w0*n_i + w1*n_{i-1}
   // inside each request's block of B rows; row 0 reads embed[last_token[r]]
   const void* conv;        // [2][d] taps (w0, w1) or NULL
+  const void* oconv;       // [2][d] taps of the producing GEMM's output conv, or NULL
   const void* embed;       // [V, d]
   const int* last_token;   // [n_req]
   int B, vocab;
-  unsigned int* err;
-};
-
-// h_i += w0*y_i + w1*y_{i-1} with y the sum of a GEMM's split-K partials and
-// y_{-1} = embed[last_token[r]] at the start of each request's block.
-struct ResidConvParams {
-  float* h;  // [M, d]
-  const float* part;
-  int n_part;
-  const void* conv;  // [2][d]
-  const void* embed;
-  const int* last_token;
-  int B, vocab, d, M;
   unsigned int* err;
 };
 
@@ -246,7 +238,6 @@ __host__ __device__ inline int split_pages(int n_units, int target, int cap) {
 }
 void launch_combine(int dtype, int dh, const CombineParams& p, hipStream_t s);
 void launch_scatter(int dtype, int dh, const ScatterParams& p, hipStream_t s);
-void launch_resid_conv(int dtype, const ResidConvParams& p, hipStream_t s);
 void launch_topk_merge(const TopkParams& p, hipStream_t s);
 void launch_finalize(const unsigned long long* keys, int rows, int vocab, int* draft,
                      hipStream_t s);

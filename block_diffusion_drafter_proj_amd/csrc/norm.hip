@@ -34,6 +34,55 @@ __device__ __forceinline__ float block_sum(float v, float* red, int slot) {
   return tot;
 }
 
+// Sum of the split-K partials of one row.
+__device__ __forceinline__ f32x4 part_sum4(const NormParams& p, int row, int k, long long plane) {
+  f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float* pp = p.part + (long long)row * p.d + k;
+  for (int q0 = 0; q0 < p.n_part; q0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q0 + q < p.n_part) v[q] = *reinterpret_cast<const f32x4*>(pp + (q0 + q) * plane);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q0 + q < p.n_part) y += v[q];
+  }
+  return y;
+}
+
+// 4 elements of the embedding row of the request's last verified token (the
+// block start's previous row at every conv point); a token outside the
+// vocabulary is clamped and recorded in the error word.
+template <typename T>
+__device__ __forceinline__ f32x4 last_embed4(const NormParams& p, int row, int k) {
+  int tok = p.last_token[row / p.B];
+  if (tok < 0 || tok >= p.vocab) {
+    if (threadIdx.x == 0) atomicOr(p.err, 1u);
+    tok = 0;
+  }
+  const T* e = reinterpret_cast<const T*>(p.embed) + (long long)tok * p.d + k;
+  f32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = to_f(e[i]);
+  return v;
+}
+
+// Residual row with a conv'd GEMM output (DFlash 2, output points):
+// x[row] = x_in[row] + w0 * y[row] + w1 * y[row-1], y the sum of the GEMM's
+// split-K partials and y[row-1] the last verified token's embedding at the
+// start of each request's block.
+template <typename T>
+__device__ __forceinline__ f32x4 load_row4_oconv(const NormParams& p, int row, int k, long long plane,
+                                                 f32x4 w0, f32x4 w1) {
+  const f32x4 h = *reinterpret_cast<const f32x4*>(p.x_in + (long long)row * p.ldx + k);
+  const f32x4 y = part_sum4(p, row, k, plane);
+  const f32x4 yp = (row % p.B) == 0 ? last_embed4<T>(p, row, k) : part_sum4(p, row - 1, k, plane);
+  f32x4 x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = h[i] + w0[i] * y[i] + w1[i] * yp[i];
+  return x;
+}
+
 template <typename T>
 __device__ __forceinline__ f32x4 load_row4(const NormParams& p, int row, int k, long long plane) {
   f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -70,10 +119,22 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(NormParams p) {
   const int t = threadIdx.x;
   const int k = 4 * t;
   const long long plane = (long long)p.M * p.d;
-  const f32x4 x = load_row4<T>(p, row, k, plane);
   const bool first = p.conv && (row % p.B) == 0;
-  f32x4 xp = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (p.conv && !first) xp = load_row4<T>(p, row - 1, k, plane);
+  f32x4 x, xp = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (p.oconv) {  // the producing GEMM's output conv folded in (this row and, for the input conv, the previous)
+    f32x4 ow0, ow1;
+    const T* o0 = reinterpret_cast<const T*>(p.oconv) + k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ow0[i] = to_f(o0[i]);
+      ow1[i] = to_f(o0[p.d + i]);
+    }
+    x = load_row4_oconv<T>(p, row, k, plane, ow0, ow1);
+    if (p.conv && !first) xp = load_row4_oconv<T>(p, row - 1, k, plane, ow0, ow1);
+  } else {
+    x = load_row4<T>(p, row, k, plane);
+    if (p.conv && !first) xp = load_row4<T>(p, row - 1, k, plane);
+  }
   // the row-independent operands are requested with the row: the reduction's
   // barrier below would otherwise hold their loads back for a second round trip
   f32x4 gm, cw0 = f32x4{0.f, 0.f, 0.f, 0.f}, cw1 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -100,14 +161,7 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(NormParams p) {
   if (p.conv) {
     f32x4 prev;
     if (first) {
-      int tok = p.last_token[row / p.B];
-      if (tok < 0 || tok >= p.vocab) {
-        if (t == 0) atomicOr(p.err, 1u);
-        tok = 0;
-      }
-      const T* e = reinterpret_cast<const T*>(p.embed) + (long long)tok * p.d + k;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) prev[i] = to_f(e[i]);
+      prev = last_embed4<T>(p, row, k);
     } else {
       const float totp = block_sum((xp[0] * xp[0] + xp[1] * xp[1]) + (xp[2] * xp[2] + xp[3] * xp[3]), red, 1);
       const float rp = 1.0f / sqrtf(totp / (float)p.d + p.eps);
@@ -217,54 +271,11 @@ __global__ __launch_bounds__(1024) void k_rmsnorm_frag(NormParams p) {
   if (p.zero_keys && t < ROWS && live) p.zero_keys[row] = 0ull;
 }
 
-// Residual add of a conv'd GEMM output (DFlash 2): one workgroup per row.
-template <typename T>
-__global__ __launch_bounds__(1024) void k_resid_conv(ResidConvParams p) {
-  const int row = blockIdx.x;
-  const int k = 4 * threadIdx.x;
-  const long long plane = (long long)p.M * p.d;
-  auto sum_parts = [&](int rw) {
-    f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float* pp = p.part + (long long)rw * p.d + k;
-    for (int q = 0; q < p.n_part; ++q) y += *reinterpret_cast<const f32x4*>(pp + q * plane);
-    return y;
-  };
-  const f32x4 y = sum_parts(row);
-  f32x4 prev;
-  if (row % p.B == 0) {
-    int tok = p.last_token[row / p.B];
-    if (tok < 0 || tok >= p.vocab) {
-      if (threadIdx.x == 0) atomicOr(p.err, 1u);
-      tok = 0;
-    }
-    const T* e = reinterpret_cast<const T*>(p.embed) + (long long)tok * p.d + k;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) prev[i] = to_f(e[i]);
-  } else {
-    prev = sum_parts(row - 1);
-  }
-  const T* w0 = reinterpret_cast<const T*>(p.conv) + k;
-  const T* w1 = w0 + p.d;
-  f32x4* hp = reinterpret_cast<f32x4*>(p.h + (long long)row * p.d + k);
-  f32x4 h = *hp;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) h[i] += to_f(w0[i]) * y[i] + to_f(w1[i]) * prev[i];
-  *hp = h;
-}
-
 }  // namespace
-
-void launch_resid_conv(int dtype, const ResidConvParams& p, hipStream_t s) {
-  if (p.M <= 0) return;
-  if (dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(k_resid_conv<bf16>, dim3(p.M), dim3(p.d / 4), 0, s, p);
-  else
-    hipLaunchKernelGGL(k_resid_conv<float>, dim3(p.M), dim3(p.d / 4), 0, s, p);
-}
 
 void launch_rmsnorm(int dtype, const NormParams& p, hipStream_t s) {
   if (p.M <= 0) return;
-  if (p.out_packed && !p.conv && p.d % 256 == 0 && p.d <= 4096) {
+  if (p.out_packed && !p.conv && !p.oconv && p.d % 256 == 0 && p.d <= 4096) {
     constexpr int R = kNormRows;
     const int nt = std::min(kNormThreads, R * p.d / 8);  // R * d / 8 chunks, at most 8 per thread
     if (dtype == DFLASH_BF16)

@@ -152,7 +152,7 @@ size_t part_rows(const dflash_config& c, GemmPlan Plans::*f, int max_rows) {
 // read): the residual stream, GEMM inputs, split-K partial planes, attention
 // split partials, selection keys and lists, inject staging.
 struct Scratch {
-  size_t h, xa, xo, qkv, part_o, part_ml, nsplit, z, keys, tlists, lpart, opart, dpart;
+  size_t h, h2, xa, xo, qkv, part_o, part_ml, nsplit, z, keys, tlists, lpart, opart, dpart;
   size_t u, f, kvo;  // inject only (0 when not laid out)
   size_t total;
 };
@@ -179,6 +179,9 @@ Scratch make_scratch(const dflash_config& c, int n_req, bool inject) {
   const size_t qd = (size_t)c.n_q_heads * c.head_dim;
   const size_t qkvw = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   S.h = take(sizeof(float) * M * c.hidden);
+  // the conv variant alternates the residual stream between two buffers (a
+  // norm re-reads the previous row of its input while writing its output)
+  S.h2 = c.conv2 ? take(sizeof(float) * M * c.hidden) : 0;
   // GEMM inputs: rows rounded up to whole 16-row fragments (fragment order)
   const size_t M16 = (M + 15) / 16 * 16;
   S.xa = take(e * M16 * c.hidden);
@@ -834,23 +837,6 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
 
   // DFlash 2 two-tap conv: taps of point k of layer l, [2][d]
   auto conv_taps = [&](int l, int k) { return wptr(h->w.layers[l].conv, (size_t)k * 2 * d, e); };
-  // h += conv(sum of partials) for the conv variant, one launch
-  auto resid_conv = [&](const float* part, int n_part, int l, int k) {
-    ResidConvParams rc{};
-    rc.h = hbuf;
-    rc.part = part;
-    rc.n_part = n_part;
-    rc.conv = conv_taps(l, k);
-    rc.embed = h->w.embed;
-    rc.last_token = last_token;
-    rc.B = B;
-    rc.vocab = c.vocab;
-    rc.d = d;
-    rc.M = M;
-    rc.err = at<unsigned int>(h, h->lay.err);
-    ProfScope ps(h, DFLASH_KERNEL_CONV, s);
-    launch_resid_conv(c.dtype, rc, s);
-  };
   auto set_conv = [&](NormParams& np, int l, int k) {
     np.conv = conv_taps(l, k);
     np.embed = h->w.embed;
@@ -859,26 +845,45 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     np.vocab = c.vocab;
     np.err = at<unsigned int>(h, h->lay.err);
   };
+  // the output conv of the GEMM whose partials a norm adds (point k of layer l)
+  auto set_oconv = [&](NormParams& np, int l, int k, const float* part, int n_part) {
+    np.oconv = conv_taps(l, k);
+    np.part = part;
+    np.n_part = n_part;
+    np.embed = h->w.embed;
+    np.last_token = last_token;
+    np.B = B;
+    np.vocab = c.vocab;
+    np.err = at<unsigned int>(h, h->lay.err);
+  };
+  auto norm = [&](const NormParams& np) {
+    ProfScope ps(h, np.conv || np.oconv ? DFLASH_KERNEL_CONV : DFLASH_KERNEL_NORM, s);
+    launch_rmsnorm(c.dtype, np, s);
+  };
+  // conv variant: the residual stream alternates between hbuf and halt
+  float* halt = c.conv2 ? sat<float>(sb, sc.h2) : hbuf;
 
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& lw = h->w.layers[l];
     // residual: block init (layer 0) or h + previous layer's down-projection
     // partials (with the conv variant folded in by its own launch first)
     NormParams n1{};
+    n1.x_out = hbuf;
     if (hidden_in) {
       n1.x_in = hidden_in + (size_t)l * M * d;  // teacher forcing
     } else if (l == 0) {
       n1.init_row = wptr(h->w.embed, (size_t)c.mask_token_id * d, e);
-    } else if (c.conv2) {
-      resid_conv(dpart, pl.down.P, l - 1, 3);
+    } else if (c.conv2) {  // previous layer's down output through its conv, into the other buffer
       n1.x_in = hbuf;
+      set_oconv(n1, l - 1, 3, dpart, pl.down.P);
+      n1.x_out = halt;
+      std::swap(hbuf, halt);
     } else {
       n1.x_in = hbuf;
       n1.part = dpart;
       n1.n_part = pl.down.P;
     }
     if (c.conv2) set_conv(n1, l, 0);
-    n1.x_out = (hidden_in || l == 0 || !c.conv2) ? hbuf : nullptr;
     n1.ldx = d;
     n1.gamma = lw.attn_norm;
     n1.eps = c.rms_eps;
@@ -888,7 +893,7 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     n1.d = d;
     n1.M = M;
     n1.dbg = debug_hidden ? debug_hidden + (size_t)l * M * d : nullptr;
-    { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, n1, s); }
+    norm(n1);
 
     GemmParams g = gemm_in(sb + sc.xa, d);
     g.a_packed = n1.out_packed;
@@ -975,9 +980,11 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
 
     NormParams n2{};
     n2.x_in = hbuf;
-    if (c.conv2) {
-      resid_conv(opart, pl.o.P, l, 1);
+    if (c.conv2) {  // O output through its conv, into the other buffer
+      set_oconv(n2, l, 1, opart, pl.o.P);
       set_conv(n2, l, 2);
+      n2.x_out = halt;
+      std::swap(hbuf, halt);
     } else {
       n2.part = opart;
       n2.n_part = pl.o.P;
@@ -991,7 +998,7 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     n2.out_packed = pl.gateup.mt == 0;
     n2.d = d;
     n2.M = M;
-    { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, n2, s); }
+    norm(n2);
 
     GemmParams gu = gemm_in(sb + sc.xa, d);
     gu.a_packed = n2.out_packed;
@@ -1022,7 +1029,7 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
   if (hidden_in) {
     nf.x_in = hidden_in + (size_t)c.n_layers * M * d;  // teacher forcing
   } else if (c.conv2) {
-    resid_conv(dpart, pl.down.P, c.n_layers - 1, 3);
+    set_oconv(nf, c.n_layers - 1, 3, dpart, pl.down.P);
   } else {
     nf.part = dpart;
     nf.n_part = pl.down.P;
@@ -1038,7 +1045,7 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
   nf.M = M;
   nf.dbg = debug_hidden ? debug_hidden + (size_t)c.n_layers * M * d : nullptr;
   nf.zero_keys = sat<unsigned long long>(sb, sc.keys);
-  { ProfScope ps(h, DFLASH_KERNEL_NORM, s); launch_rmsnorm(c.dtype, nf, s); }
+  norm(nf);
 
   GemmParams gl = gemm_in(sb + sc.xa, d);
   gl.a_packed = nf.out_packed;

@@ -301,7 +301,7 @@ dflash_status dflash_verify_accept(dflash_handle *h, void *stream, int32_t n_req
 /* Kernel classes for optional launch timing. */
 typedef enum {
   DFLASH_KERNEL_FC_GEMM = 0,     /* inject: concat + projection */
-  DFLASH_KERNEL_NORM = 1,        /* every RMSNorm (with the conv taps of the input points) */
+  DFLASH_KERNEL_NORM = 1,        /* RMSNorms without DFlash-2 conv taps */
   DFLASH_KERNEL_KV_GEMM = 2,     /* inject: all-layer K/V projection */
   DFLASH_KERNEL_SCATTER = 3,     /* inject: RoPE + page scatter */
   DFLASH_KERNEL_QKV_GEMM = 4,
@@ -315,7 +315,7 @@ typedef enum {
   DFLASH_KERNEL_FINALIZE = 12,   /* argmax decode */
   DFLASH_KERNEL_VERIFY = 13,
   DFLASH_KERNEL_SELECT = 14,     /* selection pass over split-K partial logits */
-  DFLASH_KERNEL_CONV = 15,       /* conv taps of the output points */
+  DFLASH_KERNEL_CONV = 15,       /* RMSNorms that also apply DFlash-2 conv taps */
   DFLASH_KERNEL_TOPK = 16,       /* merge of the top-16 lists */
   DFLASH_KERNEL_PATH = 17,       /* DFlash-2 path selector */
   DFLASH_KERNEL_COUNT = 18
