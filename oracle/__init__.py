@@ -31,6 +31,14 @@ Parity status per function (what pins it, see ``tests/test_oracle_*.py``):
 * ``dflash2.select_path`` (DFlash-2 path selector) pinned: zero bilinear form
                        gives the argmax chain; a hand-worked 3-position case
                        with an asymmetric form; per-position logit shifts.
+* ``dflash2.warp_sorted``, ``draft_sample``, ``spec_verify_sample`` (sampled
+                       drafting, rejection-sampling verification) pinned:
+                       hand-worked temperature / top-k / top-p warps; Monte
+                       Carlo: the first committed token follows the target's
+                       distribution and the first draft is accepted with
+                       probability sum min(p, q); a draft equal to the target
+                       is always accepted; near-zero temperature reduces to
+                       greedy verification.
 """
 from .dflash_oracle import (  # noqa: F401
     DraftOracle,
@@ -46,5 +54,13 @@ from .dflash_oracle import (  # noqa: F401
     to_f32,
     verify_accept,
 )
-from .dflash2 import pair_scores, select_path, selector_vectors  # noqa: F401
+from .dflash2 import (  # noqa: F401
+    draft_sample,
+    pair_scores,
+    select_path,
+    selector_vectors,
+    spec_verify_sample,
+    target_distribution,
+    warp_sorted,
+)
 from .tiny_target import OracleDrafter, TinyTarget, greedy_ar, spec_generate  # noqa: F401
