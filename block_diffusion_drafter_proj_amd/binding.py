@@ -52,6 +52,10 @@ class DFlashLayerWeights(ctypes.Structure):
         "wqkv", "wo", "wgateup", "wdown", "attn_norm", "mlp_norm", "conv")]
 
 
+class DFlashSampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float)]
+
+
 class DFlashDraftDebug(ctypes.Structure):
     _fields_ = [("logits", ctypes.c_void_p), ("hidden", ctypes.c_void_p), ("hidden_in", ctypes.c_void_p)]
 
@@ -92,6 +96,9 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.POINTER(DFlashDraftDebug)]),
             "dflash_draft_static_bytes": (sz, [ctypes.POINTER(DFlashConfig), i32]),
             "dflash_select_path": (i32, [vp, vp, i32, vp, vp, vp, vp]),
+            "dflash_draft_sample": (i32, [vp, vp, i32, ctypes.POINTER(DFlashSampling), vp, vp, vp, vp]),
+            "dflash_verify_sample": (i32, [vp, vp, i32, ctypes.POINTER(DFlashSampling), vp, vp, vp, vp, vp,
+                                           vp, vp, vp]),
             "dflash_verify_accept": (i32, [vp, vp, i32, vp, vp, vp, vp, vp]),
             "dflash_check": (i32, [vp, vp]),
             "dflash_profile_begin": (i32, [vp, ctypes.c_uint32]),
@@ -204,6 +211,23 @@ def dflash_select_path(h: int, stream: int, n_req: int, topk_ids: int, topk_logi
                                     vp(path or None), vp(step_scores or None)))
 
 
+def dflash_draft_sample(h: int, stream: int, n_req: int, sampling: DFlashSampling, topk_ids: int,
+                        topk_logits: int, uniforms: int, draft: int) -> None:
+    vp = ctypes.c_void_p
+    _check(lib().dflash_draft_sample(vp(h), vp(stream), n_req, ctypes.byref(sampling), vp(topk_ids or None),
+                                     vp(topk_logits or None), vp(uniforms or None), vp(draft or None)))
+
+
+def dflash_verify_sample(h: int, stream: int, n_req: int, sampling: DFlashSampling, draft: int, topk_ids: int,
+                         topk_logits: int, target_logits: int, uniforms: int, accept_len: int, committed: int,
+                         last_token: int) -> None:
+    vp = ctypes.c_void_p
+    _check(lib().dflash_verify_sample(vp(h), vp(stream), n_req, ctypes.byref(sampling), vp(draft or None),
+                                      vp(topk_ids or None), vp(topk_logits or None), vp(target_logits or None),
+                                      vp(uniforms or None), vp(accept_len or None), vp(committed or None),
+                                      vp(last_token or None)))
+
+
 def dflash_verify_accept(h: int, stream: int, n_req: int, draft: int, target_greedy: int,
                          accept_len: int, committed: int, last_token: int) -> None:
     vp = ctypes.c_void_p
@@ -218,7 +242,7 @@ def dflash_check(h: int, stream: int) -> None:
 
 KERNELS = ["fc_gemm", "norm", "kv_gemm", "scatter", "qkv_gemm", "qkv_post", "attn", "combine",
            "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "finalize", "verify", "select", "conv", "topk",
-           "path"]
+           "path", "sample"]
 
 
 def dflash_profile_begin(h: int, mask: int) -> None:

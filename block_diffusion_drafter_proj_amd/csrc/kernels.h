@@ -256,6 +256,29 @@ struct PathParams {
 void launch_sel_table(int dtype, const void* embed, const void* wu, const void* wv, float* tu, float* tv, int V,
                       int d, int r, hipStream_t s);
 void launch_select_path(const PathParams& p, int n_req, hipStream_t s);
+// Sampled drafting and rejection-sampling verification (DFlash 2).
+struct SampleParams {
+  float temperature;
+  int top_k;    // 0 (whole vocabulary) or 1..64; the draft side caps it at 16
+  float top_p;  // (0, 1]; below 1 only with top_k >= 1
+  int B, vocab;
+  const int* dids;    // [n][B][16] the draft's top-16 lists
+  const float* dlog;  // [n][B][16]
+  const float* v;     // [n][B] uniforms of the draft's draws
+  int* draft;         // [n][B] drafted tokens (written by the draft draw, read by the verification)
+  const float* tlog;  // [n][B+1][V] the target's logits
+  const float* u;     // [n][B+1][2] uniforms: accept test, final draw
+  float* row_stat;    // [n][B+1][2] (max of L/T, normaliser) without top-k
+  int* row_ids;       // [n][B+1][64] kept top-k ids
+  float* row_p;       // [n][B+1][64] their warped probabilities
+  int* row_n;         // [n][B+1] kept count
+  int* accept;        // [n]
+  int* committed;     // [n][B+1]
+  int* last;          // [n]
+  unsigned int* err;
+};
+void launch_draft_sample(const SampleParams& p, int n_req, hipStream_t s);
+void launch_verify_sample(const SampleParams& p, int n_req, hipStream_t s);
 void launch_verify(int n_req, int B, int vocab, const int* draft, const int* greedy,
                    int* accept, int* committed, int* last, unsigned int* err, hipStream_t s);
 

@@ -91,7 +91,20 @@ __global__ __launch_bounds__(1024) void k_select_path(PathParams p) {
     const float* ua = p.tu + (long long)cid[wave][row] * p.r + 8 * g;
     const float* vb = p.tv + (long long)cid[wave + 1][row] * p.r + 8 * g;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < p.r / 32; ++s) acc = mfma_step(load8<float>(ua + 32 * s), load8<float>(vb + 32 * s), acc);
+    // the rows are scattered over the tables: request 4 k-steps of both
+    // operands before multiplying, so a pair waits for r / 128 round trips
+    const int nstep = p.r / 32;
+    for (int s0 = 0; s0 < nstep; s0 += 4) {
+      f32x8 a[4], b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = s0 + j < nstep;
+        a[j] = in ? load8<float>(ua + 32 * (s0 + j)) : zero8<float>();
+        b[j] = in ? load8<float>(vb + 32 * (s0 + j)) : zero8<float>();
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = mfma_step(a[j], b[j], acc);
+    }
     // C layout: lane l holds column l % 16 (candidate b of position i+1) and
     // rows 4 * (l / 16) + q (candidate a of position i)
 #pragma unroll

@@ -146,6 +146,10 @@ size_t part_rows(const dflash_config& c, GemmPlan Plans::*f, int max_rows) {
   return m;
 }
 
+// Per target row of the sampled verification: (max, normaliser), 64 kept
+// ids, 64 probabilities, the kept count (floats and ints of 4 bytes).
+constexpr int kSampleRowFloats = 2 + 64 + 64 + 1;
+
 // Device memory of a handle, in two parts.  State (kept across calls): slot
 // state, error word, page table, RoPE tables, and the block's q / K / V tiles
 // whose rows B..15 stay zero.  Scratch (rewritten by every call before it is
@@ -153,6 +157,7 @@ size_t part_rows(const dflash_config& c, GemmPlan Plans::*f, int max_rows) {
 // split partials, selection keys and lists, inject staging.
 struct Scratch {
   size_t h, h2, xa, xo, qkv, part_o, part_ml, nsplit, z, keys, tlists, lpart, opart, dpart;
+  size_t srow;       // sampled verification: per target row statistics and kept lists
   size_t u, f, kvo;  // inject only (0 when not laid out)
   size_t total;
 };
@@ -182,6 +187,7 @@ Scratch make_scratch(const dflash_config& c, int n_req, bool inject) {
   // the conv variant alternates the residual stream between two buffers (a
   // norm re-reads the previous row of its input while writing its output)
   S.h2 = c.conv2 ? take(sizeof(float) * M * c.hidden) : 0;
+  S.srow = c.topk ? take(sizeof(float) * (size_t)n_req * (c.block_size + 1) * kSampleRowFloats) : 0;
   // GEMM inputs: rows rounded up to whole 16-row fragments (fragment order)
   const size_t M16 = (M + 15) / 16 * 16;
   S.xa = take(e * M16 * c.hidden);
@@ -1161,6 +1167,87 @@ dflash_status dflash_select_path(dflash_handle* h, void* stream, int32_t n_req, 
     launch_select_path(pp, n_req, s);
   }
   return launched("path selector");
+}
+
+static dflash_status check_sampling(const dflash_handle* h, const dflash_sampling* sp) {
+  if (!sp) return fail(DFLASH_E_INVALID, "sampling settings are NULL");
+  if (!(sp->temperature >= 1e-2f && sp->temperature <= 1e3f))
+    return fail(DFLASH_E_INVALID, "temperature %g out of [0.01, 1000]", (double)sp->temperature);
+  if (sp->top_k < 0 || sp->top_k > 64) return fail(DFLASH_E_INVALID, "top_k %d out of [0, 64]", sp->top_k);
+  if (!(sp->top_p > 0.f && sp->top_p <= 1.f)) return fail(DFLASH_E_INVALID, "top_p %g out of (0, 1]", (double)sp->top_p);
+  if (sp->top_p < 1.f && sp->top_k == 0)
+    return fail(DFLASH_E_UNSUPPORTED, "top_p below 1 needs top_k >= 1 (no nucleus over the whole vocabulary)");
+  if (!h->cfg.topk) return fail(DFLASH_E_UNSUPPORTED, "sampled drafting needs the top-16 lists (topk 16)");
+  return DFLASH_OK;
+}
+
+static SampleParams sample_params(dflash_handle* h, const dflash_sampling* sp) {
+  SampleParams p{};
+  p.temperature = sp->temperature;
+  p.top_k = sp->top_k;
+  p.top_p = sp->top_p;
+  p.B = h->cfg.block_size;
+  p.vocab = h->cfg.vocab;
+  p.err = at<unsigned int>(h, h->lay.err);
+  return p;
+}
+
+dflash_status dflash_draft_sample(dflash_handle* h, void* stream, int32_t n_req, const dflash_sampling* sampling,
+                                  const int32_t* topk_ids, const float* topk_logits, const float* uniforms,
+                                  int32_t* draft) {
+  if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
+  dflash_status st = check_sampling(h, sampling);
+  if (st) return st;
+  if (n_req < 1 || n_req > h->cfg.max_batch) return fail(DFLASH_E_INVALID, "n_req %d out of [1, %d]", n_req, h->cfg.max_batch);
+  if (!topk_ids || !topk_logits || !uniforms || !draft) return fail(DFLASH_E_INVALID, "a draft-sample pointer is NULL");
+  st = ensure_device(h);
+  if (st) return st;
+  SampleParams p = sample_params(h, sampling);
+  p.dids = topk_ids;
+  p.dlog = topk_logits;
+  p.v = uniforms;
+  p.draft = draft;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  {
+    ProfScope ps(h, DFLASH_KERNEL_SAMPLE, s);
+    launch_draft_sample(p, n_req, s);
+  }
+  return launched("draft sample");
+}
+
+dflash_status dflash_verify_sample(dflash_handle* h, void* stream, int32_t n_req, const dflash_sampling* sampling,
+                                   const int32_t* draft, const int32_t* topk_ids, const float* topk_logits,
+                                   const float* target_logits, const float* uniforms, int32_t* accept_len,
+                                   int32_t* committed, int32_t* last_token) {
+  if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
+  dflash_status st = check_sampling(h, sampling);
+  if (st) return st;
+  if (n_req < 1 || n_req > h->cfg.max_batch) return fail(DFLASH_E_INVALID, "n_req %d out of [1, %d]", n_req, h->cfg.max_batch);
+  if (!draft || !topk_ids || !topk_logits || !target_logits || !uniforms || !accept_len || !committed || !last_token)
+    return fail(DFLASH_E_INVALID, "a verify-sample pointer is NULL");
+  st = ensure_device(h);
+  if (st) return st;
+  SampleParams p = sample_params(h, sampling);
+  p.dids = topk_ids;
+  p.dlog = topk_logits;
+  p.draft = const_cast<int32_t*>(draft);
+  p.tlog = target_logits;
+  p.u = uniforms;
+  const size_t rows = (size_t)n_req * (h->cfg.block_size + 1);
+  float* sr = reinterpret_cast<float*>(h->ws + h->lay.scratch + h->lay.sc.srow);
+  p.row_stat = sr;
+  p.row_ids = reinterpret_cast<int*>(sr + 2 * rows);
+  p.row_p = sr + (2 + 64) * rows;
+  p.row_n = reinterpret_cast<int*>(sr + (2 + 128) * rows);
+  p.accept = accept_len;
+  p.committed = committed;
+  p.last = last_token;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  {
+    ProfScope ps(h, DFLASH_KERNEL_VERIFY, s);
+    launch_verify_sample(p, n_req, s);
+  }
+  return launched("verify sample");
 }
 
 dflash_status dflash_verify_accept(dflash_handle* h, void* stream, int32_t n_req,

@@ -160,6 +160,26 @@ class Drafter:
                              step_scores.data_ptr() if step_scores is not None else 0)
         return path
 
+    def draft_sample(self, sampling, topk_ids, topk_logits, uniforms, out=None):
+        """Sampled drafting: one token per position from the top-16 lists."""
+        n = topk_ids.shape[0]
+        out = out if out is not None else torch.empty((n, self.cfg.block_size), dtype=torch.int32, device=self.dev)
+        B.dflash_draft_sample(self.h, self.stream, n, sampling, topk_ids.data_ptr(), topk_logits.data_ptr(),
+                              uniforms.data_ptr(), out.data_ptr())
+        return out
+
+    def verify_sample(self, sampling, draft, topk_ids, topk_logits, target_logits, uniforms):
+        """Rejection-sampling verification -> (accept [n], committed [n, B+1], last [n])."""
+        n = draft.shape[0]
+        Bk = self.cfg.block_size
+        accept = torch.empty(n, dtype=torch.int32, device=self.dev)
+        committed = torch.empty((n, Bk + 1), dtype=torch.int32, device=self.dev)
+        last = torch.empty(n, dtype=torch.int32, device=self.dev)
+        B.dflash_verify_sample(self.h, self.stream, n, sampling, draft.data_ptr(), topk_ids.data_ptr(),
+                               topk_logits.data_ptr(), target_logits.data_ptr(), uniforms.data_ptr(),
+                               accept.data_ptr(), committed.data_ptr(), last.data_ptr())
+        return accept, committed, last
+
     def verify(self, draft: torch.Tensor, greedy: torch.Tensor, accept=None, committed=None, last=None):
         n = draft.shape[0]
         Bk = self.cfg.block_size

@@ -284,6 +284,54 @@ dflash_status dflash_select_path(dflash_handle *h, void *stream, int32_t n_req,
                                  const int32_t *topk_ids, const float *topk_logits,
                                  int32_t *path, float *step_scores);
 
+/* Sampling settings of sampled drafting and verification, applied to a row
+ * of logits in this order: divide by temperature (0.01 .. 1000), keep the
+ * top_k largest (0 = all; 1 .. 64; ties to the lower id), softmax, keep the
+ * smallest prefix (probability descending, then id) whose cumulative
+ * probability reaches top_p (0 < top_p <= 1; below 1 only with top_k >= 1),
+ * renormalise.  The draft side has only its top-16 candidates per position,
+ * so its top-k is capped at 16. */
+typedef struct dflash_sampling {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+} dflash_sampling;
+
+/* Sampled drafting ([guide] section 7: the path is walked greedily or by
+ * sampling): one token per block position drawn from the draft's warped
+ * distribution over its top-16 list, with uniform number v: the first list
+ * entry whose running probability sum exceeds v times the total.
+ *   topk_ids, topk_logits  device [n_req, B, 16] (dflash_draft_block's lists)
+ *   uniforms               device [n_req, B] fp32 in [0, 1), one per position
+ *   draft                  device [n_req, B] int32 output
+ * DFLASH_E_UNSUPPORTED for a handle without top-16 lists or for top_p below 1
+ * with top_k 0; DFLASH_E_INVALID for settings out of range. */
+dflash_status dflash_draft_sample(dflash_handle *h, void *stream, int32_t n_req,
+                                  const dflash_sampling *sampling, const int32_t *topk_ids,
+                                  const float *topk_logits, const float *uniforms, int32_t *draft);
+
+/* Lossless sampled verification ([guide] section 7: rejection sampling keeps
+ * the output distribution exactly the target's; section 3.3: rejected
+ * positions are resampled): position i's draft x is accepted while
+ * u[i][0] < p_i(x) / q_i(x) (p the target's warped distribution, q the
+ * draft's over its top-16 list); at the first rejection the committed token
+ * is drawn with u[i][1] from max(0, p_i - q_i) renormalised, after B
+ * acceptances from p_B with u[B][1].  Draws walk the target's kept top-k list
+ * (probability descending, then id), or token ids ascending when top_k is 0.
+ *   draft          device [n_req, B] int32 drafted tokens (e.g. from
+ *                  dflash_draft_sample with the same settings)
+ *   topk_ids, topk_logits  device [n_req, B, 16] the draft's lists
+ *   target_logits  device [n_req, B+1, V] fp32 the target's logits at
+ *                  positions n .. n+B
+ *   uniforms       device [n_req, B+1, 2] fp32 in [0, 1)
+ *   accept_len, committed, last_token  as dflash_verify_accept
+ * Errors as dflash_draft_sample. */
+dflash_status dflash_verify_sample(dflash_handle *h, void *stream, int32_t n_req,
+                                   const dflash_sampling *sampling, const int32_t *draft,
+                                   const int32_t *topk_ids, const float *topk_logits,
+                                   const float *target_logits, const float *uniforms,
+                                   int32_t *accept_len, int32_t *committed, int32_t *last_token);
+
 /* Step 5 ([news] "DFlash 2 的核心：一次写一块"; [guide] 3.3): a = number of
  * leading positions where draft equals the target's greedy token; commits
  * draft[0..a) followed by target_greedy[a], which becomes the next pending
@@ -313,12 +361,13 @@ typedef enum {
   DFLASH_KERNEL_DOWN_GEMM = 10,
   DFLASH_KERNEL_LM_HEAD = 11,    /* vocabulary GEMM + argmax */
   DFLASH_KERNEL_FINALIZE = 12,   /* argmax decode */
-  DFLASH_KERNEL_VERIFY = 13,
+  DFLASH_KERNEL_VERIFY = 13,     /* greedy or sampled verification */
   DFLASH_KERNEL_SELECT = 14,     /* selection pass over split-K partial logits */
   DFLASH_KERNEL_CONV = 15,       /* RMSNorms that also apply DFlash-2 conv taps */
   DFLASH_KERNEL_TOPK = 16,       /* merge of the top-16 lists */
   DFLASH_KERNEL_PATH = 17,       /* DFlash-2 path selector */
-  DFLASH_KERNEL_COUNT = 18
+  DFLASH_KERNEL_SAMPLE = 18,     /* sampled drafting */
+  DFLASH_KERNEL_COUNT = 19
 } dflash_kernel;
 
 /* Launch timing for measurement runs.  After dflash_profile_begin(h, mask),

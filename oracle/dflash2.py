@@ -181,7 +181,8 @@ def target_distribution(logits_row, temperature, top_k, top_p):
     return p, order
 
 
-def spec_verify_sample(draft, draft_ids, draft_logits, target_logits, temperature, top_k, top_p, u):
+def spec_verify_sample(draft, draft_ids, draft_logits, target_logits, temperature, top_k, top_p, u,
+                       return_draw=False):
     """Rejection-sampling verification of one request's block.
 
     draft [B] drafted tokens; draft_ids, draft_logits [B, 16] the draft's
@@ -193,7 +194,8 @@ def spec_verify_sample(draft, draft_ids, draft_logits, target_logits, temperatur
     drafts, committed = draft[:a] + [drawn token]; margins[i] = |u[i,0] -
     p(x)/q(x)| for the tested positions and, last, the distance of the final
     draw's threshold to the nearest running-sum boundary (relative to the
-    total), which tells how close a decision came to flipping.
+    total), which tells how close a decision came to flipping.  With
+    return_draw, also (walk order, weights, threshold) of the final draw.
     """
     B = len(draft)
     margins = []
@@ -222,4 +224,6 @@ def spec_verify_sample(draft, draft_ids, draft_logits, target_logits, temperatur
     margins.append(float(np.min(np.abs(c - thr)) / c[-1]))
     tok = int(order[j])
     committed = [int(t) for t in draft[:a]] + [tok]
+    if return_draw:
+        return a, committed, tok, np.asarray(margins), (order, r, thr)
     return a, committed, tok, np.asarray(margins)

@@ -211,6 +211,27 @@ def make_weights(cfg: dict, seed: int | None = None, norm_std: float = 0.0,
     return w
 
 
+def uniforms(cfg: dict, shape, key: int = 0) -> np.ndarray:
+    """Uniform numbers in [0, 1) (float32) for the sampled draws."""
+    g = rng(cfg["seed"], S_TARGET, 41, key)
+    return g.random(shape, dtype=np.float32)
+
+
+def target_logits_near(cfg: dict, ids: np.ndarray, lg: np.ndarray, key: int = 0, scale: float = 2.0,
+                       agree: float = 1.0) -> np.ndarray:
+    """Synthetic target logits [n, B+1, V] (float32) for sampled
+    verification: N(0, scale) everywhere, plus ``agree`` times the draft's
+    own logits at its top-16 candidates of positions 0..B-1, so the target
+    and the draft partly agree and acceptance is neither certain nor rare."""
+    n, B, K = ids.shape
+    g = rng(cfg["seed"], S_TARGET, 51, key)
+    t = g.standard_normal((n, B + 1, cfg["vocab"]), dtype=np.float32) * np.float32(scale)
+    for r in range(n):
+        for i in range(B):
+            t[r, i, ids[r, i]] += np.float32(agree) * lg[r, i]
+    return t
+
+
 def candidate_lists(cfg: dict, n_req: int, key: int = 0):
     """Synthetic top-16 lists for the path selector: per request and block
     position 16 distinct token ids and logits sorted descending, N(0, 2)."""

@@ -1,0 +1,162 @@
+"""Sampled drafting and rejection-sampling verification on the GPU against
+the oracle (needs an MI355X).
+
+[guide] section 7: the DFlash-2 path may be walked by sampling, with
+rejection sampling keeping the output distribution exactly the target's.
+
+* Parity: seeded top-16 draft lists, target logits that partly agree with
+  them and uniform numbers go to both sides.  Drafted tokens match exactly
+  except where the oracle's draw threshold lies within 1e-5 (relative) of a
+  running-sum boundary.  In lock step (both sides verify the oracle's
+  drafts) accept lengths, committed tokens and the next pending token match
+  exactly except where an accept test u < p/q lies within 1e-5 of its
+  boundary; a final draw whose threshold lies that close to a running-sum
+  boundary must pick a token whose interval holds it up to that rounding.  Settings: the whole vocabulary at temperature 1
+  (the final draw walks every token id), the guide's CLI settings (top-k 20
+  or 64, top-p 0.95), a small top-k; small and full (151,936) vocabularies.
+* Lossless in distribution: 4,096 verifications of one block with fresh
+  uniform numbers; the first committed token's frequencies match the
+  target's warped distribution at that position within 5 sigma, and the
+  first draft is accepted at the rate sum_x min(p(x), q(x)).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from block_diffusion_drafter_proj_amd import binding as Bnd
+from oracle.dflash2 import draft_distribution, draft_sample, spec_verify_sample, target_distribution
+
+pytestmark = pytest.mark.gpu
+TIE = 1e-5  # fp32 running sums over up to 151,936 terms in 149-term chunks: ~1e-6 relative
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda")
+
+
+_HANDLES = {}
+
+
+def _handle(shape, n):
+    """A one-layer handle of the shape (the sampling calls read only its
+    sizes and error word), kept across the settings of a shape."""
+    from block_diffusion_drafter_proj_amd.drafter import Drafter
+
+    key = (shape["name"], shape["vocab"], shape["block_size"], n)
+    if key not in _HANDLES:
+        sh = dict(shape, n_layers=1, selector_rank=0)
+        w = synth.make_weights(sh)
+        _HANDLES.clear()
+        _HANDLES[key] = Drafter(sh, w, max_batch=n, max_pages=4, max_pages_per_req=2 if not shape["window"]
+                                else shape["window"] // 16 + 1, max_position=shape["block_size"] + 64)
+    return _HANDLES[key]
+
+
+def _draw_margin(w, v):
+    c = np.cumsum(w)
+    return float(np.min(np.abs(c - v * c[-1])) / c[-1])
+
+
+SETTINGS = [(1.0, 0, 1.0), (1.0, 20, 0.95), (0.7, 64, 0.95), (1.3, 5, 1.0)]
+
+
+@pytest.mark.parametrize("name,n", [("small_conv", 48), ("dflash2_long", 4)], ids=["vocab3001", "vocab151936"])
+@pytest.mark.parametrize("T,top_k,top_p", SETTINGS, ids=["whole_vocab", "k20_p095", "k64_p095", "k5"])
+def test_sampled_parity(name, n, T, top_k, top_p):
+    dev = _dev()
+    shape = synth.config(name)
+    B, V = shape["block_size"], shape["vocab"]
+    dr = _handle(shape, n)
+    key = top_k * 7 + int(T * 10)
+    ids, lg = synth.candidate_lists(shape, n, key)
+    tl = synth.target_logits_near(shape, ids, lg, key, scale=1.0, agree=2.0)
+    v = synth.uniforms(shape, (n, B), key)
+    u = synth.uniforms(shape, (n, B + 1, 2), key + 1000)
+    sp = Bnd.DFlashSampling(T, top_k, top_p)
+    t_ids, t_lg = torch.from_numpy(ids).to(dev), torch.from_numpy(lg).to(dev)
+    g_draft = dr.draft_sample(sp, t_ids, t_lg, torch.from_numpy(v).to(dev)).cpu().numpy()
+    checked = exempt = 0
+    ref_drafts = []
+    for r in range(n):
+        ref = draft_sample(ids[r], lg[r], T, top_k, top_p, v[r])
+        ref_drafts.append(ref)
+        for i in range(B):
+            _, q = draft_distribution(ids[r, i], lg[r, i], T, top_k, top_p)
+            if _draw_margin(q, v[r, i]) < TIE:
+                exempt += 1
+                continue
+            assert g_draft[r, i] == ref[i], (r, i, g_draft[r, i], ref[i])
+            checked += 1
+    # lock step: both sides verify the oracle's drafts
+    rd = np.stack(ref_drafts).astype(np.int32)
+    acc, com, last = dr.verify_sample(sp, torch.from_numpy(rd).to(dev), t_ids, t_lg, torch.from_numpy(tl).to(dev),
+                                      torch.from_numpy(u).to(dev))
+    acc, com, last = acc.cpu().numpy(), com.cpu().numpy(), last.cpu().numpy()
+    vexempt = 0
+    accepted = 0
+    for r in range(n):
+        a, c, nx, margins, (order, wts, thr) = spec_verify_sample(rd[r], ids[r], lg[r], tl[r], T, top_k, top_p,
+                                                                  u[r], return_draw=True)
+        if len(margins) > 1 and np.min(margins[:-1]) < TIE:  # an accept test at its boundary
+            vexempt += 1
+            continue
+        assert acc[r] == a, (r, acc[r], a)
+        assert com[r, :a].tolist() == c[:a] and np.all(com[r, a + 1:] == -1) and com[r, a] == last[r]
+        if margins[-1] >= TIE:
+            assert last[r] == nx, (r, last[r], nx)
+        else:
+            # the draw's threshold sits within rounding of a boundary (a support of
+            # 10^5 tokens has intervals of ~1e-5 of the total): the GPU's token must
+            # hold the threshold in its running-sum interval up to that rounding
+            cs = np.cumsum(wts)
+            j = int(np.nonzero(order == last[r])[0][0])
+            tol = TIE * cs[-1]
+            assert wts[j] > 0 and cs[j] - wts[j] - tol <= thr < cs[j] + tol, (r, last[r], nx)
+        accepted += a
+    dr.check()
+    print(f"[sample {name} T={T} k={top_k} p={top_p}] drafts {checked} compared, {exempt} at a boundary; "
+          f"verifications {n - vexempt} compared ({accepted} accepted), {vexempt} at a boundary", flush=True)
+    assert checked >= 0.95 * n * B and vexempt <= max(1, n // 10)
+
+
+@pytest.mark.parametrize("T,top_k,top_p", [(1.0, 0, 1.0), (1.0, 20, 0.95)], ids=["whole_vocab", "k20_p095"])
+def test_sampled_verification_is_lossless(T, top_k, top_p):
+    """4,096 independent verifications of one block (256 requests x 16 calls
+    with fresh uniforms): the first committed token follows the target's
+    warped distribution at position 0 and the first draft is accepted with
+    probability sum_x min(p(x), q(x))."""
+    dev = _dev()
+    shape = synth.config("small_conv", block_size=4, vocab=64)
+    B, V, n = 4, 64, 256
+    dr = _handle(shape, n)
+    ids1, lg1 = synth.candidate_lists(shape, 1, 3)
+    tl1 = synth.target_logits_near(shape, ids1, lg1, 3, scale=1.0)
+    ids, lg, tl = (np.repeat(x, n, axis=0) for x in (ids1, lg1, tl1))
+    t_ids, t_lg, t_tl = (torch.from_numpy(x).to(dev) for x in (ids, lg, tl))
+    sp = Bnd.DFlashSampling(T, top_k, top_p)
+    counts = np.zeros(V)
+    acc1 = 0
+    calls = 16
+    for c in range(calls):
+        v = torch.from_numpy(synth.uniforms(shape, (n, B), 100 + c)).to(dev)
+        u = torch.from_numpy(synth.uniforms(shape, (n, B + 1, 2), 200 + c)).to(dev)
+        d = dr.draft_sample(sp, t_ids, t_lg, v)
+        acc, com, _ = dr.verify_sample(sp, d, t_ids, t_lg, t_tl, u)
+        com = com.cpu().numpy()
+        acc1 += int((acc.cpu().numpy() >= 1).sum())
+        np.add.at(counts, com[:, 0], 1)
+    N = n * calls
+    p0, _ = target_distribution(tl1[0, 0], T, top_k, top_p)
+    qd0, _ = draft_distribution(ids1[0, 0], lg1[0, 0], T, top_k, top_p)
+    acc_prob = sum(min(p0[t], w) for t, w in qd0.items())
+    freq = counts / N
+    sig = np.sqrt(p0 * (1 - p0) / N)
+    assert np.all(np.abs(freq - p0) <= 5 * sig + 1e-9), np.max(np.abs(freq - p0) / (sig + 1e-12))
+    assert abs(acc1 / N - acc_prob) <= 5 * np.sqrt(acc_prob * (1 - acc_prob) / N)
+    dr.check()
+    print(f"[lossless T={T} k={top_k} p={top_p}] {N} draws, first-draft acceptance {acc1 / N:.3f} "
+          f"(expected {acc_prob:.3f}), max |freq - p| / sigma "
+          f"{np.max(np.abs(freq - p0) / (sig + 1e-12)):.2f}", flush=True)
