@@ -39,6 +39,9 @@ Parity status per function (what pins it, see ``tests/test_oracle_*.py``):
                        probability sum min(p, q); a draft equal to the target
                        is always accepted; near-zero temperature reduces to
                        greedy verification.
+* ``target.TargetOracle`` (target verify forward) pinned: equals the tiny
+                       target row by row (fp32, MHA); causal; chunked equals
+                       one block; GQA equals MHA with repeated K/V heads.
 """
 from .dflash_oracle import (  # noqa: F401
     DraftOracle,
@@ -63,4 +66,5 @@ from .dflash2 import (  # noqa: F401
     target_distribution,
     warp_sorted,
 )
+from .target import TargetOracle  # noqa: F401
 from .tiny_target import OracleDrafter, TinyTarget, greedy_ar, spec_generate  # noqa: F401
