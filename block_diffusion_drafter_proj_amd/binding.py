@@ -18,7 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdflash.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "dflash.h")
 
-MAX_LAYERS = 16
+MAX_LAYERS = 64
 MAX_FEAT = 8
 MAX_BATCH = 256
 PAGE = 16
@@ -44,7 +44,7 @@ class DFlashConfig(ctypes.Structure):
         "block_size", "n_feat", "dtype", "mask_token_id", "page_size", "window", "conv2",
         "topk", "max_batch", "max_pages", "max_pages_per_req", "max_position",
         "max_inject_rows")] + [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-                               ("selector_rank", ctypes.c_int32)]
+                               ("selector_rank", ctypes.c_int32), ("target", ctypes.c_int32)]
 
 
 class DFlashLayerWeights(ctypes.Structure):
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.POINTER(DFlashDraftDebug)]),
             "dflash_draft_static_bytes": (sz, [ctypes.POINTER(DFlashConfig), i32]),
             "dflash_select_path": (i32, [vp, vp, i32, vp, vp, vp, vp]),
+            "dflash_target_forward": (i32, [vp, vp, i32, pi32, i32, vp, vp, vp, i32, pi32, ctypes.POINTER(vp)]),
+            "dflash_set_context_length": (i32, [vp, i32, i32]),
             "dflash_draft_sample": (i32, [vp, vp, i32, ctypes.POINTER(DFlashSampling), vp, vp, vp, vp]),
             "dflash_verify_sample": (i32, [vp, vp, i32, ctypes.POINTER(DFlashSampling), vp, vp, vp, vp, vp,
                                            vp, vp, vp]),
@@ -204,6 +206,19 @@ def dflash_draft_static_bytes(cfg: DFlashConfig, n_req: int) -> int:
     return int(lib().dflash_draft_static_bytes(ctypes.byref(cfg), n_req))
 
 
+def dflash_target_forward(h: int, stream: int, slots, n_rows: int, tokens: int, greedy: int, logits: int = 0,
+                          feat_layers=(), feat_out=()) -> None:
+    arr = (ctypes.c_void_p * max(1, len(feat_out)))(*[ctypes.c_void_p(p) for p in feat_out])
+    _check(lib().dflash_target_forward(ctypes.c_void_p(h), ctypes.c_void_p(stream), len(slots), _i32s(slots),
+                                       n_rows, ctypes.c_void_p(tokens), ctypes.c_void_p(greedy),
+                                       ctypes.c_void_p(logits or None), len(feat_layers), _i32s(feat_layers),
+                                       arr))
+
+
+def dflash_set_context_length(h: int, slot: int, ctx_len: int) -> None:
+    _check(lib().dflash_set_context_length(ctypes.c_void_p(h), slot, ctx_len))
+
+
 def dflash_select_path(h: int, stream: int, n_req: int, topk_ids: int, topk_logits: int, path: int,
                        step_scores: int = 0) -> None:
     vp = ctypes.c_void_p
@@ -242,7 +257,7 @@ def dflash_check(h: int, stream: int) -> None:
 
 KERNELS = ["fc_gemm", "norm", "kv_gemm", "scatter", "qkv_gemm", "qkv_post", "attn", "combine",
            "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "finalize", "verify", "select", "conv", "topk",
-           "path", "sample"]
+           "path", "sample", "target_attn"]
 
 
 def dflash_profile_begin(h: int, mask: int) -> None:

@@ -760,8 +760,8 @@ __global__ __launch_bounds__(256) void k_scatter(ScatterParams p) {
     const InjectReq q = p.req[t];
     p.state[q.slot].ctx_len = q.pos0 + q.count;
   }
-  const float* src = p.kv + (long long)row * (p.L * 2 * p.Hkv * DH) + (long long)l * 2 * p.Hkv * DH;
-  const long long plane = (long long)p.rows * p.L * 2 * p.Hkv * DH;
+  const float* src = p.kv + (long long)row * p.ld + p.col0 + (long long)l * 2 * p.Hkv * DH;
+  const long long plane = (long long)p.rows * p.ld;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const int nk = p.Hkv * KQ, nv = p.Hkv * VQ;
   // Rounds of 2 groups per thread and kind.  The row's K/V sums depend on the

@@ -81,6 +81,8 @@ struct GemmPlan {
 struct NormParams {
   const float* x_in;       // [M, ld] fp32 residual, or NULL
   const void* init_row;    // storage dtype [d]: every row starts from it, or NULL
+  const int* init_tokens;  // [M]: row m starts from init_row[init_tokens[m]] (an embedding table), or NULL
+  void* feat;              // optional storage-dtype copy of x [M, d] (a target feature layer)
   const float* part;       // [n_part][M][d] fp32 split-K partials, or NULL
   int n_part;
   float* x_out;            // [M, ld] receives x, or NULL
@@ -188,7 +190,8 @@ struct InjectReq {
   int row_start, count, slot, pos0, final_ctx;
 };
 struct ScatterParams {
-  const float* kv;  // [n_part][rows, L*2*Hkv*dh] split-K partials
+  const float* kv;  // [n_part][rows][ld] split-K partials; a row's K/V of layer l at col0 + l*2*Hkv*dh
+  int ld, col0;
   int n_part;
   int rows, L, Hkv;
   int n_req;
@@ -241,6 +244,33 @@ void launch_scatter(int dtype, int dh, const ScatterParams& p, hipStream_t s);
 void launch_topk_merge(const TopkParams& p, hipStream_t s);
 void launch_finalize(const unsigned long long* keys, int rows, int vocab, int* draft,
                      hipStream_t s);
+// Target verify forward: q of the new rows with RoPE (row-major), and causal
+// attention over the request's pages (new rows' K/V already scattered).
+struct TargetQParams {
+  const float* qkv;  // [n_part][M][ld] split-K partials of the QKV product
+  int n_part, M, ld, R, Hq, dh;
+  const float* cos_t;
+  const float* sin_t;
+  void* q;  // [M][Hq][dh] storage dtype
+  int pos0[DFLASH_MAX_BATCH];  // position of each request's first new row
+};
+struct CausalAttnParams {
+  const void* q;     // [M][Hq][dh]
+  const void* pool;  // this layer's pages
+  const int* page_table;
+  int pt_stride;
+  const SlotState* state;
+  int max_pages, Hq, Hkv, R;
+  float scale;
+  void* out;  // [M][ldo] storage dtype, or fragment order
+  int ldo, out_packed;
+  unsigned int* err;
+  int slots[DFLASH_MAX_BATCH];
+  int pos0[DFLASH_MAX_BATCH];
+};
+void launch_target_q(int dtype, const TargetQParams& p, hipStream_t s);
+void launch_causal_attn(int dtype, int dh, int n_req, const CausalAttnParams& p, hipStream_t s);
+
 // DFlash-2 path selector: projected embedding tables (once) and the greedy
 // path per request over its top-16 lists.
 struct PathParams {

@@ -88,6 +88,14 @@ __device__ __forceinline__ f32x4 load_row4(const NormParams& p, int row, int k, 
   f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
   if (p.init_row) {
     const T* init = reinterpret_cast<const T*>(p.init_row) + k;
+    if (p.init_tokens) {  // token embeddings (ids were checked by the caller's kernel or the host)
+      int tok = p.init_tokens[row];
+      if (tok < 0 || tok >= p.vocab) {
+        if (threadIdx.x == 0 && p.err) atomicOr(p.err, 1u);
+        tok = 0;
+      }
+      init += (long long)tok * p.d;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = to_f(init[i]);
   } else if (p.x_in) {
@@ -153,6 +161,12 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(NormParams p) {
   }
   if (p.x_out) *reinterpret_cast<f32x4*>(p.x_out + (long long)row * p.ldx + k) = x;
   if (p.dbg) *reinterpret_cast<f32x4*>(p.dbg + (long long)row * p.d + k) = x;
+  if (p.feat) {
+    typename Out4<T>::type fo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fo[i] = from_f<T>(x[i]);
+    *reinterpret_cast<typename Out4<T>::type*>(reinterpret_cast<T*>(p.feat) + (long long)row * p.d + k) = fo;
+  }
   const float tot = block_sum((x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3]), red, 0);
   const float r = 1.0f / sqrtf(tot / (float)p.d + p.eps);
   f32x4 y;
@@ -275,7 +289,7 @@ __global__ __launch_bounds__(1024) void k_rmsnorm_frag(NormParams p) {
 
 void launch_rmsnorm(int dtype, const NormParams& p, hipStream_t s) {
   if (p.M <= 0) return;
-  if (p.out_packed && !p.conv && !p.oconv && p.d % 256 == 0 && p.d <= 4096) {
+  if (p.out_packed && !p.conv && !p.oconv && !p.feat && !p.init_tokens && p.d % 256 == 0 && p.d <= 4096) {
     constexpr int R = kNormRows;
     const int nt = std::min(kNormThreads, R * p.d / 8);  // R * d / 8 chunks, at most 8 per thread
     if (dtype == DFLASH_BF16)

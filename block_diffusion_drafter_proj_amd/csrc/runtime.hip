@@ -81,7 +81,7 @@ int tiles_of(int n) { return (n + 15) / 16; }
 // The skinny QKV product writes q and the block K/V itself (RoPE epilogue,
 // no split-K); the tiled one writes split-K partials for k_qkv_post.
 bool qkv_rope(const dflash_config& c, int M) {
-  return !gemm_use_big(c.dtype, M) && !gemm_use_mt4(c.dtype, M) &&
+  return !c.target && !gemm_use_big(c.dtype, M) && !gemm_use_mt4(c.dtype, M) &&
          (M + c.block_size - 1) / c.block_size <= kMaxRopeReq;
 }
 
@@ -158,6 +158,7 @@ constexpr int kSampleRowFloats = 2 + 64 + 64 + 1;
 struct Scratch {
   size_t h, h2, xa, xo, qkv, part_o, part_ml, nsplit, z, keys, tlists, lpart, opart, dpart;
   size_t srow;       // sampled verification: per target row statistics and kept lists
+  size_t tq;         // target: q of the new rows [M][Hq*dh]
   size_t u, f, kvo;  // inject only (0 when not laid out)
   size_t total;
 };
@@ -188,6 +189,7 @@ Scratch make_scratch(const dflash_config& c, int n_req, bool inject) {
   // norm re-reads the previous row of its input while writing its output)
   S.h2 = c.conv2 ? take(sizeof(float) * M * c.hidden) : 0;
   S.srow = c.topk ? take(sizeof(float) * (size_t)n_req * (c.block_size + 1) * kSampleRowFloats) : 0;
+  S.tq = c.target ? take(e * M * qd) : 0;
   // GEMM inputs: rows rounded up to whole 16-row fragments (fragment order)
   const size_t M16 = (M + 15) / 16 * 16;
   S.xa = take(e * M16 * c.hidden);
@@ -240,7 +242,7 @@ Layout make_layout(const dflash_config& c) {
   L.sin_t = take(sizeof(float) * (size_t)c.max_position * (c.head_dim / 2));
   L.qb = take(e * (size_t)c.max_batch * c.n_q_heads * 16 * c.head_dim);
   L.blk = take(e * (size_t)c.max_batch * page_elems);
-  L.sc = make_scratch(c, c.max_batch, true);
+  L.sc = make_scratch(c, c.max_batch, !c.target);
   L.scratch = take(L.sc.total);
   L.total = off;
   return L;
@@ -267,7 +269,7 @@ PackedLayout make_packed(const dflash_config& c) {
   const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   P.lm_head = take(c.vocab, d);
-  P.fc = take(d, c.n_feat * d);
+  P.fc = c.target ? 0 : take(d, c.n_feat * d);
   for (int l = 0; l < c.n_layers; ++l) {
     P.wqkv[l] = take(qkvw, d);
     P.wo[l] = take(d, qd);
@@ -297,7 +299,14 @@ dflash_status validate(const dflash_config* c) {
   if (c->ffn <= 0 || c->ffn % 256) return bad("ffn must be a positive multiple of 256");
   if (c->vocab <= 0) return bad("vocab must be positive");
   if (c->n_layers < 1 || c->n_layers > DFLASH_MAX_LAYERS) return bad("n_layers out of range");
-  if (c->block_size < 1 || c->block_size > 16) return bad("block_size must be in [1, 16]");
+  if (c->target != 0 && c->target != 1) return bad("target must be 0 or 1");
+  if (c->target) {
+    if (c->block_size < 1 || c->block_size > 64) return bad("a target takes 1 to 64 rows per request");
+    if (c->window || c->conv2 || c->topk || c->selector_rank)
+      return bad("a target has no window, conv taps, top-16 lists or path selector");
+  } else if (c->block_size < 1 || c->block_size > 16) {
+    return bad("block_size must be in [1, 16]");
+  }
   if (c->n_feat < 1 || c->n_feat > DFLASH_MAX_FEAT) return bad("n_feat out of range");
   if (c->dtype != DFLASH_BF16 && c->dtype != DFLASH_F32) return bad("unknown dtype");
   if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return bad("mask_token_id out of range");
@@ -400,7 +409,7 @@ dflash_status ensure_device(dflash_handle* h) {
   const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   launch_pack(c.dtype, h->w.lm_head, h->packed + h->pk.lm_head, c.vocab, d, nullptr);
-  launch_pack(c.dtype, h->w.fc, h->packed + h->pk.fc, d, c.n_feat * d, nullptr);
+  if (!c.target) launch_pack(c.dtype, h->w.fc, h->packed + h->pk.fc, d, c.n_feat * d, nullptr);
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& lw = h->w.layers[l];
     launch_pack(c.dtype, lw.wqkv, h->packed + h->pk.wqkv[l], qkvw, d, nullptr);
@@ -548,7 +557,7 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
   if ((reinterpret_cast<uintptr_t>(kv_pool) | reinterpret_cast<uintptr_t>(workspace) |
        reinterpret_cast<uintptr_t>(packed)) & 255)
     return fail(DFLASH_E_INVALID, "kv_pool, workspace and packed must be 256-byte aligned");
-  if (!w->embed || !w->lm_head || !w->fc || !w->fc_norm || !w->final_norm)
+  if (!w->embed || !w->lm_head || !w->final_norm || (!cfg->target && (!w->fc || !w->fc_norm)))
     return fail(DFLASH_E_INVALID, "a model weight pointer is NULL");
   for (int l = 0; l < cfg->n_layers; ++l) {
     const dflash_layer_weights& lw = w->layers[l];
@@ -622,6 +631,7 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
                                     const void* const* hidden, void* debug_f) {
   if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
   const dflash_config& c = h->cfg;
+  if (c.target) return fail(DFLASH_E_INVALID, "a target handle has no injection (use dflash_target_forward)");
   dflash_status st = check_slots(h, n_req, slots);
   if (st) return st;
   if (!n_new) return fail(DFLASH_E_INVALID, "n_new is NULL");
@@ -733,6 +743,8 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
     { ProfScope ps(h, DFLASH_KERNEL_KV_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.kv, kv, s); }
 
     sp.kv = sat<float>(sb, sc.kvo);
+    sp.ld = kvw;
+    sp.col0 = 0;
     sp.n_part = pl.kv.P;
     sp.rows = rows;
     sp.L = c.n_layers;
@@ -756,6 +768,92 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
   return DFLASH_OK;
 }
 
+// Final step of a forward whose normed rows are in xa (fragment order when
+// xa_packed): the shared LM head and greedy selection (argmax ids with ties
+// to the lowest id; with top-16, the sorted lists as well).  Below 17 rows the
+// skinny kernel's argmax or top-16 epilogue; from 17 to 64 rows split-K
+// partial logits and the selection pass; from 64 rows the tiled kernel's
+// epilogue.
+static dflash_status lm_head(dflash_handle* h, hipStream_t s, char* sb, const Scratch& sc, const Plans& pl, int M,
+                             int xa_packed, int32_t* draft, int32_t* topk_ids, float* topk_logits,
+                             float* debug_logits) {
+  const dflash_config& c = h->cfg;
+  const int d = c.hidden;
+  GemmParams gl{};
+  gl.a[0] = sb + sc.xa;
+  gl.a_parts = 1;
+  gl.a_part_k = d;
+  gl.lda = d;
+  gl.M = M;
+  gl.K = d;
+  gl.a_packed = xa_packed;
+  gl.w[0] = h->packed + h->pk.lm_head;
+  gl.tiles = tiles_of(c.vocab);
+  gl.N = c.vocab;
+  gl.P = 1;
+  if (pl.lm.mt == 4) {  // 17..64 rows: split-K partial logits, then the selection pass
+    gl.P = pl.lm.P;
+    gl.out_f32 = sat<float>(sb, sc.lpart);
+    {
+      ProfScope ps(h, DFLASH_KERNEL_LM_HEAD, s);
+      launch_gemm(c.dtype, EPI_PARTIAL, pl.lm, gl, s);
+    }
+    LogitSelParams lp{};
+    lp.part = gl.out_f32;
+    lp.n_part = pl.lm.P;
+    lp.M = M;
+    lp.N = c.vocab;
+    lp.dbg = debug_logits;
+    lp.ld_dbg = c.vocab;
+    lp.keys = sat<unsigned long long>(sb, sc.keys);
+    lp.lists = sat<unsigned long long>(sb, sc.tlists);
+    lp.n_lists = logit_sel_lists(c.vocab);
+    {
+      ProfScope ps(h, DFLASH_KERNEL_SELECT, s);
+      launch_logit_select(c.topk != 0, lp, s);
+    }
+    if (c.topk) {
+      TopkParams tp{};
+      tp.lists = lp.lists;
+      tp.n_lists = lp.n_lists;
+      tp.M = M;
+      tp.vocab = c.vocab;
+      tp.draft = draft;
+      tp.topk_ids = topk_ids;
+      tp.topk_logits = topk_logits;
+      ProfScope ps(h, DFLASH_KERNEL_TOPK, s);
+      launch_topk_merge(tp, s);
+    } else {
+      ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
+      launch_finalize(lp.keys, M, c.vocab, draft, s);
+    }
+    return launched("draft head");
+  }
+  gl.keys = sat<unsigned long long>(sb, c.topk ? sc.tlists : sc.keys);
+  gl.dbg = debug_logits;
+  gl.ld_dbg = c.vocab;
+  {
+    ProfScope ps(h, DFLASH_KERNEL_LM_HEAD, s);
+    launch_gemm(c.dtype, c.topk ? EPI_TOPK : EPI_ARGMAX, pl.lm, gl, s);
+  }
+  if (c.topk) {
+    TopkParams tp{};
+    tp.lists = gl.keys;
+    tp.n_lists = pl.lm.mt == 0 ? gemm_big_lists(gl.tiles) : pl.lm.GP;
+    tp.M = M;
+    tp.vocab = c.vocab;
+    tp.draft = draft;
+    tp.topk_ids = topk_ids;
+    tp.topk_logits = topk_logits;
+    ProfScope ps(h, DFLASH_KERNEL_TOPK, s);
+    launch_topk_merge(tp, s);
+  } else {
+    ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
+    launch_finalize(sat<unsigned long long>(sb, sc.keys), M, c.vocab, draft, s);
+  }
+  return launched("draft head");
+}
+
 // Steps 3 and 4 with the scratch part at the handle's workspace or, with
 // from_static, in the library's static device array.
 static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots,
@@ -766,6 +864,7 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
   const float* hidden_in = debug ? debug->hidden_in : nullptr;
   if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
   const dflash_config& c = h->cfg;
+  if (c.target) return fail(DFLASH_E_INVALID, "a target handle does not draft (use dflash_target_forward)");
   dflash_status st = check_slots(h, n_req, slots);
   if (st) return st;
   if (!draft) return fail(DFLASH_E_INVALID, "draft is NULL");
@@ -1053,73 +1152,7 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
   nf.zero_keys = sat<unsigned long long>(sb, sc.keys);
   norm(nf);
 
-  GemmParams gl = gemm_in(sb + sc.xa, d);
-  gl.a_packed = nf.out_packed;
-  gl.w[0] = h->packed + h->pk.lm_head;
-  gl.tiles = tiles_of(c.vocab);
-  gl.N = c.vocab;
-  gl.P = 1;
-  if (pl.lm.mt == 4) {  // 17..64 rows: split-K partial logits, then the selection pass
-    gl.P = pl.lm.P;
-    gl.out_f32 = sat<float>(sb, sc.lpart);
-    {
-      ProfScope ps(h, DFLASH_KERNEL_LM_HEAD, s);
-      launch_gemm(c.dtype, EPI_PARTIAL, pl.lm, gl, s);
-    }
-    LogitSelParams lp{};
-    lp.part = gl.out_f32;
-    lp.n_part = pl.lm.P;
-    lp.M = M;
-    lp.N = c.vocab;
-    lp.dbg = debug_logits;
-    lp.ld_dbg = c.vocab;
-    lp.keys = sat<unsigned long long>(sb, sc.keys);
-    lp.lists = sat<unsigned long long>(sb, sc.tlists);
-    lp.n_lists = logit_sel_lists(c.vocab);
-    {
-      ProfScope ps(h, DFLASH_KERNEL_SELECT, s);
-      launch_logit_select(c.topk != 0, lp, s);
-    }
-    if (c.topk) {
-      TopkParams tp{};
-      tp.lists = lp.lists;
-      tp.n_lists = lp.n_lists;
-      tp.M = M;
-      tp.vocab = c.vocab;
-      tp.draft = draft;
-      tp.topk_ids = topk_ids;
-      tp.topk_logits = topk_logits;
-      ProfScope ps(h, DFLASH_KERNEL_TOPK, s);
-      launch_topk_merge(tp, s);
-    } else {
-      ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
-      launch_finalize(lp.keys, M, c.vocab, draft, s);
-    }
-    return launched("draft head");
-  }
-  gl.keys = sat<unsigned long long>(sb, c.topk ? sc.tlists : sc.keys);
-  gl.dbg = debug_logits;
-  gl.ld_dbg = c.vocab;
-  {
-    ProfScope ps(h, DFLASH_KERNEL_LM_HEAD, s);
-    launch_gemm(c.dtype, c.topk ? EPI_TOPK : EPI_ARGMAX, pl.lm, gl, s);
-  }
-  if (c.topk) {
-    TopkParams tp{};
-    tp.lists = gl.keys;
-    tp.n_lists = pl.lm.mt == 0 ? gemm_big_lists(gl.tiles) : pl.lm.GP;
-    tp.M = M;
-    tp.vocab = c.vocab;
-    tp.draft = draft;
-    tp.topk_ids = topk_ids;
-    tp.topk_logits = topk_logits;
-    ProfScope ps(h, DFLASH_KERNEL_TOPK, s);
-    launch_topk_merge(tp, s);
-  } else {
-    ProfScope ps(h, DFLASH_KERNEL_FINALIZE, s);
-    launch_finalize(sat<unsigned long long>(sb, sc.keys), M, c.vocab, draft, s);
-  }
-  return launched("draft head");
+  return lm_head(h, s, sb, sc, pl, M, nf.out_packed, draft, topk_ids, topk_logits, debug_logits);
 }
 
 dflash_status dflash_draft_block(dflash_handle* h, void* stream, int32_t n_req,
@@ -1139,6 +1172,252 @@ dflash_status dflash_draft_block_static(dflash_handle* h, void* stream, int32_t 
 size_t dflash_draft_static_bytes(const dflash_config* cfg, int32_t n_req) {
   if (validate(cfg) != DFLASH_OK || n_req < 1 || n_req > cfg->max_batch) return 0;
   return make_scratch(*cfg, n_req, false).total;
+}
+
+dflash_status dflash_set_context_length(dflash_handle* h, int32_t slot, int32_t ctx_len) {
+  if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
+  if (slot < 0 || slot >= h->cfg.max_batch || !h->slots[slot].bound)
+    return fail(DFLASH_E_INVALID, "slot %d is not bound", slot);
+  HostSlot& hs = h->slots[slot];
+  if (ctx_len < hs.kv_begin || ctx_len > hs.ctx_len)
+    return fail(DFLASH_E_INVALID, "ctx_len %d out of [%d, %d]", ctx_len, hs.kv_begin, hs.ctx_len);
+  dflash_status st = ensure_device(h);
+  if (st) return st;
+  SlotState ss{ctx_len, hs.kv_begin, hs.n_pages, 0};
+  hipError_t e = hipMemcpy(h->ws + h->lay.state + sizeof(SlotState) * slot, &ss, sizeof(ss), hipMemcpyHostToDevice);
+  if (e) return hip_fail(e, "slot state upload");
+  hs.ctx_len = ctx_len;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_target_forward(dflash_handle* h, void* stream, int32_t n_req, const int32_t* slots,
+                                    int32_t n_rows, const int32_t* tokens, int32_t* greedy, float* logits,
+                                    int32_t n_feat_out, const int32_t* feat_layers, void* const* feat_out) {
+  if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
+  const dflash_config& c = h->cfg;
+  if (!c.target) return fail(DFLASH_E_INVALID, "dflash_target_forward needs a target handle (target 1)");
+  dflash_status st = check_slots(h, n_req, slots);
+  if (st) return st;
+  if (n_rows < 1 || n_rows > c.block_size)
+    return fail(DFLASH_E_INVALID, "n_rows %d out of [1, %d]", n_rows, c.block_size);
+  if (!tokens || !greedy) return fail(DFLASH_E_INVALID, "tokens and greedy must be set");
+  if (n_feat_out < 0 || n_feat_out > DFLASH_MAX_FEAT) return fail(DFLASH_E_INVALID, "n_feat_out out of range");
+  if (n_feat_out && (!feat_layers || !feat_out)) return fail(DFLASH_E_INVALID, "feature outputs are NULL");
+  for (int k = 0; k < n_feat_out; ++k) {
+    if (feat_layers[k] < 0 || feat_layers[k] >= c.n_layers || (k && feat_layers[k] <= feat_layers[k - 1]))
+      return fail(DFLASH_E_INVALID, "feature layers must be ascending ids below %d", c.n_layers);
+    if (!feat_out[k]) return fail(DFLASH_E_INVALID, "feat_out[%d] is NULL", k);
+  }
+  for (int i = 0; i < n_req; ++i) {
+    const HostSlot& hs = h->slots[slots[i]];
+    if ((long long)hs.ctx_len + n_rows > (long long)hs.n_pages * 16)
+      return fail(DFLASH_E_CAPACITY, "slot %d: %d + %d positions exceed %d bound pages", slots[i], hs.ctx_len,
+                  n_rows, hs.n_pages);
+    if (hs.ctx_len + n_rows >= c.max_position)
+      return fail(DFLASH_E_CAPACITY, "slot %d: positions beyond max_position", slots[i]);
+  }
+  st = ensure_device(h);
+  if (st) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t e = elt(c);
+  const int d = c.hidden, M = n_req * n_rows;
+  const int qd = c.n_q_heads * c.head_dim;
+  const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const Plans pl = make_plans(c, M);
+  char* sb = h->ws + h->lay.scratch;
+  const Scratch& sc = h->lay.sc;
+  float* hbuf = sat<float>(sb, sc.h);
+  float* dpart = sat<float>(sb, sc.dpart);
+  float* opart = sat<float>(sb, sc.opart);
+  const size_t page_layer = (size_t)c.max_pages * 2 * c.n_kv_heads * 16 * c.head_dim;
+  auto feat_of = [&](int layer) -> void* {  // output of feature layer `layer`, or NULL
+    for (int k = 0; k < n_feat_out; ++k)
+      if (feat_layers[k] == layer) return feat_out[k];
+    return nullptr;
+  };
+  auto gemm_in = [&](const void* a, int K) {
+    GemmParams g{};
+    g.a[0] = a;
+    g.a_parts = 1;
+    g.a_part_k = K;
+    g.lda = K;
+    g.M = M;
+    g.K = K;
+    return g;
+  };
+  auto norm = [&](const NormParams& np) {
+    ProfScope ps(h, DFLASH_KERNEL_NORM, s);
+    launch_rmsnorm(c.dtype, np, s);
+  };
+  TargetQParams tq{};
+  CausalAttnParams ca{};
+  for (int i = 0; i < n_req; ++i) {
+    tq.pos0[i] = ca.pos0[i] = h->slots[slots[i]].ctx_len;
+    ca.slots[i] = slots[i];
+  }
+  for (int l = 0; l < c.n_layers; ++l) {
+    const dflash_layer_weights& lw = h->w.layers[l];
+    NormParams n1{};
+    if (l == 0) {  // token embeddings
+      n1.init_row = h->w.embed;
+      n1.init_tokens = tokens;
+      n1.vocab = c.vocab;
+      n1.err = at<unsigned int>(h, h->lay.err);
+    } else {  // residual + previous layer's down partials; the feature after layer l-1
+      n1.x_in = hbuf;
+      n1.part = dpart;
+      n1.n_part = pl.down.P;
+      n1.feat = feat_of(l - 1);
+    }
+    n1.x_out = hbuf;
+    n1.ldx = d;
+    n1.gamma = lw.attn_norm;
+    n1.eps = c.rms_eps;
+    n1.out = sb + sc.xa;
+    n1.ldo = d;
+    n1.out_packed = pl.qkv.mt == 0;
+    n1.d = d;
+    n1.M = M;
+    norm(n1);
+
+    GemmParams g = gemm_in(sb + sc.xa, d);
+    g.a_packed = n1.out_packed;
+    g.w[0] = h->packed + h->pk.wqkv[l];
+    g.N = qkvw;
+    g.P = pl.qkv.P;
+    g.tiles = tiles_of(qkvw);
+    g.out_f32 = sat<float>(sb, sc.qkv);
+    { ProfScope ps(h, DFLASH_KERNEL_QKV_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.qkv, g, s); }
+    {
+      ProfScope ps(h, DFLASH_KERNEL_TARGET_ATTN, s);
+      // q of the new rows with RoPE at their positions
+      tq.qkv = g.out_f32;
+      tq.n_part = pl.qkv.P;
+      tq.M = M;
+      tq.ld = qkvw;
+      tq.R = n_rows;
+      tq.Hq = c.n_q_heads;
+      tq.dh = c.head_dim;
+      tq.cos_t = at<float>(h, h->lay.cos_t);
+      tq.sin_t = at<float>(h, h->lay.sin_t);
+      tq.q = sb + sc.tq;
+      launch_target_q(c.dtype, tq, s);
+      // K (RoPE) and V of the new rows appended to the slots' pages, in chunks of requests
+      for (int r0 = 0; r0 < n_req; r0 += kMaxChunkReq) {
+        const int nr = std::min(kMaxChunkReq, n_req - r0);
+        ScatterParams sp{};
+        sp.kv = g.out_f32 + (size_t)r0 * n_rows * qkvw;
+        sp.ld = qkvw;
+        sp.col0 = qd;
+        sp.n_part = pl.qkv.P;
+        sp.rows = nr * n_rows;
+        sp.L = 1;
+        sp.Hkv = c.n_kv_heads;
+        sp.n_req = nr;
+        for (int i = 0; i < nr; ++i) {
+          InjectReq& q = sp.req[i];
+          q.row_start = i * n_rows;
+          q.count = n_rows;
+          q.slot = slots[r0 + i];
+          q.pos0 = tq.pos0[r0 + i];
+          q.final_ctx = q.pos0 + n_rows;
+        }
+        sp.cos_t = tq.cos_t;
+        sp.sin_t = tq.sin_t;
+        sp.pool = h->kv + (size_t)l * page_layer * e;
+        sp.layer_stride = 0;
+        sp.page_table = at<int>(h, h->lay.page_table);
+        sp.pt_stride = c.max_pages_per_req;
+        sp.state = at<SlotState>(h, h->lay.state);
+        sp.window = 0;
+        sp.max_pages = c.max_pages;
+        sp.err = at<unsigned int>(h, h->lay.err);
+        launch_scatter(c.dtype, c.head_dim, sp, s);
+      }
+      // causal attention over the pages
+      ca.q = sb + sc.tq;
+      ca.pool = h->kv + (size_t)l * page_layer * e;
+      ca.page_table = at<int>(h, h->lay.page_table);
+      ca.pt_stride = c.max_pages_per_req;
+      ca.state = at<SlotState>(h, h->lay.state);
+      ca.max_pages = c.max_pages;
+      ca.Hq = c.n_q_heads;
+      ca.Hkv = c.n_kv_heads;
+      ca.R = n_rows;
+      ca.scale = (float)(1.0 / sqrt((double)c.head_dim));
+      ca.out = sb + sc.xo;
+      ca.ldo = qd;
+      ca.out_packed = pl.o.mt == 0;
+      ca.err = at<unsigned int>(h, h->lay.err);
+      launch_causal_attn(c.dtype, c.head_dim, n_req, ca, s);
+    }
+
+    GemmParams go = gemm_in(sb + sc.xo, qd);
+    go.a_packed = ca.out_packed;
+    go.w[0] = h->packed + h->pk.wo[l];
+    go.tiles = tiles_of(d);
+    go.N = d;
+    go.P = pl.o.P;
+    go.out_f32 = opart;
+    { ProfScope ps(h, DFLASH_KERNEL_O_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.o, go, s); }
+
+    NormParams n2{};
+    n2.x_in = hbuf;
+    n2.part = opart;
+    n2.n_part = pl.o.P;
+    n2.x_out = hbuf;
+    n2.ldx = d;
+    n2.gamma = lw.mlp_norm;
+    n2.eps = c.rms_eps;
+    n2.out = sb + sc.xa;
+    n2.ldo = d;
+    n2.out_packed = pl.gateup.mt == 0;
+    n2.d = d;
+    n2.M = M;
+    norm(n2);
+
+    GemmParams gu = gemm_in(sb + sc.xa, d);
+    gu.a_packed = n2.out_packed;
+    gu.out_packed = pl.gateup.mt == 0 && pl.down.mt == 0;
+    gu.w[0] = h->packed + h->pk.wgateup[l];
+    gu.tiles = tiles_of(c.ffn);
+    gu.up_tile_off = tiles_of(c.ffn);
+    gu.N = c.ffn;
+    gu.P = 1;
+    gu.out_t = sb + sc.z;
+    gu.ldt = c.ffn;
+    { ProfScope ps(h, DFLASH_KERNEL_GATEUP_GEMM, s); launch_gemm(c.dtype, EPI_SWIGLU, pl.gateup, gu, s); }
+
+    GemmParams gd = gemm_in(sb + sc.z, c.ffn);
+    gd.a_packed = gu.out_packed;
+    gd.w[0] = h->packed + h->pk.wdown[l];
+    gd.tiles = tiles_of(d);
+    gd.N = d;
+    gd.P = pl.down.P;
+    gd.out_f32 = dpart;
+    { ProfScope ps(h, DFLASH_KERNEL_DOWN_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.down, gd, s); }
+    st = launched("target layer");
+    if (st) return st;
+  }
+  NormParams nf{};
+  nf.x_in = hbuf;
+  nf.part = dpart;
+  nf.n_part = pl.down.P;
+  nf.feat = feat_of(c.n_layers - 1);
+  nf.ldx = d;
+  nf.gamma = h->w.final_norm;
+  nf.eps = c.rms_eps;
+  nf.out = sb + sc.xa;
+  nf.ldo = d;
+  nf.out_packed = pl.lm.mt == 0;
+  nf.d = d;
+  nf.M = M;
+  nf.zero_keys = sat<unsigned long long>(sb, sc.keys);
+  norm(nf);
+  st = lm_head(h, s, sb, sc, pl, M, nf.out_packed, greedy, nullptr, nullptr, logits);
+  if (st) return st;
+  for (int i = 0; i < n_req; ++i) h->slots[slots[i]].ctx_len += n_rows;
+  return DFLASH_OK;
 }
 
 dflash_status dflash_select_path(dflash_handle* h, void* stream, int32_t n_req, const int32_t* topk_ids,

@@ -47,6 +47,7 @@ def make_config(shape: dict, *, max_batch: int, max_pages: int, max_pages_per_re
     c.rms_eps = shape["rms_eps"]
     c.rope_theta = shape["rope_theta"]
     c.selector_rank = int(shape.get("selector_rank") or 0)
+    c.target = int(shape.get("target") or 0)
     return c
 
 
@@ -76,8 +77,9 @@ class Drafter:
         w = B.DFlashWeights()
         w.embed = up(weights["embed"])
         w.lm_head = up(weights["lm_head"])
-        w.fc = up(weights["fc"])
-        w.fc_norm = up(weights["fc_norm"])
+        if not shape.get("target"):
+            w.fc = up(weights["fc"])
+            w.fc_norm = up(weights["fc_norm"])
         w.final_norm = up(weights["final_norm"])
         for l, lw in enumerate(weights["layers"]):
             L = w.layers[l]
@@ -192,3 +194,22 @@ class Drafter:
 
     def check(self):
         B.dflash_check(self.h, self.stream)
+
+
+class Target(Drafter):
+    """A target-model handle (config ``target`` = 1): causal verify forwards
+    over its own paged KV cache.  ``block_size`` of the shape is the largest
+    number of rows per request of one call."""
+
+    def forward(self, slots, n_rows: int, tokens: torch.Tensor, feat_layers=(), logits=None):
+        """tokens [len(slots) * n_rows] int32 (device) -> (greedy [rows], features {layer: [rows, d]})."""
+        rows = len(slots) * n_rows
+        greedy = torch.empty(rows, dtype=torch.int32, device=self.dev)
+        feats = {l: torch.empty((rows, self.cfg.hidden), dtype=self.tdt, device=self.dev) for l in feat_layers}
+        B.dflash_target_forward(self.h, self.stream, list(slots), n_rows, tokens.data_ptr(), greedy.data_ptr(),
+                                logits.data_ptr() if logits is not None else 0, list(feat_layers),
+                                [feats[l].data_ptr() for l in feat_layers])
+        return greedy, feats
+
+    def set_context_length(self, slot: int, ctx_len: int):
+        B.dflash_set_context_length(self.h, slot, ctx_len)

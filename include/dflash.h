@@ -55,8 +55,8 @@
 extern "C" {
 #endif
 
-#define DFLASH_ABI_VERSION 2
-#define DFLASH_MAX_LAYERS 16
+#define DFLASH_ABI_VERSION 3
+#define DFLASH_MAX_LAYERS 64
 #define DFLASH_MAX_FEAT 8
 #define DFLASH_MAX_BATCH 256
 #define DFLASH_PAGE_SIZE 16
@@ -81,7 +81,9 @@ typedef enum { DFLASH_BF16 = 0, DFLASH_F32 = 1 } dflash_dtype;
  *   1 <= n_layers <= DFLASH_MAX_LAYERS; 1 <= n_feat <= DFLASH_MAX_FEAT;
  *   0 <= mask_token_id < vocab; window 0 (unbounded) or a positive multiple
  *   of 16; topk 0 or 16; max_batch <= DFLASH_MAX_BATCH; selector_rank 0,
- *   or a multiple of 64 up to 512 with topk 16. */
+ *   or a multiple of 64 up to 512 with topk 16.  A target handle (target 1)
+ *   takes 1 <= block_size <= 64 rows per request and no window, conv, top-16
+ *   or selector; its fc and fc_norm may be NULL. */
 typedef struct dflash_config {
   int32_t hidden;            /* d */
   int32_t n_q_heads;         /* Hq */
@@ -106,6 +108,9 @@ typedef struct dflash_config {
   float rms_eps;             /* RMSNorm epsilon */
   float rope_theta;          /* RoPE base */
   int32_t selector_rank;     /* DFlash-2 path selector rank r ([guide] 7); 0 = none */
+  int32_t target;            /* 1 = the handle is a target model (dflash_target_forward):
+                                causal attention over its own KV cache, token inputs;
+                                block_size is then the rows per request of one call */
 } dflash_config;
 
 /* Per-layer weights (device pointers, dtype of the config).
@@ -264,6 +269,38 @@ dflash_status dflash_draft_block_static(dflash_handle *h, void *stream, int32_t 
  * Host only. */
 size_t dflash_draft_static_bytes(const dflash_config *cfg, int32_t n_req);
 
+/* Target-side verify forward ([guide] section 4: the target runs once over
+ * the context plus the drafted block and checks every drafted token; section
+ * 3.2: its feature layers feed the draft).  On a target handle: for each of
+ * the n_req requests, n_rows (<= block_size) new tokens at positions
+ * ctx_len .. ctx_len+n_rows-1 go through the causal decoder (row i attends
+ * to every cached position and to new rows 0..i); their K/V are appended to
+ * the slot's pages and ctx_len advances by n_rows.  Per row: the greedy token
+ * (argmax of the logits, ties to the lowest id) and, optionally, the logits
+ * and the residual stream after each listed feature layer (storage dtype),
+ * ready for dflash_inject_context of the draft.
+ *   slots        host [n_req] distinct bound slots
+ *   tokens       device [n_req * n_rows] int32, rows grouped by request
+ *   greedy       device [n_req * n_rows] int32 output
+ *   logits       device [n_req * n_rows, V] fp32 output, or NULL
+ *   feat_layers  host [n_feat_out] 0-based layer ids (< n_layers), ascending
+ *   feat_out     host array of n_feat_out device pointers, each
+ *                [n_req * n_rows, d] storage dtype output
+ * The verify of a B-token draft takes the pending token and the B drafts
+ * (n_rows = B + 1); after acceptance, dflash_set_context_length rolls the
+ * slot back to the committed length.  DFLASH_E_CAPACITY if a slot's pages or
+ * max_position cannot hold the new rows; DFLASH_E_INVALID on a draft handle. */
+dflash_status dflash_target_forward(dflash_handle *h, void *stream, int32_t n_req, const int32_t *slots,
+                                    int32_t n_rows, const int32_t *tokens, int32_t *greedy,
+                                    float *logits, int32_t n_feat_out, const int32_t *feat_layers,
+                                    void *const *feat_out);
+
+/* Sets a bound slot's context length to ctx_len (kv_begin <= ctx_len <=
+ * the current length): positions from ctx_len on become invisible and are
+ * overwritten by later writes (the target's rollback after verification).
+ * Synchronous (updates the slot state on the device). */
+dflash_status dflash_set_context_length(dflash_handle *h, int32_t slot, int32_t ctx_len);
+
 /* DFlash-2 path selector ([guide] section 7, path selector bullet): from
  * the top-16 candidates of every block position (dflash_draft_block's
  * topk_ids / topk_logits), one path per request: position 0 takes its top-1
@@ -367,7 +404,8 @@ typedef enum {
   DFLASH_KERNEL_TOPK = 16,       /* merge of the top-16 lists */
   DFLASH_KERNEL_PATH = 17,       /* DFlash-2 path selector */
   DFLASH_KERNEL_SAMPLE = 18,     /* sampled drafting */
-  DFLASH_KERNEL_COUNT = 19
+  DFLASH_KERNEL_TARGET_ATTN = 19, /* target: q RoPE, K/V append, causal attention */
+  DFLASH_KERNEL_COUNT = 20
 } dflash_kernel;
 
 /* Launch timing for measurement runs.  After dflash_profile_begin(h, mask),

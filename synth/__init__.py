@@ -88,6 +88,10 @@ CONFIGS = {
         vocab=3001, n_layers=2, window=128, batch=2, ctx=None,
         ctx_range=(150, 420), seed=16,
     ),
+    "small_target": dict(
+        hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1536,
+        vocab=3001, n_layers=6, block_size=17, target=1, seed=17,
+    ),
     "small_conv": dict(
         hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1536,
         vocab=3001, n_layers=2, conv2=1, topk=16, window=128, batch=2,

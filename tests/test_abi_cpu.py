@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function():
     assert len(names) >= 14
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/dflash.h but not exported"
-    assert B.dflash_abi_version() == 2
+    assert B.dflash_abi_version() == 3
 
 
 def test_feature_layers_entry_point_matches_rule():
@@ -77,7 +77,7 @@ def test_every_workload_config_is_valid(name):
 
 @pytest.mark.parametrize("field,value", [
     ("hidden", 300), ("head_dim", 96), ("n_kv_heads", 3), ("ffn", 1000), ("n_layers", 0),
-    ("n_layers", 17), ("block_size", 0), ("block_size", 17), ("n_feat", 0), ("n_feat", 9),
+    ("n_layers", 65), ("block_size", 0), ("block_size", 17), ("target", 2), ("n_feat", 0), ("n_feat", 9),
     ("dtype", 7), ("mask_token_id", 3001), ("page_size", 32), ("window", 100), ("topk", 8),
     ("max_batch", 0), ("max_batch", 257), ("max_pages", 0), ("max_position", 3),
     ("max_inject_rows", 0), ("conv2", 2),
@@ -228,3 +228,36 @@ def test_selector_config_rules_and_entry_validation():
     with pytest.raises(B.DFlashError) as e:
         B.dflash_create(c1, w, 1 << 30, 2 << 30, 3 << 30)
     assert e.value.status == B.E_INVALID
+
+
+def test_target_handle_rules():
+    """A target handle takes up to 64 rows per request and none of the draft's
+    extras; draft entry points refuse it and the target forward refuses a
+    draft handle, before any device work."""
+    c = _cfg("small_target", max_batch=2)
+    B.dflash_validate_config(c)
+    for field, val in (("block_size", 65), ("window", 16), ("conv2", 1), ("topk", 16)):
+        c2 = _cfg("small_target", max_batch=2)
+        setattr(c2, field, val)
+        with pytest.raises(B.DFlashError):
+            B.dflash_validate_config(c2)
+    w = _fake_weights(c.n_layers)
+    w.fc = w.fc_norm = None  # a target has no context projection
+    h = B.dflash_create(c, w, 1 << 30, 2 << 30, 3 << 30)
+    try:
+        with pytest.raises(B.DFlashError) as e:
+            B.dflash_draft_block(h, 0, [0], 0, 1 << 20)
+        assert e.value.status == B.E_INVALID and "target" in str(e.value)
+        with pytest.raises(B.DFlashError) as e:  # the slot is not bound
+            B.dflash_target_forward(h, 0, [0], 17, 1 << 20, 1 << 20)
+        assert e.value.status == B.E_INVALID
+    finally:
+        B.dflash_destroy(h)
+    d = _cfg("small_bf16", max_batch=2)
+    hd = B.dflash_create(d, _fake_weights(d.n_layers), 1 << 30, 2 << 30, 3 << 30)
+    try:
+        with pytest.raises(B.DFlashError) as e:
+            B.dflash_target_forward(hd, 0, [0], 1, 1 << 20, 1 << 20)
+        assert e.value.status == B.E_INVALID and "target" in str(e.value)
+    finally:
+        B.dflash_destroy(hd)
