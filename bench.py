@@ -257,6 +257,8 @@ def main():
     ap.add_argument("--single", action="store_true",
                     help="run only --config (the default run adds the other measured workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-target", action="store_true",
+                    help="skip the speculative cycle against a full-depth target (qwen3_8b only)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (counter calibration)")
     args = ap.parse_args()
@@ -276,7 +278,8 @@ def main():
         print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30}))
         return
 
-    result = run_workload(args.config, args.steps, args.warmup, cpu=not args.no_cpu_baseline)
+    result = run_workload(args.config, args.steps, args.warmup, cpu=not args.no_cpu_baseline,
+                          target=args.config == "qwen3_8b" and not args.no_target)
     if not args.single and args.config == "qwen3_8b":
         # the other measured workloads, each in its own handle, reported beside the headline
         result["workloads"] = {}
@@ -289,10 +292,10 @@ def main():
 SUMMARY_KEYS = ("value", "unit", "config", "dtype", "ms_per_step", "accepted_tok_per_s", "mean_accept",
                 "draft_ms", "draft_ms_percentiles", "draft_only_blocks_per_s", "draft_hbm_frac",
                 "gemm_mfma_frac", "gemm_tflops", "cycle_hbm_frac", "kernel_ms_per_draft", "roofline",
-                "memory_bytes", "shares_of_cycle")
+                "memory_bytes", "shares_of_cycle", "sampled_verification", "speculative_cycle")
 
 
-def run_workload(config, steps, warmup, cpu=False):
+def run_workload(config, steps, warmup, cpu=False, target=False):
     """One workload in its own handle: draft-only rate (with per-call
     percentiles), kernel breakdown, the timed speculative cycles and the
     roofline of the dominant kernel class; for the DFlash-2 workload, the
@@ -556,12 +559,200 @@ def run_workload(config, steps, warmup, cpu=False):
                 "counted": "the path walk through the top-16 lists (pair scores on the matrix cores)"}
         shares["pages"] = "0.7 % (conv) and 0.6 % (path selector) of the cycle, hardware not stated"
         result["shares_of_cycle"] = shares
+    if topk:
+        # sampled mode (the guide's CLI settings: temperature 1, top-k 20, top-p 0.95): draw the block
+        # from the draft's top-16 lists, then rejection-sample it against synthetic target logits
+        sp = Bnd.DFlashSampling(1.0, 20, 0.95)
+        tlog = torch.randn((n, B + 1, V), dtype=torch.float32, device=dev)
+        uv = torch.rand((n, B), dtype=torch.float32, device=dev)
+        uu = torch.rand((n, B + 1, 2), dtype=torch.float32, device=dev)
+        sd = torch.empty((n, B), dtype=torch.int32, device=dev)
+        draft(last0_dev)
+        for _ in range(warmup):
+            dr.draft_sample(sp, tk_ids, tk_val, uv, out=sd)
+            dr.verify_sample(sp, sd, tk_ids, tk_val, tlog, uu)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            dr.draft_sample(sp, tk_ids, tk_val, uv, out=sd)
+            dr.verify_sample(sp, sd, tk_ids, tk_val, tlog, uu)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tb = n * (B + 1) * V * 4
+        result["sampled_verification"] = {
+            "settings": "temperature 1, top-k 20, top-p 0.95", "ms_per_call": round(ms, 4),
+            "target_logit_bytes": tb, "achieved_GBps": round(tb / (ms * 1e-3) / 1e9, 1),
+            "share_of_cycle": round(ms / cycle_ms, 4),
+            "counted": "sampled draw of the block from the top-16 lists + rejection sampling against "
+                       "the target's logits (top-k by radix select over each row)"}
+        del tlog
+    if target:
+        result["speculative_cycle"] = speculative_cycle(shape, dr, reset, reqs[0]["sched"], steps, warmup, draft_ms)
     if cpu:
         result["cpu_baseline"] = cpu_baseline(shape, weights, a_mean, int(np.median(visible0)))
     dr.close()
     del dr, reqs, Gs, Hc
     torch.cuda.empty_cache()
     return result
+
+
+def target_bytes(tshape, rows, visible):
+    """Algorithmic HBM bytes of one target forward of ``rows`` new rows of
+    one request over ``visible`` cached positions: every weight matrix once
+    (QKV, O, gate/up, down per layer, the LM head), the embedding rows, the
+    cached K/V read, the new K/V written and the feature rows written."""
+    e = 2 if tshape["dtype"] == "bf16" else 4
+    d, hq, hkv, dh, F, V, L = (tshape[k] for k in ("hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn",
+                                                   "vocab", "n_layers"))
+    per_layer = ((hq + 2 * hkv) * dh * d + d * hq * dh + 2 * F * d + d * F + 2 * d) * e
+    kv = L * 2 * hkv * dh * e
+    return int(L * per_layer + V * d * e + d * e + rows * d * e + (visible + rows) * kv + rows * kv
+               + tshape["n_feat"] * rows * d * e)
+
+
+def speculative_cycle(shape, dr, reset, sched, steps, warmup, draft_ms):
+    """The whole speculative cycle against a full-depth target of the same
+    family: draft the block, run the target's verify forward over the pending
+    token and the block (its feature layers' rows come out of the same call),
+    accept, inject the accepted rows' target features into the draft, roll the
+    target back.  Random weights make real acceptance near zero, so the
+    accept step checks the drafts against seeded target tokens with the
+    workload's accept-length schedule, as in the draft-only cycle; everything
+    else is the real computation.  Beside it: the target's autoregressive
+    step (one row), which speculative decoding replaces."""
+    import torch
+
+    import synth
+    from block_diffusion_drafter_proj_amd import binding as Bnd
+    from block_diffusion_drafter_proj_amd.drafter import Target
+
+    dev = torch.device("cuda")
+    B, V, d, ctx = shape["block_size"], shape["vocab"], shape["hidden"], shape["ctx"]
+    Lt = shape["target_layers"]
+    fl = Bnd.dflash_feature_layers(Lt, shape["n_feat"])
+    n_cycles = warmup + steps
+    sched = [int(x) for x in sched[:n_cycles]]
+    grow = sum(sched) + n_cycles + 2 * (B + 1) + steps
+    npg = (ctx + grow) // 16 + 2
+    tshape = dict(shape, n_layers=Lt, target=1, block_size=B + 1, topk=0, conv2=0, selector_rank=0, window=0)
+    t_setup = time.perf_counter()
+    tgt = Target(tshape, synth.target_weights_device(tshape, Lt, dev), max_batch=1, max_pages=npg,
+                 max_pages_per_req=npg, max_position=ctx + grow + 32)
+    # the target's cached context: synthetic K/V N(0, 1) drawn on the device
+    kv = tgt.kv_view()
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(synth.rng(shape["seed"], synth.S_TARGET, 81).integers(1 << 62)))
+    for l in range(Lt):
+        kv[l].copy_(torch.randn(kv[l].shape, generator=g, device=dev, dtype=torch.float32))
+    tgt.bind(0, list(range(npg)))
+    tgt.set_context_length(0, ctx)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    toks = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    toks.copy_(torch.from_numpy(synth.rng(shape["seed"], synth.S_ACCEPT, 97).integers(0, V, size=B + 1)
+                                .astype(np.int32)))
+    greedy = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    feats = {l: torch.empty((B + 1, d), dtype=dr.tdt, device=dev) for l in fl}
+
+    def timed(fn, k):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(k):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    # the target alone: verify forward of B + 1 rows (rolled back after each), one autoregressive row
+    def verify_fwd():
+        tgt.forward([0], B + 1, toks, fl, greedy=greedy, feats=feats)
+        tgt.set_context_length(0, ctx)
+
+    verify_ms = timed(verify_fwd, steps)
+    Bnd.dflash_profile_begin(tgt.h, (1 << len(Bnd.KERNELS)) - 1)
+    for _ in range(3):
+        verify_fwd()
+    tprof = {k: round(ms / 3, 4) for k, (ms, cnt) in Bnd.dflash_profile_end(tgt.h).items()}
+    ar_ms = timed(lambda: tgt.forward([0], 1, toks, fl, greedy=greedy, feats=feats), steps)
+    tgt.set_context_length(0, ctx)
+
+    # ---- the closed cycle: record pass (drafts -> seeded target tokens), then timed replay ----
+    out = torch.empty((1, B), dtype=torch.int32, device=dev)
+    acc = torch.empty((n_cycles, 1), dtype=torch.int32, device=dev)
+    com = torch.empty((n_cycles, 1, B + 1), dtype=torch.int32, device=dev)
+    last = torch.empty((n_cycles, 1), dtype=torch.int32, device=dev)
+    pend0 = toks[:1].clone()
+    gen = synth.rng(shape["seed"], synth.S_ACCEPT, 96)
+    Gs = []
+
+    def cycle(i, n, record):
+        dd = dr.draft([0], out=out)
+        toks[:1].copy_(last[i - 1] if i else pend0)
+        toks[1:].copy_(dd[0])
+        tgt.forward([0], B + 1, toks, fl, greedy=greedy, feats=feats)
+        a = sched[i]
+        if record:
+            Gs.append(torch.from_numpy(synth.synthetic_greedy(dd.cpu().numpy()[0], a, V, gen)[None]).to(dev))
+        dr.verify(dd, Gs[i], acc[i], com[i], last[i])
+        dr.inject([0], [a + 1], [feats[l][:a + 1] for l in fl])
+        tgt.set_context_length(0, n + a)  # keep the context, the pending token and the a accepted drafts
+        return n + a + 1
+
+    def run(record, lo, hi, n):
+        for i in range(lo, hi):
+            n = cycle(i, n, record)
+        return n
+
+    for record in (True, False):
+        reset()
+        tgt.set_context_length(0, ctx)
+        n = run(record, 0, warmup, ctx + 1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        run(record, warmup, n_cycles, n)
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    assert acc.cpu().numpy()[:, 0].tolist() == sched, "accept lengths differ from the schedule"
+    tgt.check()
+    dr.check()
+    cycle_ms = e0.elapsed_time(e1) / steps
+    committed = float(np.mean(sched[warmup:])) + 1.0
+    tb = target_bytes(tshape, B + 1, ctx)
+    res = {
+        "target": (f"{Lt}-layer target of the draft's family (hidden {d}, {shape['n_q_heads']}/"
+                   f"{shape['n_kv_heads']} heads x {shape['head_dim']}, ffn {shape['ffn']}, vocab {V}), "
+                   f"random init N(0, 0.02), bf16, batch 1, cached context {ctx} (synthetic K/V)"),
+        "feature_layers": fl,
+        "target_verify_ms": round(verify_ms, 4),
+        "target_verify_rows": B + 1,
+        "target_verify_bytes": tb,
+        "target_verify_hbm_frac": round(tb / (verify_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "target_kernel_ms_per_verify": tprof,
+        "target_ar_step_ms": round(ar_ms, 4),
+        "cycle_ms": round(cycle_ms, 4),
+        "cycle_wall_ms": round((t1 - t0) * 1e3 / steps, 4),
+        "draft_share_of_cycle": round(draft_ms / cycle_ms, 4),
+        "mean_committed_per_cycle": round(committed, 3),
+        "ms_per_token": round(cycle_ms / committed, 4),
+        "ar_ms_per_token": round(ar_ms, 4),
+        "speedup_vs_ar": round(ar_ms / (cycle_ms / committed), 3),
+        "tok_per_s": round(committed * 1e3 / cycle_ms, 1),
+        "acceptance": "seeded accept lengths U{1..B} (the workload's schedule; random weights accept ~0)",
+        "setup_s": round(setup_s, 1),
+        "pages": "one cycle = one draft + one target verification, 3 ms + 20 ms in the news example "
+                 "(hardware not stated); over 6x lossless speedup over autoregressive decoding",
+    }
+    tgt.close()
+    del tgt, kv
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

@@ -97,7 +97,7 @@ def lib() -> ctypes.CDLL:
             "dflash_draft_static_bytes": (sz, [ctypes.POINTER(DFlashConfig), i32]),
             "dflash_select_path": (i32, [vp, vp, i32, vp, vp, vp, vp]),
             "dflash_target_forward": (i32, [vp, vp, i32, pi32, i32, vp, vp, vp, i32, pi32, ctypes.POINTER(vp)]),
-            "dflash_set_context_length": (i32, [vp, i32, i32]),
+            "dflash_set_context_length": (i32, [vp, vp, i32, i32]),
             "dflash_draft_sample": (i32, [vp, vp, i32, ctypes.POINTER(DFlashSampling), vp, vp, vp, vp]),
             "dflash_verify_sample": (i32, [vp, vp, i32, ctypes.POINTER(DFlashSampling), vp, vp, vp, vp, vp,
                                            vp, vp, vp]),
@@ -215,8 +215,8 @@ def dflash_target_forward(h: int, stream: int, slots, n_rows: int, tokens: int, 
                                        arr))
 
 
-def dflash_set_context_length(h: int, slot: int, ctx_len: int) -> None:
-    _check(lib().dflash_set_context_length(ctypes.c_void_p(h), slot, ctx_len))
+def dflash_set_context_length(h: int, stream: int, slot: int, ctx_len: int) -> None:
+    _check(lib().dflash_set_context_length(ctypes.c_void_p(h), ctypes.c_void_p(stream), slot, ctx_len))
 
 
 def dflash_select_path(h: int, stream: int, n_req: int, topk_ids: int, topk_logits: int, path: int,

@@ -954,4 +954,12 @@ void launch_scatter(int dtype, int dh, const ScatterParams& p, hipStream_t s) {
     scatter_t<float>(dh, p, s);
 }
 
+__global__ void k_set_ctx(SlotState* state, int slot, int ctx_len) {
+  if (threadIdx.x == 0) state[slot].ctx_len = ctx_len;
+}
+
+void launch_set_ctx(SlotState* state, int slot, int ctx_len, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_ctx, dim3(1), dim3(64), 0, s, state, slot, ctx_len);
+}
+
 }  // namespace dflash

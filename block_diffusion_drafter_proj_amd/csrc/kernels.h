@@ -241,6 +241,8 @@ __host__ __device__ inline int split_pages(int n_units, int target, int cap) {
 }
 void launch_combine(int dtype, int dh, const CombineParams& p, hipStream_t s);
 void launch_scatter(int dtype, int dh, const ScatterParams& p, hipStream_t s);
+// Stream-ordered update of one slot's context length on the device.
+void launch_set_ctx(SlotState* state, int slot, int ctx_len, hipStream_t s);
 void launch_topk_merge(const TopkParams& p, hipStream_t s);
 void launch_finalize(const unsigned long long* keys, int rows, int vocab, int* draft,
                      hipStream_t s);

@@ -1174,18 +1174,20 @@ size_t dflash_draft_static_bytes(const dflash_config* cfg, int32_t n_req) {
   return make_scratch(*cfg, n_req, false).total;
 }
 
-dflash_status dflash_set_context_length(dflash_handle* h, int32_t slot, int32_t ctx_len) {
+dflash_status dflash_set_context_length(dflash_handle* h, void* stream, int32_t slot, int32_t ctx_len) {
   if (!h) return fail(DFLASH_E_INVALID, "handle is NULL");
   if (slot < 0 || slot >= h->cfg.max_batch || !h->slots[slot].bound)
     return fail(DFLASH_E_INVALID, "slot %d is not bound", slot);
   HostSlot& hs = h->slots[slot];
-  if (ctx_len < hs.kv_begin || ctx_len > hs.ctx_len)
-    return fail(DFLASH_E_INVALID, "ctx_len %d out of [%d, %d]", ctx_len, hs.kv_begin, hs.ctx_len);
+  // without a window, any length the bound pages hold; with one, only a rollback
+  const int top = h->cfg.window ? hs.ctx_len : std::min(hs.n_pages * 16, h->cfg.max_position - 1);
+  if (ctx_len < hs.kv_begin || ctx_len > top)
+    return fail(DFLASH_E_INVALID, "ctx_len %d out of [%d, %d]", ctx_len, hs.kv_begin, top);
   dflash_status st = ensure_device(h);
   if (st) return st;
-  SlotState ss{ctx_len, hs.kv_begin, hs.n_pages, 0};
-  hipError_t e = hipMemcpy(h->ws + h->lay.state + sizeof(SlotState) * slot, &ss, sizeof(ss), hipMemcpyHostToDevice);
-  if (e) return hip_fail(e, "slot state upload");
+  launch_set_ctx(at<SlotState>(h, h->lay.state), slot, ctx_len, reinterpret_cast<hipStream_t>(stream));
+  st = launched("set context length");
+  if (st) return st;
   hs.ctx_len = ctx_len;
   return DFLASH_OK;
 }

@@ -201,15 +201,19 @@ class Target(Drafter):
     over its own paged KV cache.  ``block_size`` of the shape is the largest
     number of rows per request of one call."""
 
-    def forward(self, slots, n_rows: int, tokens: torch.Tensor, feat_layers=(), logits=None):
-        """tokens [len(slots) * n_rows] int32 (device) -> (greedy [rows], features {layer: [rows, d]})."""
+    def forward(self, slots, n_rows: int, tokens: torch.Tensor, feat_layers=(), logits=None, greedy=None,
+                feats=None):
+        """tokens [len(slots) * n_rows] int32 (device) -> (greedy [rows], features {layer: [rows, d]}).
+        ``greedy`` and ``feats`` may be given preallocated (at least rows long)."""
         rows = len(slots) * n_rows
-        greedy = torch.empty(rows, dtype=torch.int32, device=self.dev)
-        feats = {l: torch.empty((rows, self.cfg.hidden), dtype=self.tdt, device=self.dev) for l in feat_layers}
+        if greedy is None:
+            greedy = torch.empty(rows, dtype=torch.int32, device=self.dev)
+        if feats is None:
+            feats = {l: torch.empty((rows, self.cfg.hidden), dtype=self.tdt, device=self.dev) for l in feat_layers}
         B.dflash_target_forward(self.h, self.stream, list(slots), n_rows, tokens.data_ptr(), greedy.data_ptr(),
                                 logits.data_ptr() if logits is not None else 0, list(feat_layers),
                                 [feats[l].data_ptr() for l in feat_layers])
         return greedy, feats
 
     def set_context_length(self, slot: int, ctx_len: int):
-        B.dflash_set_context_length(self.h, slot, ctx_len)
+        B.dflash_set_context_length(self.h, self.stream, slot, ctx_len)

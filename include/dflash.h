@@ -295,11 +295,17 @@ dflash_status dflash_target_forward(dflash_handle *h, void *stream, int32_t n_re
                                     float *logits, int32_t n_feat_out, const int32_t *feat_layers,
                                     void *const *feat_out);
 
-/* Sets a bound slot's context length to ctx_len (kv_begin <= ctx_len <=
- * the current length): positions from ctx_len on become invisible and are
- * overwritten by later writes (the target's rollback after verification).
- * Synchronous (updates the slot state on the device). */
-dflash_status dflash_set_context_length(dflash_handle *h, int32_t slot, int32_t ctx_len);
+/* Sets a bound slot's context length to ctx_len.  Lowering it is the
+ * target's rollback after verification: positions from ctx_len on become
+ * invisible and are overwritten by later writes.  Raising it (handles
+ * without a window only, up to what the bound pages hold and below
+ * max_position) declares positions that the caller has already written into
+ * the slot's pages visible, e.g. a cached prefix copied in.  The device copy
+ * of the slot state is updated by a kernel on `stream`: the call does not
+ * wait for the device, and later work on that stream sees the new length.
+ * DFLASH_E_INVALID for an unbound slot or a length outside [kv_begin, that
+ * limit] (with a window: [kv_begin, current length]). */
+dflash_status dflash_set_context_length(dflash_handle *h, void *stream, int32_t slot, int32_t ctx_len);
 
 /* DFlash-2 path selector ([guide] section 7, path selector bullet): from
  * the top-16 candidates of every block position (dflash_draft_block's

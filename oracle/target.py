@@ -42,6 +42,13 @@ class TargetOracle:
         self.d, self.hq, self.hkv, self.dh = cfg["hidden"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
         self.F, self.V, self.L = cfg["ffn"], cfg["vocab"], cfg["n_layers"]
         self.eps, self.theta = cfg["rms_eps"], cfg["rope_theta"]
+        self._f64 = {}
+
+    def _mat(self, key, a):
+        """float64 copy of a weight matrix, converted once."""
+        if key not in self._f64:
+            self._f64[key] = np.asarray(a, dtype=np.float64)
+        return self._f64[key]
 
     def new_cache(self):
         """Per layer K, V lists of [Hkv, dh] rows, one per cached position."""
@@ -63,12 +70,12 @@ class TargetOracle:
         R = len(tokens)
         p0 = len(cache[0]["k"])
         pos = p0 + np.arange(R)
-        h = np.asarray(self.w["embed"], dtype=np.float64)[tokens].copy()
+        h = np.asarray(np.asarray(self.w["embed"])[tokens], dtype=np.float64)
         G = self.hq // self.hkv
         feats = {}
         for l in range(self.L):
             lw = self.w["layers"][l]
-            wqkv = np.asarray(lw["wqkv"], dtype=np.float64)
+            wqkv = self._mat(("wqkv", l), lw["wqkv"])
             wq = wqkv[: self.hq * self.dh]
             wk = wqkv[self.hq * self.dh: (self.hq + self.hkv) * self.dh]
             wv = wqkv[(self.hq + self.hkv) * self.dh:]
@@ -89,13 +96,13 @@ class TargetOracle:
                 s = np.where(mask, s, -np.inf)
                 o[:, j] = softmax(s) @ Vv[:, g]
             o = st(o.reshape(R, -1))
-            h = h + o @ np.asarray(lw["wo"], dtype=np.float64).T
+            h = h + o @ self._mat(("wo", l), lw["wo"]).T
             m = st(rmsnorm(h, lw["mlp_norm"], self.eps))
-            gu = m @ np.asarray(lw["wgateup"], dtype=np.float64).T
+            gu = m @ self._mat(("wgateup", l), lw["wgateup"]).T
             z = st(swiglu(gu[:, : self.F], gu[:, self.F:]))
-            h = h + z @ np.asarray(lw["wdown"], dtype=np.float64).T
+            h = h + z @ self._mat(("wdown", l), lw["wdown"]).T
             if l in feat_layers:
                 feats[l] = st(h)
         hn = st(rmsnorm(h, self.w["final_norm"], self.eps))
-        logits = hn @ np.asarray(self.w["lm_head"], dtype=np.float64).T
+        logits = hn @ self._mat("lm_head", self.w["lm_head"]).T
         return logits, feats

@@ -215,6 +215,51 @@ def make_weights(cfg: dict, seed: int | None = None, norm_std: float = 0.0,
     return w
 
 
+def context_kv(cfg: dict, req: int, layer: int, count: int):
+    """Synthetic cached K and V of a target's first ``count`` positions for
+    one request and layer: two arrays [count, Hkv, dh] of N(0, 1) values in
+    the storage dtype (stands in for a prefill that is not recomputed)."""
+    g = rng(cfg["seed"], S_TARGET, 61, req, layer)
+    shp = (count, cfg["n_kv_heads"], cfg["head_dim"])
+    k = g.standard_normal(shp, dtype=np.float32)
+    v = g.standard_normal(shp, dtype=np.float32)
+    return to_storage(k, cfg["dtype"]), to_storage(v, cfg["dtype"])
+
+
+def target_weights_device(cfg: dict, n_layers: int, device) -> dict:
+    """Random-init target decoder of the shape's dimensions and ``n_layers``
+    layers, drawn by torch's generator on ``device`` (a 36-layer 8B-shaped
+    target is ~8.2 G values, too many to draw on the host): every matrix
+    N(0, 0.02) in the storage dtype, all gains 1, untied embedding and LM
+    head.  Same (seed, n_layers) always gives the same weights."""
+    import torch
+
+    d, hq, hkv, dh = cfg["hidden"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    F, V = cfg["ffn"], cfg["vocab"]
+    dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    g = torch.Generator(device=device)
+
+    def mat(tid, shape, layer=0):
+        g.manual_seed(int(rng(cfg["seed"], S_TARGET, 71, tid, layer).integers(1 << 62)))
+        t = torch.empty(shape, dtype=dt, device=device)
+        rows = max(1, (1 << 26) // shape[1])
+        for r0 in range(0, shape[0], rows):  # fp32 draws in slices of <= 64 M values
+            blk = t[r0:r0 + rows]
+            blk.copy_(torch.randn(blk.shape, generator=g, device=device, dtype=torch.float32) * 0.02)
+        return t
+
+    def ones():
+        return torch.ones(d, dtype=dt, device=device)
+
+    w = dict(embed=mat(0, (V, d)), lm_head=mat(1, (V, d)), final_norm=ones(), layers=[])
+    for l in range(n_layers):
+        w["layers"].append(dict(
+            wqkv=mat(10, ((hq + 2 * hkv) * dh, d), l), wo=mat(11, (d, hq * dh), l),
+            wgateup=mat(12, (2 * F, d), l), wdown=mat(13, (d, F), l),
+            attn_norm=ones(), mlp_norm=ones()))
+    return w
+
+
 def uniforms(cfg: dict, shape, key: int = 0) -> np.ndarray:
     """Uniform numbers in [0, 1) (float32) for the sampled draws."""
     g = rng(cfg["seed"], S_TARGET, 41, key)

@@ -251,6 +251,9 @@ def test_target_handle_rules():
         with pytest.raises(B.DFlashError) as e:  # the slot is not bound
             B.dflash_target_forward(h, 0, [0], 17, 1 << 20, 1 << 20)
         assert e.value.status == B.E_INVALID
+        with pytest.raises(B.DFlashError) as e:  # nor can its length be set
+            B.dflash_set_context_length(h, 0, 0, 5)
+        assert e.value.status == B.E_INVALID and "not bound" in str(e.value)
     finally:
         B.dflash_destroy(h)
     d = _cfg("small_bf16", max_batch=2)

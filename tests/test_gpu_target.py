@@ -69,7 +69,7 @@ def test_target_forward_parity(n_req):
     caches = [o.new_cache() for _ in range(n_req)]
     rng = np.random.default_rng(20 + n_req)
     exempt = 0
-    for call, R in enumerate([17, 17, 17, 12, 17]):
+    for call, R in enumerate([17, 17, 17, 12, 1, 17]):
         toks = rng.integers(0, V, size=(n_req, R)).astype(np.int32)
         _force_kv(t, shape, pages, caches, n_req)
         lg = torch.empty((n_req * R, V), dtype=torch.float32, device=dev)
@@ -153,3 +153,62 @@ def test_speculative_loop_on_gpu_equals_greedy():
     assert not mism, f"first mismatch at {mism[0]}: gpu {out[mism[0]]} greedy {ref[mism[0]]}"
     print(f"[gpu speculative loop] {new} tokens in {cycles} cycles (mean accepted {new / cycles - 1:.2f}) "
           f"= greedy AR of the target", flush=True)
+
+
+@pytest.mark.parametrize("ctxs", [[4096], [0, 77, 2049]])
+def test_target_full_size(ctxs):
+    """Qwen3-8B-shaped layers (hidden 4096, 32/8 heads x 128, ffn 12288,
+    vocab 151936; 2 of the 36 layers, each layer's launches being the same),
+    a cached context of synthetic K/V written into the pages and into the
+    oracle's cache, then a 17-row verify call and a 1-row call (the
+    autoregressive step): logits, greedy, both layers' features and the
+    appended K/V match the oracle."""
+    dev = _dev()
+    from block_diffusion_drafter_proj_amd.drafter import Target
+
+    shape = synth.config("qwen3_8b", n_layers=2, target=1, block_size=17)
+    w = synth.make_weights(shape)
+    V, d, L = shape["vocab"], shape["hidden"], shape["n_layers"]
+    n = len(ctxs)
+    ppr = (max(ctxs) + 40) // 16 + 1
+    t = Target(shape, w, max_batch=n, max_pages=n * ppr, max_pages_per_req=ppr,
+               max_position=max(ctxs) + 64, poison_kv=True)
+    perm = synth.page_permutation(shape, n * ppr)
+    pages = [[int(x) for x in perm[r * ppr:(r + 1) * ppr]] for r in range(n)]
+    o = TargetOracle(shape, w)
+    caches = [o.new_cache() for _ in range(n)]
+    view = t.kv_view()
+    for r, c in enumerate(ctxs):
+        t.bind(r, pages[r])
+        for l in range(L):
+            K, Vv = synth.context_kv(shape, r, l, c)
+            caches[r][l]["k"].extend(list(K))
+            caches[r][l]["v"].extend(list(Vv))
+            if c:
+                write_kv(view, l, pages[r], list(range(c)), K, Vv)
+        t.set_context_length(r, c)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(31 + n)
+    exempt = 0
+    for call, R in enumerate([17, 1]):
+        toks = rng.integers(0, V, size=(n, R)).astype(np.int32)
+        lg = torch.empty((n * R, V), dtype=torch.float32, device=dev)
+        greedy, gf = t.forward(list(range(n)), R, torch.from_numpy(toks.reshape(-1)).to(dev), [0, 1], logits=lg)
+        torch.cuda.synchronize()
+        print(f"[target full size ctxs={ctxs}] call {call} ({R} rows) done on the GPU", flush=True)
+        g_lg = lg.cpu().numpy().reshape(n, R, V)
+        g_greedy = greedy.cpu().numpy().reshape(n, R)
+        for r in range(n):
+            p0 = len(caches[r][0]["k"])
+            ref_lg, ref_f = o.forward(caches[r], toks[r], [0, 1])
+            assert_rows_close(g_lg[r], ref_lg, what=f"call {call} req {r} logits")
+            exempt += assert_tokens_match(g_greedy[r], ref_lg, what=f"call {call} req {r} greedy")
+            for l in (0, 1):
+                assert_rows_close(gf[l].float().cpu().numpy().reshape(n, R, d)[r], ref_f[l],
+                                  what=f"call {call} req {r} feature {l}")
+            for l in range(L):
+                kg, vg = unpack_kv(view, l, pages[r], list(range(p0, p0 + R)))
+                assert_rows_close(kg, np.stack(caches[r][l]["k"][p0:p0 + R]), what=f"call {call} req {r} K {l}")
+                assert_rows_close(vg, np.stack(caches[r][l]["v"][p0:p0 + R]), what=f"call {call} req {r} V {l}")
+    t.check()
+    print(f"[target full size ctxs={ctxs}] near-tie greedy positions exempt: {exempt}", flush=True)
