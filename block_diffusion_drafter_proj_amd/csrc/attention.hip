@@ -404,18 +404,25 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
   __shared__ __attribute__((aligned(1024))) bf16 ring[kRing * STAGE];
   const float NEG = -INFINITY;
 
+  // r: the request, or in causal mode the (request, tile) pair
   const int gkv = blockIdx.x, s = blockIdx.y, r = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = gkv * G + wave;
   const int lane = lane_id(), l16 = lane & 15, g4 = lane >> 4;
-  const int slot = sl.slots[r];
+  const bool causal = p.causal_R > 0;
+  const int req = causal ? r / p.n_tiles : r;
+  const int slot = sl.slots[req];
   const SlotState st = p.state[slot];
-  const int hi = st.ctx_len;
+  // causal: the tile's rows sit at positions cpos .. cpos + 15 (capped at the
+  // last new row); a key is visible to every row of the tile up to cpos
+  const int cpos = causal ? st.ctx_len - p.causal_R + (r - req * p.n_tiles) * 16 : 0;
+  const int hi = causal ? min(st.ctx_len, cpos + 16) : st.ctx_len;
+  const int hi_all = causal ? cpos + 1 : hi;
   int lo = st.kv_begin;
   if (p.window > 0) lo = max(lo, hi - p.window);
   const int lp0 = lo / 16;
   const int n_lp = hi > lo ? (hi - 1) / 16 - lp0 + 1 : 0;
-  const int n_units = n_lp + 1;
+  const int n_units = causal ? n_lp : n_lp + 1;
   const int pps = split_pages(n_units, p.split_target, p.pps_cap);
   const int n_split = (n_units + pps - 1) / pps;
   if (s == 0 && gkv == 0 && threadIdx.x == 0) p.n_split[r] = n_split;
@@ -425,7 +432,7 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
   const int n_pairs = (u_end - u_begin + 1) / 2;
   const long long page_elems = 2LL * p.Hkv * 16 * DH;
   const bf16* pool = reinterpret_cast<const bf16*>(p.pool);
-  const bf16* blk = reinterpret_cast<const bf16*>(p.blk) + (long long)r * page_elems;
+  const bf16* blk = reinterpret_cast<const bf16*>(p.blk) + (long long)req * page_elems;  // per request
 
   bf16x8 qf[NJ];
   {
@@ -436,8 +443,10 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
   // Per-unit tables, lane L describing unit u_begin + L of the split (pps <=
   // 64): its base (the block page stands in for a missing unit, whose keys
   // are masked) and its visible positions as a 16-bit mask.
+  // In causal mode a missing unit (odd count) also reads the block page,
+  // which is allocated and masked.
   const bf16* my_base = blk;
-  unsigned my_vis = 0;
+  unsigned my_vis = 0, my_vis_all = 0;
   {
     const int uu = u_begin + lane;
     if (uu < u_end) {
@@ -451,15 +460,17 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
           my_base = pool + (long long)page * page_elems;
           const int pos0 = lp * 16;
           const int a0 = max(lo - pos0, 0), a1 = min(hi - pos0, 16);
-          my_vis = ((1u << a1) - 1u) & ~((1u << a0) - 1u);
+          my_vis = a1 > a0 ? ((1u << a1) - 1u) & ~((1u << a0) - 1u) : 0u;
+          const int a2 = min(hi_all - pos0, 16);
+          my_vis_all = a2 > a0 ? ((1u << a2) - 1u) & ~((1u << a0) - 1u) : 0u;
         }
       } else {
-        my_vis = (1u << p.B) - 1u;
+        my_vis = my_vis_all = (1u << p.B) - 1u;
       }
     }
   }
-  // units whose 16 positions are all visible: those pairs skip masking
-  const unsigned long long full_mask = __ballot(my_vis == 0xffffu);
+  // units whose 16 positions are visible to every row: those pairs skip masking
+  const unsigned long long full_mask = __ballot(my_vis_all == 0xffffu);
   const unsigned long long base_lo = reinterpret_cast<unsigned long long>(my_base);
   const unsigned b_lo32 = (unsigned)base_lo, b_hi32 = (unsigned)(base_lo >> 32);
   auto unit_ptr = [&](int lane_idx) -> const bf16* {
@@ -545,13 +556,21 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
     // unit's visibility mask.  Masking is written as selects: a divergent
     // branch that stored into one element of the score vector lost that store
     // in code generation.
+    // In causal mode a key is further hidden from the query rows before it.
     unsigned vbits = 0xffu;
     if (!fast) {
       const unsigned m0 = __builtin_amdgcn_readlane(my_vis, 2 * it);
       const unsigned m1 = __builtin_amdgcn_readlane(my_vis, 2 * it + 1);
       vbits = (((g4 >> 1) ? m1 : m0) >> (8 * (g4 & 1))) & 0xffu;
+      unsigned pbits = vbits;
+      if (causal) {
+        // key e of this lane: position 16 (lp0 + unit) + 8 (g4 % 2) + e
+        const int k0 = 16 * (lp0 + u_begin + 2 * it + (g4 >> 1)) + 8 * (g4 & 1);
+        const int lim = cpos + l16 - k0;  // keys e <= lim are at or before this row
+        pbits &= lim >= 7 ? 0xffu : lim < 0 ? 0u : (2u << lim) - 1u;
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = ((vbits >> e) & 1u) ? sv[e] : NEG;
+      for (int e = 0; e < 8; ++e) sv[e] = ((pbits >> e) & 1u) ? sv[e] : NEG;
     }
     float lmx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     if (__ballot(lmx * sl2 > m_run + 8.0f)) {  // false for a lane whose keys are all masked
@@ -603,9 +622,9 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
 
   // lane holds query row l16, dims dt*16 + 4*g4 + i
   if (n_split == 1) {
-    if (l16 < p.B) {
+    int m;
+    if (attn_out_row(p.causal_R, p.n_tiles, p.B, r, l16, m)) {
       const float inv = 1.0f / l_run;
-      const int m = r * p.B + l16;
       bf16* out = reinterpret_cast<bf16*>(p.out);
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
@@ -642,6 +661,8 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p) {
   const int rh = wid / 16;  // r * Hq + h
   if (rh >= p.n_rh || q >= p.B) return;
   const int r = rh / p.Hq, h = rh - r * p.Hq;
+  int m;
+  if (!attn_out_row(p.causal_R, p.n_tiles, p.B, r, q, m)) return;
   const int S = p.n_splits;
   const int ns = p.n_split[r];
   const long long pb = (long long)rh * S * 16 + q;
@@ -685,7 +706,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p) {
     }
   }
   const float inv = 1.0f / L;
-  const int m = r * p.B + q, k = h * DH + lane * C;  // C consecutive k stay contiguous
+  const int k = h * DH + lane * C;  // C consecutive k stay contiguous
   T* out = reinterpret_cast<T*>(p.out) + (p.out_packed ? frag_index(m, k, p.ldo) : (long long)m * p.ldo + k);
 #pragma unroll
   for (int c = 0; c < C; ++c) out[c] = from_f<T>(acc[c] * inv);
@@ -705,8 +726,9 @@ __global__ __launch_bounds__(256) void k_combine2(CombineParams p) {
   const int q = (wid & 7) * 2 + half;
   const int rh = wid >> 3;  // r * Hq + h
   if (rh >= p.n_rh) return;
-  const bool live = q < p.B;
   const int r = rh / p.Hq, h = rh - r * p.Hq;
+  int m;
+  const bool live = attn_out_row(p.causal_R, p.n_tiles, p.B, r, q, m);
   const int S = p.n_splits;
   const int ns = p.n_split[r];
   if (ns <= 1) return;  // written by the attention kernel
@@ -742,7 +764,7 @@ __global__ __launch_bounds__(256) void k_combine2(CombineParams p) {
   }
   if (!live) return;
   const float inv = 1.0f / L;
-  const int m = r * p.B + q, k = h * DH + hl * 4;  // 4 consecutive k stay contiguous
+  const int k = h * DH + hl * 4;  // 4 consecutive k stay contiguous
   typename Vec4<T>::type o;
 #pragma unroll
   for (int c = 0; c < 4; ++c) o[c] = from_f<T>(acc[c] * inv);

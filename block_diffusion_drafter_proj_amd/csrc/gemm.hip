@@ -267,6 +267,30 @@ __global__ __launch_bounds__(256) void k_pack(const T* src, T* dst, int N, int K
   *reinterpret_cast<Frag*>(dst + idx * 8) = v;
 }
 
+// One thread per 4 consecutive columns of one row: 16-byte loads of every
+// split's gate and up partials, summed in split order (the SwiGLU epilogue's
+// formula on the summed values).
+template <typename T>
+__global__ __launch_bounds__(256) void k_swiglu_parts(const float* part, int P, int M, int F, T* z, int ldo) {
+  const int f = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int m = blockIdx.y;
+  if (f >= F) return;
+  const long long plane = (long long)M * 2 * F;
+  const float* g = part + (long long)m * 2 * F + f;
+  f32x4 gs = *reinterpret_cast<const f32x4*>(g);
+  f32x4 us = *reinterpret_cast<const f32x4*>(g + F);
+  for (int q = 1; q < P; ++q) {
+    gs += *reinterpret_cast<const f32x4*>(g + q * plane);
+    us += *reinterpret_cast<const f32x4*>(g + q * plane + F);
+  }
+  T* o = z + (long long)m * ldo + f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float sg = gs[i] / (1.0f + expf(-gs[i]));
+    o[i] = from_f<T>(sg * us[i]);
+  }
+}
+
 template <typename T, int EPI>
 void launch_t(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
   if constexpr (sizeof(T) == 2 && EPI == EPI_PARTIAL) {
@@ -344,6 +368,15 @@ void launch_gemm(int dtype, int epi, const GemmPlan& pl, const GemmParams& p, hi
     launch_dt<bf16>(epi, pl, p, s);
   else
     launch_dt<float>(epi, pl, p, s);
+}
+
+void launch_swiglu_parts(int dtype, const float* part, int P, int M, int F, void* z, int ldo, hipStream_t s) {
+  if (M <= 0 || F <= 0) return;
+  const dim3 grid((F / 4 + 255) / 256, M);
+  if (dtype == DFLASH_BF16)
+    hipLaunchKernelGGL(k_swiglu_parts<bf16>, grid, dim3(256), 0, s, part, P, M, F, reinterpret_cast<bf16*>(z), ldo);
+  else
+    hipLaunchKernelGGL(k_swiglu_parts<float>, grid, dim3(256), 0, s, part, P, M, F, reinterpret_cast<float*>(z), ldo);
 }
 
 size_t packed_elems(int N, int K) { return (size_t)((N + 15) / 16) * 16 * (size_t)K; }

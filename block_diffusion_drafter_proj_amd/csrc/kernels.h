@@ -174,6 +174,12 @@ struct AttnParams {
   int ldo;
   int out_packed;  // out in fragment order with ldo columns
   unsigned int* err;
+  // Causal mode (a target's verify forward, bf16 only): causal_R new rows per
+  // request, already appended to the pages (the slot's device ctx_len counts
+  // them), attend causally; there is no block unit.  The grid's z runs over
+  // (request, 16-row tile) pairs, n_tiles tiles per request, and qb, part_*
+  // and n_split are indexed by that pair.  causal_R = 0: the draft's block.
+  int causal_R, n_tiles;
 };
 
 struct CombineParams {
@@ -184,7 +190,20 @@ struct CombineParams {
   void* out;  // storage dtype [n_req*B, Hq*dh]
   int ldo;
   int out_packed;  // out in fragment order with ldo columns
+  int causal_R, n_tiles;  // causal mode as in AttnParams (B = 16, n_rh over (request, tile) pairs)
 };
+
+// Output row of query row q of request (or, in causal mode, (request, tile)
+// pair) rv; false for a padding row.
+__host__ __device__ inline bool attn_out_row(int causal_R, int n_tiles, int B, int rv, int q, int& m) {
+  if (causal_R) {
+    const int r = rv / n_tiles, row = (rv - r * n_tiles) * 16 + q;
+    m = r * causal_R + row;
+    return row < causal_R;
+  }
+  m = rv * B + q;
+  return q < B;
+}
 
 struct InjectReq {
   int row_start, count, slot, pos0, final_ctx;
@@ -222,6 +241,10 @@ GemmPlan plan_gemm(int tiles, int K, int kblock, bool single_split, int max_nw =
 void launch_gemm(int dtype, int epi, const GemmPlan& pl, const GemmParams& p, hipStream_t s);
 size_t packed_elems(int N, int K);
 void launch_pack(int dtype, const void* src, void* dst, int N, int K, hipStream_t s);
+// z[m][f] = silu(g) * u rounded to the storage dtype, g and u summed in split
+// order from the gate/up product's split-K partials part[P][M][2F] (gate
+// columns 0..F-1, up columns F..2F-1); z row-major with row stride ldo.
+void launch_swiglu_parts(int dtype, const float* part, int P, int M, int F, void* z, int ldo, hipStream_t s);
 void launch_rmsnorm(int dtype, const NormParams& p, hipStream_t s);
 void launch_qkv_post(int dtype, int dh, int n_req, const QkvPostParams& p, const SlotArgs& sl,
                      hipStream_t s);
@@ -253,7 +276,8 @@ struct TargetQParams {
   int n_part, M, ld, R, Hq, dh;
   const float* cos_t;
   const float* sin_t;
-  void* q;  // [M][Hq][dh] storage dtype
+  void* q;  // [M][Hq][dh] storage dtype, or with n_tiles > 0 [n_req * n_tiles][Hq][16][dh] (zero padding rows)
+  int n_tiles;
   int pos0[DFLASH_MAX_BATCH];  // position of each request's first new row
 };
 struct CausalAttnParams {

@@ -89,7 +89,8 @@ Plans make_plans(const dflash_config& c, int M) {
   const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   // 17..64 rows: the split-K products stream their weights once for all
-  // rows (skinny kernel, 64-row block); the others keep their kernel below.
+  // rows (skinny kernel, 64-row block); so does the gate/up product, whose
+  // SwiGLU then runs on its partials.
   // At exactly 64 rows the tiled kernel (split-K 8 and 12) streams the O and
   // down weights faster than the 64-row block (measured 13 vs 15.5 us per O
   // launch at 33.6 MB), and the QKV and injection products slower.
@@ -106,7 +107,9 @@ Plans make_plans(const dflash_config& c, int M) {
     Plans p;
     p.qkv = mt4(tiles_of(qkvw), d);
     p.o = tiled_ok ? tiled(tiles_of(d), qd) : mt4(tiles_of(d), qd);
-    p.gateup = tiled_ok ? one : plan_gemm(tiles_of(c.ffn), d, gemm_kblock(c.dtype, 1), true);
+    // gate/up as one split-K product of 2F columns (weights streamed once for
+    // all rows), then the SwiGLU from its partials
+    p.gateup = tiled_ok ? one : mt4(tiles_of(2 * c.ffn), d);
     p.down = tiled_ok ? tiled(tiles_of(d), c.ffn) : mt4(tiles_of(d), c.ffn);
     p.lm = mt4(tiles_of(c.vocab), d);  // partial logits, then k_logit_select
     p.fc = mt4(tiles_of(d), c.n_feat * d);
@@ -159,6 +162,7 @@ struct Scratch {
   size_t h, h2, xa, xo, qkv, part_o, part_ml, nsplit, z, keys, tlists, lpart, opart, dpart;
   size_t srow;       // sampled verification: per target row statistics and kept lists
   size_t tq;         // target: q of the new rows [M][Hq*dh]
+  size_t gpart;      // split-K partials of the gate/up product (17..63 rows)
   size_t u, f, kvo;  // inject only (0 when not laid out)
   size_t total;
 };
@@ -189,16 +193,18 @@ Scratch make_scratch(const dflash_config& c, int n_req, bool inject) {
   // norm re-reads the previous row of its input while writing its output)
   S.h2 = c.conv2 ? take(sizeof(float) * M * c.hidden) : 0;
   S.srow = c.topk ? take(sizeof(float) * (size_t)n_req * (c.block_size + 1) * kSampleRowFloats) : 0;
-  S.tq = c.target ? take(e * M * qd) : 0;
+  // a target's split attention takes q in 16-row tiles per request
+  const size_t n_tiles = c.target ? (size_t)(c.block_size + 15) / 16 : 1;
+  S.tq = c.target ? take(e * (size_t)n_req * n_tiles * 16 * qd) : 0;
   // GEMM inputs: rows rounded up to whole 16-row fragments (fragment order)
   const size_t M16 = (M + 15) / 16 * 16;
   S.xa = take(e * M16 * c.hidden);
   S.xo = take(e * M16 * qd);
   S.qkv = take(sizeof(float) * part_rows(c, &Plans::qkv, (int)M) * qkvw);
-  const size_t pp = (size_t)n_req * max_splits(c) * c.n_q_heads * 16;
+  const size_t pp = (size_t)n_req * n_tiles * max_splits(c) * c.n_q_heads * 16;
   S.part_o = take(sizeof(float) * pp * c.head_dim);
   S.part_ml = take(sizeof(float) * pp * 2);
-  S.nsplit = take(sizeof(int) * n_req);
+  S.nsplit = take(sizeof(int) * n_req * n_tiles);
   S.z = take(e * M16 * c.ffn);
   S.keys = take(sizeof(unsigned long long) * M);
   S.tlists = c.topk ? take(sizeof(unsigned long long) * M * 16 *
@@ -211,6 +217,14 @@ Scratch make_scratch(const dflash_config& c, int n_req, bool inject) {
       if (g.mt == 4) lrows = std::max(lrows, (size_t)g.P * m);
     }
     S.lpart = lrows ? take(sizeof(float) * lrows * c.vocab) : 0;
+  }
+  {  // split-K partials of the gate/up product, where it runs split
+    size_t grows = 0;
+    for (int m = 1; m <= (int)M; ++m) {
+      const GemmPlan g = make_plans(c, m).gateup;
+      if (g.mt == 4) grows = std::max(grows, (size_t)g.P * m);
+    }
+    S.gpart = grows ? take(sizeof(float) * grows * 2 * c.ffn) : 0;
   }
   S.opart = take(sizeof(float) * part_rows(c, &Plans::o, (int)M) * c.hidden);
   S.dpart = take(sizeof(float) * part_rows(c, &Plans::down, (int)M) * c.hidden);
@@ -768,6 +782,43 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
   return DFLASH_OK;
 }
 
+// The MLP's gate/up product of the normed rows in xa (fragment order when
+// xa_packed) into z = silu(gate) * up (fragment order when z_packed): the
+// skinny or tiled kernel's SwiGLU epilogue, or from 17 to 63 rows one split-K
+// product of all 2F columns and the SwiGLU over its partials.
+static void gateup_swiglu(dflash_handle* h, hipStream_t s, char* sb, const Scratch& sc, const Plans& pl, int M,
+                          int l, int xa_packed, int z_packed) {
+  const dflash_config& c = h->cfg;
+  GemmParams gu{};
+  gu.a[0] = sb + sc.xa;
+  gu.a_parts = 1;
+  gu.a_part_k = c.hidden;
+  gu.lda = c.hidden;
+  gu.M = M;
+  gu.K = c.hidden;
+  gu.a_packed = xa_packed;
+  gu.w[0] = h->packed + h->pk.wgateup[l];
+  ProfScope ps(h, DFLASH_KERNEL_GATEUP_GEMM, s);
+  if (pl.gateup.mt == 4) {
+    float* part = sat<float>(sb, sc.gpart);
+    gu.tiles = tiles_of(2 * c.ffn);
+    gu.N = 2 * c.ffn;
+    gu.P = pl.gateup.P;
+    gu.out_f32 = part;
+    launch_gemm(c.dtype, EPI_PARTIAL, pl.gateup, gu, s);
+    launch_swiglu_parts(c.dtype, part, pl.gateup.P, M, c.ffn, sb + sc.z, c.ffn, s);
+    return;
+  }
+  gu.out_packed = z_packed;
+  gu.tiles = tiles_of(c.ffn);
+  gu.up_tile_off = tiles_of(c.ffn);
+  gu.N = c.ffn;
+  gu.P = 1;
+  gu.out_t = sb + sc.z;
+  gu.ldt = c.ffn;
+  launch_gemm(c.dtype, EPI_SWIGLU, pl.gateup, gu, s);
+}
+
 // Final step of a forward whose normed rows are in xa (fragment order when
 // xa_packed): the shared LM head and greedy selection (argmax ids with ties
 // to the lowest id; with top-16, the sorted lists as well).  Below 17 rows the
@@ -1105,20 +1156,11 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     n2.M = M;
     norm(n2);
 
-    GemmParams gu = gemm_in(sb + sc.xa, d);
-    gu.a_packed = n2.out_packed;
-    gu.out_packed = pl.gateup.mt == 0 && pl.down.mt == 0;  // z for a tiled down product
-    gu.w[0] = h->packed + h->pk.wgateup[l];
-    gu.tiles = tiles_of(c.ffn);
-    gu.up_tile_off = tiles_of(c.ffn);
-    gu.N = c.ffn;
-    gu.P = 1;
-    gu.out_t = sb + sc.z;
-    gu.ldt = c.ffn;
-    { ProfScope ps(h, DFLASH_KERNEL_GATEUP_GEMM, s); launch_gemm(c.dtype, EPI_SWIGLU, pl.gateup, gu, s); }
+    const int z_packed = pl.gateup.mt == 0 && pl.down.mt == 0;  // z for a tiled down product
+    gateup_swiglu(h, s, sb, sc, pl, M, l, n2.out_packed, z_packed);
 
     GemmParams gd = gemm_in(sb + sc.z, c.ffn);
-    gd.a_packed = gu.out_packed;
+    gd.a_packed = z_packed;
     gd.w[0] = h->packed + h->pk.wdown[l];
     gd.tiles = tiles_of(d);
     gd.N = d;
@@ -1253,10 +1295,24 @@ dflash_status dflash_target_forward(dflash_handle* h, void* stream, int32_t n_re
   };
   TargetQParams tq{};
   CausalAttnParams ca{};
+  SlotArgs sl{};
   for (int i = 0; i < n_req; ++i) {
     tq.pos0[i] = ca.pos0[i] = h->slots[slots[i]].ctx_len;
-    ca.slots[i] = slots[i];
+    ca.slots[i] = sl.slots[i] = slots[i];
   }
+  // bf16: split-K attention over (request, 16-row tile) pairs; the grid
+  // covers the splits of the longest request's last tile
+  const bool split_attn = c.dtype == DFLASH_BF16;
+  const int n_tiles = (n_rows + 15) / 16;
+  int splits = 1;
+  for (int i = 0; i < n_req; ++i) {
+    const HostSlot& hs = h->slots[slots[i]];
+    const int hi = hs.ctx_len + n_rows;
+    const int u = hi > hs.kv_begin ? (hi - 1) / 16 - hs.kv_begin / 16 + 1 : 0;
+    const int pps = split_pages(u, split_target(c), kPpsCap);
+    splits = std::max(splits, (u + pps - 1) / pps);
+  }
+  tq.n_tiles = split_attn ? n_tiles : 0;
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& lw = h->w.layers[l];
     NormParams n1{};
@@ -1336,26 +1392,70 @@ dflash_status dflash_target_forward(dflash_handle* h, void* stream, int32_t n_re
         sp.err = at<unsigned int>(h, h->lay.err);
         launch_scatter(c.dtype, c.head_dim, sp, s);
       }
-      // causal attention over the pages
-      ca.q = sb + sc.tq;
-      ca.pool = h->kv + (size_t)l * page_layer * e;
-      ca.page_table = at<int>(h, h->lay.page_table);
-      ca.pt_stride = c.max_pages_per_req;
-      ca.state = at<SlotState>(h, h->lay.state);
-      ca.max_pages = c.max_pages;
-      ca.Hq = c.n_q_heads;
-      ca.Hkv = c.n_kv_heads;
-      ca.R = n_rows;
-      ca.scale = (float)(1.0 / sqrt((double)c.head_dim));
-      ca.out = sb + sc.xo;
-      ca.ldo = qd;
-      ca.out_packed = pl.o.mt == 0;
-      ca.err = at<unsigned int>(h, h->lay.err);
-      launch_causal_attn(c.dtype, c.head_dim, n_req, ca, s);
+      if (split_attn) {  // the split ring kernel in causal mode, then the merge
+        AttnParams ap{};
+        ap.qb = sb + sc.tq;
+        ap.blk = h->ws + h->lay.blk;
+        ap.pool = h->kv + (size_t)l * page_layer * e;
+        ap.page_table = at<int>(h, h->lay.page_table);
+        ap.pt_stride = c.max_pages_per_req;
+        ap.state = at<SlotState>(h, h->lay.state);
+        ap.max_pages = c.max_pages;
+        ap.Hq = c.n_q_heads;
+        ap.Hkv = c.n_kv_heads;
+        ap.B = 16;
+        ap.split_target = split_target(c);
+        ap.pps_cap = kPpsCap;
+        ap.n_split = sat<int>(sb, sc.nsplit);
+        ap.n_splits = splits;
+        ap.KQ = 1;
+        ap.scale = (float)(1.0 / sqrt((double)c.head_dim));
+        ap.part_o = sat<float>(sb, sc.part_o);
+        ap.part_ml = sat<float>(sb, sc.part_ml);
+        ap.out = sb + sc.xo;
+        ap.ldo = qd;
+        ap.out_packed = pl.o.mt == 0;
+        ap.err = at<unsigned int>(h, h->lay.err);
+        ap.causal_R = n_rows;
+        ap.n_tiles = n_tiles;
+        launch_attention(c.dtype, c.head_dim, n_req * n_tiles, ap, sl, s);
+        if (splits > 1) {
+          CombineParams cp{};
+          cp.part_o = ap.part_o;
+          cp.part_ml = ap.part_ml;
+          cp.n_split = ap.n_split;
+          cp.n_splits = splits;
+          cp.n_rh = n_req * n_tiles * c.n_q_heads;
+          cp.Hq = c.n_q_heads;
+          cp.B = 16;
+          cp.out = ap.out;
+          cp.ldo = qd;
+          cp.out_packed = ap.out_packed;
+          cp.causal_R = n_rows;
+          cp.n_tiles = n_tiles;
+          launch_combine(c.dtype, c.head_dim, cp, s);
+        }
+      } else {  // fp32: one workgroup per (head, request, tile) over all pages
+        ca.q = sb + sc.tq;
+        ca.pool = h->kv + (size_t)l * page_layer * e;
+        ca.page_table = at<int>(h, h->lay.page_table);
+        ca.pt_stride = c.max_pages_per_req;
+        ca.state = at<SlotState>(h, h->lay.state);
+        ca.max_pages = c.max_pages;
+        ca.Hq = c.n_q_heads;
+        ca.Hkv = c.n_kv_heads;
+        ca.R = n_rows;
+        ca.scale = (float)(1.0 / sqrt((double)c.head_dim));
+        ca.out = sb + sc.xo;
+        ca.ldo = qd;
+        ca.out_packed = pl.o.mt == 0;
+        ca.err = at<unsigned int>(h, h->lay.err);
+        launch_causal_attn(c.dtype, c.head_dim, n_req, ca, s);
+      }
     }
 
     GemmParams go = gemm_in(sb + sc.xo, qd);
-    go.a_packed = ca.out_packed;
+    go.a_packed = pl.o.mt == 0;
     go.w[0] = h->packed + h->pk.wo[l];
     go.tiles = tiles_of(d);
     go.N = d;
@@ -1378,20 +1478,11 @@ dflash_status dflash_target_forward(dflash_handle* h, void* stream, int32_t n_re
     n2.M = M;
     norm(n2);
 
-    GemmParams gu = gemm_in(sb + sc.xa, d);
-    gu.a_packed = n2.out_packed;
-    gu.out_packed = pl.gateup.mt == 0 && pl.down.mt == 0;
-    gu.w[0] = h->packed + h->pk.wgateup[l];
-    gu.tiles = tiles_of(c.ffn);
-    gu.up_tile_off = tiles_of(c.ffn);
-    gu.N = c.ffn;
-    gu.P = 1;
-    gu.out_t = sb + sc.z;
-    gu.ldt = c.ffn;
-    { ProfScope ps(h, DFLASH_KERNEL_GATEUP_GEMM, s); launch_gemm(c.dtype, EPI_SWIGLU, pl.gateup, gu, s); }
+    const int z_packed = pl.gateup.mt == 0 && pl.down.mt == 0;  // z for a tiled down product
+    gateup_swiglu(h, s, sb, sc, pl, M, l, n2.out_packed, z_packed);
 
     GemmParams gd = gemm_in(sb + sc.z, c.ffn);
-    gd.a_packed = gu.out_packed;
+    gd.a_packed = z_packed;
     gd.w[0] = h->packed + h->pk.wdown[l];
     gd.tiles = tiles_of(d);
     gd.N = d;

@@ -7,8 +7,12 @@
 //
 //  * k_target_q: q of the new rows, split-K partial sums in order, RoPE at
 //    each row's absolute position, rounded to the storage dtype, row-major
-//    [rows][Hq][dh].  (K and V of the new rows go into the request's pages
-//    through the injection's scatter kernel.)
+//    [rows][Hq][dh], or tiled for the split attention.  (K and V of the new
+//    rows go into the request's pages through the injection's scatter
+//    kernel.)
+//
+// In bf16 the attention runs on the draft's split-K ring kernel in its
+// causal mode (the attention source holds it); fp32 handles use:
 //  * k_causal_attn: one workgroup per (query head, request, 16-row tile) of
 //    8 waves; wave w takes every 8th pair of 16-position pages of the
 //    visible range [kv_begin, last row's position] and runs S^T = K Q^T and
@@ -30,15 +34,34 @@ template <typename T> struct Vec4T;
 template <> struct Vec4T<bf16> { typedef bf16x4 type; };
 template <> struct Vec4T<float> { typedef f32x4 type; };
 
-// One workgroup of dh/2 threads per (row, query head): thread j rotates the
-// pair (j, j + dh/2).
+// One workgroup of dh/2 threads per (output row, query head): thread j
+// rotates the pair (j, j + dh/2).  Output rows are the new rows (row-major
+// layout) or, in the tiled layout of the split attention, 16 rows per
+// (request, tile) pair with the rows past the request's last one zeroed.
 template <typename T>
 __global__ __launch_bounds__(64) void k_target_q(TargetQParams p) {
-  const int row = blockIdx.x, hh = blockIdx.y;
+  const int orow = blockIdx.x, hh = blockIdx.y;
   const int j = threadIdx.x;
   const int h2 = p.dh / 2;
-  const int r = row / p.R;
-  const int pos = p.pos0[r] + (row - r * p.R);
+  int r, i;  // request, new row of the request
+  T* dst;
+  if (p.n_tiles) {
+    const int rv = orow >> 4;
+    r = rv / p.n_tiles;
+    i = (rv - r * p.n_tiles) * 16 + (orow & 15);
+    dst = reinterpret_cast<T*>(p.q) + ((long long)(rv * p.Hq + hh) * 16 + (orow & 15)) * p.dh;
+    if (i >= p.R) {
+      dst[j] = from_f<T>(0.f);
+      dst[j + h2] = from_f<T>(0.f);
+      return;
+    }
+  } else {
+    r = orow / p.R;
+    i = orow - r * p.R;
+    dst = reinterpret_cast<T*>(p.q) + ((long long)orow * p.Hq + hh) * p.dh;
+  }
+  const int row = r * p.R + i;
+  const int pos = p.pos0[r] + i;
   const long long plane = (long long)p.M * p.ld;
   const float* src = p.qkv + (long long)row * p.ld + hh * p.dh;
   float x1 = 0.f, x2 = 0.f;
@@ -47,7 +70,6 @@ __global__ __launch_bounds__(64) void k_target_q(TargetQParams p) {
     x2 += src[q * plane + j + h2];
   }
   const float c = p.cos_t[(long long)pos * h2 + j], sn = p.sin_t[(long long)pos * h2 + j];
-  T* dst = reinterpret_cast<T*>(p.q) + ((long long)row * p.Hq + hh) * p.dh;
   dst[j] = from_f<T>(x1 * c - x2 * sn);
   dst[j + h2] = from_f<T>(x2 * c + x1 * sn);
 }
@@ -245,7 +267,7 @@ __global__ __launch_bounds__(64 * kCausalWaves) void k_causal_attn(CausalAttnPar
 
 void launch_target_q(int dtype, const TargetQParams& p, hipStream_t s) {
   if (p.M <= 0) return;
-  const dim3 grid(p.M, p.Hq);
+  const dim3 grid(p.n_tiles ? p.M / p.R * p.n_tiles * 16 : p.M, p.Hq);
   if (dtype == DFLASH_BF16)
     hipLaunchKernelGGL(k_target_q<bf16>, grid, dim3(p.dh / 2), 0, s, p);
   else
