@@ -585,7 +585,8 @@ def run_workload(config, steps, warmup, cpu=False, target=False):
             "target_logit_bytes": tb, "achieved_GBps": round(tb / (ms * 1e-3) / 1e9, 1),
             "share_of_cycle": round(ms / cycle_ms, 4),
             "counted": "sampled draw of the block from the top-16 lists + rejection sampling against "
-                       "the target's logits (top-k by radix select over each row)"}
+                       "the target's logits (per row chunk a sorted top-64 of the keys above a threshold, the "
+                       "chunks merged per row, then the accept test and the final draw)"}
         del tlog
     if target:
         result["speculative_cycle"] = speculative_cycle(shape, dr, reset, reqs[0]["sched"], steps, warmup, draft_ms)

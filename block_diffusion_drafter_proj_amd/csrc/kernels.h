@@ -313,6 +313,7 @@ void launch_sel_table(int dtype, const void* embed, const void* wu, const void* 
                       int d, int r, hipStream_t s);
 void launch_select_path(const PathParams& p, int n_req, hipStream_t s);
 // Sampled drafting and rejection-sampling verification (DFlash 2).
+constexpr int kRowChunks = 16;  // chunks per target row in the sampled verification's first pass
 struct SampleParams {
   float temperature;
   int top_k;    // 0 (whole vocabulary) or 1..64; the draft side caps it at 16
@@ -328,6 +329,8 @@ struct SampleParams {
   int* row_ids;       // [n][B+1][64] kept top-k ids
   float* row_p;       // [n][B+1][64] their warped probabilities
   int* row_n;         // [n][B+1] kept count
+  float* chunk_stat;                // [n][B+1][kRowChunks][2] per-chunk (max, sum) without top-k
+  unsigned long long* chunk_list;   // [n][B+1][kRowChunks][64] per-chunk sorted top-64 keys
   int* accept;        // [n]
   int* committed;     // [n][B+1]
   int* last;          // [n]

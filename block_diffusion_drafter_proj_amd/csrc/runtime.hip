@@ -161,6 +161,7 @@ constexpr int kSampleRowFloats = 2 + 64 + 64 + 1;
 struct Scratch {
   size_t h, h2, xa, xo, qkv, part_o, part_ml, nsplit, z, keys, tlists, lpart, opart, dpart;
   size_t srow;       // sampled verification: per target row statistics and kept lists
+  size_t schunk;     // sampled verification: per row chunk lists (u64) and statistics
   size_t tq;         // target: q of the new rows [M][Hq*dh]
   size_t gpart;      // split-K partials of the gate/up product (17..63 rows)
   size_t u, f, kvo;  // inject only (0 when not laid out)
@@ -193,6 +194,9 @@ Scratch make_scratch(const dflash_config& c, int n_req, bool inject) {
   // norm re-reads the previous row of its input while writing its output)
   S.h2 = c.conv2 ? take(sizeof(float) * M * c.hidden) : 0;
   S.srow = c.topk ? take(sizeof(float) * (size_t)n_req * (c.block_size + 1) * kSampleRowFloats) : 0;
+  S.schunk = c.topk ? take((2 * sizeof(float) + 64 * sizeof(unsigned long long)) * (size_t)n_req *
+                           (c.block_size + 1) * kRowChunks)
+                    : 0;
   // a target's split attention takes q in 16-row tiles per request
   const size_t n_tiles = c.target ? (size_t)(c.block_size + 15) / 16 : 1;
   S.tq = c.target ? take(e * (size_t)n_req * n_tiles * 16 * qd) : 0;
@@ -1611,6 +1615,9 @@ dflash_status dflash_verify_sample(dflash_handle* h, void* stream, int32_t n_req
   p.row_ids = reinterpret_cast<int*>(sr + 2 * rows);
   p.row_p = sr + (2 + 64) * rows;
   p.row_n = reinterpret_cast<int*>(sr + (2 + 128) * rows);
+  char* sc = h->ws + h->lay.scratch + h->lay.sc.schunk;
+  p.chunk_list = reinterpret_cast<unsigned long long*>(sc);
+  p.chunk_stat = reinterpret_cast<float*>(sc + sizeof(unsigned long long) * 64 * kRowChunks * rows);
   p.accept = accept_len;
   p.committed = committed;
   p.last = last_token;
