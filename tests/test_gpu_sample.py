@@ -122,6 +122,45 @@ def test_sampled_parity(name, n, T, top_k, top_p):
     assert checked >= 0.95 * n * B and vexempt <= max(1, n // 10)
 
 
+def test_drafts_deep_in_the_target_list():
+    """The drafted tokens sit at ranks 30 and beyond of the target's top-64:
+    30 other tokens per position are lifted above every draft candidate, so
+    p(x) comes from list entries past the first 16 lanes.  Lock-step accept
+    lengths and committed tokens equal the oracle's."""
+    dev = _dev()
+    shape = synth.config("small_conv")
+    n, B, V = 48, shape["block_size"], shape["vocab"]
+    dr = _handle(shape, n)
+    ids, lg = synth.candidate_lists(shape, n, 77)
+    tl = synth.target_logits_near(shape, ids, lg, 77, scale=1.0, agree=2.0)
+    g = np.random.default_rng(78)
+    for r in range(n):
+        for i in range(B + 1):
+            others = np.setdiff1d(np.arange(V), ids[r, i] if i < B else [])
+            lift = g.choice(others, size=30, replace=False)
+            tl[r, i, lift] = tl[r, i].max() + 0.1 * g.random(30).astype(np.float32)
+    T, top_k, top_p = 3.0, 64, 1.0  # a flat warp, so that drafts at those ranks are still accepted
+    u = synth.uniforms(shape, (n, B + 1, 2), 79)
+    v = synth.uniforms(shape, (n, B), 80)
+    rd = np.stack([draft_sample(ids[r], lg[r], T, top_k, top_p, v[r]) for r in range(n)]).astype(np.int32)
+    sp = Bnd.DFlashSampling(T, top_k, top_p)
+    acc, com, last = dr.verify_sample(sp, torch.from_numpy(rd).to(dev), torch.from_numpy(ids).to(dev),
+                                      torch.from_numpy(lg).to(dev), torch.from_numpy(tl).to(dev),
+                                      torch.from_numpy(u).to(dev))
+    acc, com, last = acc.cpu().numpy(), com.cpu().numpy(), last.cpu().numpy()
+    compared = accepted = 0
+    for r in range(n):
+        a, c, nx, margins = spec_verify_sample(rd[r], ids[r], lg[r], tl[r], T, top_k, top_p, u[r])
+        if np.min(margins) < TIE:
+            continue
+        assert acc[r] == a and com[r, :a + 1].tolist() == c and last[r] == nx, (r, acc[r], a)
+        compared += 1
+        accepted += a
+    dr.check()
+    print(f"[sample deep ranks] {compared} verifications compared, {accepted} drafts accepted", flush=True)
+    assert compared >= 0.9 * n and accepted > 0
+
+
 @pytest.mark.parametrize("T,top_k,top_p", [(1.0, 0, 1.0), (1.0, 20, 0.95)], ids=["whole_vocab", "k20_p095"])
 def test_sampled_verification_is_lossless(T, top_k, top_p):
     """4,096 independent verifications of one block (256 requests x 16 calls
