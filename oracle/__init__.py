@@ -42,6 +42,12 @@ Parity status per function (what pins it, see ``tests/test_oracle_*.py``):
 * ``target.TargetOracle`` (target verify forward) pinned: equals the tiny
                        target row by row (fp32, MHA); causal; chunked equals
                        one block; GQA equals MHA with repeated K/V heads.
+* ``quant.quantize_q4``, ``dequantize_q4``, ``q4_draft_weights`` (4-bit draft
+                       weights) pinned: weights already on a 4-bit grid come
+                       back exactly (codes, scales, biases and values); a
+                       constant group; the error bound of a half step on
+                       random weights; a draft whose weights lie on the grid
+                       drafts exactly as the unquantised draft.
 """
 from .dflash_oracle import (  # noqa: F401
     DraftOracle,
@@ -66,5 +72,6 @@ from .dflash2 import (  # noqa: F401
     target_distribution,
     warp_sorted,
 )
+from .quant import dequantize_q4, q4_draft_weights, quantize_q4  # noqa: F401
 from .target import TargetOracle  # noqa: F401
 from .tiny_target import OracleDrafter, TinyTarget, greedy_ar, spec_generate  # noqa: F401
