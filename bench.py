@@ -17,6 +17,9 @@ Default workload ``qwen3_8b``:
 ``--config`` selects another workload of ``synth.CONFIGS``:
   * ``llama31_8b``: block 10, context 8192;
   * ``coder_b64``: 8 layers, 64 requests with ragged contexts U[512, 8192];
+  * ``qwen3_8b_q4``: the headline workload with a 4-bit draft (its own
+    matrices as 4-bit codes with a bf16 scale and bias per 64 inputs; the
+    shared LM head stays bf16);
   * ``dflash2_long``: conv taps, top-16 and the path selector (rank 256;
     the target verifies the path), batch 4, context 32768 with a
     4096-token window.
@@ -49,7 +52,7 @@ Output is one JSON line:
   * the CPU oracle, timed on the host (prefill inject, median of 3 drafts,
     3 steady-state cycles of one request);
   * by default (``--config qwen3_8b`` without ``--single``), a ``workloads``
-    object with the same figures for llama31_8b, coder_b64 (batch 64: the
+    object with the same figures for qwen3_8b_q4, llama31_8b, coder_b64 (batch 64: the
     GEMMs' share of the bf16 MFMA peak) and dflash2_long (with the conv's
     and the top-16 selection's share of the cycle), each in its own handle.
 """
@@ -82,6 +85,12 @@ def elt(shape):
     return 2 if shape["dtype"] == "bf16" else 4
 
 
+def welt(shape):
+    """Bytes per weight of the draft's own matrices: the storage dtype, or
+    for a 4-bit draft half a byte plus a bf16 (scale, bias) pair per 64."""
+    return 0.5 + 4.0 / 64 if shape.get("weight_bits") == 4 else elt(shape)
+
+
 def draft_bytes(shape, visible):
     """Algorithmic HBM bytes of one draft forward of requests with ``visible``
     context positions each: every weight the forward multiplies once, each
@@ -91,7 +100,7 @@ def draft_bytes(shape, visible):
                                                    "ffn", "vocab", "n_layers"))
     layer = (hq + 2 * hkv) * dh * d + d * hq * dh + 2 * F * d + d * F
     kv = L * sum(visible) * 2 * hkv * dh
-    return e * (L * layer + V * d + kv)
+    return int(welt(shape) * L * layer + e * (V * d + kv))
 
 
 def inject_bytes(shape, rows):
@@ -99,7 +108,7 @@ def inject_bytes(shape, rows):
     layer's K/V projection once, the hidden rows in and the K/V rows out."""
     e = elt(shape)
     d, hkv, dh, L, K = (shape[k] for k in ("hidden", "n_kv_heads", "head_dim", "n_layers", "n_feat"))
-    return e * (K * d * d + L * 2 * hkv * dh * d + rows * (K * d + L * 2 * hkv * dh))
+    return int(welt(shape) * (K * d * d + L * 2 * hkv * dh * d) + e * rows * (K * d + L * 2 * hkv * dh))
 
 
 def class_work(shape, cls, M, visible):
@@ -117,7 +126,8 @@ def class_work(shape, cls, M, visible):
     if cls in nk:
         N, K = nk[cls]
         n_out = 0 if cls == "lm_head" else (F if cls == "gateup_gemm" else N)
-        return 2.0 * M * N * K, e * (N * K + M * K + M * n_out)
+        we = e if cls == "lm_head" else welt(shape)
+        return 2.0 * M * N * K, int(we * N * K + e * (M * K + M * n_out))
     if cls == "attn":
         keys = sum(v + B for v in visible)
         flops = 4.0 * hq * dh * B * keys
@@ -136,7 +146,7 @@ def file_sha(*paths):
 def kernel_sources(shape, cls, M):
     """Source files whose kernels a class launches at this row count."""
     if cls in GEMM_CLASSES:
-        big = shape["dtype"] == "bf16" and M >= 64
+        big = shape["dtype"] == "bf16" and M >= 64 and (cls == "lm_head" or shape.get("weight_bits") != 4)
         if cls in ("qkv_gemm", "lm_head") and M == 64:
             big = False  # these products of 64 rows run on the skinny kernel's 64-row block
         return [os.path.join(CSRC, "gemm_big.hip" if big else "gemm.hip")]
@@ -283,7 +293,7 @@ def main():
     if not args.single and args.config == "qwen3_8b":
         # the other measured workloads, each in its own handle, reported beside the headline
         result["workloads"] = {}
-        for name in ("llama31_8b", "coder_b64", "dflash2_long"):
+        for name in ("qwen3_8b_q4", "llama31_8b", "coder_b64", "dflash2_long"):
             r = run_workload(name, args.steps, args.warmup, cpu=False)
             result["workloads"][name] = {k: r[k] for k in SUMMARY_KEYS if k in r}
     print(json.dumps(result))
@@ -493,7 +503,8 @@ def run_workload(config, steps, warmup, cpu=False, target=False):
             f"ffn {shape['ffn']}, vocab {V}, block {B}, batch {n}, ctx "
             + (f"{ctxs[0]}" if len(set(ctxs)) == 1 else f"ragged {min(ctxs)}..{max(ctxs)} (mean {np.mean(ctxs):.0f})")
             + (f", window {W}" if W else "") + (", two-tap conv" if conv else "")
-            + (f", top-{topk}" if topk else ""))
+            + (f", top-{topk}" if topk else "")
+            + (", 4-bit draft weights (groups of 64, bf16 scale and bias)" if shape.get("weight_bits") == 4 else ""))
     result = {
         "metric": METRIC,
         "value": round(n * 1e3 / cycle_ms, 2),

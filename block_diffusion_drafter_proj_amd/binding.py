@@ -44,7 +44,8 @@ class DFlashConfig(ctypes.Structure):
         "block_size", "n_feat", "dtype", "mask_token_id", "page_size", "window", "conv2",
         "topk", "max_batch", "max_pages", "max_pages_per_req", "max_position",
         "max_inject_rows")] + [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-                               ("selector_rank", ctypes.c_int32), ("target", ctypes.c_int32)]
+                               ("selector_rank", ctypes.c_int32), ("target", ctypes.c_int32),
+                               ("weight_bits", ctypes.c_int32)]
 
 
 class DFlashLayerWeights(ctypes.Structure):

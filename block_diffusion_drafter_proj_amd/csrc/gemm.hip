@@ -40,13 +40,57 @@ struct Shape {
   static constexpr int KS = (sizeof(T) == 2 && MT == 1) ? 8 : 4;  // k-steps per wave per tile
   static constexpr int NBUF = (sizeof(T) == 2 ? 16 : 8) / KS;     // tiles in the W ring
 };
+// 4-bit weights: a tile's KS k-steps are KS / 4 16-byte code loads and as
+// many 8-byte (scale, bias) loads per lane, so the ring holds more tiles.
+// (The RoPE epilogue's state leaves room for two tiles in the 16-row form.)
+template <int MT, int EPI>
+struct Shape4 {
+  static constexpr int NBUF = MT == 1 ? (EPI == EPI_ROPE ? 2 : 3) : 8;
+};
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// One tile's weights for the wave's k-steps, in registers.
+template <typename T, int KS, bool W4>
+struct WRing {
+  typename Frag8<T>::type f[KS];
+};
+template <typename T, int KS>
+struct WRing<T, KS, true> {
+  u32x4 q[KS / 4];   // codes of k-steps 4i .. 4i+3
+  u32x2 sb[KS / 4];  // (scale, bias) of the two groups of 64 inputs they cover
+};
+
+// The 8 codes of one lane's k-step (nibble e = element e) as bf16 values
+// 1 + q / 16: each code goes to mantissa bits 3..6 of a bf16 whose exponent
+// is that of 1 (0x3F80 | q << 3).  Byte i of x holds codes 2i (low nibble)
+// and 2i + 1 (high nibble); they are moved to bits 3..6 of separate bytes,
+// paired into 16-bit halves and given the exponent.
+__device__ __forceinline__ bf16x8 expand_q4(unsigned x) {
+  const unsigned lo = (x << 3) & 0x78787878u, hi = (x >> 1) & 0x78787878u;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x3F803F80u;
+  r[1] = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x3F803F80u;
+  r[2] = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x3F803F80u;
+  r[3] = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x3F803F80u;
+  return __builtin_bit_cast(bf16x8, r);
+}
 
 // Workgroups of MT > 1 have at most 8 waves (their activation and weight
 // registers need two waves per SIMD at most).
-template <typename T, int MT, int EPI, bool FEW>
+//
+// 4-bit weights (W4): per group of 64 inputs the product is
+// 16 s * sum x (1 + q / 16) + (b - 16 s) * sum x, which equals
+// sum x (s q + b) exactly in real arithmetic: the codes enter the MFMA as
+// bf16 values 1 + q / 16 (exact), the group's partial tile is scaled by 16 s
+// and the activation sums of the group (formed once per wave on the matrix
+// cores with a tile of ones) times (b - 16 s) are added, in fp32.  (The
+// offset 1 keeps the cancelled part 16 s * sum x small beside the result.)
+template <typename T, int MT, int EPI, bool FEW, bool W4>
 __global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(GemmParams p) {
   constexpr int KS = Shape<T, MT>::KS;
-  constexpr int NBUF = Shape<T, MT>::NBUF;
+  constexpr int NBUF = W4 ? Shape4<MT, EPI>::NBUF : Shape<T, MT>::NBUF;
+  static_assert(!W4 || (sizeof(T) == 2 && KS % 4 == 0), "4-bit weights: bf16 activations, whole code loads");
   constexpr int NSUB = (EPI == EPI_SWIGLU || EPI == EPI_ROPE) ? 2 : 1;
   typedef typename Frag8<T>::type Frag;
   __shared__ float red[2][MT > 1 ? 8 : 16][MT][256];
@@ -84,6 +128,18 @@ __global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(Gemm
     }
   }
 
+  // 4-bit weights: the activation sums of each group of 64 inputs, in the
+  // accumulator layout (a product with a tile of ones)
+  f32x4 xs[W4 ? MT : 1][W4 ? KS / 2 : 1];
+  if constexpr (W4) {
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int g2 = 0; g2 < KS / 2; ++g2)
+        xs[mt][g2] = mfma_step(af[mt][2 * g2 + 1], ones, mfma_step(af[mt][2 * g2], ones, f32x4{0.f, 0.f, 0.f, 0.f}));
+  }
+
   // weight tile of sub-unit `sub` of this workgroup
   auto tile_of = [&](int sub) {
     const int u = sub / NSUB;
@@ -92,25 +148,34 @@ __global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(Gemm
     if (EPI == EPI_ROPE) t = (t / rope_half) * rope_tph + t % rope_half + (sub & 1) * rope_half;
     return t;
   };
-  auto wsrc = [&](int sub) -> const T* {
+  typedef WRing<T, KS, W4> Ring;
+  auto load_tile = [&](int sub, Ring& r) {
     int t = tile_of(sub);
     int seg = 0, lt = t;
     if (p.seg_tiles) {
       seg = t / p.seg_tiles;
       lt = t - seg * p.seg_tiles;
     }
-    return reinterpret_cast<const T*>(p.w[seg]) + ((long long)lt * S + s0) * kFragElems + lane * 8;
+    if constexpr (W4) {
+      const long long u = (long long)lt * (S / 4) + s0 / 4;  // first code unit (4 k-steps) of the wave
+      const u32x4* q = reinterpret_cast<const u32x4*>(p.w[seg]) + u * 64 + lane;
+      const u32x2* sb = reinterpret_cast<const u32x2*>(p.sb[seg]) + u * 16 + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < KS / 4; ++i) {
+        r.q[i] = q[i * 64];
+        r.sb[i] = sb[i * 16];
+      }
+    } else {
+      const T* src = reinterpret_cast<const T*>(p.w[seg]) + ((long long)lt * S + s0) * kFragElems + lane * 8;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) r.f[j] = load8<T>(src + j * kFragElems);
+    }
   };
 
-  Frag wb[NBUF][KS];
+  Ring wb[NBUF];
 #pragma unroll
-  for (int b = 0; b < NBUF; ++b) {
-    if (b < n_sub) {
-      const T* src = wsrc(b);
-#pragma unroll
-      for (int j = 0; j < KS; ++j) wb[b][j] = load8<T>(src + j * kFragElems);
-    }
-  }
+  for (int b = 0; b < NBUF; ++b)
+    if (b < n_sub) load_tile(b, wb[b]);
 
   // epilogue: element e = t + it * blockDim of the 16 x 16 tile (per m-tile);
   // workgroups with fewer than 4 waves (FEW) take several elements per thread,
@@ -147,15 +212,36 @@ __global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(Gemm
         f32x4 acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (W4) {
 #pragma unroll
-        for (int j = 0; j < KS; ++j)
+          for (int i = 0; i < KS / 4; ++i)
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_step(af[mt][j], wb[b][j], acc[mt]);
-        if (sub + NBUF < n_sub) {
-          const T* src = wsrc(sub + NBUF);
+            for (int gg = 0; gg < 2; ++gg) {
+              const unsigned sbw = wb[b].sb[i][gg];
+              const float sc = 16.0f * __uint_as_float(sbw << 16), bi = __uint_as_float(sbw & 0xFFFF0000u);
+              const float bp = bi - sc;
+              f32x4 tmp[MT];
 #pragma unroll
-          for (int j = 0; j < KS; ++j) wb[b][j] = load8<T>(src + j * kFragElems);
+              for (int mt = 0; mt < MT; ++mt) tmp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int jj = 0; jj < 2; ++jj) {
+                const bf16x8 wf = expand_q4(wb[b].q[i][2 * gg + jj]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) tmp[mt] = mfma_step(af[mt][4 * i + 2 * gg + jj], wf, tmp[mt]);
+              }
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  acc[mt][e] = fmaf(sc, tmp[mt][e], fmaf(bp, xs[mt][2 * i + gg][e], acc[mt][e]));
+            }
+        } else {
+#pragma unroll
+          for (int j = 0; j < KS; ++j)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_step(af[mt][j], wb[b].f[j], acc[mt]);
         }
+        if (sub + NBUF < n_sub) load_tile(sub + NBUF, wb[b]);
         const int rb = sub & 1;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -291,15 +377,75 @@ __global__ __launch_bounds__(256) void k_swiglu_parts(const float* part, int P, 
   }
 }
 
-template <typename T, int EPI>
-void launch_t(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
+// bf16 rounding (nearest even) of a finite float
+__device__ __forceinline__ float round_bf16(float x) {
+  unsigned u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return __uint_as_float(u & 0xFFFF0000u);
+}
+
+// One thread per (tile, group of 64 inputs, tile row): the group's min and
+// max, its bf16 scale and bias, the codes (fp32 steps, IEEE division, round
+// half to even), written into the code and scale layouts of the q4 format.
+__global__ __launch_bounds__(256) void k_pack_q4(const bf16* src, unsigned* dst, int N, int K, long long total) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int G = K / 64, S4 = K / 128;
+  const int r16 = (int)(idx & 15);
+  const long long tg = idx >> 4;
+  const int g = (int)(tg % G);
+  const long long t = tg / G;
+  const long long row = t * 16 + r16;
+  float w[64];
+  if (row < N) {
+    const bf16* sp = src + row * K + (long long)g * 64;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x8 v = load8<bf16>(sp + 8 * i);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[8 * i + e] = (float)v[e];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) w[i] = 0.f;
+  }
+  float lo = w[0], hi = w[0];
+#pragma unroll
+  for (int i = 1; i < 64; ++i) {
+    lo = fminf(lo, w[i]);
+    hi = fmaxf(hi, w[i]);
+  }
+  const float sc = round_bf16(__fdiv_rn(hi - lo, 15.0f));
+  const float b = round_bf16(lo);
+  unsigned* codes = dst + ((t * S4 + g / 2) * 64) * 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {  // the group's two k-steps
+    const int js = 2 * (g & 1) + h;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {  // lanes r16 + 16 c hold inputs 8 c .. 8 c + 7 of the k-step
+      unsigned word = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qf = sc > 0.f ? rintf(__fdiv_rn(w[32 * h + 8 * c + e] - b, sc)) : 0.f;
+        const unsigned q = (unsigned)fminf(fmaxf(qf, 0.f), 15.f);
+        word |= q << (4 * e);
+      }
+      codes[(r16 + 16 * c) * 4 + js] = word;
+    }
+  }
+  unsigned* sb = dst + q4_codes_bytes(N, K) / 4 + ((t * S4 + g / 2) * 16 + r16) * 2 + (g & 1);
+  *sb = (__float_as_uint(sc) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+}
+
+template <typename T, int EPI, bool W4>
+void launch_w(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
   if constexpr (sizeof(T) == 2 && EPI == EPI_PARTIAL) {
-    if (pl.mt == 4) {  // one block of up to 64 rows: W streamed once
+    if (pl.mt == 4) {  // blocks of up to 64 rows: W streamed once per block
       const dim3 grid(pl.GP * p.P, (p.M + 63) / 64);
       if (pl.NW < 4)
-        hipLaunchKernelGGL((k_gemm<T, 4, EPI, true>), grid, dim3(64 * pl.NW), 0, s, p);
+        hipLaunchKernelGGL((k_gemm<T, 4, EPI, true, W4>), grid, dim3(64 * pl.NW), 0, s, p);
       else
-        hipLaunchKernelGGL((k_gemm<T, 4, EPI, false>), grid, dim3(64 * pl.NW), 0, s, p);
+        hipLaunchKernelGGL((k_gemm<T, 4, EPI, false, W4>), grid, dim3(64 * pl.NW), 0, s, p);
       return;
     }
   }
@@ -307,9 +453,20 @@ void launch_t(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
   dim3 grid(pl.GP * p.P, (p.M + 15) / 16);
   dim3 block(64 * pl.NW);
   if (pl.NW < 4)
-    hipLaunchKernelGGL((k_gemm<T, 1, EPI, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((k_gemm<T, 1, EPI, true, W4>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((k_gemm<T, 1, EPI, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((k_gemm<T, 1, EPI, false, W4>), grid, block, 0, s, p);
+}
+
+template <typename T, int EPI>
+void launch_t(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
+  if constexpr (sizeof(T) == 2 && (EPI == EPI_PARTIAL || EPI == EPI_SWIGLU || EPI == EPI_ROPE)) {
+    if (p.w4) {
+      launch_w<T, EPI, true>(pl, p, s);
+      return;
+    }
+  }
+  launch_w<T, EPI, false>(pl, p, s);
 }
 
 template <typename T>
@@ -377,6 +534,13 @@ void launch_swiglu_parts(int dtype, const float* part, int P, int M, int F, void
     hipLaunchKernelGGL(k_swiglu_parts<bf16>, grid, dim3(256), 0, s, part, P, M, F, reinterpret_cast<bf16*>(z), ldo);
   else
     hipLaunchKernelGGL(k_swiglu_parts<float>, grid, dim3(256), 0, s, part, P, M, F, reinterpret_cast<float*>(z), ldo);
+}
+
+void launch_pack_q4(const void* src, void* dst, int N, int K, hipStream_t s) {
+  const long long total = (long long)((N + 15) / 16) * (K / 64) * 16;
+  const int blocks = (int)((total + 255) / 256);
+  hipLaunchKernelGGL(k_pack_q4, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const bf16*>(src),
+                     reinterpret_cast<unsigned*>(dst), N, K, total);
 }
 
 size_t packed_elems(int N, int K) { return (size_t)((N + 15) / 16) * 16 * (size_t)K; }

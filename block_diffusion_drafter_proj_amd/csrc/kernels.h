@@ -62,7 +62,22 @@ struct GemmParams {
   // tiled kernel only: A (one part) and the SwiGLU output stored in fragment
   // order (frag_index) instead of row-major
   int a_packed, out_packed;
+  // 4-bit weights (skinny kernel only): w[seg] points at the codes of the
+  // segment's first tile, sb[seg] at its (scale, bias) pairs (q4 layout below)
+  int w4;
+  const void* sb[kMaxSeg];
 };
+
+// 4-bit packed matrix [N, K] (N16 = N rounded up to 16, K a multiple of 128):
+//   codes  [N16/16 tiles][K/128][64 lanes][4] u32: lane l of k-step 4 kq + j
+//          holds row 16 t + l%16, inputs 32 (4 kq + j) + 8 (l/16) .. +7, one
+//          nibble each (byte i: element 2i low, 2i+1 high)
+//   scales [N16/16][K/128][16 rows][2] u32, after the codes: (s | b << 16) as
+//          bf16 bit patterns, for the groups of 64 inputs 2 kq and 2 kq + 1
+__host__ __device__ inline size_t q4_codes_bytes(int N, int K) { return (size_t)((N + 15) / 16) * 16 * K / 2; }
+__host__ __device__ inline size_t q4_bytes(int N, int K) { return q4_codes_bytes(N, K) + (size_t)((N + 15) / 16) * 16 * (K / 64) * 4; }
+// quantise the storage-dtype (bf16) matrix src [N, K] into the q4 layout at dst
+void launch_pack_q4(const void* src, void* dst, int N, int K, hipStream_t s);
 
 struct GemmPlan {
   int P, NW, GP;  // split-K factor, waves per workgroup, workgroups per split

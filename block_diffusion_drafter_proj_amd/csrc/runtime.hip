@@ -85,7 +85,7 @@ bool qkv_rope(const dflash_config& c, int M) {
          (M + c.block_size - 1) / c.block_size <= kMaxRopeReq;
 }
 
-Plans make_plans(const dflash_config& c, int M) {
+Plans plans16(const dflash_config& c, int M) {
   const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   // 17..64 rows: the split-K products stream their weights once for all
@@ -138,6 +138,32 @@ Plans make_plans(const dflash_config& c, int M) {
   p.lm = plan_gemm(tiles_of(c.vocab), d, kb, true);
   p.fc = plan_gemm(tiles_of(d), c.n_feat * d, kb, false);
   p.kv = plan_gemm(c.n_layers * tiles_of(2 * c.n_kv_heads * c.head_dim), d, kb, false);
+  return p;
+}
+
+// The products' plans for M rows.  A 4-bit draft runs every product of its
+// quantised matrices on the skinny kernel (one 16-row block up to 16 rows,
+// 64-row blocks above, each block streaming the codes once; gate/up above
+// 16 rows as split-K partials and the SwiGLU pass); the LM head keeps its
+// plan.
+Plans make_plans(const dflash_config& c, int M) {
+  Plans p = plans16(c, M);
+  if (c.weight_bits != 4) return p;
+  const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
+  const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const int kb1 = gemm_kblock(c.dtype, 1), kb4 = gemm_kblock(c.dtype, 4);
+  auto w4 = [&](int tiles, int K) {
+    if (M <= 16) return plan_gemm(tiles, K, kb1, false);
+    GemmPlan g = plan_gemm(tiles, K, kb4, false, 8);
+    g.mt = 4;
+    return g;
+  };
+  p.qkv = qkv_rope(c, M) ? plan_gemm(tiles_of(qkvw) / 2, d, kb1, true) : w4(tiles_of(qkvw), d);
+  p.o = w4(tiles_of(d), qd);
+  p.gateup = M <= 16 ? plan_gemm(tiles_of(c.ffn), d, kb1, true) : w4(tiles_of(2 * c.ffn), d);
+  p.down = w4(tiles_of(d), c.ffn);
+  p.fc = w4(tiles_of(d), c.n_feat * d);
+  p.kv = w4(c.n_layers * tiles_of(2 * c.n_kv_heads * c.head_dim), d);
   return p;
 }
 
@@ -284,15 +310,22 @@ PackedLayout make_packed(const dflash_config& c) {
     off = align_up(off + packed_elems(N, K) * e);
     return o;
   };
+  // the draft's own matrices: 4-bit codes and scales for a 4-bit draft
+  auto takeq = [&](int N, int K) {
+    if (c.weight_bits != 4) return take(N, K);
+    size_t o = off;
+    off = align_up(off + q4_bytes(N, K));
+    return o;
+  };
   const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   P.lm_head = take(c.vocab, d);
-  P.fc = c.target ? 0 : take(d, c.n_feat * d);
+  P.fc = c.target ? 0 : takeq(d, c.n_feat * d);
   for (int l = 0; l < c.n_layers; ++l) {
-    P.wqkv[l] = take(qkvw, d);
-    P.wo[l] = take(d, qd);
-    P.wgateup[l] = take(2 * c.ffn, d);
-    P.wdown[l] = take(d, c.ffn);
+    P.wqkv[l] = takeq(qkvw, d);
+    P.wo[l] = takeq(d, qd);
+    P.wgateup[l] = takeq(2 * c.ffn, d);
+    P.wdown[l] = takeq(d, c.ffn);
   }
   if (c.selector_rank) {
     const size_t tb = sizeof(float) * (size_t)c.vocab * c.selector_rank;
@@ -318,6 +351,9 @@ dflash_status validate(const dflash_config* c) {
   if (c->vocab <= 0) return bad("vocab must be positive");
   if (c->n_layers < 1 || c->n_layers > DFLASH_MAX_LAYERS) return bad("n_layers out of range");
   if (c->target != 0 && c->target != 1) return bad("target must be 0 or 1");
+  if (c->weight_bits != 16 && c->weight_bits != 4) return bad("weight_bits must be 16 or 4");
+  if (c->weight_bits == 4 && (c->dtype != DFLASH_BF16 || c->target))
+    return bad("4-bit weights need a bf16 draft (not a target)");
   if (c->target) {
     if (c->block_size < 1 || c->block_size > 64) return bad("a target takes 1 to 64 rows per request");
     if (c->window || c->conv2 || c->topk || c->selector_rank)
@@ -382,6 +418,19 @@ struct dflash_handle {
   std::vector<Scratch> static_sc;  // scratch layouts of static-scratch calls, by request count
 };
 
+// Points segment `seg` of g at tile `tile0` of the packed [N, K] matrix at
+// offset `off` (4-bit: its codes and scales).
+static void set_weights(const dflash_handle* h, GemmParams& g, int seg, size_t off, int N, int K, int tile0 = 0) {
+  if (h->cfg.weight_bits == 4) {
+    g.w4 = 1;
+    g.w[seg] = h->packed + off + (size_t)tile0 * K * 8;
+    g.sb[seg] = h->packed + off + q4_codes_bytes(N, K) + (size_t)tile0 * K;
+  } else {
+    g.w[seg] = h->packed + off + (size_t)tile0 * 16 * K * elt(h->cfg);
+  }
+}
+
+
 namespace {
 
 template <typename P>
@@ -427,13 +476,20 @@ dflash_status ensure_device(dflash_handle* h) {
   const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   launch_pack(c.dtype, h->w.lm_head, h->packed + h->pk.lm_head, c.vocab, d, nullptr);
-  if (!c.target) launch_pack(c.dtype, h->w.fc, h->packed + h->pk.fc, d, c.n_feat * d, nullptr);
+  // the draft's own matrices: fragment order, or quantised to 4-bit codes
+  auto packq = [&](const void* src, size_t off, int N, int K) {
+    if (c.weight_bits == 4)
+      launch_pack_q4(src, h->packed + off, N, K, nullptr);
+    else
+      launch_pack(c.dtype, src, h->packed + off, N, K, nullptr);
+  };
+  if (!c.target) packq(h->w.fc, h->pk.fc, d, c.n_feat * d);
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& lw = h->w.layers[l];
-    launch_pack(c.dtype, lw.wqkv, h->packed + h->pk.wqkv[l], qkvw, d, nullptr);
-    launch_pack(c.dtype, lw.wo, h->packed + h->pk.wo[l], d, qd, nullptr);
-    launch_pack(c.dtype, lw.wgateup, h->packed + h->pk.wgateup[l], 2 * c.ffn, d, nullptr);
-    launch_pack(c.dtype, lw.wdown, h->packed + h->pk.wdown[l], d, c.ffn, nullptr);
+    packq(lw.wqkv, h->pk.wqkv[l], qkvw, d);
+    packq(lw.wo, h->pk.wo[l], d, qd);
+    packq(lw.wgateup, h->pk.wgateup[l], 2 * c.ffn, d);
+    packq(lw.wdown, h->pk.wdown[l], d, c.ffn);
   }
   if (c.selector_rank)
     launch_sel_table(c.dtype, h->w.embed, h->w.sel_u, h->w.sel_v, reinterpret_cast<float*>(h->packed + h->pk.sel_u),
@@ -717,7 +773,7 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
     g.a_part_k = d;
     g.lda = d;
     g.M = rows;
-    g.w[0] = h->packed + h->pk.fc;
+    set_weights(h, g, 0, h->pk.fc, d, c.n_feat * d);
     g.tiles = tiles_of(d);
     g.N = d;
     g.K = c.n_feat * d;
@@ -751,7 +807,8 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
     kv.M = rows;
     // the K/V rows of every layer's fused QKV weight, in place
     for (int l = 0; l < c.n_layers; ++l)
-      kv.w[l] = h->packed + h->pk.wqkv[l] + (size_t)tiles_of(c.n_q_heads * c.head_dim) * 16 * d * e;
+      set_weights(h, kv, l, h->pk.wqkv[l], (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, d,
+                  tiles_of(c.n_q_heads * c.head_dim));
     kv.seg_tiles = kv_seg_tiles;
     kv.tiles = c.n_layers * kv_seg_tiles;
     kv.N = kvw;
@@ -801,7 +858,7 @@ static void gateup_swiglu(dflash_handle* h, hipStream_t s, char* sb, const Scrat
   gu.M = M;
   gu.K = c.hidden;
   gu.a_packed = xa_packed;
-  gu.w[0] = h->packed + h->pk.wgateup[l];
+  set_weights(h, gu, 0, h->pk.wgateup[l], 2 * c.ffn, c.hidden);
   ProfScope ps(h, DFLASH_KERNEL_GATEUP_GEMM, s);
   if (pl.gateup.mt == 4) {
     float* part = sat<float>(sb, sc.gpart);
@@ -1057,7 +1114,7 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
 
     GemmParams g = gemm_in(sb + sc.xa, d);
     g.a_packed = n1.out_packed;
-    g.w[0] = h->packed + h->pk.wqkv[l];
+    set_weights(h, g, 0, h->pk.wqkv[l], qkvw, d);
     g.N = qkvw;
     g.P = pl.qkv.P;
     if (rope) {
@@ -1131,7 +1188,7 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
 
     GemmParams go = gemm_in(sb + sc.xo, qd);
     go.a_packed = ap.out_packed;
-    go.w[0] = h->packed + h->pk.wo[l];
+    set_weights(h, go, 0, h->pk.wo[l], d, qd);
     go.tiles = tiles_of(d);
     go.N = d;
     go.P = pl.o.P;
@@ -1165,7 +1222,7 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
 
     GemmParams gd = gemm_in(sb + sc.z, c.ffn);
     gd.a_packed = z_packed;
-    gd.w[0] = h->packed + h->pk.wdown[l];
+    set_weights(h, gd, 0, h->pk.wdown[l], d, c.ffn);
     gd.tiles = tiles_of(d);
     gd.N = d;
     gd.P = pl.down.P;
@@ -1344,7 +1401,7 @@ dflash_status dflash_target_forward(dflash_handle* h, void* stream, int32_t n_re
 
     GemmParams g = gemm_in(sb + sc.xa, d);
     g.a_packed = n1.out_packed;
-    g.w[0] = h->packed + h->pk.wqkv[l];
+    set_weights(h, g, 0, h->pk.wqkv[l], qkvw, d);
     g.N = qkvw;
     g.P = pl.qkv.P;
     g.tiles = tiles_of(qkvw);
@@ -1460,7 +1517,7 @@ dflash_status dflash_target_forward(dflash_handle* h, void* stream, int32_t n_re
 
     GemmParams go = gemm_in(sb + sc.xo, qd);
     go.a_packed = pl.o.mt == 0;
-    go.w[0] = h->packed + h->pk.wo[l];
+    set_weights(h, go, 0, h->pk.wo[l], d, qd);
     go.tiles = tiles_of(d);
     go.N = d;
     go.P = pl.o.P;
@@ -1487,7 +1544,7 @@ dflash_status dflash_target_forward(dflash_handle* h, void* stream, int32_t n_re
 
     GemmParams gd = gemm_in(sb + sc.z, c.ffn);
     gd.a_packed = z_packed;
-    gd.w[0] = h->packed + h->pk.wdown[l];
+    set_weights(h, gd, 0, h->pk.wdown[l], d, c.ffn);
     gd.tiles = tiles_of(d);
     gd.N = d;
     gd.P = pl.down.P;

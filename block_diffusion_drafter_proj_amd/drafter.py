@@ -48,6 +48,7 @@ def make_config(shape: dict, *, max_batch: int, max_pages: int, max_pages_per_re
     c.rope_theta = shape["rope_theta"]
     c.selector_rank = int(shape.get("selector_rank") or 0)
     c.target = int(shape.get("target") or 0)
+    c.weight_bits = int(shape.get("weight_bits") or 16)
     return c
 
 

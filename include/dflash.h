@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define DFLASH_ABI_VERSION 3
+#define DFLASH_ABI_VERSION 4
 #define DFLASH_MAX_LAYERS 64
 #define DFLASH_MAX_FEAT 8
 #define DFLASH_MAX_BATCH 256
@@ -111,6 +111,14 @@ typedef struct dflash_config {
   int32_t target;            /* 1 = the handle is a target model (dflash_target_forward):
                                 causal attention over its own KV cache, token inputs;
                                 block_size is then the rows per request of one call */
+  int32_t weight_bits;       /* 16 = the draft's matrices in the storage dtype; 4 = a 4-bit
+                                draft ([guide] 8: --draft-bits 4): W_fc and every layer's
+                                W_qkv, W_o, W_gate/up, W_down quantised by dflash_create,
+                                per output row and group of 64 inputs, to codes q in 0..15
+                                with scale s = bf16((max - min) / 15) and bias b = min
+                                (q = round_half_even((w - b) / s) in fp32, 0 when s = 0);
+                                the draft computes with s * q + b.  bf16 drafts only; the
+                                shared embedding and LM head stay bf16 */
 } dflash_config;
 
 /* Per-layer weights (device pointers, dtype of the config).

@@ -43,7 +43,7 @@ _BASE = dict(
     vocab=151936, n_layers=5, block_size=16, n_feat=5, dtype="bf16",
     rope_theta=1.0e6, rms_eps=1.0e-6, window=0, conv2=0, topk=0, selector_rank=0,
     batch=1, ctx=4096, ctx_range=None, target_layers=36, page_size=16,
-    seed=2,
+    seed=2, weight_bits=16,
 )
 
 CONFIGS = {
@@ -61,6 +61,7 @@ CONFIGS = {
     "coder_b64": dict(
         n_layers=8, batch=64, ctx=None, ctx_range=(512, 8192), seed=4,
     ),
+    "qwen3_8b_q4": dict(weight_bits=4, seed=2),
     "dflash2_long": dict(
         conv2=1, topk=16, ctx=32768, window=4096, batch=4, seed=5, selector_rank=256,
     ),
@@ -91,6 +92,11 @@ CONFIGS = {
     "small_target": dict(
         hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1536,
         vocab=3001, n_layers=6, block_size=17, target=1, seed=17,
+    ),
+    "small_q4": dict(
+        hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1536,
+        vocab=3001, n_layers=2, batch=3, ctx=None, ctx_range=(40, 400), weight_bits=4,
+        seed=18,
     ),
     "small_conv": dict(
         hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1536,

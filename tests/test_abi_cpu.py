@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function():
     assert len(names) >= 14
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/dflash.h but not exported"
-    assert B.dflash_abi_version() == 3
+    assert B.dflash_abi_version() == 4
 
 
 def test_feature_layers_entry_point_matches_rule():
@@ -80,7 +80,7 @@ def test_every_workload_config_is_valid(name):
     ("n_layers", 65), ("block_size", 0), ("block_size", 17), ("target", 2), ("n_feat", 0), ("n_feat", 9),
     ("dtype", 7), ("mask_token_id", 3001), ("page_size", 32), ("window", 100), ("topk", 8),
     ("max_batch", 0), ("max_batch", 257), ("max_pages", 0), ("max_position", 3),
-    ("max_inject_rows", 0), ("conv2", 2),
+    ("max_inject_rows", 0), ("conv2", 2), ("weight_bits", 8), ("weight_bits", 0),
 ])
 def test_invalid_configs_are_rejected(field, value):
     cfg = _cfg()
@@ -122,6 +122,28 @@ def test_packed_weights_bytes():
     with pytest.raises(B.DFlashError) as e:
         B.dflash_validate_config(big)
     assert e.value.status == B.E_UNSUPPORTED
+
+
+def test_q4_packed_bytes_and_rules():
+    """A 4-bit draft packs its own matrices as 4-bit codes plus a (scale,
+    bias) pair of bf16 per 64 inputs (0.5625 bytes per weight); the LM head
+    stays bf16.  4-bit weights need a bf16 draft handle."""
+    shape = synth.config("qwen3_8b_q4")
+    cfg = make_config(shape, max_batch=1, max_pages=300, max_pages_per_req=300, max_position=8192)
+    d, F, V, L = 4096, 12288, 151936, 5
+    qkv = (32 + 16) * 128
+
+    def q4(N, K):
+        return N * K // 2 + N * (K // 64) * 4
+
+    expect = 2 * V * d + q4(d, 5 * d) + L * (q4(qkv, d) + q4(d, 4096) + q4(2 * F, d) + q4(d, F))
+    assert B.dflash_packed_weights_bytes(cfg) == expect
+    for field, val in (("dtype", 1), ("target", 1)):
+        c2 = make_config(shape, max_batch=1, max_pages=300, max_pages_per_req=300, max_position=8192)
+        setattr(c2, field, val)
+        with pytest.raises(B.DFlashError) as e:
+            B.dflash_validate_config(c2)
+        assert e.value.status == B.E_INVALID
 
 
 @pytest.fixture()

@@ -24,12 +24,12 @@ import torch
 
 import synth
 from helpers import FREE_ELEM_TOL, assert_rows_close, assert_tokens_match, unpack_kv, write_kv
-from oracle import DraftOracle, verify_accept
+from oracle import DraftOracle, q4_draft_weights, verify_accept
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["qwen3_8b", "llama31_8b"])
+@pytest.mark.parametrize("name", ["qwen3_8b", "llama31_8b", "qwen3_8b_q4"])
 def test_full_size_block(name):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -48,7 +48,7 @@ def test_full_size_block(name):
     f_gpu = torch.empty((ctx, d), dtype=dr.tdt, device=dev)
     dr.inject([0], [ctx], [torch.from_numpy(h).to(dr.tdt).to(dev) for h in H], debug_f=f_gpu)
     print(f"[{name}] gpu inject done", flush=True)
-    o = DraftOracle(shape, w)
+    o = DraftOracle(shape, q4_draft_weights(w) if shape.get("weight_bits") == 4 else w)
     st = o.new_request()
     ref = o.inject(st, H)
     print(f"[{name}] oracle inject done", flush=True)

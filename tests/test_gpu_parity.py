@@ -20,7 +20,7 @@ import torch
 
 import synth
 from helpers import assert_rows_close, assert_tokens_match, pages_needed, unpack_kv, write_kv
-from oracle import DraftOracle, verify_accept
+from oracle import DraftOracle, q4_draft_weights, verify_accept
 
 pytestmark = pytest.mark.gpu
 
@@ -199,7 +199,7 @@ def _check_topk(ids, vals, g_logits, ref_logits, g_draft):
 
 
 @pytest.mark.parametrize("name", ["small_bf16", "small_block10", "small_dh64", "small_batch", "small_window",
-                                  "small_conv"])
+                                  "small_conv", "small_q4"])
 def test_draft_parity_lockstep(name):
     _lockstep(name)
 
@@ -220,8 +220,13 @@ def test_draft_parity_lockstep(name):
     # 32 requests x 8 query heads = 256 (request, head) pairs, 4 attention
     # splits per request: the two-rows-per-wave split merge with up to 4 splits
     ("small_batch", {"batch": 32, "ctx": None, "ctx_range": (200, 900)}),
+    # 4-bit draft: 16 rows (the RoPE and SwiGLU epilogues on 4-bit codes), 80
+    # rows (two 64-row blocks), and with the DFlash-2 conv and top-16
+    ("small_q4", {"batch": 1}),
+    ("small_q4", {"batch": 5}),
+    ("small_q4", {"conv2": 1, "topk": 16, "window": 128}),
 ], ids=["block1", "batch5_block1", "rows64", "conv_rows48", "block10_rows70", "rows64_vocab4", "conv_rows48_vocab4",
-        "conv_rows80_topk_tiled", "batch32_merge_splits"])
+        "conv_rows80_topk_tiled", "batch32_merge_splits", "q4_rows16", "q4_rows80", "q4_conv_topk_window"])
 def test_draft_parity_lockstep_shapes(name, over):
     if over.get("batch") == 32:
         # premise: every request has several splits (target 256 / (32 * 2) = 4)
@@ -243,9 +248,15 @@ def _attn_splits(shape, ctx):
     return (units + pps - 1) // pps
 
 
+def _oracle(shape, w):
+    """The oracle of the handle's draft (a 4-bit draft computes with its
+    dequantised matrices)."""
+    return DraftOracle(shape, q4_draft_weights(w) if shape.get("weight_bits") == 4 else w)
+
+
 def _lockstep(name, **over):
     dev, shape, w, dr, ctxs, pages = _setup(name, **over)
-    o = DraftOracle(shape, w)
+    o = _oracle(shape, w)
     n = shape["batch"]
     slots = list(range(n))
     states = [o.new_request() for _ in slots]
