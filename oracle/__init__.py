@@ -42,6 +42,12 @@ Parity status per function (what pins it, see ``tests/test_oracle_*.py``):
 * ``target.TargetOracle`` (target verify forward) pinned: equals the tiny
                        target row by row (fp32, MHA); causal; chunked equals
                        one block; GQA equals MHA with repeated K/V heads.
+* ``dynamic_taps``, ``dynamic_conv`` (the DFlash-2 conv's dynamic taps)
+                       pinned: a small case worked by hand; identity static
+                       taps with a zero form equal the draft without conv;
+                       a row's source moves only its own and the next row's
+                       output; the reading's parameter count against the
+                       page's 16.5 M.
 * ``quant.quantize_q4``, ``dequantize_q4``, ``q4_draft_weights`` (4-bit draft
                        weights) pinned: weights already on a 4-bit grid come
                        back exactly (codes, scales, biases and values); a
@@ -53,6 +59,8 @@ from .dflash_oracle import (  # noqa: F401
     DraftOracle,
     RequestState,
     attention,
+    dynamic_conv,
+    dynamic_taps,
     feature_layers,
     per_token_cost,
     rmsnorm,

@@ -154,6 +154,37 @@ def two_tap_conv(x: np.ndarray, w: np.ndarray, x_prev0: np.ndarray) -> np.ndarra
     return w[0][None, :] * x + w[1][None, :] * prev
 
 
+def dynamic_taps(src, D, U, w_static):
+    """Dynamic two-tap conv taps of every row ([guide] section 7: the conv
+    is "dynamic"; the page gives no form and puts the cost at 16.5 M
+    parameters).
+
+    Reading: the taps of a row are a rank-r linear function of that row of
+    the conv's own input, added to the static taps: t = D src (D [r, d]),
+    then [a; b] = w_static + U t (U [2d, r]: rows 0..d-1 give a, rows
+    d..2d-1 give b).  The input is the stored normed rows for the convs
+    before attention and the MLP, and the projection's output (W_o o,
+    W_down z) for the convs after them.  With r = 64 and d = 4096 the four
+    convs of one layer hold 4 * 3 * 4096 * 64 = 3.1 M parameters, 15.7 M
+    over five layers, the page's 16.5 M within 5 %.
+
+    src [rows, d]; w_static [2, d].  Returns (a, b), each [rows, d], float64.
+    """
+    t = np.asarray(src, dtype=np.float64) @ np.asarray(D, dtype=np.float64).T
+    delta = t @ np.asarray(U, dtype=np.float64).T
+    d = delta.shape[1] // 2
+    w = np.asarray(w_static, dtype=np.float64)
+    return w[0][None, :] + delta[:, :d], w[1][None, :] + delta[:, d:]
+
+
+def dynamic_conv(x, a, b, x_prev0):
+    """y[i] = a[i] * x[i] + b[i] * x[i-1] with per-row taps; row 0 reads
+    ``x_prev0`` in place of x[-1]."""
+    x = np.asarray(x, dtype=np.float64)
+    prev = np.concatenate([np.asarray(x_prev0, dtype=np.float64)[None, :], x[:-1]], axis=0)
+    return a * x + b * prev
+
+
 def select(logits: np.ndarray, topk: int = 0):
     """Greedy choice per position from float logits [rows, V].
 
@@ -331,6 +362,7 @@ class DraftOracle:
         qpos = np.arange(n, n + B)
         st_ = self.store
         conv = bool(cfg.get("conv2"))
+        dyn = conv and int(cfg.get("conv_rank") or 0) > 0
         e_prev = None
         if conv:
             if last_token is None:
@@ -343,7 +375,11 @@ class DraftOracle:
             lw = self.w["layers"][l]
             wq, wk, wv = self._kv_rows(l)
             x = rmsnorm(h, lw["attn_norm"], self.eps)
-            if conv:
+            if dyn:  # the stored normed rows are the taps' source and the conv's input
+                xs = self._w64(st_(x))
+                ta, tb = dynamic_taps(xs, lw["dconv_d"][0], lw["dconv_u"][0], lw["conv"][0])
+                x = dynamic_conv(xs, ta, tb, e_prev)
+            elif conv:
                 x = two_tap_conv(x, lw["conv"][0], e_prev)
             a = self._w64(st_(x))
             q = st_(rope((a @ self._w64(wq).T).reshape(B, hq, dh), qpos, self.theta))
@@ -353,18 +389,28 @@ class DraftOracle:
             o = attention(q, np.concatenate([kc, kb], 0), np.concatenate([vc, vb], 0))
             o = self._w64(st_(o.reshape(B, hq * dh)))
             y = o @ self._w64(lw["wo"]).T
-            if conv:
+            if dyn:
+                ta, tb = dynamic_taps(y, lw["dconv_d"][1], lw["dconv_u"][1], lw["conv"][1])
+                y = dynamic_conv(y, ta, tb, e_prev)
+            elif conv:
                 y = two_tap_conv(y, lw["conv"][1], e_prev)
             h = h + y
             x = rmsnorm(h, lw["mlp_norm"], self.eps)
-            if conv:
+            if dyn:
+                xs = self._w64(st_(x))
+                ta, tb = dynamic_taps(xs, lw["dconv_d"][2], lw["dconv_u"][2], lw["conv"][2])
+                x = dynamic_conv(xs, ta, tb, e_prev)
+            elif conv:
                 x = two_tap_conv(x, lw["conv"][2], e_prev)
             m = self._w64(st_(x))
             wg = self._w64(lw["wgateup"][: self.F])
             wu = self._w64(lw["wgateup"][self.F:])
             z = self._w64(st_(swiglu(m @ wg.T, m @ wu.T)))
             y = z @ self._w64(lw["wdown"]).T
-            if conv:
+            if dyn:
+                ta, tb = dynamic_taps(y, lw["dconv_d"][3], lw["dconv_u"][3], lw["conv"][3])
+                y = dynamic_conv(y, ta, tb, e_prev)
+            elif conv:
                 y = two_tap_conv(y, lw["conv"][3], e_prev)
             h = h + y
             if trace:

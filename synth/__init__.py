@@ -18,6 +18,7 @@ LM head) and the five workloads this project measures:
 * ``llama31_8b``    LLaMA-3.1-8B-shaped draft, bf16, batch 1, ctx 8192, block 10.
 * ``coder_b64``     8-layer Qwen3-8B-shaped draft, 64 ragged requests.
 * ``dflash2_long``  qwen3_8b + two-tap conv + top-16, ctx 32768, window 4096.
+* ``dflash2_dyn``   dflash2_long with dynamic conv taps of rank 64.
 
 The ``small_*`` shapes are parity cases: small enough for the oracle to finish
 in seconds, ragged enough (vocab, context, block) to leave partial tiles.
@@ -43,7 +44,7 @@ _BASE = dict(
     vocab=151936, n_layers=5, block_size=16, n_feat=5, dtype="bf16",
     rope_theta=1.0e6, rms_eps=1.0e-6, window=0, conv2=0, topk=0, selector_rank=0,
     batch=1, ctx=4096, ctx_range=None, target_layers=36, page_size=16,
-    seed=2, weight_bits=16,
+    seed=2, weight_bits=16, conv_rank=0,
 )
 
 CONFIGS = {
@@ -62,6 +63,9 @@ CONFIGS = {
         n_layers=8, batch=64, ctx=None, ctx_range=(512, 8192), seed=4,
     ),
     "qwen3_8b_q4": dict(weight_bits=4, seed=2),
+    "dflash2_dyn": dict(
+        conv2=1, conv_rank=64, topk=16, ctx=32768, window=4096, batch=4, seed=6, selector_rank=256,
+    ),
     "dflash2_long": dict(
         conv2=1, topk=16, ctx=32768, window=4096, batch=4, seed=5, selector_rank=256,
     ),
@@ -92,6 +96,11 @@ CONFIGS = {
     "small_target": dict(
         hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1536,
         vocab=3001, n_layers=6, block_size=17, target=1, seed=17,
+    ),
+    "small_dconv": dict(
+        hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1536,
+        vocab=3001, n_layers=2, conv2=1, conv_rank=32, topk=16, window=128, batch=2,
+        ctx=500, seed=19,
     ),
     "small_q4": dict(
         hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn=1536,
@@ -162,7 +171,8 @@ def _normal(seed, stream, keys, shape, std, mean=0.0):
 
 # tensor ids for weight streams
 _TID = dict(embed=0, lm_head=1, fc=2, fc_norm=3, final_norm=4, wqkv=10,
-            wo=11, wgateup=12, wdown=13, attn_norm=14, mlp_norm=15, conv=16, sel_u=20, sel_v=21)
+            wo=11, wgateup=12, wdown=13, attn_norm=14, mlp_norm=15, conv=16, sel_u=20, sel_v=21,
+            dconv_d=22, dconv_u=23)
 
 
 def make_weights(cfg: dict, seed: int | None = None, norm_std: float = 0.0,
@@ -174,7 +184,9 @@ def make_weights(cfg: dict, seed: int | None = None, norm_std: float = 0.0,
 
     Every matrix is N(0, 0.02).  RMSNorm gains are 1 (``norm_std`` > 0 draws
     them as 1 + N(0, norm_std) instead, to make the gain visible in tests).
-    Conv taps (when ``conv2``) are w0 = 1 + N(0, 0.02), w1 = N(0, 0.02).
+    Conv taps (when ``conv2``) are w0 = 1 + N(0, 0.02), w1 = N(0, 0.02);
+    with ``conv_rank`` r the dynamic taps' forms D ([4, r, d]) and U
+    ([4, 2d, r]) are N(0, 0.02).
     The path selector's forms (when ``selector_rank``) are [r, d] matrices of
     N(0, cfg["sel_std"]) (0.02 unless the shape says otherwise).
     """
@@ -212,6 +224,10 @@ def make_weights(cfg: dict, seed: int | None = None, norm_std: float = 0.0,
             c = _normal(seed, S_WEIGHTS, (_TID["conv"], l), (4, 2, d), 0.02)
             c[:, 0, :] += 1.0
             lw["conv"] = to_storage(c, dt)
+            r = int(cfg.get("conv_rank") or 0)
+            if r:  # dynamic taps: D [4, r, d], U [4, 2d, r]
+                lw["dconv_d"] = to_storage(_normal(seed, S_WEIGHTS, (_TID["dconv_d"], l), (4, r, d), 0.02), dt)
+                lw["dconv_u"] = to_storage(_normal(seed, S_WEIGHTS, (_TID["dconv_u"], l), (4, 2 * d, r), 0.02), dt)
         w["layers"].append(lw)
     r = int(cfg.get("selector_rank") or 0)
     if r:
