@@ -20,6 +20,7 @@ Default workload ``qwen3_8b``:
   * ``qwen3_8b_q4``: the headline workload with a 4-bit draft (its own
     matrices as 4-bit codes with a bf16 scale and bias per 64 inputs; the
     shared LM head stays bf16);
+  * ``dflash2_dyn``: dflash2_long with dynamic conv taps (rank 64);
   * ``dflash2_long``: conv taps, top-16 and the path selector (rank 256;
     the target verifies the path), batch 4, context 32768 with a
     4096-token window.
@@ -99,8 +100,10 @@ def draft_bytes(shape, visible):
     d, hq, hkv, dh, F, V, L = (shape[k] for k in ("hidden", "n_q_heads", "n_kv_heads", "head_dim",
                                                    "ffn", "vocab", "n_layers"))
     layer = (hq + 2 * hkv) * dh * d + d * hq * dh + 2 * F * d + d * F
+    r = int(shape.get("conv_rank") or 0) if shape.get("conv2") else 0
+    dyn = L * 4 * 3 * d * r  # dynamic conv taps: D [r, d] and U [2d, r] at four points per layer
     kv = L * sum(visible) * 2 * hkv * dh
-    return int(welt(shape) * L * layer + e * (V * d + kv))
+    return int(welt(shape) * L * layer + e * (V * d + kv + dyn))
 
 
 def inject_bytes(shape, rows):
@@ -293,7 +296,7 @@ def main():
     if not args.single and args.config == "qwen3_8b":
         # the other measured workloads, each in its own handle, reported beside the headline
         result["workloads"] = {}
-        for name in ("qwen3_8b_q4", "llama31_8b", "coder_b64", "dflash2_long"):
+        for name in ("qwen3_8b_q4", "llama31_8b", "coder_b64", "dflash2_long", "dflash2_dyn"):
             r = run_workload(name, args.steps, args.warmup, cpu=False)
             result["workloads"][name] = {k: r[k] for k in SUMMARY_KEYS if k in r}
     print(json.dumps(result))
@@ -553,8 +556,12 @@ def run_workload(config, steps, warmup, cpu=False, target=False):
             shares["two_tap_conv"] = {
                 "ms_per_cycle": breakdown.get("conv", 0.0),
                 "share": round(breakdown.get("conv", 0.0) / cycle_ms, 4),
-                "counted": "the norm launches that apply the conv taps (all four points run inside them); "
-                           "an upper bound, since the RMSNorm work of those launches is included"}
+                "counted": ("the norm launches that apply the conv taps, the taps' rank-r projections of the "
+                            "input convs and the kernels that form the dynamic taps (the output convs' "
+                            "projections ride in the O and down products and are not counted)"
+                            if shape.get("conv_rank") else
+                            "the norm launches that apply the conv taps (all four points run inside them)")
+                           + "; an upper bound, since the RMSNorm work of those launches is included"}
         if topk:
             sel = breakdown.get("select", 0.0) + breakdown.get("topk", 0.0)
             shares["top16_selection"] = {

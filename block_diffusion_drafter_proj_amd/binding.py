@@ -45,12 +45,12 @@ class DFlashConfig(ctypes.Structure):
         "topk", "max_batch", "max_pages", "max_pages_per_req", "max_position",
         "max_inject_rows")] + [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
                                ("selector_rank", ctypes.c_int32), ("target", ctypes.c_int32),
-                               ("weight_bits", ctypes.c_int32)]
+                               ("weight_bits", ctypes.c_int32), ("conv_rank", ctypes.c_int32)]
 
 
 class DFlashLayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "wqkv", "wo", "wgateup", "wdown", "attn_norm", "mlp_norm", "conv")]
+        "wqkv", "wo", "wgateup", "wdown", "attn_norm", "mlp_norm", "conv", "dconv_d", "dconv_u")]
 
 
 class DFlashSampling(ctypes.Structure):

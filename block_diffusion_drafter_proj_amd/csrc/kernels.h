@@ -118,7 +118,36 @@ struct NormParams {
   const int* last_token;   // [n_req]
   int B, vocab;
   unsigned int* err;
+  int ldp;                 // row stride of the partials (0: d)
+  const float* otaps;      // dynamic output conv: per-row taps [M][2d] (a, then b) in place of oconv, or NULL
 };
+
+// Dynamic two-tap conv taps (DFlash 2): per row and channel c,
+//   a = w0[c] + U[c] . t,  b = w1[c] + U[d + c] . t,  t = sum_p t_part[p][row]
+// (t the rank-r projection of the conv's input row, from split-K partials).
+// The apply form convolves the stored input rows x: out[row] = a x[row] +
+// b x[row-1] (x[-1] of a request's block: the embedding of its last verified
+// token); the taps form writes (a, b) for a norm that applies them.
+struct DConvParams {
+  const void* x;        // [M, d] storage dtype (apply), or NULL (taps)
+  const float* t;       // t partials: element j of row m, split p at t[p * plane + m * ldt + j]
+  int n_part, ldt;
+  int lo_off;           // > 0: t also adds the partials lo_off columns further (a hi + lo folded form)
+  long long plane;
+  const void* U;        // [2d, r] storage dtype
+  const void* w;        // static taps [2][d] storage dtype
+  int d, r, M, B, vocab;
+  const void* embed;    // [V, d]
+  const int* last_token;
+  void* out;            // apply: storage dtype [M, d] (row stride ldo), or fragment order
+  int ldo, out_packed;
+  float* taps;          // taps: [M][2d]
+  unsigned int* err;
+};
+void launch_dconv(int dtype, const DConvParams& p, hipStream_t s);
+// out [2r, K]: D [r, d] x W [d, K] (fp32 sums) as hi (rows 0..r-1, the sums
+// rounded to the storage dtype) + lo (rows r..2r-1, the rest), r <= 64
+void launch_fold(int dtype, const void* D, const void* W, void* out, int r, int d, int K, hipStream_t s);
 
 // Greedy selection over split-K partial logits (the vocabulary product of
 // 17..64 rows): one workgroup of 4 waves per (chunk of kSelChunk columns,

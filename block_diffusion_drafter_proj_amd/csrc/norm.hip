@@ -37,7 +37,7 @@ __device__ __forceinline__ float block_sum(float v, float* red, int slot) {
 // Sum of the split-K partials of one row.
 __device__ __forceinline__ f32x4 part_sum4(const NormParams& p, int row, int k, long long plane) {
   f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float* pp = p.part + (long long)row * p.d + k;
+  const float* pp = p.part + (long long)row * (p.ldp ? p.ldp : p.d) + k;
   for (int q0 = 0; q0 < p.n_part; q0 += 8) {
     f32x4 v[8];
 #pragma unroll
@@ -102,7 +102,7 @@ __device__ __forceinline__ f32x4 load_row4(const NormParams& p, int row, int k, 
     x = *reinterpret_cast<const f32x4*>(p.x_in + (long long)row * p.ldx + k);
   }
   if (p.n_part) {
-    const float* pp = p.part + (long long)row * p.d + k;
+    const float* pp = p.part + (long long)row * (p.ldp ? p.ldp : p.d) + k;
     for (int q0 = 0; q0 < p.n_part; q0 += 8) {
       f32x4 v[8];
 #pragma unroll
@@ -126,10 +126,14 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(NormParams p) {
   const int row = blockIdx.x;
   const int t = threadIdx.x;
   const int k = 4 * t;
-  const long long plane = (long long)p.M * p.d;
+  const long long plane = (long long)p.M * (p.ldp ? p.ldp : p.d);
   const bool first = p.conv && (row % p.B) == 0;
   f32x4 x, xp = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (p.oconv) {  // the producing GEMM's output conv folded in (this row and, for the input conv, the previous)
+  if (p.otaps) {  // the producing GEMM's output conv with this row's dynamic taps
+    const float* ta = p.otaps + (long long)row * 2 * p.d + k;
+    x = load_row4_oconv<T>(p, row, k, plane, *reinterpret_cast<const f32x4*>(ta),
+                           *reinterpret_cast<const f32x4*>(ta + p.d));
+  } else if (p.oconv) {  // the producing GEMM's output conv folded in (this row and, for the input conv, the previous)
     f32x4 ow0, ow1;
     const T* o0 = reinterpret_cast<const T*>(p.oconv) + k;
 #pragma unroll
@@ -289,7 +293,8 @@ __global__ __launch_bounds__(1024) void k_rmsnorm_frag(NormParams p) {
 
 void launch_rmsnorm(int dtype, const NormParams& p, hipStream_t s) {
   if (p.M <= 0) return;
-  if (p.out_packed && !p.conv && !p.oconv && !p.feat && !p.init_tokens && p.d % 256 == 0 && p.d <= 4096) {
+  if (p.out_packed && !p.conv && !p.oconv && !p.otaps && !p.ldp && !p.feat && !p.init_tokens && p.d % 256 == 0 &&
+      p.d <= 4096) {
     constexpr int R = kNormRows;
     const int nt = std::min(kNormThreads, R * p.d / 8);  // R * d / 8 chunks, at most 8 per thread
     if (dtype == DFLASH_BF16)

@@ -74,7 +74,12 @@ int part_pairs(const dflash_config& c) { return c.max_batch * max_splits(c); }
 // their partial planes).
 struct Plans {
   GemmPlan qkv, o, gateup, down, lm, fc, kv;
+  GemmPlan dconv;  // rank-r projection of a conv input (dynamic conv taps)
 };
+
+// Width of the O and down products: with dynamic conv taps they carry 2r
+// extra output rows (the taps' projection folded into them, as hi + lo).
+int out_width(const dflash_config& c) { return c.hidden + (c.conv2 && c.conv_rank ? 2 * c.conv_rank : 0); }
 
 int tiles_of(int n) { return (n + 15) / 16; }
 
@@ -86,7 +91,7 @@ bool qkv_rope(const dflash_config& c, int M) {
 }
 
 Plans plans16(const dflash_config& c, int M) {
-  const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
+  const int d = c.hidden, qd = c.n_q_heads * c.head_dim, dn = out_width(c);
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   // 17..64 rows: the split-K products stream their weights once for all
   // rows (skinny kernel, 64-row block); so does the gate/up product, whose
@@ -106,11 +111,11 @@ Plans plans16(const dflash_config& c, int M) {
     const GemmPlan one{1, 4, 1, 0};
     Plans p;
     p.qkv = mt4(tiles_of(qkvw), d);
-    p.o = tiled_ok ? tiled(tiles_of(d), qd) : mt4(tiles_of(d), qd);
+    p.o = tiled_ok ? tiled(tiles_of(dn), qd) : mt4(tiles_of(dn), qd);
     // gate/up as one split-K product of 2F columns (weights streamed once for
     // all rows), then the SwiGLU from its partials
     p.gateup = tiled_ok ? one : mt4(tiles_of(2 * c.ffn), d);
-    p.down = tiled_ok ? tiled(tiles_of(d), c.ffn) : mt4(tiles_of(d), c.ffn);
+    p.down = tiled_ok ? tiled(tiles_of(dn), c.ffn) : mt4(tiles_of(dn), c.ffn);
     p.lm = mt4(tiles_of(c.vocab), d);  // partial logits, then k_logit_select
     p.fc = mt4(tiles_of(d), c.n_feat * d);
     p.kv = mt4(c.n_layers * tiles_of(2 * c.n_kv_heads * c.head_dim), d);
@@ -121,9 +126,9 @@ Plans plans16(const dflash_config& c, int M) {
     const GemmPlan one{1, 4, 1, 0};
     Plans p;
     p.qkv = tiled(tiles_of(qkvw), d);
-    p.o = tiled(tiles_of(d), qd);
+    p.o = tiled(tiles_of(dn), qd);
     p.gateup = one;
-    p.down = tiled(tiles_of(d), c.ffn);
+    p.down = tiled(tiles_of(dn), c.ffn);
     p.lm = one;
     p.fc = tiled(tiles_of(d), c.n_feat * d);
     p.kv = tiled(c.n_layers * tiles_of(2 * c.n_kv_heads * c.head_dim), d);
@@ -132,9 +137,9 @@ Plans plans16(const dflash_config& c, int M) {
   const int kb = gemm_kblock(c.dtype, 1);
   Plans p;
   p.qkv = qkv_rope(c, M) ? plan_gemm(tiles_of(qkvw) / 2, d, kb, true) : plan_gemm(tiles_of(qkvw), d, kb, false);
-  p.o = plan_gemm(tiles_of(d), qd, kb, false);
+  p.o = plan_gemm(tiles_of(dn), qd, kb, false);
   p.gateup = plan_gemm(tiles_of(c.ffn), d, kb, true);
-  p.down = plan_gemm(tiles_of(d), c.ffn, kb, false);
+  p.down = plan_gemm(tiles_of(dn), c.ffn, kb, false);
   p.lm = plan_gemm(tiles_of(c.vocab), d, kb, true);
   p.fc = plan_gemm(tiles_of(d), c.n_feat * d, kb, false);
   p.kv = plan_gemm(c.n_layers * tiles_of(2 * c.n_kv_heads * c.head_dim), d, kb, false);
@@ -148,6 +153,14 @@ Plans plans16(const dflash_config& c, int M) {
 // plan.
 Plans make_plans(const dflash_config& c, int M) {
   Plans p = plans16(c, M);
+  if (c.conv2 && c.conv_rank) {  // the skinny kernel for the small projection (64-row blocks above 16 rows)
+    if (M <= 16) {
+      p.dconv = plan_gemm(c.conv_rank / 16, c.hidden, gemm_kblock(c.dtype, 1), false);
+    } else {
+      p.dconv = plan_gemm(c.conv_rank / 16, c.hidden, gemm_kblock(c.dtype, 4), false, 8);
+      p.dconv.mt = c.dtype == DFLASH_BF16 ? 4 : 1;
+    }
+  }
   if (c.weight_bits != 4) return p;
   const int d = c.hidden, qd = c.n_q_heads * c.head_dim;
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
@@ -190,6 +203,7 @@ struct Scratch {
   size_t schunk;     // sampled verification: per row chunk lists (u64) and statistics
   size_t tq;         // target: q of the new rows [M][Hq*dh]
   size_t gpart;      // split-K partials of the gate/up product (17..63 rows)
+  size_t xn, tpart, otaps;  // dynamic conv taps
   size_t u, f, kvo;  // inject only (0 when not laid out)
   size_t total;
 };
@@ -256,8 +270,13 @@ Scratch make_scratch(const dflash_config& c, int n_req, bool inject) {
     }
     S.gpart = grows ? take(sizeof(float) * grows * 2 * c.ffn) : 0;
   }
-  S.opart = take(sizeof(float) * part_rows(c, &Plans::o, (int)M) * c.hidden);
-  S.dpart = take(sizeof(float) * part_rows(c, &Plans::down, (int)M) * c.hidden);
+  S.opart = take(sizeof(float) * part_rows(c, &Plans::o, (int)M) * out_width(c));
+  S.dpart = take(sizeof(float) * part_rows(c, &Plans::down, (int)M) * out_width(c));
+  if (c.conv2 && c.conv_rank) {  // dynamic conv taps: stored normed rows, the projection's partials, taps
+    S.xn = take(e * M16 * c.hidden);
+    S.tpart = take(sizeof(float) * part_rows(c, &Plans::dconv, (int)M) * c.conv_rank);
+    S.otaps = take(sizeof(float) * M * 2 * c.hidden);
+  }
   if (inject) {
     const size_t R = c.max_inject_rows;
     S.u = take(sizeof(float) * part_rows(c, &Plans::fc, (int)R) * c.hidden);
@@ -292,11 +311,16 @@ Layout make_layout(const dflash_config& c) {
   return L;
 }
 
+const char* wptr(const void* p, size_t elem_off, size_t e) {
+  return reinterpret_cast<const char*>(p) + elem_off * e;
+}
+
 // Packed (MFMA fragment order) copies of every weight matrix.
 // With a path selector, also the projected embedding tables (fp32 [V, r]).
 struct PackedLayout {
   size_t lm_head, fc, wqkv[DFLASH_MAX_LAYERS], wo[DFLASH_MAX_LAYERS], wgateup[DFLASH_MAX_LAYERS],
       wdown[DFLASH_MAX_LAYERS];
+  size_t dconv[DFLASH_MAX_LAYERS][2];  // dynamic conv: D of the convs before attention and the MLP
   size_t sel_u, sel_v;
   size_t total;
 };
@@ -321,11 +345,16 @@ PackedLayout make_packed(const dflash_config& c) {
   const int qkvw = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   P.lm_head = take(c.vocab, d);
   P.fc = c.target ? 0 : takeq(d, c.n_feat * d);
+  const int dn = out_width(c);  // W_o and W_down with D W of the output convs appended
   for (int l = 0; l < c.n_layers; ++l) {
     P.wqkv[l] = takeq(qkvw, d);
-    P.wo[l] = takeq(d, qd);
+    P.wo[l] = takeq(dn, qd);
     P.wgateup[l] = takeq(2 * c.ffn, d);
-    P.wdown[l] = takeq(d, c.ffn);
+    P.wdown[l] = takeq(dn, c.ffn);
+    if (c.conv2 && c.conv_rank) {
+      P.dconv[l][0] = take(c.conv_rank, d);
+      P.dconv[l][1] = take(c.conv_rank, d);
+    }
   }
   if (c.selector_rank) {
     const size_t tb = sizeof(float) * (size_t)c.vocab * c.selector_rank;
@@ -354,6 +383,10 @@ dflash_status validate(const dflash_config* c) {
   if (c->weight_bits != 16 && c->weight_bits != 4) return bad("weight_bits must be 16 or 4");
   if (c->weight_bits == 4 && (c->dtype != DFLASH_BF16 || c->target))
     return bad("4-bit weights need a bf16 draft (not a target)");
+  if (c->conv_rank != 0 && c->conv_rank != 16 && c->conv_rank != 32 && c->conv_rank != 48 && c->conv_rank != 64)
+    return bad("conv_rank must be 0, 16, 32, 48 or 64");
+  if (c->conv_rank && (!c->conv2 || c->weight_bits != 16))
+    return bad("dynamic conv taps need conv2 and storage-dtype weights");
   if (c->target) {
     if (c->block_size < 1 || c->block_size > 64) return bad("a target takes 1 to 64 rows per request");
     if (c->window || c->conv2 || c->topk || c->selector_rank)
@@ -484,12 +517,26 @@ dflash_status ensure_device(dflash_handle* h) {
       launch_pack(c.dtype, src, h->packed + off, N, K, nullptr);
   };
   if (!c.target) packq(h->w.fc, h->pk.fc, d, c.n_feat * d);
+  const int r = c.conv2 ? c.conv_rank : 0;
+  const size_t es = elt(c);
+  char* fold = h->ws + h->lay.scratch;  // scratch is free at set-up: D W of an output conv before packing
+  if (r && (size_t)2 * r * std::max(qd, c.ffn) * es > h->lay.sc.total)
+    return fail(DFLASH_E_CAPACITY, "workspace scratch too small to fold the conv taps' forms");
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& lw = h->w.layers[l];
     packq(lw.wqkv, h->pk.wqkv[l], qkvw, d);
     packq(lw.wo, h->pk.wo[l], d, qd);
     packq(lw.wgateup, h->pk.wgateup[l], 2 * c.ffn, d);
     packq(lw.wdown, h->pk.wdown[l], d, c.ffn);
+    if (r) {  // dynamic conv taps: D of the input convs; D W joins W_o and W_down as r extra rows
+      const size_t dpt = (size_t)r * d * es;  // bytes of one point's D
+      launch_pack(c.dtype, wptr(lw.dconv_d, 0, 1), h->packed + h->pk.dconv[l][0], r, d, nullptr);
+      launch_pack(c.dtype, wptr(lw.dconv_d, 2 * dpt, 1), h->packed + h->pk.dconv[l][1], r, d, nullptr);
+      launch_fold(c.dtype, wptr(lw.dconv_d, dpt, 1), lw.wo, fold, r, d, qd, nullptr);
+      launch_pack(c.dtype, fold, h->packed + h->pk.wo[l] + (size_t)d * qd * es, 2 * r, qd, nullptr);
+      launch_fold(c.dtype, wptr(lw.dconv_d, 3 * dpt, 1), lw.wdown, fold, r, d, c.ffn, nullptr);
+      launch_pack(c.dtype, fold, h->packed + h->pk.wdown[l] + (size_t)d * c.ffn * es, 2 * r, c.ffn, nullptr);
+    }
   }
   if (c.selector_rank)
     launch_sel_table(c.dtype, h->w.embed, h->w.sel_u, h->w.sel_v, reinterpret_cast<float*>(h->packed + h->pk.sel_u),
@@ -582,10 +629,6 @@ dflash_status launched(const char* what) {
   return DFLASH_OK;
 }
 
-const char* wptr(const void* p, size_t elem_off, size_t e) {
-  return reinterpret_cast<const char*>(p) + elem_off * e;
-}
-
 }  // namespace
 
 extern "C" {
@@ -638,6 +681,8 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
     if (!lw.wqkv || !lw.wo || !lw.wgateup || !lw.wdown || !lw.attn_norm || !lw.mlp_norm)
       return fail(DFLASH_E_INVALID, "layer %d: a weight pointer is NULL", l);
     if (cfg->conv2 && !lw.conv) return fail(DFLASH_E_INVALID, "layer %d: conv taps are NULL", l);
+    if (cfg->conv_rank && (!lw.dconv_d || !lw.dconv_u))
+      return fail(DFLASH_E_INVALID, "layer %d: dynamic conv forms are NULL", l);
   }
   if (cfg->selector_rank && (!w->sel_u || !w->sel_v))
     return fail(DFLASH_E_INVALID, "selector_rank is set but sel_u / sel_v are NULL");
@@ -1074,11 +1119,76 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     np.err = at<unsigned int>(h, h->lay.err);
   };
   auto norm = [&](const NormParams& np) {
-    ProfScope ps(h, np.conv || np.oconv ? DFLASH_KERNEL_CONV : DFLASH_KERNEL_NORM, s);
+    ProfScope ps(h, np.conv || np.oconv || np.otaps ? DFLASH_KERNEL_CONV : DFLASH_KERNEL_NORM, s);
     launch_rmsnorm(c.dtype, np, s);
   };
   // conv variant: the residual stream alternates between hbuf and halt
   float* halt = c.conv2 ? sat<float>(sb, sc.h2) : hbuf;
+  // dynamic conv taps (rank r): the O and down products carry 2r extra output
+  // columns, t = (D W) o as hi + lo, from which each output conv's taps are formed; the
+  // input convs take the stored normed rows through a D product and apply
+  // their taps into the next GEMM's input
+  const int r = c.conv2 ? c.conv_rank : 0;
+  const int dn = out_width(c);
+  float* otaps = r ? sat<float>(sb, sc.otaps) : nullptr;
+  auto dconv_base = [&](DConvParams& dp, int l, int k) {
+    dp.U = wptr(h->w.layers[l].dconv_u, (size_t)k * 2 * d * r, e);
+    dp.w = conv_taps(l, k);
+    dp.d = d;
+    dp.r = r;
+    dp.M = M;
+    dp.B = B;
+    dp.vocab = c.vocab;
+    dp.embed = h->w.embed;
+    dp.last_token = last_token;
+    dp.err = at<unsigned int>(h, h->lay.err);
+  };
+  // output conv k of layer l: taps from the extra columns of the product's partials
+  auto dyn_taps = [&](int l, int k, const float* part, int n_part) {
+    DConvParams dp{};
+    dconv_base(dp, l, k);
+    dp.t = part + d;
+    dp.lo_off = r;
+    dp.ldt = dn;
+    dp.plane = (long long)M * dn;
+    dp.n_part = n_part;
+    dp.taps = otaps;
+    ProfScope ps(h, DFLASH_KERNEL_CONV, s);
+    launch_dconv(c.dtype, dp, s);
+  };
+  // input conv k (0 or 2) of layer l: D product of the stored normed rows in xn, then the conv into xa
+  auto dyn_in = [&](int l, int k, int out_packed) {
+    GemmParams gt = gemm_in(sb + sc.xn, d);
+    set_weights(h, gt, 0, h->pk.dconv[l][k / 2], r, d);
+    gt.tiles = r / 16;
+    gt.N = r;
+    gt.P = pl.dconv.P;
+    gt.out_f32 = sat<float>(sb, sc.tpart);
+    DConvParams dp{};
+    dconv_base(dp, l, k);
+    dp.x = sb + sc.xn;
+    dp.t = gt.out_f32;
+    dp.ldt = r;
+    dp.plane = (long long)M * r;
+    dp.n_part = pl.dconv.P;
+    dp.out = sb + sc.xa;
+    dp.ldo = d;
+    dp.out_packed = out_packed;
+    ProfScope ps(h, DFLASH_KERNEL_CONV, s);
+    launch_gemm(c.dtype, EPI_PARTIAL, pl.dconv, gt, s);
+    launch_dconv(c.dtype, dp, s);
+  };
+  auto set_otaps = [&](NormParams& np, const float* part, int n_part) {
+    np.otaps = otaps;
+    np.part = part;
+    np.n_part = n_part;
+    np.ldp = dn;
+    np.embed = h->w.embed;
+    np.last_token = last_token;
+    np.B = B;
+    np.vocab = c.vocab;
+    np.err = at<unsigned int>(h, h->lay.err);
+  };
 
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& lw = h->w.layers[l];
@@ -1092,7 +1202,10 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
       n1.init_row = wptr(h->w.embed, (size_t)c.mask_token_id * d, e);
     } else if (c.conv2) {  // previous layer's down output through its conv, into the other buffer
       n1.x_in = hbuf;
-      set_oconv(n1, l - 1, 3, dpart, pl.down.P);
+      if (r)
+        set_otaps(n1, dpart, pl.down.P);
+      else
+        set_oconv(n1, l - 1, 3, dpart, pl.down.P);
       n1.x_out = halt;
       std::swap(hbuf, halt);
     } else {
@@ -1100,20 +1213,21 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
       n1.part = dpart;
       n1.n_part = pl.down.P;
     }
-    if (c.conv2) set_conv(n1, l, 0);
+    if (c.conv2 && !r) set_conv(n1, l, 0);
     n1.ldx = d;
     n1.gamma = lw.attn_norm;
     n1.eps = c.rms_eps;
-    n1.out = sb + sc.xa;
+    n1.out = sb + (r ? sc.xn : sc.xa);
     n1.ldo = d;
-    n1.out_packed = pl.qkv.mt == 0;  // the tiled QKV product reads fragment order
+    n1.out_packed = !r && pl.qkv.mt == 0;  // the tiled QKV product reads fragment order
     n1.d = d;
     n1.M = M;
     n1.dbg = debug_hidden ? debug_hidden + (size_t)l * M * d : nullptr;
     norm(n1);
+    if (r) dyn_in(l, 0, pl.qkv.mt == 0);
 
     GemmParams g = gemm_in(sb + sc.xa, d);
-    g.a_packed = n1.out_packed;
+    g.a_packed = pl.qkv.mt == 0;  // written so by the norm, or by the dynamic conv
     set_weights(h, g, 0, h->pk.wqkv[l], qkvw, d);
     g.N = qkvw;
     g.P = pl.qkv.P;
@@ -1188,18 +1302,23 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
 
     GemmParams go = gemm_in(sb + sc.xo, qd);
     go.a_packed = ap.out_packed;
-    set_weights(h, go, 0, h->pk.wo[l], d, qd);
-    go.tiles = tiles_of(d);
-    go.N = d;
+    set_weights(h, go, 0, h->pk.wo[l], dn, qd);
+    go.tiles = tiles_of(dn);
+    go.N = dn;
     go.P = pl.o.P;
     go.out_f32 = opart;
     { ProfScope ps(h, DFLASH_KERNEL_O_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.o, go, s); }
+    if (r) dyn_taps(l, 1, opart, pl.o.P);
 
     NormParams n2{};
     n2.x_in = hbuf;
     if (c.conv2) {  // O output through its conv, into the other buffer
-      set_oconv(n2, l, 1, opart, pl.o.P);
-      set_conv(n2, l, 2);
+      if (r) {
+        set_otaps(n2, opart, pl.o.P);
+      } else {
+        set_oconv(n2, l, 1, opart, pl.o.P);
+        set_conv(n2, l, 2);
+      }
       n2.x_out = halt;
       std::swap(hbuf, halt);
     } else {
@@ -1210,24 +1329,26 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     n2.ldx = d;
     n2.gamma = lw.mlp_norm;
     n2.eps = c.rms_eps;
-    n2.out = sb + sc.xa;
+    n2.out = sb + (r ? sc.xn : sc.xa);
     n2.ldo = d;
-    n2.out_packed = pl.gateup.mt == 0;
+    n2.out_packed = !r && pl.gateup.mt == 0;
     n2.d = d;
     n2.M = M;
     norm(n2);
+    if (r) dyn_in(l, 2, pl.gateup.mt == 0);
 
     const int z_packed = pl.gateup.mt == 0 && pl.down.mt == 0;  // z for a tiled down product
-    gateup_swiglu(h, s, sb, sc, pl, M, l, n2.out_packed, z_packed);
+    gateup_swiglu(h, s, sb, sc, pl, M, l, pl.gateup.mt == 0, z_packed);
 
     GemmParams gd = gemm_in(sb + sc.z, c.ffn);
     gd.a_packed = z_packed;
-    set_weights(h, gd, 0, h->pk.wdown[l], d, c.ffn);
-    gd.tiles = tiles_of(d);
-    gd.N = d;
+    set_weights(h, gd, 0, h->pk.wdown[l], dn, c.ffn);
+    gd.tiles = tiles_of(dn);
+    gd.N = dn;
     gd.P = pl.down.P;
     gd.out_f32 = dpart;
     { ProfScope ps(h, DFLASH_KERNEL_DOWN_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.down, gd, s); }
+    if (r && !hidden_in) dyn_taps(l, 3, dpart, pl.down.P);  // taken by the next norm (forced rows skip it)
     st = launched("draft layer");
     if (st) return st;
   }
@@ -1237,7 +1358,10 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
   if (hidden_in) {
     nf.x_in = hidden_in + (size_t)c.n_layers * M * d;  // teacher forcing
   } else if (c.conv2) {
-    set_oconv(nf, c.n_layers - 1, 3, dpart, pl.down.P);
+    if (r)
+      set_otaps(nf, dpart, pl.down.P);
+    else
+      set_oconv(nf, c.n_layers - 1, 3, dpart, pl.down.P);
   } else {
     nf.part = dpart;
     nf.n_part = pl.down.P;

@@ -49,6 +49,7 @@ def make_config(shape: dict, *, max_batch: int, max_pages: int, max_pages_per_re
     c.selector_rank = int(shape.get("selector_rank") or 0)
     c.target = int(shape.get("target") or 0)
     c.weight_bits = int(shape.get("weight_bits") or 16)
+    c.conv_rank = int(shape.get("conv_rank") or 0) if c.conv2 else 0
     return c
 
 
@@ -91,6 +92,8 @@ class Drafter:
             L.attn_norm = up(lw["attn_norm"])
             L.mlp_norm = up(lw["mlp_norm"])
             L.conv = up(lw["conv"]) if "conv" in lw else None
+            L.dconv_d = up(lw["dconv_d"]) if "dconv_d" in lw else None
+            L.dconv_u = up(lw["dconv_u"]) if "dconv_u" in lw else None
         if self.cfg.selector_rank:
             w.sel_u = up(weights["sel_u"])
             w.sel_v = up(weights["sel_v"])

@@ -119,6 +119,10 @@ typedef struct dflash_config {
                                 (q = round_half_even((w - b) / s) in fp32, 0 when s = 0);
                                 the draft computes with s * q + b.  bf16 drafts only; the
                                 shared embedding and LM head stay bf16 */
+  int32_t conv_rank;         /* conv2 only: 0 = static conv taps; r in {16, 32, 48, 64} = dynamic
+                                taps ([guide] 7): per row, the static taps plus U D x, x that row
+                                of the conv's input, D [r, d], U [2d, r] per conv point
+                                (storage-dtype weights only) */
 } dflash_config;
 
 /* Per-layer weights (device pointers, dtype of the config).
@@ -128,9 +132,14 @@ typedef struct dflash_config {
  *   wdown     [d, F]
  *   attn_norm [d], mlp_norm [d]     RMSNorm gains
  *   conv      [4][2][d] two-tap conv taps (w0, w1) at the four conv points, or
- *             NULL when conv2 == 0 */
+ *             NULL when conv2 == 0
+ *   dconv_d   [4][r][d] dynamic taps: the rank-r projection of the conv input
+ *             at each point (before attention, after it, before the MLP, after
+ *             it), or NULL when conv_rank == 0
+ *   dconv_u   [4][2d][r] dynamic taps: rows 0..d-1 add to w0, rows d..2d-1 to w1 */
 typedef struct dflash_layer_weights {
   const void *wqkv, *wo, *wgateup, *wdown, *attn_norm, *mlp_norm, *conv;
+  const void *dconv_d, *dconv_u;
 } dflash_layer_weights;
 
 /* Model weights (device pointers).

@@ -10,7 +10,12 @@ through 5-8 layers.  Measured worst ratios on an MI355X: 2.2e-2 for lock-step
 logits at the small shapes, 6.1e-3 for the full-size K/V and forced checks,
 4.4e-2 for the full-size free-running forwards (coder_b64, 8 layers); the
 conftest prints them per test.  A single wrong column or a dropped term
-still shows up there when the row norm hides it.  Integer outputs are
+still shows up there when the row norm hides it.  Free-running forwards with
+dynamic conv taps take FREE_ELEM_TOL_DYN = 9e-2: their taps are formed from
+the conv inputs themselves (t sums d perturbed inputs), so each layer's
+rounding differences also move the next taps, and the free-running divergence
+at full size grows about twice as fast (worst row error 1.5e-2 against 7.9e-3
+with static taps; worst element ratio 6.2e-2).  Integer outputs are
 compared exactly; a draft position is exempt when the oracle's top-1 / top-2
 logit margin is below 1e-2 (a near tie that fp32 rounding may flip).
 """
@@ -23,6 +28,7 @@ import numpy as np
 TOL = 2e-2
 ELEM_TOL = 3e-2
 FREE_ELEM_TOL = 6e-2
+FREE_ELEM_TOL_DYN = 9e-2
 MARGIN = 1e-2
 
 # Worst ratios seen by assert_rows_close in the running test (conftest prints

@@ -81,6 +81,7 @@ def test_every_workload_config_is_valid(name):
     ("dtype", 7), ("mask_token_id", 3001), ("page_size", 32), ("window", 100), ("topk", 8),
     ("max_batch", 0), ("max_batch", 257), ("max_pages", 0), ("max_position", 3),
     ("max_inject_rows", 0), ("conv2", 2), ("weight_bits", 8), ("weight_bits", 0),
+    ("conv_rank", 16), ("conv_rank", 8),
 ])
 def test_invalid_configs_are_rejected(field, value):
     cfg = _cfg()

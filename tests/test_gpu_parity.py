@@ -199,7 +199,7 @@ def _check_topk(ids, vals, g_logits, ref_logits, g_draft):
 
 
 @pytest.mark.parametrize("name", ["small_bf16", "small_block10", "small_dh64", "small_batch", "small_window",
-                                  "small_conv", "small_q4"])
+                                  "small_conv", "small_q4", "small_dconv"])
 def test_draft_parity_lockstep(name):
     _lockstep(name)
 
@@ -225,8 +225,14 @@ def test_draft_parity_lockstep(name):
     ("small_q4", {"batch": 1}),
     ("small_q4", {"batch": 5}),
     ("small_q4", {"conv2": 1, "topk": 16, "window": 128}),
+    # dynamic conv taps: 16 rows, and 80 rows (tiled products: the taps' rows
+    # appended to W_o and W_down in the tiled kernel, the conv applied into
+    # fragment order)
+    ("small_dconv", {"batch": 1}),
+    ("small_dconv", {"batch": 5, "ctx": None, "ctx_range": (60, 300)}),
 ], ids=["block1", "batch5_block1", "rows64", "conv_rows48", "block10_rows70", "rows64_vocab4", "conv_rows48_vocab4",
-        "conv_rows80_topk_tiled", "batch32_merge_splits", "q4_rows16", "q4_rows80", "q4_conv_topk_window"])
+        "conv_rows80_topk_tiled", "batch32_merge_splits", "q4_rows16", "q4_rows80", "q4_conv_topk_window",
+        "dconv_rows16", "dconv_rows80"])
 def test_draft_parity_lockstep_shapes(name, over):
     if over.get("batch") == 32:
         # premise: every request has several splits (target 256 / (32 * 2) = 4)
