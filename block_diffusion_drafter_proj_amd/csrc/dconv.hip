@@ -6,13 +6,13 @@
 // function of that row of the conv's input: t = D x (r values), then
 // a = w0 + U_a t and b = w1 + U_b t per channel.
 //
-//  * k_dconv: one workgroup per (256 channels, row); t is summed from the
+//  * k_dconv: one workgroup per (64 channels, 16 rows); t is summed from the
 //    split-K partials of the product that formed it (the D product of the
 //    stored normed rows before attention and the MLP; rows appended to W_o
-//    and W_down after them) into LDS, then each thread forms its channel's
-//    two taps from its rows of U (16-byte loads) and either applies them to
-//    the stored input rows (writing the next GEMM's input) or writes them for
-//    the norm that adds the conv'd projection output into the residual.
+//    and W_down after them) into LDS, the rank-r parts of the taps are formed
+//    on the matrix cores, and each lane either applies its taps to the stored
+//    input rows (writing the next GEMM's input) or writes them for the norm
+//    that adds the conv'd projection output into the residual.
 //  * k_fold: once per handle, D W for the output convs (their input is the
 //    projection's output W o, so D (W o) = (D W) o joins the projection as
 //    extra output rows); fp32 sums over 64-wide chunks of D staged in LDS,
@@ -25,60 +25,122 @@ namespace dflash {
 
 namespace {
 
-template <typename T> struct Pack8;
-template <> struct Pack8<bf16> { typedef bf16x8 type; };
-template <> struct Pack8<float> { typedef f32x8 type; };
-
+// One workgroup of 4 waves per (64 channels, 16 rows); wave w takes 16
+// channels.  The taps' rank-r parts U_a t and U_b t of the 16 rows are two
+// 16 x 16 products over r (r = 32 or 64: one or two 32-wide k-steps) on the
+// matrix cores: U's rows are the A operand (16-byte loads of a channel's r
+// values), t the B operand from LDS (fp32; in bf16 as an exact-to-16-bits
+// hi + lo pair, two MFMAs).  A lane then holds one row and four consecutive
+// channels of each product.
+constexpr int kDcRows = 16, kDcChan = 64, kDcMaxPart = 16;
 template <typename T>
 __global__ __launch_bounds__(256) void k_dconv(DConvParams p) {
-  __shared__ float ts[64];
-  const int row = blockIdx.y;
-  const int t = threadIdx.x;
-  const int c = blockIdx.x * 256 + t;
-  if (t < p.r) {
-    const float* tp = p.t + (long long)row * p.ldt + t;
-    float v = 0.f;
-    for (int q = 0; q < p.n_part; ++q) v += tp[q * p.plane];
-    if (p.lo_off)  // the folded form's low part (a second set of r columns)
-      for (int q = 0; q < p.n_part; ++q) v += tp[q * p.plane + p.lo_off];
-    ts[t] = v;
+  typedef typename Frag8<T>::type Frag;
+  __shared__ float ts[kDcRows][64 + 4];
+  const int row0 = blockIdx.y * kDcRows;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int nk = p.r / 32;  // k-steps (1 or 2)
+  // U rows of this wave's 16 channels (A operand), requested first
+  const int cw = blockIdx.x * kDcChan + wave * 16;  // first channel of the wave
+  const int ca = min(cw + l16, p.d - 1);
+  const T* U = reinterpret_cast<const T*>(p.U);
+  Frag fa[2], fb[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int ss = min(s, nk - 1);
+    fa[s] = load8<T>(U + (long long)ca * p.r + 32 * ss + 8 * g4);
+    fb[s] = load8<T>(U + (long long)(p.d + ca) * p.r + 32 * ss + 8 * g4);
+  }
+  // this lane's outputs: row row0 + l16, channels c .. c+3; their static taps
+  // and input rows are requested now too, so the kernel waits for memory once
+  const int orow = row0 + l16;
+  const int oc = cw + 4 * g4;
+  const int crow = min(orow, p.M - 1);
+  const T* w = reinterpret_cast<const T*>(p.w);
+  float w0[4], w1[4], xv[4], xpv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w0[i] = to_f(w[oc + i]);
+    w1[i] = to_f(w[p.d + oc + i]);
+  }
+  if (p.x) {
+    const T* X = reinterpret_cast<const T*>(p.x);
+    const T* xr = X + (long long)crow * p.d + oc;
+    const T* xpr;
+    if (crow % p.B == 0) {
+      int tok = p.last_token[crow / p.B];
+      if (tok < 0 || tok >= p.vocab) {
+        if (orow < p.M) atomicOr(p.err, 1u);
+        tok = 0;
+      }
+      xpr = reinterpret_cast<const T*>(p.embed) + (long long)tok * p.d + oc;
+    } else {
+      xpr = xr - p.d;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xv[i] = to_f(xr[i]);
+      xpv[i] = to_f(xpr[i]);
+    }
+  }
+  // t of the block's rows, summed over the splits (and the low part): thread
+  // (row, 4 consecutive j) reads 16 bytes per split; every load uses a clamped,
+  // valid index and a select, so all are in flight together
+  {
+    const int n4 = p.r / 4;
+    const int rr = min(t / n4, kDcRows - 1), j = (t - (t / n4) * n4) * 4;
+    const int row = min(row0 + rr, p.M - 1);
+    const int nlo = p.lo_off ? 2 : 1;
+    const float* tp = p.t + (long long)row * p.ldt + j;
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int q = 0; q < kDcMaxPart; ++q) {
+        const f32x4 x =
+            *reinterpret_cast<const f32x4*>(tp + (long long)min(q, p.n_part - 1) * p.plane + min(h, nlo - 1) * p.lo_off);
+        if (q < p.n_part && h < nlo) v += x;
+      }
+    if (t < kDcRows * n4) {
+      const bool live = row0 + t / n4 < p.M;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ts[t / n4][j + e] = live ? v[e] : 0.f;
+    }
   }
   __syncthreads();
-  if (c >= p.d) return;
-  const T* U = reinterpret_cast<const T*>(p.U);
-  const T* ua = U + (long long)c * p.r;
-  const T* ub = U + (long long)(p.d + c) * p.r;
-  const T* w = reinterpret_cast<const T*>(p.w);
-  float a = to_f(w[c]), b = to_f(w[p.d + c]);
-  for (int j = 0; j < p.r; j += 8) {
-    const typename Pack8<T>::type va = *reinterpret_cast<const typename Pack8<T>::type*>(ua + j);
-    const typename Pack8<T>::type vb = *reinterpret_cast<const typename Pack8<T>::type*>(ub + j);
+  // C[channel][row] = sum_j U[channel][j] t[row][j]
+  f32x4 acc_a = f32x4{0.f, 0.f, 0.f, 0.f}, acc_b = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nk; ++s) {
+    const float* tr = &ts[l16][32 * s + 8 * g4];
+    Frag th, tl;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      a += to_f(va[e]) * ts[j + e];
-      b += to_f(vb[e]) * ts[j + e];
+      th[e] = from_f<T>(tr[e]);
+      tl[e] = from_f<T>(tr[e] - to_f(th[e]));
     }
+    acc_a = mfma_step(fa[s], th, acc_a);
+    acc_b = mfma_step(fb[s], th, acc_b);
+    if (sizeof(T) == 2) {
+      acc_a = mfma_step(fa[s], tl, acc_a);
+      acc_b = mfma_step(fb[s], tl, acc_b);
+    }
+  }
+  if (orow >= p.M) return;
+  f32x4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = w0[i] + acc_a[i];
+    b[i] = w1[i] + acc_b[i];
   }
   if (!p.x) {
-    p.taps[(long long)row * 2 * p.d + c] = a;
-    p.taps[(long long)row * 2 * p.d + p.d + c] = b;
+    *reinterpret_cast<f32x4*>(p.taps + (long long)orow * 2 * p.d + oc) = a;
+    *reinterpret_cast<f32x4*>(p.taps + (long long)orow * 2 * p.d + p.d + oc) = b;
     return;
   }
-  const T* X = reinterpret_cast<const T*>(p.x);
-  const float x = to_f(X[(long long)row * p.d + c]);
-  float xp;
-  if (row % p.B == 0) {
-    int tok = p.last_token[row / p.B];
-    if (tok < 0 || tok >= p.vocab) {
-      if (t == 0) atomicOr(p.err, 1u);
-      tok = 0;
-    }
-    xp = to_f(reinterpret_cast<const T*>(p.embed)[(long long)tok * p.d + c]);
-  } else {
-    xp = to_f(X[(long long)(row - 1) * p.d + c]);
-  }
-  const long long oi = p.out_packed ? frag_index(row, c, p.d) : (long long)row * p.ldo + c;
-  reinterpret_cast<T*>(p.out)[oi] = from_f<T>(a * x + b * xp);
+  T* out = reinterpret_cast<T*>(p.out) + (p.out_packed ? frag_index(orow, oc, p.d) : (long long)orow * p.ldo + oc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = from_f<T>(a[i] * xv[i] + b[i] * xpv[i]);
 }
 
 template <typename T>
@@ -116,8 +178,8 @@ __global__ __launch_bounds__(256) void k_fold(const T* D, const T* W, T* out, in
 }  // namespace
 
 void launch_dconv(int dtype, const DConvParams& p, hipStream_t s) {
-  if (p.M <= 0) return;
-  const dim3 grid((p.d + 255) / 256, p.M);
+  if (p.M <= 0 || p.n_part < 1 || p.n_part > kDcMaxPart) return;  // the host checks the split count
+  const dim3 grid((p.d + kDcChan - 1) / kDcChan, (p.M + kDcRows - 1) / kDcRows);
   if (dtype == DFLASH_BF16)
     hipLaunchKernelGGL(k_dconv<bf16>, grid, dim3(256), 0, s, p);
   else

@@ -383,8 +383,7 @@ dflash_status validate(const dflash_config* c) {
   if (c->weight_bits != 16 && c->weight_bits != 4) return bad("weight_bits must be 16 or 4");
   if (c->weight_bits == 4 && (c->dtype != DFLASH_BF16 || c->target))
     return bad("4-bit weights need a bf16 draft (not a target)");
-  if (c->conv_rank != 0 && c->conv_rank != 16 && c->conv_rank != 32 && c->conv_rank != 48 && c->conv_rank != 64)
-    return bad("conv_rank must be 0, 16, 32, 48 or 64");
+  if (c->conv_rank != 0 && c->conv_rank != 32 && c->conv_rank != 64) return bad("conv_rank must be 0, 32 or 64");
   if (c->conv_rank && (!c->conv2 || c->weight_bits != 16))
     return bad("dynamic conv taps need conv2 and storage-dtype weights");
   if (c->target) {
@@ -1131,6 +1130,8 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
   const int r = c.conv2 ? c.conv_rank : 0;
   const int dn = out_width(c);
   float* otaps = r ? sat<float>(sb, sc.otaps) : nullptr;
+  if (r && (pl.o.P > 16 || pl.down.P > 16 || pl.dconv.P > 16))  // the taps kernel sums at most 16 splits
+    return fail(DFLASH_E_UNSUPPORTED, "dynamic conv taps with more than 16 split-K planes");
   auto dconv_base = [&](DConvParams& dp, int l, int k) {
     dp.U = wptr(h->w.layers[l].dconv_u, (size_t)k * 2 * d * r, e);
     dp.w = conv_taps(l, k);

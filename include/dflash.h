@@ -119,7 +119,7 @@ typedef struct dflash_config {
                                 (q = round_half_even((w - b) / s) in fp32, 0 when s = 0);
                                 the draft computes with s * q + b.  bf16 drafts only; the
                                 shared embedding and LM head stay bf16 */
-  int32_t conv_rank;         /* conv2 only: 0 = static conv taps; r in {16, 32, 48, 64} = dynamic
+  int32_t conv_rank;         /* conv2 only: 0 = static conv taps; r in {32, 64} = dynamic
                                 taps ([guide] 7): per row, the static taps plus U D x, x that row
                                 of the conv's input, D [r, d], U [2d, r] per conv point
                                 (storage-dtype weights only) */
