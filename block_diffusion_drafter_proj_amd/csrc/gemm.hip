@@ -100,7 +100,10 @@ __global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(Gemm
 
   const int NW = blockDim.x >> 6;
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform (scalar) so that the kernel-argument pointer arrays indexed
+  // by the wave's k range are read with scalar loads, not a vector load and
+  // a full wait at kernel start
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const int GP = gridDim.x / p.P;
@@ -172,10 +175,45 @@ __global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(Gemm
     }
   };
 
+  // EPI_RESID: the residual values and gains of the first unit's elements,
+  // requested before the weights
+  constexpr int EIT0 = (FEW ? 4 : 1) * MT;
+  // (clamped addresses; the gains stay in the storage dtype until the
+  // epilogue, so nothing waits for them here)
+  float pre_x[EPI == EPI_RESID ? EIT0 : 1];
+  T pre_g[EPI == EPI_RESID ? EIT0 : 1];
+  if (EPI == EPI_RESID) {
+#pragma unroll
+    for (int it = 0; it < EIT0; ++it) {
+      const int e = threadIdx.x + it * (int)blockDim.x;
+      const int em = min(m_base + (e >> 8) * 16 + ((e >> 4) & 15), p.M - 1);
+      const int n = min(bl * 16 + (e & 15), p.N - 1);
+      pre_x[it] = p.resid[(long long)em * p.ldr + n];
+      pre_g[it] = reinterpret_cast<const T*>(p.gain)[n];
+    }
+  }
+
   Ring wb[NBUF];
 #pragma unroll
   for (int b = 0; b < NBUF; ++b)
     if (b < n_sub) load_tile(b, wb[b]);
+
+  // EPI_SWIGLU after a residual epilogue: wave w sums the per-tile squares of
+  // block row w.  The loads follow the weight ring's (issued before it, the
+  // sum would hold the ring back until they arrive); each has a clamped, valid
+  // address and its value is selected afterwards.
+  constexpr int kSsqMax = 8;  // tiles per lane: hidden sizes up to 64 * 8 * 16
+  float ssv[EPI == EPI_SWIGLU ? kSsqMax : 1];
+  if (EPI == EPI_SWIGLU && p.ssq) {
+    const int m = m_base + wave;
+    const long long mc = min(m, p.M - 1);
+#pragma unroll
+    for (int i = 0; i < kSsqMax; ++i) {
+      const int t2 = lane + 64 * i;
+      const float x = p.ssq[mc * p.ssq_tiles + min(t2, p.ssq_tiles - 1)];  // a row's tiles are contiguous
+      ssv[i] = wave < 16 * MT && m < p.M && t2 < p.ssq_tiles ? x : 0.f;
+    }
+  }
 
   // epilogue: element e = t + it * blockDim of the 16 x 16 tile (per m-tile);
   // workgroups with fewer than 4 waves (FEW) take several elements per thread,
@@ -201,6 +239,27 @@ __global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(Gemm
       const int e = t + it * (int)blockDim.x;
       const int em = m_base + (e >> 8) * 16 + ((e >> 4) & 15);
       if (e < 256 * MT && em < p.M) rope_n[it] = p.rope.state[p.rope.slots[em / p.rope.B]].ctx_len + 1;
+    }
+  }
+
+  // EPI_SWIGLU after a residual epilogue: 1/rms of each row of the block from
+  // the producer's per-tile sums of squares (tiles in order per lane, then the
+  // wave's lanes by a butterfly), formed while the weights stream
+  __shared__ float rs_inv[EPI == EPI_SWIGLU ? 16 * MT : 1];
+  if (EPI == EPI_SWIGLU && p.ssq) {
+    // row `wave` from the loads above; with fewer waves than rows, the other
+    // rows' squares are read here (the same order of additions)
+    for (int rr = wave; rr < 16 * MT; rr += NW) {
+      float acc = 0.f;
+      if (rr == wave) {
+#pragma unroll
+        for (int i = 0; i < kSsqMax; ++i) acc += ssv[i];
+      } else if (m_base + rr < p.M) {
+        for (int t2 = lane; t2 < p.ssq_tiles; t2 += 64) acc += p.ssq[(long long)(m_base + rr) * p.ssq_tiles + t2];
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      if (lane == 0) rs_inv[rr] = 1.0f / sqrtf(acc / (float)p.ssq_d + p.eps);
     }
   }
 
@@ -264,8 +323,22 @@ __global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(Gemm
           if (EPI == EPI_PARTIAL) {
             if (ok) p.out_f32[((long long)pidx * p.M + em) * p.N + n] = v;
           } else if (EPI == EPI_RESID) {
-            if (ok) p.resid[(long long)em * p.ldr + n] += v;
+            float x = 0.f;
+            if (ok) {
+              float* rp = p.resid + (long long)em * p.ldr + n;
+              x = (u == 0 ? pre_x[it] : *rp) + v;
+              *rp = x;
+              const float gn = to_f(u == 0 ? pre_g[it] : reinterpret_cast<const T*>(p.gain)[n]);
+              reinterpret_cast<T*>(p.out_t)[(long long)em * p.ldt + n] = from_f<T>(x * gn);
+            }
+            // the 16 columns of row em sit in 16 adjacent lanes (every lane of
+            // the first 256 * MT threads takes part)
+            float sq = x * x;
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
+            if (ecol == 0 && em < p.M) p.ssq[(long long)em * p.ssq_tiles + tile] = sq;
           } else if (EPI == EPI_SWIGLU) {
+            if (p.ssq) v *= rs_inv[emt * 16 + ((e >> 4) & 15)];
             if (!(sub & 1)) {
               gate_v[it] = v;
             } else if (ok) {
@@ -460,7 +533,7 @@ void launch_w(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
 
 template <typename T, int EPI>
 void launch_t(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
-  if constexpr (sizeof(T) == 2 && (EPI == EPI_PARTIAL || EPI == EPI_SWIGLU || EPI == EPI_ROPE)) {
+  if constexpr (sizeof(T) == 2 && (EPI == EPI_PARTIAL || EPI == EPI_RESID || EPI == EPI_SWIGLU || EPI == EPI_ROPE)) {
     if (p.w4) {
       launch_w<T, EPI, true>(pl, p, s);
       return;

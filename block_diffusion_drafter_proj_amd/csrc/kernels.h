@@ -53,8 +53,19 @@ struct GemmParams {
   float* out_f32;   // EPI_PARTIAL
   void* out_t;      // EPI_SWIGLU (storage dtype)
   int ldt;
-  float* resid;  // EPI_RESID
+  // EPI_RESID (one split): resid[m][n] += y; out_t[m][n] (row stride ldt) =
+  // the new residual times gain[n] in the storage dtype, and
+  // ssq[m][tile] (ssq_tiles per row) = the sum of squares of the tile's 16 new
+  // residual values of row m, so the next product can apply the RMSNorm's
+  // 1/rms to its own output
+  float* resid;
   int ldr;
+  const void* gain;
+  float* ssq;
+  // EPI_SWIGLU: when ssq is set, each row's gate and up values are scaled by
+  // 1 / sqrt(sum over ssq_tiles tiles of ssq / ssq_d + eps) before the SwiGLU
+  int ssq_tiles, ssq_d;
+  float eps;
   unsigned long long* keys;  // EPI_ARGMAX: one per row; EPI_TOPK: [M][gridDim.x][16] sorted lists
   float* dbg;                // EPI_ARGMAX / EPI_TOPK, optional fp32 logits
   int ld_dbg;

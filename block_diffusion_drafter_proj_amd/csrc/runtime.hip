@@ -204,6 +204,7 @@ struct Scratch {
   size_t tq;         // target: q of the new rows [M][Hq*dh]
   size_t gpart;      // split-K partials of the gate/up product (17..63 rows)
   size_t xn, tpart, otaps;  // dynamic conv taps
+  size_t ssq;               // per 16-column tile sums of squares of the residual rows [M][d/16]
   size_t u, f, kvo;  // inject only (0 when not laid out)
   size_t total;
 };
@@ -233,6 +234,7 @@ Scratch make_scratch(const dflash_config& c, int n_req, bool inject) {
   // the conv variant alternates the residual stream between two buffers (a
   // norm re-reads the previous row of its input while writing its output)
   S.h2 = c.conv2 ? take(sizeof(float) * M * c.hidden) : 0;
+  S.ssq = take(sizeof(float) * M * (size_t)tiles_of(c.hidden));
   S.srow = c.topk ? take(sizeof(float) * (size_t)n_req * (c.block_size + 1) * kSampleRowFloats) : 0;
   S.schunk = c.topk ? take((2 * sizeof(float) + 64 * sizeof(unsigned long long)) * (size_t)n_req *
                            (c.block_size + 1) * kRowChunks)
@@ -891,8 +893,10 @@ dflash_status dflash_inject_context(dflash_handle* h, void* stream, int32_t n_re
 // xa_packed) into z = silu(gate) * up (fragment order when z_packed): the
 // skinny or tiled kernel's SwiGLU epilogue, or from 17 to 63 rows one split-K
 // product of all 2F columns and the SwiGLU over its partials.
+// ssq: the rows in xa are the residual times the MLP gain, not yet scaled by
+// 1/rms; the product applies it from these per-tile sums of squares.
 static void gateup_swiglu(dflash_handle* h, hipStream_t s, char* sb, const Scratch& sc, const Plans& pl, int M,
-                          int l, int xa_packed, int z_packed) {
+                          int l, int xa_packed, int z_packed, const float* ssq = nullptr) {
   const dflash_config& c = h->cfg;
   GemmParams gu{};
   gu.a[0] = sb + sc.xa;
@@ -921,6 +925,10 @@ static void gateup_swiglu(dflash_handle* h, hipStream_t s, char* sb, const Scrat
   gu.P = 1;
   gu.out_t = sb + sc.z;
   gu.ldt = c.ffn;
+  gu.ssq = const_cast<float*>(ssq);
+  gu.ssq_tiles = tiles_of(c.hidden);
+  gu.ssq_d = c.hidden;
+  gu.eps = c.rms_eps;
   launch_gemm(c.dtype, EPI_SWIGLU, pl.gateup, gu, s);
 }
 
@@ -1191,6 +1199,14 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     np.err = at<unsigned int>(h, h->lay.err);
   };
 
+  // One-block plans with an unsplit O product (batch 1, no conv): the O
+  // epilogue adds into the residual and leaves the gained MLP input with its
+  // sums of squares; the gate/up product scales its rows by 1/rms (the
+  // RMSNorm's operations, with the scale applied after the product), so no
+  // norm launch sits between them.
+  const bool resid_o = !c.conv2 && pl.o.mt == 1 && pl.o.P == 1 && pl.gateup.mt == 1 && M <= 16 && d <= 8192;
+  float* ssq = sat<float>(sb, sc.ssq);
+
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& lw = h->w.layers[l];
     // residual: block init (layer 0) or h + previous layer's down-projection
@@ -1308,7 +1324,20 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     go.N = dn;
     go.P = pl.o.P;
     go.out_f32 = opart;
-    { ProfScope ps(h, DFLASH_KERNEL_O_GEMM, s); launch_gemm(c.dtype, EPI_PARTIAL, pl.o, go, s); }
+    if (resid_o) {  // residual, gained MLP input and its sums of squares from the O epilogue
+      go.resid = hbuf;
+      go.ldr = d;
+      go.gain = lw.mlp_norm;
+      go.out_t = sb + sc.xa;
+      go.ldt = d;
+      go.ssq = ssq;
+      go.ssq_tiles = tiles_of(d);
+      { ProfScope ps(h, DFLASH_KERNEL_O_GEMM, s); launch_gemm(c.dtype, EPI_RESID, pl.o, go, s); }
+      gateup_swiglu(h, s, sb, sc, pl, M, l, 0, 0, ssq);
+    } else {
+      ProfScope ps(h, DFLASH_KERNEL_O_GEMM, s);
+      launch_gemm(c.dtype, EPI_PARTIAL, pl.o, go, s);
+    }
     if (r) dyn_taps(l, 1, opart, pl.o.P);
 
     NormParams n2{};
@@ -1335,11 +1364,12 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     n2.out_packed = !r && pl.gateup.mt == 0;
     n2.d = d;
     n2.M = M;
-    norm(n2);
-    if (r) dyn_in(l, 2, pl.gateup.mt == 0);
-
     const int z_packed = pl.gateup.mt == 0 && pl.down.mt == 0;  // z for a tiled down product
-    gateup_swiglu(h, s, sb, sc, pl, M, l, pl.gateup.mt == 0, z_packed);
+    if (!resid_o) {
+      norm(n2);
+      if (r) dyn_in(l, 2, pl.gateup.mt == 0);
+      gateup_swiglu(h, s, sb, sc, pl, M, l, pl.gateup.mt == 0, z_packed);
+    }
 
     GemmParams gd = gemm_in(sb + sc.z, c.ffn);
     gd.a_packed = z_packed;
