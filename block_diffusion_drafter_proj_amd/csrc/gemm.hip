@@ -188,7 +188,7 @@ __global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(Gemm
       const int e = threadIdx.x + it * (int)blockDim.x;
       const int em = min(m_base + (e >> 8) * 16 + ((e >> 4) & 15), p.M - 1);
       const int n = min(bl * 16 + (e & 15), p.N - 1);
-      pre_x[it] = p.resid[(long long)em * p.ldr + n];
+      pre_x[it] = p.resid_row ? to_f(reinterpret_cast<const T*>(p.resid_row)[n]) : p.resid[(long long)em * p.ldr + n];
       pre_g[it] = reinterpret_cast<const T*>(p.gain)[n];
     }
   }
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(Gemm
             float x = 0.f;
             if (ok) {
               float* rp = p.resid + (long long)em * p.ldr + n;
-              x = (u == 0 ? pre_x[it] : *rp) + v;
+              x = (u == 0 ? pre_x[it] : p.resid_row ? to_f(reinterpret_cast<const T*>(p.resid_row)[n]) : *rp) + v;
               *rp = x;
               const float gn = to_f(u == 0 ? pre_g[it] : reinterpret_cast<const T*>(p.gain)[n]);
               reinterpret_cast<T*>(p.out_t)[(long long)em * p.ldt + n] = from_f<T>(x * gn);

@@ -60,6 +60,7 @@ struct GemmParams {
   // 1/rms to its own output
   float* resid;
   int ldr;
+  const void* resid_row;  // when set, every row's old residual is this storage-dtype row (the block init)
   const void* gain;
   float* ssq;
   // EPI_SWIGLU: when ssq is set, each row's gate and up values are scaled by

@@ -211,6 +211,7 @@ struct Scratch {
 
 struct Layout {
   size_t state, err, page_table, cos_t, sin_t, qb, blk;
+  size_t xa0;  // the block's layer-0 input row, RMSNorm(mask embedding) * g, formed once
   size_t scratch;  // offset of the scratch part in the workspace
   Scratch sc;
   size_t total;
@@ -307,6 +308,7 @@ Layout make_layout(const dflash_config& c) {
   L.sin_t = take(sizeof(float) * (size_t)c.max_position * (c.head_dim / 2));
   L.qb = take(e * (size_t)c.max_batch * c.n_q_heads * 16 * c.head_dim);
   L.blk = take(e * (size_t)c.max_batch * page_elems);
+  L.xa0 = take(e * (size_t)c.hidden);
   L.sc = make_scratch(c, c.max_batch, !c.target);
   L.scratch = take(L.sc.total);
   L.total = off;
@@ -542,6 +544,17 @@ dflash_status ensure_device(dflash_handle* h) {
   if (c.selector_rank)
     launch_sel_table(c.dtype, h->w.embed, h->w.sel_u, h->w.sel_v, reinterpret_cast<float*>(h->packed + h->pk.sel_u),
                      reinterpret_cast<float*>(h->packed + h->pk.sel_v), c.vocab, d, c.selector_rank, nullptr);
+  if (!c.target && !c.conv2) {  // every block row enters layer 0 as this row
+    NormParams np{};
+    np.init_row = wptr(h->w.embed, (size_t)c.mask_token_id * d, es);
+    np.gamma = h->w.layers[0].attn_norm;
+    np.eps = c.rms_eps;
+    np.out = h->ws + h->lay.xa0;
+    np.ldo = d;
+    np.d = d;
+    np.M = 1;
+    launch_rmsnorm(c.dtype, np, nullptr);
+  }
   if ((e = hipGetLastError())) return hip_fail(e, "weight packing");
   if ((e = hipDeviceSynchronize())) return hip_fail(e, "device init");
   h->dev_init = true;
@@ -1206,6 +1219,11 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
   // norm launch sits between them.
   const bool resid_o = !c.conv2 && pl.o.mt == 1 && pl.o.P == 1 && pl.gateup.mt == 1 && M <= 16 && d <= 8192;
   float* ssq = sat<float>(sb, sc.ssq);
+  // Layer 0 of a block without conv: every row is the mask embedding, so the
+  // QKV product reads the row formed once at set-up (row stride 0) and the
+  // first residual add starts from the embedding row; no norm launch.
+  const bool init0 = !c.conv2 && !hidden_in && !debug_hidden && pl.qkv.mt != 0;
+  const void* mask_row = wptr(h->w.embed, (size_t)c.mask_token_id * d, e);
 
   for (int l = 0; l < c.n_layers; ++l) {
     const dflash_layer_weights& lw = h->w.layers[l];
@@ -1240,10 +1258,12 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     n1.d = d;
     n1.M = M;
     n1.dbg = debug_hidden ? debug_hidden + (size_t)l * M * d : nullptr;
-    norm(n1);
+    const bool skip_n1 = init0 && l == 0;
+    if (!skip_n1) norm(n1);
     if (r) dyn_in(l, 0, pl.qkv.mt == 0);
 
-    GemmParams g = gemm_in(sb + sc.xa, d);
+    GemmParams g = gemm_in(skip_n1 ? h->ws + h->lay.xa0 : sb + sc.xa, d);
+    if (skip_n1) g.lda = 0;
     g.a_packed = pl.qkv.mt == 0;  // written so by the norm, or by the dynamic conv
     set_weights(h, g, 0, h->pk.wqkv[l], qkvw, d);
     g.N = qkvw;
@@ -1327,6 +1347,7 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
     if (resid_o) {  // residual, gained MLP input and its sums of squares from the O epilogue
       go.resid = hbuf;
       go.ldr = d;
+      go.resid_row = skip_n1 ? mask_row : nullptr;
       go.gain = lw.mlp_norm;
       go.out_t = sb + sc.xa;
       go.ldt = d;
@@ -1355,6 +1376,10 @@ static dflash_status draft_impl(dflash_handle* h, void* stream, int32_t n_req, c
       n2.part = opart;
       n2.n_part = pl.o.P;
       n2.x_out = hbuf;
+      if (skip_n1) {  // the residual so far is the block init
+        n2.x_in = nullptr;
+        n2.init_row = mask_row;
+      }
     }
     n2.ldx = d;
     n2.gamma = lw.mlp_norm;
