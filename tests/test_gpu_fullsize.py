@@ -72,6 +72,12 @@ def test_full_size_block(name):
     for l in range(L + 1):
         assert_rows_close(hs[l].cpu().numpy(), hr[l], what=f"free-running hidden {l}", elem_tol=FREE_ELEM_TOL)
     assert_rows_close(lg[0].cpu().numpy(), logits, what="free-running logits", elem_tol=FREE_ELEM_TOL)
+    # without the hidden-state copy (layer 0's input formed once at set-up, as
+    # in a timed run): the same logits bit for bit
+    lg_plain = torch.empty_like(lg)
+    dr.draft([0], debug_logits=lg_plain)
+    torch.cuda.synchronize()
+    assert np.array_equal(lg_plain.cpu().numpy(), lg.cpu().numpy())
     # per-layer teacher forcing: exact tokens
     hin = torch.from_numpy(np.stack(hr).astype(np.float32)).to(dev)
     draft = dr.draft([0], debug_logits=lg, debug_hidden=hs, hidden_in=hin)

@@ -156,6 +156,15 @@ def _draft_both(dev, shape, dr, o, states, slots, last_tokens=None, free=False):
     g_draft = draft.cpu().numpy()
     g_logits = dbg_logits.cpu().numpy()
     g_hidden = dbg_hidden.cpu().numpy().reshape(L + 1, n, B, d)
+    # the same call without the hidden-state copy takes the shortcuts that the
+    # copy turns off (layer 0's input formed once at set-up): bit for bit the
+    # same logits and drafts
+    lg2 = torch.empty_like(dbg_logits)
+    tk2 = (None, None) if tk_ids is None else (torch.empty_like(tk_ids), torch.empty_like(tk_val))
+    d2 = dr.draft(slots, lt, debug_logits=lg2, topk_ids=tk2[0], topk_logits=tk2[1])
+    torch.cuda.synchronize()
+    assert np.array_equal(d2.cpu().numpy(), g_draft), "drafts differ without the hidden-state copy"
+    assert np.array_equal(lg2.cpu().numpy(), g_logits), "logits differ without the hidden-state copy"
     ref_drafts = []
     exempt = 0
     for i, r in enumerate(slots):
