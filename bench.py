@@ -138,6 +138,36 @@ def class_work(shape, cls, M, visible):
     return None
 
 
+def library_gemm(shape, M, reps=20):
+    """The vendor library on the same products: torch.nn.functional.linear
+    (hipBLASLt / rocBLAS) of M random bf16 rows by each weight matrix of the
+    workload, timed with events (a reference point for the hand-written
+    kernels' rates, not part of the path)."""
+    import torch
+    d, hq, hkv, dh, F, V = (shape[k] for k in ("hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "vocab"))
+    nk = {"qkv_gemm": ((hq + 2 * hkv) * dh, d), "o_gemm": (d, hq * dh), "gateup_gemm": (2 * F, d),
+          "down_gemm": (d, F), "lm_head": (V, d)}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    out = {}
+    for cls, (N, K) in nk.items():
+        x = torch.randn((M, K), generator=g, device="cuda", dtype=torch.bfloat16)
+        w = torch.randn((N, K), generator=g, device="cuda", dtype=torch.bfloat16) * 0.02
+        for _ in range(3):
+            torch.nn.functional.linear(x, w)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            torch.nn.functional.linear(x, w)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        out[cls] = {"ms": round(ms, 4), "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1),
+                    "GBps": round(2.0 * (N * K + M * K + M * N) / (ms * 1e-3) / 1e9, 1)}
+        del x, w
+    torch.cuda.empty_cache()
+    return out
+
+
 def file_sha(*paths):
     h = hashlib.sha256()
     for p in paths:
@@ -305,7 +335,7 @@ def main():
 SUMMARY_KEYS = ("value", "unit", "config", "dtype", "ms_per_step", "accepted_tok_per_s", "mean_accept",
                 "draft_ms", "draft_ms_percentiles", "draft_only_blocks_per_s", "draft_hbm_frac",
                 "gemm_mfma_frac", "gemm_tflops", "cycle_hbm_frac", "kernel_ms_per_draft", "roofline",
-                "memory_bytes", "shares_of_cycle", "sampled_verification", "speculative_cycle")
+                "memory_bytes", "shares_of_cycle", "sampled_verification", "speculative_cycle", "library_gemm")
 
 
 def run_workload(config, steps, warmup, cpu=False, target=False):
@@ -544,6 +574,9 @@ def run_workload(config, steps, warmup, cpu=False, target=False):
     result["draft_ms_percentiles"] = draft_pct
     result["gemm_tflops"] = {k: round(class_work(shape, k, M, visible0)[0] * launches[k] / (breakdown[k] * 1e-3) / 1e12, 1)
                              for k in GEMM_CLASSES if breakdown.get(k)}
+    if shape["dtype"] == "bf16" and shape.get("weight_bits", 16) == 16:
+        result["library_gemm"] = {"library": "torch.nn.functional.linear (hipBLASLt / rocBLAS), same shapes, "
+                                             "random bf16 operands", "rows": M, "products": library_gemm(shape, M)}
     weight_bytes = sum(t.numel() * t.element_size() for t in dr._keep)
     result["memory_bytes"] = {"weights": int(weight_bytes), "packed_weights": int(dr.packed.numel()),
                               "kv_pool": int(dr.kv_pool.numel()), "workspace": int(dr.workspace.numel()),
