@@ -165,13 +165,14 @@ __global__ __launch_bounds__(FEW ? 256 : (MT > 1 ? 512 : 1024)) void k_gemm(Gemm
       const u32x2* sb = reinterpret_cast<const u32x2*>(p.sb[seg]) + u * 16 + (lane & 15);
 #pragma unroll
       for (int i = 0; i < KS / 4; ++i) {
-        r.q[i] = q[i * 64];
-        r.sb[i] = sb[i * 16];
+        r.q[i] = __builtin_nontemporal_load(q + i * 64);
+        r.sb[i] = __builtin_nontemporal_load(sb + i * 16);
       }
     } else {
       const T* src = reinterpret_cast<const T*>(p.w[seg]) + ((long long)lt * S + s0) * kFragElems + lane * 8;
 #pragma unroll
-      for (int j = 0; j < KS; ++j) r.f[j] = load8<T>(src + j * kFragElems);
+      for (int j = 0; j < KS; ++j)
+        r.f[j] = __builtin_nontemporal_load(reinterpret_cast<const Frag*>(src + j * kFragElems));
     }
   };
 
