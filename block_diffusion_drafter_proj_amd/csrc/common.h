@@ -78,6 +78,10 @@ __device__ __forceinline__ long long frag_index(int m, int k, int K) {
 __device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
+// The same with the nontemporal hint (data read once: weights, context K/V).
+__device__ __forceinline__ void dma16_nt(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 2);
+}
 
 // At most N of this wave's vector-memory loads still outstanding and every
 // LDS access of this wave complete, then the workgroup barrier.  The asm

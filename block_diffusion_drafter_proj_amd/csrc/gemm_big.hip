@@ -147,7 +147,7 @@ void k_gemm_tile(GemmParams p) {
     for (int i = 0; i < LA; ++i) dma16(abase + a_off[i], dst + (wv * LA + i) * kFrag);
 #pragma unroll
     for (int i = 0; i < LB; ++i)
-      dma16(b_src[i] + (long long)kt * KF * kFrag + lane * 8, dst + (FA + wv * LB + i) * kFrag);
+      dma16_nt(b_src[i] + (long long)kt * KF * kFrag + lane * 8, dst + (FA + wv * LB + i) * kFrag);
   };
 
 
