@@ -165,7 +165,8 @@ void launch_fold(int dtype, const void* D, const void* W, void* out, int r, int 
 // 17..64 rows): one workgroup of 4 waves per (chunk of kSelChunk columns,
 // row) sums the planes in split order and leaves its best packed key
 // (atomic max into keys[row]) or one sorted top-16 list per wave
-// (lists[row][chunk * 4 + wave]).
+// (lists[row][chunk * 4 + wave]; a second kernel settles the few lists the
+// first one marks).
 constexpr int kSelChunk = 4096;
 struct LogitSelParams {
   const float* part;  // [n_part][M][N] fp32
@@ -175,6 +176,7 @@ struct LogitSelParams {
   unsigned long long* keys;   // argmax: one per row (zero on entry)
   unsigned long long* lists;  // top-16: [M][n_lists][16]
   int n_lists;                // 4 * chunks
+  int exact;                  // top-16: every list through the exact pass
 };
 inline int logit_sel_lists(int N) { return 4 * ((N + kSelChunk - 1) / kSelChunk); }
 void launch_logit_select(bool topk, const LogitSelParams& p, hipStream_t s);

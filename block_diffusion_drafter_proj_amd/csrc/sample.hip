@@ -104,34 +104,6 @@ __global__ __launch_bounds__(1024) void k_draft_sample(SampleParams p) {
   }
 }
 
-// 64 keys, one per lane, sorted descending (bitonic network over the wave).
-__device__ __forceinline__ unsigned long long sort64_desc(unsigned long long v, int lane) {
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const unsigned long long o = __shfl_xor(v, j, 64);
-      const bool desc = (lane & k) == 0;
-      const bool lower = (lane & j) == 0;
-      v = (lower == desc) ? key_max(v, o) : key_min(v, o);
-    }
-  }
-  return v;
-}
-
-// cur and nw are sorted descending over the 64 lanes; returns the 64 largest
-// of both, sorted descending (the reversed second list against the first is
-// bitonic, then a half-cleaner network).
-__device__ __forceinline__ unsigned long long merge64_desc(unsigned long long cur, unsigned long long nw, int lane) {
-  unsigned long long v = key_max(cur, __shfl(nw, 63 - lane, 64));
-#pragma unroll
-  for (int j = 32; j >= 1; j >>= 1) {
-    const unsigned long long o = __shfl_xor(v, j, 64);
-    v = ((lane & j) == 0) ? key_max(v, o) : key_min(v, o);
-  }
-  return v;
-}
-
 // Selection key of logit x at id i: larger logit first, then the lower id.
 __device__ __forceinline__ unsigned long long sel_key(float x, int i) {
   return ((unsigned long long)float_key(x) << 32) | (0xffffffffu - (unsigned)i);

@@ -9,6 +9,15 @@
 //             request: a ballot of mismatches, the first set bit is the
 //             accept length a; the cycle commits d[0..a) and the target's
 //             own token G[a], which becomes the next pending token.
+// k_logit_select  sums the split-K partial logits of 17..64 rows over one
+//             vocabulary chunk and keeps the row's argmax key or one sorted
+//             top-16 list per wave (a threshold from the lanes' maxima, then
+//             one sort of the few keys that pass);
+// k_topk_redo recomputes, by an exact bisection pass, the lists that the
+//             threshold pass could not settle;
+// k_topk_merge merges a row's lists into its top 16 and draft token.
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -50,51 +59,170 @@ __global__ __launch_bounds__(64) void k_verify(int B, int vocab, const int* draf
   }
 }
 
-// Sums the split-K partial logits of one row over one chunk of the
-// vocabulary (planes in split order, so the result does not depend on
-// scheduling).  Wave w takes the 64-column blocks w, w+4, ... of the chunk;
-// every lane requests all of its partial values before the first sum, then
-// argmax keeps a running maximum key per lane and top-16 a running sorted
-// list per 16-lane group, merged across the wave's four groups at the end.
-template <bool TOPK>
-__global__ __launch_bounds__(256) void k_logit_select(LogitSelParams p) {
-  constexpr int NB = kSelChunk / 256;  // column blocks per wave
-  __shared__ unsigned long long red[4];
-  const int chunk = blockIdx.x, row = blockIdx.y;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, i16 = lane & 15;
+// A wave's top-16 list that the candidate pass left to the exact pass.  No
+// key has all bits set: its low word, vocab - 1 - id, is below 2^31.
+constexpr unsigned long long kListRedo = ~0ull;
+
+// Packs the keys >= thr into the wave's 64 LDS slots by ballot rank (key
+// index, then lane); returns how many passed (all counted, the first 64
+// stored).  The slots are the wave's own: a wave-level fence orders the
+// lanes' LDS writes before the reads.
+template <int NK>
+__device__ __forceinline__ int pack_candidates(const unsigned long long (&key)[NK], unsigned long long thr,
+                                               unsigned long long* cand) {
+  int cnt = 0;  // wave-uniform
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const bool f = key[k] >= thr;
+    const unsigned long long m = __ballot(f);
+    const int slot = cnt + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+    if (f && slot < 64) cand[slot] = key[k];
+    cnt += (int)__popcll(m);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  return cnt;
+}
+
+// The 16 largest of the wave's 64 * NK keys (key[k] of every lane), sorted
+// descending in lanes 0..15, or kListRedo.  Let tau be the 16th largest of
+// the 64 per-lane maxima: those 16 maxima are keys >= tau, so the 16th
+// largest key is >= tau and only keys >= tau can rank.  With tau = 0 (fewer
+// than 16 lanes hold a nonzero key: the end of the vocabulary) the
+// candidates are the nonzero keys and the zero padding fills the list.
+// About 20 keys pass for logits without ties; at most 64 are sorted in one
+// pass, and a wave with more (which takes many large logits packed into
+// fewer than 16 lanes) returns kListRedo, as every wave does with `redo`.
+template <int NK>
+__device__ __forceinline__ unsigned long long wave_top16(const unsigned long long (&key)[NK],
+                                                         unsigned long long* cand, int lane, bool redo) {
+  unsigned long long lm = key[0];
+#pragma unroll
+  for (int k = 1; k < NK; ++k) lm = key_max(lm, key[k]);
+  const unsigned long long tau = __shfl(sort64_desc(lm, lane), 15, 64);
+  const int cnt = pack_candidates(key, tau ? tau : 1ull, cand);
+  const unsigned long long s = sort64_desc(lane < cnt ? cand[lane] : 0ull, lane);
+  return cnt <= 64 && !redo ? s : kListRedo;
+}
+
+// The same list for any keys: the 16th largest key t by bisection over the
+// key range (at least 16 keys >= lo, fewer than 16 >= hi), then the keys
+// >= max(t, 1) sorted: the valid keys are distinct, so at most 16 pass, and
+// with t = 0 (fewer than 16 nonzero keys) the list is padded with zero keys
+// as the padding itself would be.
+template <int NK>
+__device__ __forceinline__ unsigned long long wave_top16_exact(const unsigned long long (&key)[NK],
+                                                               unsigned long long* cand, int lane) {
+  static_assert(64 * NK >= 16, "at least 16 keys");
+  unsigned long long lo = 0ull, hi = ~0ull;
+#pragma unroll 1
+  while (hi - lo > 1) {
+    const unsigned long long mid = lo + ((hi - lo) >> 1);
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) c += (int)__popcll(__ballot(key[k] >= mid));
+    if (c >= 16)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int cnt = pack_candidates(key, lo ? lo : 1ull, cand);
+  return sort64_desc(lane < cnt ? cand[lane] : 0ull, lane);
+}
+
+// Sum of the split-K partial planes (in split order, so the result does not
+// depend on scheduling) at the 16 columns lane `lane` of wave `wave` covers
+// in one chunk of the vocabulary, as packed keys (zero past the vocabulary);
+// every load is requested before the first sum.  Two layouts:
+//  VEC4 (vocabulary a multiple of 4, every row 16-byte aligned): the wave
+//    takes the 256-column blocks wave, wave + 4, ... of the chunk, each lane
+//    4 consecutive columns of a block (column c0 + 1024 b + k, key 4 b + k);
+//  scalar: the 64-column blocks wave, wave + 4, ... (column c0 + 256 b).
+// The selected keys do not depend on the order in which columns are visited.
+template <bool VEC4>
+__device__ __forceinline__ void wave_keys(const LogitSelParams& p, int row, int chunk, int wave, int lane,
+                                          unsigned long long (&key)[16], bool dbg) {
   const long long plane = (long long)p.M * p.N;
   const float* src = p.part + (long long)row * p.N;
-  const int c0 = chunk * kSelChunk + wave * 64 + lane;
-  float v[NB];
+  if constexpr (VEC4) {
+    constexpr int NB = kSelChunk / 1024;
+    static_assert(4 * NB == 16, "16 keys per lane");
+    const int c0 = chunk * kSelChunk + wave * 256 + lane * 4;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 v[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) v[b] = 0.f;
-  for (int q = 0; q < p.n_part; ++q) {
-    float x[NB];
+    for (int b = 0; b < NB; ++b) v[b] = zero;
+    for (int q0 = 0; q0 < p.n_part; q0 += 4) {
+      f32x4 x[4][NB];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int n = c0 + 1024 * b;
+          x[q][b] = q0 + q < p.n_part && n < p.N ? *reinterpret_cast<const f32x4*>(src + (q0 + q) * plane + n) : zero;
+        }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (q0 + q < p.n_part) v[b] += x[q][b];
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int n = c0 + 1024 * b + k;
+        const bool ok = n < p.N;
+        if (dbg && ok && p.dbg) p.dbg[(long long)row * p.ld_dbg + n] = v[b][k];
+        key[4 * b + k] = ok ? argmax_key(v[b][k], n, p.N) : 0ull;
+      }
+  } else {
+    constexpr int NB = kSelChunk / 256;
+    static_assert(NB == 16, "16 keys per lane");
+    const int c0 = chunk * kSelChunk + wave * 64 + lane;
+    float v[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) v[b] = 0.f;
+    for (int q = 0; q < p.n_part; ++q) {
+      float x[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int n = c0 + 256 * b;
+        x[b] = n < p.N ? src[q * plane + n] : 0.f;
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) v[b] += x[b];
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int n = c0 + 256 * b;
-      x[b] = n < p.N ? src[q * plane + n] : 0.f;
+      const bool ok = n < p.N;
+      if (dbg && ok && p.dbg) p.dbg[(long long)row * p.ld_dbg + n] = v[b];
+      key[b] = ok ? argmax_key(v[b], n, p.N) : 0ull;
     }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) v[b] += x[b];
   }
-  unsigned long long best = 0ull;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int n = c0 + 256 * b;
-    const bool ok = n < p.N;
-    if (ok && p.dbg) p.dbg[(long long)row * p.ld_dbg + n] = v[b];
-    const unsigned long long key = ok ? argmax_key(v[b], n, p.N) : 0ull;
-    if (TOPK)
-      best = merge16_desc(best, sort16_desc(key, i16), i16);
-    else
-      best = key_max(best, key);
-  }
-  if (TOPK) {
-    best = merge16_desc(best, __shfl_xor(best, 16, 64), i16);
-    best = merge16_desc(best, __shfl_xor(best, 32, 64), i16);
+}
+
+// One workgroup of 4 waves per (chunk, row): argmax reduces the keys to the
+// row's maximum (atomic max into keys[row]); top-16 writes each wave's 16
+// largest keys as one sorted list, or kListRedo for k_topk_redo.
+template <bool VEC4, bool TOPK>
+__global__ __launch_bounds__(256) void k_logit_select(LogitSelParams p) {
+  __shared__ unsigned long long red[4];
+  __shared__ unsigned long long cand[TOPK ? 4 : 1][64];
+  const int chunk = blockIdx.x, row = blockIdx.y;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  unsigned long long key[16];
+  wave_keys<VEC4>(p, row, chunk, wave, lane, key, true);
+  if constexpr (TOPK) {
+    const unsigned long long best = wave_top16(key, cand[wave], lane, p.exact != 0);
     if (lane < 16) p.lists[((long long)row * p.n_lists + chunk * 4 + wave) * 16 + lane] = best;
   } else {
+    unsigned long long best = key[0];
+#pragma unroll
+    for (int b = 1; b < 16; ++b) best = key_max(best, key[b]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) best = key_max(best, __shfl_xor(best, o, 64));
     if (lane == 0) red[wave] = best;
@@ -103,64 +231,28 @@ __global__ __launch_bounds__(256) void k_logit_select(LogitSelParams p) {
   }
 }
 
-// The same selection with 16-byte reads, for a vocabulary that is a multiple
-// of 4 (every row then starts 16-byte aligned): wave w takes the 256-column
-// blocks w, w+4, ... of the chunk, each lane 4 consecutive columns of a
-// block, and the loads of up to 4 planes are all issued before any sum.  The
-// selected keys do not depend on the order in which columns are visited.
-template <bool TOPK>
-__global__ __launch_bounds__(256) void k_logit_select4(LogitSelParams p) {
-  constexpr int NB = kSelChunk / 1024;  // 256-column blocks per wave
-  __shared__ unsigned long long red[4];
-  const int chunk = blockIdx.x, row = blockIdx.y;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, i16 = lane & 15;
-  const long long plane = (long long)p.M * p.N;
-  const float* src = p.part + (long long)row * p.N;
-  const int c0 = chunk * kSelChunk + wave * 256 + lane * 4;
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  f32x4 v[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) v[b] = zero;
-  for (int q0 = 0; q0 < p.n_part; q0 += 4) {
-    f32x4 x[4][NB];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int n = c0 + 1024 * b;
-        x[q][b] = q0 + q < p.n_part && n < p.N ? *reinterpret_cast<const f32x4*>(src + (q0 + q) * plane + n) : zero;
-      }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        if (q0 + q < p.n_part) v[b] += x[q][b];
-  }
-  unsigned long long best = 0ull;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int n = c0 + 1024 * b + k;
-      const bool ok = n < p.N;
-      if (ok && p.dbg) p.dbg[(long long)row * p.ld_dbg + n] = v[b][k];
-      const unsigned long long key = ok ? argmax_key(v[b][k], n, p.N) : 0ull;
-      if (TOPK)
-        best = merge16_desc(best, sort16_desc(key, i16), i16);
-      else
-        best = key_max(best, key);
+// One workgroup per row: wave w looks at the row's lists w, w + 4, ... 64 at
+// a time (one load per lane) and recomputes each list marked kListRedo from
+// the partial planes with the exact pass.
+template <bool VEC4>
+__global__ __launch_bounds__(256) void k_topk_redo(LogitSelParams p) {
+  __shared__ unsigned long long cand[4][64];
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  unsigned long long* lists = p.lists + (long long)row * p.n_lists * 16;
+  for (int base = 0; base < p.n_lists; base += 256) {
+    const int li = base + 4 * lane + wave;
+    const bool redo = li < p.n_lists && lists[(long long)li * 16] == kListRedo;
+    unsigned long long m = __ballot(redo);
+    while (m) {
+      const int l = (int)__builtin_ctzll(m);
+      m &= m - 1;
+      const int lj = base + 4 * l + wave;  // chunk lj / 4, wave lj % 4 == wave
+      unsigned long long key[16];
+      wave_keys<VEC4>(p, row, lj >> 2, wave, lane, key, false);
+      const unsigned long long best = wave_top16_exact(key, cand[wave], lane);
+      if (lane < 16) lists[(long long)lj * 16 + lane] = best;
     }
-  }
-  if (TOPK) {
-    best = merge16_desc(best, __shfl_xor(best, 16, 64), i16);
-    best = merge16_desc(best, __shfl_xor(best, 32, 64), i16);
-    if (lane < 16) p.lists[((long long)row * p.n_lists + chunk * 4 + wave) * 16 + lane] = best;
-  } else {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) best = key_max(best, __shfl_xor(best, o, 64));
-    if (lane == 0) red[wave] = best;
-    __syncthreads();
-    if (t == 0) atomicMax(p.keys + row, key_max(key_max(red[0], red[1]), key_max(red[2], red[3])));
   }
 }
 
@@ -222,18 +314,26 @@ __global__ __launch_bounds__(256) void k_topk_merge(TopkParams p) {
 
 }  // namespace
 
-void launch_logit_select(bool topk, const LogitSelParams& p, hipStream_t s) {
-  if (p.M <= 0) return;
+void launch_logit_select(bool topk, const LogitSelParams& lp, hipStream_t s) {
+  if (lp.M <= 0) return;
+  LogitSelParams p = lp;
+  // every top-16 list through the exact pass when DFLASH_SELECT_EXACT is set
+  // (the same lists, slower: a check of the candidate pass)
+  const char* ex = getenv("DFLASH_SELECT_EXACT");
+  p.exact = ex && ex[0] && ex[0] != '0';
   const dim3 grid((p.N + kSelChunk - 1) / kSelChunk, p.M);
   if (p.N % 4 == 0) {
-    if (topk)
-      hipLaunchKernelGGL(k_logit_select4<true>, grid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL(k_logit_select4<false>, grid, dim3(256), 0, s, p);
+    if (topk) {
+      hipLaunchKernelGGL((k_logit_select<true, true>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL(k_topk_redo<true>, dim3(p.M), dim3(256), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((k_logit_select<true, false>), grid, dim3(256), 0, s, p);
+    }
   } else if (topk) {
-    hipLaunchKernelGGL(k_logit_select<true>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_logit_select<false, true>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(k_topk_redo<false>, dim3(p.M), dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL(k_logit_select<false>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_logit_select<false, false>), grid, dim3(256), 0, s, p);
   }
 }
 

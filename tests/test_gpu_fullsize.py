@@ -18,6 +18,8 @@ two.  The draft forward is compared teacher-forced (the oracle's K/V cache
 written into the GPU's pages first); the injection is compared on every
 position of every layer.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -155,6 +157,16 @@ def test_full_size_dflash2_long_context(name):
     lt = torch.tensor(last, dtype=torch.int32, device=dev)
     dr.draft(list(range(n)), lt, debug_logits=lg, debug_hidden=hs, topk_ids=tk_ids, topk_logits=tk_val)
     torch.cuda.synchronize()
+    # every top-16 list through the exact (bisection) pass instead of the
+    # threshold pass: the same lists, bit for bit
+    tk3, tv3 = torch.empty_like(tk_ids), torch.empty_like(tk_val)
+    os.environ["DFLASH_SELECT_EXACT"] = "1"
+    try:
+        dr.draft(list(range(n)), lt, topk_ids=tk3, topk_logits=tv3)
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["DFLASH_SELECT_EXACT"]
+    assert torch.equal(tk3, tk_ids) and torch.equal(tv3, tk_val), "top-16 differs with the exact pass"
     hs = hs.cpu().numpy().reshape(L + 1, n, B, d)
     ref = {}
     ftol = FREE_ELEM_TOL_DYN if shape.get("conv_rank") else FREE_ELEM_TOL

@@ -14,6 +14,8 @@ weights (an average of a few hundred values that nearly cancel) amplifies
 those flips to ~1e-3 relative in the layer outputs.  The free-running path
 (no forcing) is checked separately on row error and on the drafted tokens.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -165,6 +167,19 @@ def _draft_both(dev, shape, dr, o, states, slots, last_tokens=None, free=False):
     torch.cuda.synchronize()
     assert np.array_equal(d2.cpu().numpy(), g_draft), "drafts differ without the hidden-state copy"
     assert np.array_equal(lg2.cpu().numpy(), g_logits), "logits differ without the hidden-state copy"
+    if tk_ids is not None:
+        # every top-16 list through the exact (bisection) pass instead of the
+        # threshold pass: the same lists, bit for bit
+        tk3 = (torch.empty_like(tk_ids), torch.empty_like(tk_val))
+        os.environ["DFLASH_SELECT_EXACT"] = "1"
+        try:
+            d3 = dr.draft(slots, lt, topk_ids=tk3[0], topk_logits=tk3[1])
+            torch.cuda.synchronize()
+        finally:
+            del os.environ["DFLASH_SELECT_EXACT"]
+        assert np.array_equal(d3.cpu().numpy(), g_draft), "drafts differ with the exact top-16 pass"
+        assert np.array_equal(tk3[0].cpu().numpy(), tk_ids.cpu().numpy()), "top-16 ids differ with the exact pass"
+        assert np.array_equal(tk3[1].cpu().numpy(), tk_val.cpu().numpy()), "top-16 logits differ with the exact pass"
     ref_drafts = []
     exempt = 0
     for i, r in enumerate(slots):
@@ -223,6 +238,10 @@ def test_draft_parity_lockstep(name):
     # partial logits reads 16 bytes per lane (argmax, then top-16)
     ("small_batch", {"batch": 4, "vocab": 3000}),
     ("small_conv", {"batch": 3, "ctx": None, "ctx_range": (60, 300), "vocab": 3000}),
+    # top-16 over a last vocabulary chunk of 40 columns: its waves have fewer
+    # than 16 valid lanes, so the lanes' threshold is zero and the nonzero
+    # keys are the candidates
+    ("small_conv", {"batch": 3, "ctx": None, "ctx_range": (60, 300), "vocab": 4136}),
     # 80 rows with top-16: the tiled LM head's top-16 epilogue and the merge
     # of its per-workgroup lists
     ("small_conv", {"batch": 5, "ctx": None, "ctx_range": (60, 300)}),
@@ -239,7 +258,7 @@ def test_draft_parity_lockstep(name):
     # fragment order)
     ("small_dconv", {"batch": 1}),
     ("small_dconv", {"batch": 5, "ctx": None, "ctx_range": (60, 300)}),
-], ids=["block1", "batch5_block1", "rows64", "conv_rows48", "block10_rows70", "rows64_vocab4", "conv_rows48_vocab4",
+], ids=["block1", "batch5_block1", "rows64", "conv_rows48", "block10_rows70", "rows64_vocab4", "conv_rows48_vocab4", "conv_rows48_topk_tail_chunk",
         "conv_rows80_topk_tiled", "batch32_merge_splits", "q4_rows16", "q4_rows80", "q4_conv_topk_window",
         "dconv_rows16", "dconv_rows80"])
 def test_draft_parity_lockstep_shapes(name, over):
