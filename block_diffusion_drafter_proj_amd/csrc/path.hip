@@ -11,10 +11,11 @@
 //  * k_select_path (per draft): one workgroup of 16 waves per request.  Wave
 //    i forms the 16 x 16 score matrix of positions (i, i+1) on the matrix
 //    cores (16x16x4 fp32 MFMA over r; A = the u rows of position i's
-//    candidates, B = the v rows of position i+1's), into LDS; wave 0 then
-//    walks the positions: step i+1 takes the candidate maximising its logit
-//    plus the score from the candidate chosen at step i (packed keys, ties to
-//    the lower candidate index).
+//    candidates, B = the v rows of position i+1's) and, for each candidate a
+//    of position i, the candidate b of position i+1 maximising logit(b) +
+//    s(a, b) (packed keys, ties to the lower candidate index), into LDS; one
+//    lane then walks the positions through that table: step i+1 takes the
+//    successor of the candidate chosen at step i.
 #include "common.h"
 #include "kernels.h"
 
@@ -65,7 +66,8 @@ __global__ __launch_bounds__(256) void k_sel_table(const T* E, const T* Wu, cons
 }
 
 __global__ __launch_bounds__(1024) void k_select_path(PathParams p) {
-  __shared__ float S[15][16][17];
+  __shared__ int nxt[15][16];    // best successor of each candidate
+  __shared__ float nsc[15][16];  // and its score
   __shared__ int cid[16][16];
   __shared__ float clg[16][16];
   const int req = blockIdx.x;
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(1024) void k_select_path(PathParams p) {
       t = 0;
     }
     cid[threadIdx.x >> 4][threadIdx.x & 15] = t;
-    clg[threadIdx.x >> 4][threadIdx.x & 15] = lg[threadIdx.x];  // the walk reads logits from LDS
+    clg[threadIdx.x >> 4][threadIdx.x & 15] = lg[threadIdx.x];
   }
   __syncthreads();
   if (wave < B - 1) {
@@ -105,35 +107,37 @@ __global__ __launch_bounds__(1024) void k_select_path(PathParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc = mfma_step(a[j], b[j], acc);
     }
-    // C layout: lane l holds column l % 16 (candidate b of position i+1) and
-    // rows 4 * (l / 16) + q (candidate a of position i)
+    // C layout: lane l holds column b = l % 16 (candidate of position i+1)
+    // and rows a = 4 * (l / 16) + q (candidates of position i); the 16
+    // columns of a row sit in 16 adjacent lanes.  Larger logit(b) + s(a, b)
+    // wins, ties to the lower b.
+    const float lb = clg[wave + 1][row];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) S[wave][4 * g + q][row] = acc[q];
+    for (int q = 0; q < 4; ++q) {
+      unsigned long long key = ((unsigned long long)float_key(lb + acc[q]) << 32) | (unsigned)(15 - row);
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) {
+        const unsigned long long other = __shfl_xor(key, o, 64);
+        key = other > key ? other : key;
+      }
+      if (row == 0) {
+        nxt[wave][4 * g + q] = 15 - (int)(key & 0xffffffffu);
+        nsc[wave][4 * g + q] = key_float((uint32_t)(key >> 32));
+      }
+    }
   }
   __syncthreads();
-  if (wave != 0) return;
+  if (threadIdx.x != 0) return;
   int* path = p.path + (long long)req * B;
   float* score = p.step_scores ? p.step_scores + (long long)req * B : nullptr;
-  if (lane == 0) {
-    path[0] = cid[0][0];
-    if (score) score[0] = clg[0][0];
-  }
+  path[0] = cid[0][0];
+  if (score) score[0] = clg[0][0];
   int k = 0;
   for (int i = 0; i + 1 < B; ++i) {
-    const float sc = lane < 16 ? clg[i + 1][lane] + S[i][k][lane] : 0.f;
-    // larger score wins, ties to the lower candidate index; lanes 16.. never win
-    unsigned long long key = lane < 16 ? ((unsigned long long)float_key(sc) << 32) | (unsigned)(15 - lane) : 0ull;
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) {
-      const unsigned long long other = __shfl_xor(key, o, 64);
-      key = other > key ? other : key;
-    }
-    key = __shfl(key, 0, 64);
-    k = 15 - (int)(key & 0xffffffffu);
-    if (lane == 0) {
-      path[i + 1] = cid[i + 1][k];
-      if (score) score[i + 1] = key_float((uint32_t)(key >> 32));
-    }
+    const int kn = nxt[i][k];
+    path[i + 1] = cid[i + 1][kn];
+    if (score) score[i + 1] = nsc[i][k];
+    k = kn;
   }
 }
 

@@ -256,59 +256,63 @@ __global__ __launch_bounds__(256) void k_topk_redo(LogitSelParams p) {
   }
 }
 
-// Merge two lists sorted descending into the 16 largest, sorted descending.
-__device__ __forceinline__ void merge_lists(const unsigned long long* a, const unsigned long long* b,
-                                            unsigned long long* out) {
-  int ia = 0, ib = 0;
+// a := the 16 largest of lists a and b (both sorted descending), sorted
+// descending: the elementwise maximum of a and reversed b holds the 16
+// largest of the 32 as a bitonic sequence, which four half-cleaner stages
+// sort.
+__device__ __forceinline__ void top16_merge(unsigned long long (&a)[16], const unsigned long long (&b)[16]) {
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const unsigned long long va = a[ia], vb = b[ib];  // ia + ib = k <= 15
-    if (va >= vb) {
-      out[k] = va;
-      ++ia;
-    } else {
-      out[k] = vb;
-      ++ib;
-    }
-  }
+  for (int i = 0; i < 16; ++i) a[i] = key_max(a[i], b[15 - i]);
+#pragma unroll
+  for (int j = 8; j >= 1; j >>= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((i & j) == 0) {
+        const unsigned long long hi = key_max(a[i], a[i + j]), lo = key_min(a[i], a[i + j]);
+        a[i] = hi;
+        a[i + j] = lo;
+      }
 }
 
-// One workgroup per row: every thread first folds lists t, t+256, ... into a
-// running top-16, then the 256 running lists are merged pairwise in LDS until
-// one list remains; rank 0 is the greedy draft token.
-__global__ __launch_bounds__(256) void k_topk_merge(TopkParams p) {
-  __shared__ unsigned long long lst[256 * 16];
+// One wave per row: lane l folds the row's lists l, l + 64, ... into a
+// running top 16 in registers (up to four lists requested at once), then the
+// lanes' lists are merged across lanes in six rounds (lane l takes lane
+// l + o's, o = 32 .. 1); lane 0 ends with the row's top 16, whose rank 0 is
+// the greedy draft token.
+__global__ __launch_bounds__(64) void k_topk_merge(TopkParams p) {
   const int row = blockIdx.x;
-  const int t = threadIdx.x;
+  const int lane = threadIdx.x;
   const unsigned long long* src = p.lists + (long long)row * p.n_lists * 16;
-  unsigned long long run[16], nxt[16], tmp[16];
+  unsigned long long run[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) run[k] = 0ull;
-  for (int li = t; li < p.n_lists; li += 256) {
+  for (int l0 = lane; l0 < p.n_lists; l0 += 256) {
+    unsigned long long nxt[4][16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) nxt[k] = src[(long long)li * 16 + k];
-    merge_lists(run, nxt, tmp);
+    for (int q = 0; q < 4; ++q) {
+      const int li = l0 + 64 * q;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) run[k] = tmp[k];
-  }
-#pragma unroll
-  for (int k = 0; k < 16; ++k) lst[t * 16 + k] = run[k];
-  __syncthreads();
-  for (int half = 128; half >= 1; half >>= 1) {
-    if (t < half) merge_lists(lst + t * 16, lst + (t + half) * 16, tmp);
-    __syncthreads();
-    if (t < half) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) lst[t * 16 + k] = tmp[k];
+      for (int k = 0; k < 16; ++k) nxt[q][k] = li < p.n_lists ? src[(long long)li * 16 + k] : 0ull;
     }
-    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) top16_merge(run, nxt[q]);
   }
-  if (t < 16) {
-    const unsigned long long key = lst[t];
-    const int id = p.vocab - 1 - (int)(uint32_t)(key & 0xffffffffull);
-    p.topk_ids[(long long)row * 16 + t] = id;
-    p.topk_logits[(long long)row * 16 + t] = key_float((uint32_t)(key >> 32));
-    if (t == 0) p.draft[row] = id;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    unsigned long long nxt[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) nxt[k] = __shfl_down(run[k], o, 64);
+    top16_merge(run, nxt);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const unsigned long long key = run[k];
+      const int id = p.vocab - 1 - (int)(uint32_t)(key & 0xffffffffull);
+      p.topk_ids[(long long)row * 16 + k] = id;
+      p.topk_logits[(long long)row * 16 + k] = key_float((uint32_t)(key >> 32));
+      if (k == 0) p.draft[row] = id;
+    }
   }
 }
 
@@ -339,7 +343,7 @@ void launch_logit_select(bool topk, const LogitSelParams& lp, hipStream_t s) {
 
 void launch_topk_merge(const TopkParams& p, hipStream_t s) {
   if (p.M <= 0) return;
-  hipLaunchKernelGGL(k_topk_merge, dim3(p.M), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_topk_merge, dim3(p.M), dim3(64), 0, s, p);
 }
 
 void launch_finalize(const unsigned long long* keys, int rows, int vocab, int* draft,
