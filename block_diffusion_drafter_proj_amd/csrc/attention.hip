@@ -643,9 +643,24 @@ __global__ __launch_bounds__(64 * G) void k_attn_ring(AttnParams p, SlotArgs sl)
     p.part_ml[pb * 2 + 0] = l_run > 0.f ? m_run * 0.693147180559945309f : NEG;
     p.part_ml[pb * 2 + 1] = l_run;
   }
-  float* po = p.part_o + pb * DH + 4 * g4;
+  // The wave's 16 rows of O are contiguous in part_o: staged through the
+  // (now idle) ring, rows padded by 4 floats against bank conflicts where
+  // that fits, so that each store writes 1 KB of whole lines instead of 64
+  // bytes of each of 16 rows.
+  constexpr int LDO = G * 16 * (DH + 4) * 4 <= kRing * STAGE * 2 ? DH + 4 : DH;
+  __syncthreads();  // every wave is done with the ring
+  float* stg = reinterpret_cast<float*>(ring) + wave * 16 * LDO;
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
+  for (int dt = 0; dt < ND; ++dt) *reinterpret_cast<f32x4*>(stg + l16 * LDO + dt * 16 + 4 * g4) = o[dt];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float* po = p.part_o + (pb - l16) * DH;
+#pragma unroll
+  for (int k = 0; k < 16 * DH / 256; ++k) {
+    const int e = k * 256 + lane * 4;  // element of the wave's block, row e / DH
+    *reinterpret_cast<f32x4*>(po + e) = *reinterpret_cast<const f32x4*>(stg + (e / DH) * LDO + e % DH);
+  }
 }
 
 // One wave per (request, query head, block row): the split partials of the
