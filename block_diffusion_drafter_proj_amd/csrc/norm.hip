@@ -141,8 +141,19 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(NormParams p) {
       ow0[i] = to_f(o0[i]);
       ow1[i] = to_f(o0[p.d + i]);
     }
-    x = load_row4_oconv<T>(p, row, k, plane, ow0, ow1);
-    if (p.conv && !first) xp = load_row4_oconv<T>(p, row - 1, k, plane, ow0, ow1);
+    // y[row - 1] serves both rows: the GEMM output sums y[row], y[row - 1]
+    // (and y[row - 2] for the previous row) are each formed once
+    const f32x4 h0 = *reinterpret_cast<const f32x4*>(p.x_in + (long long)row * p.ldx + k);
+    const f32x4 y0 = part_sum4(p, row, k, plane);
+    const f32x4 y1 = (row % p.B) == 0 ? last_embed4<T>(p, row, k) : part_sum4(p, row - 1, k, plane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = h0[i] + ow0[i] * y0[i] + ow1[i] * y1[i];
+    if (p.conv && !first) {  // row - 1 is in the block: y1 is its own y
+      const f32x4 h1 = *reinterpret_cast<const f32x4*>(p.x_in + (long long)(row - 1) * p.ldx + k);
+      const f32x4 y2 = ((row - 1) % p.B) == 0 ? last_embed4<T>(p, row - 1, k) : part_sum4(p, row - 2, k, plane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xp[i] = h1[i] + ow0[i] * y1[i] + ow1[i] * y2[i];
+    }
   } else {
     x = load_row4<T>(p, row, k, plane);
     if (p.conv && !first) xp = load_row4<T>(p, row - 1, k, plane);
